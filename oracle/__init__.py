@@ -1,0 +1,121 @@
+"""fp64 CPU oracle for the selective scan (S6) -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never imports, links or
+calls it, and this package imports nothing from the HIP library.
+
+The arithmetic lives in ``msscan_oracle.c`` (plain C, double precision, OpenMP
+over independent channels).  This module only converts numpy/torch arrays to
+contiguous float64 and calls it through ctypes.  See the C file's header for
+the passages of the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msscan_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_scan.argtypes = [dp] * 9 + [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                               dp, dp, ctypes.c_int]
+        lib.oracle_step.restype = ctypes.c_int
+        lib.oracle_step.argtypes = [dp] * 9 + [ctypes.c_int, ctypes.c_int, i64, i64, i64, dp]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: exact widening on the host
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
+         softplus: bool = True, zoh: bool = False, nthreads: int = 0
+         ) -> Tuple[np.ndarray, np.ndarray]:
+    """Selective scan in fp64.
+
+    u, delta, z: [batch, L, Dn]; B, C: [batch, L, N]; A: [Dn, N];
+    D, delta_bias: [Dn]; h0: [batch, Dn, N].  Returns (y [batch, L, Dn],
+    h_last [batch, Dn, N]) as float64 arrays.
+    """
+    lib = _load()
+    u, delta, A, B, C = (_f64(t) for t in (u, delta, A, B, C))
+    D, z, delta_bias, h0 = (_f64(t) for t in (D, z, delta_bias, h0))
+    batch, L, Dn = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and A.shape == (Dn, N)
+    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    assert z is None or z.shape == u.shape
+    assert D is None or D.shape == (Dn,)
+    assert delta_bias is None or delta_bias.shape == (Dn,)
+    assert h0 is None or h0.shape == (batch, Dn, N)
+    y = np.empty((batch, L, Dn), dtype=np.float64)
+    h_last = np.empty((batch, Dn, N), dtype=np.float64)
+    rc = lib.oracle_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                         _ptr(delta_bias), _ptr(h0), int(bool(softplus)), int(bool(zoh)),
+                         batch, L, Dn, N, _ptr(y), _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan failed with code {rc}")
+    return y, h_last
+
+
+def step(h, x, delta, A, B, C, D=None, z=None, delta_bias=None,
+         softplus: bool = True, zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode step in fp64.  h: [batch, Dn, N] (not modified; the updated
+    state is returned); x, delta, z: [batch, Dn]; B, C: [batch, N].
+    Returns (y [batch, Dn], h_new [batch, Dn, N])."""
+    lib = _load()
+    h = _f64(h).copy()
+    x, delta, A, B, C = (_f64(t) for t in (x, delta, A, B, C))
+    D, z, delta_bias = (_f64(t) for t in (D, z, delta_bias))
+    batch, Dn = x.shape
+    N = A.shape[1]
+    assert h.shape == (batch, Dn, N) and B.shape == (batch, N) and C.shape == (batch, N)
+    y = np.empty((batch, Dn), dtype=np.float64)
+    rc = lib.oracle_step(_ptr(h), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                         _ptr(z), _ptr(delta_bias), int(bool(softplus)), int(bool(zoh)),
+                         batch, Dn, N, _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle_step failed with code {rc}")
+    return y, h

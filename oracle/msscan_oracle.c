@@ -1,0 +1,169 @@
+/*
+ * msscan_oracle.c -- plain, slow, fp64 CPU oracle for the selective scan (S6).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load or call this file's library.  It shares
+ * no code, header, table or helper with the HIP library; the HIP library never
+ * includes, links or calls it.
+ *
+ * Every function below follows the pages' statement of the method:
+ *
+ *   * The recurrence and its readout are the per-timestep loop of the naive
+ *     PyTorch selective scan on the page "从RNN到Mamba：状态空间模型原理与长序列
+ *     建模实战" (lmnt.cn/news/271401), section 3.2: A_bar = exp(dt*A),
+ *     B_bar = dt*B_t (broadcast over channels), h = A_bar*h + B_bar*x_t,
+ *     y_t = sum_n h*C_t, then y += x*D, then y * silu(z).
+ *   * The step size is softplus of a linear map plus bias: page "Mamba架构原理与
+ *     工业级长文本处理实战指南" (jsqmd.com/news/861956), section 2.2, first
+ *     equation; softplus is log(1+e^x) there.
+ *   * The zero-order-hold alternative B_bar = (exp(dt*A) - 1)/A * B is the
+ *     discretisation of page "Mamba模型解析：从状态空间到序列建模实践"
+ *     (intelliparadigm.com), section 3.2, and the integral form of the jsqmd
+ *     page, section 2.3; for a diagonal A the matrix inverse is a division.
+ *   * Inference runs the same recurrence one token at a time with one kept
+ *     state (lmnt page, sections 2.2 and 5.3): oracle_step.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   the state starts at zero unless h0 is given; "Euler" keeps A_bar=exp(dt*A)
+ *   and only replaces B_bar by dt*B; the bias goes inside softplus; D*u is added
+ *   before the gate; silu(z) = z/(1+exp(-z)); B_t and C_t are shared by all
+ *   channels; at A == 0 the ZOH factor takes its limit dt.
+ *
+ * Arithmetic: every input is first converted to double by the caller (bf16 and
+ * fp32 convert exactly); all arithmetic here is double precision libm.
+ * Layouts (row-major, contiguous):
+ *   u, delta_raw, z, y : [batch][L][Dn]
+ *   B, C               : [batch][L][N]
+ *   A                  : [Dn][N]
+ *   D, delta_bias      : [Dn]
+ *   h0, h_last, h      : [batch][Dn][N]
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(x) = log(1 + e^x), written so that neither e^x overflows nor the
+ * 1 + small sum loses digits: max(x,0) + log1p(e^-|x|).  Same value as the
+ * pages' definition, in exact arithmetic. */
+static double sp_softplus(double x) {
+    return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+}
+
+/* silu(v) = v * sigmoid(v). */
+static double sp_silu(double v) {
+    return v / (1.0 + exp(-v));
+}
+
+/* Step size of one element: dt = softplus(delta_raw + bias) when softplus is
+ * on, else delta_raw + bias. */
+static double step_size(double draw, const double* delta_bias, int64_t d, int softplus) {
+    double v = draw + (delta_bias ? delta_bias[d] : 0.0);
+    return softplus ? sp_softplus(v) : v;
+}
+
+/* One timestep of one channel: updates h[0..N) in place, returns the gated
+ * output.  The body is the loop body of the lmnt page section 3.2, with the
+ * ZOH factor of the intelliparadigm page section 3.2 when zoh != 0. */
+static double one_step(double* h, double ut, double dt, const double* Arow,
+                       const double* Bt, const double* Ct, int64_t N,
+                       double Dd, int has_D, double zt, int has_z, int zoh) {
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double a = Arow[n];
+        double abar = exp(dt * a);
+        double bfac;
+        if (zoh)
+            bfac = (a == 0.0) ? dt : expm1(dt * a) / a;
+        else
+            bfac = dt;
+        h[n] = abar * h[n] + bfac * Bt[n] * ut;
+        acc += Ct[n] * h[n];
+    }
+    if (has_D) acc += Dd * ut;
+    if (has_z) acc *= sp_silu(zt);
+    return acc;
+}
+
+/* Full-sequence scan.  Channels (b, d) are independent; OpenMP runs them in
+ * parallel, each channel strictly in time order.  Returns 0 on success,
+ * -1 on bad arguments, -2 on allocation failure. */
+int oracle_scan(const double* u, const double* delta_raw, const double* A,
+                const double* B, const double* C, const double* D,
+                const double* z, const double* delta_bias, const double* h0,
+                int softplus, int zoh, int64_t batch, int64_t L, int64_t Dn,
+                int64_t N, double* y, double* h_last, int nthreads) {
+    if (!u || !delta_raw || !A || !B || !C || !y) return -1;
+    if (batch < 0 || L < 0 || Dn < 0 || N < 1) return -1;
+    int64_t nch = batch * Dn;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+    {
+        double* h = (double*)malloc(sizeof(double) * (size_t)N);
+        if (!h) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+        }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t ch = 0; ch < nch; ++ch) {
+            if (!h) continue;
+            int64_t b = ch / Dn, d = ch % Dn;
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                int64_t e = (b * L + t) * Dn + d;
+                const double* Bt = B + (b * L + t) * N;
+                const double* Ct = C + (b * L + t) * N;
+                double dt = step_size(delta_raw[e], delta_bias, d, softplus);
+                y[e] = one_step(h, u[e], dt, A + d * N, Bt, Ct, N,
+                                D ? D[d] : 0.0, D != NULL, z ? z[e] : 0.0,
+                                z != NULL, zoh);
+            }
+            if (h_last)
+                for (int64_t n = 0; n < N; ++n) h_last[(b * Dn + d) * N + n] = h[n];
+        }
+        free(h);
+    }
+    return failed ? -2 : 0;
+}
+
+/* One decode step with the state kept by the caller (lmnt page, section 5.3:
+ * generation token by token with one fixed-size state).  h is [batch][Dn][N]
+ * and is updated in place; x, delta_raw, z, y are [batch][Dn]; B, C are
+ * [batch][N].  Same body as one timestep of oracle_scan. */
+int oracle_step(double* h, const double* x, const double* delta_raw,
+                const double* A, const double* B, const double* C,
+                const double* D, const double* z, const double* delta_bias,
+                int softplus, int zoh, int64_t batch, int64_t Dn, int64_t N,
+                double* y) {
+    if (!h || !x || !delta_raw || !A || !B || !C || !y) return -1;
+    if (batch < 0 || Dn < 0 || N < 1) return -1;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t d = 0; d < Dn; ++d) {
+            int64_t e = b * Dn + d;
+            double dt = step_size(delta_raw[e], delta_bias, d, softplus);
+            y[e] = one_step(h + e * N, x[e], dt, A + d * N, B + b * N, C + b * N,
+                            N, D ? D[d] : 0.0, D != NULL, z ? z[e] : 0.0,
+                            z != NULL, zoh);
+        }
+    return 0;
+}
+
+/* Number of threads OpenMP would use (for reporting the CPU baseline). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
