@@ -1,0 +1,153 @@
+/*
+ * msscan.h -- C ABI of libmsscan, the selective scan (S6) on AMD MI355X (gfx950).
+ *
+ * What is computed.  For every batch b, channel d (d_inner) and state n
+ * (d_state), along the sequence t = 0..L-1:
+ *
+ *   dt    = softplus(delta[b,t,d] + delta_bias[d])    (MS_SOFTPLUS set)
+ *         =          delta[b,t,d] + delta_bias[d]     (otherwise)
+ *   A_bar = exp(dt * A[d,n])
+ *   B_bar = dt * B[b,t,n]                             (Euler, default)
+ *         = (exp(dt*A[d,n]) - 1) / A[d,n] * B[b,t,n]  (MS_ZOH; dt*B when A == 0)
+ *   h[n]  = A_bar * h[n] + B_bar * u[b,t,d]           (h starts at h0, else 0)
+ *   y     = sum_n C[b,t,n] * h[n]  +  D[d] * u[b,t,d]
+ *   out[b,t,d] = y * z * sigmoid(z),  z = z[b,t,d]    (when z is given; else y)
+ *
+ * Passages followed (page titles as published; section numbers are the pages'):
+ *   - the per-timestep loop of the naive selective scan, with B and C shared by
+ *     all channels and D*u added before the silu(z) gate: "从RNN到Mamba：状态空间
+ *     模型原理与长序列建模实战" (lmnt.cn), section 3.2; the block data flow in
+ *     section 3.1;
+ *   - dt = softplus(W x + b): "Mamba架构原理与工业级长文本处理实战指南"
+ *     (jsqmd.com), section 2.2;
+ *   - zero-order hold A_bar = exp(dt A), B_bar = (A_bar - I) A^-1 B: "Mamba模型
+ *     解析：从状态空间到序列建模实践" (intelliparadigm.com), section 3.2, and the
+ *     integral form on the jsqmd page, section 2.3;
+ *   - the scan as a composition of per-step affine maps, evaluated in parallel:
+ *     jsqmd page section 3.4, lmnt page section 2.2;
+ *   - single-token recurrent inference with one kept fp32 state: lmnt page,
+ *     sections 2.2 and 5.3; the state cache of the jsqmd page, section 5.3.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers (HIP global memory) unless stated.
+ *     The caller owns every buffer; the library never allocates or frees.
+ *   - Layouts are contiguous row-major:
+ *       u, delta, z, y : [batch][L][d_inner]      (io dtype)
+ *       B, C           : [batch][L][d_state]      (io dtype)
+ *       A              : [d_inner][d_state]       (fp32)
+ *       D, delta_bias  : [d_inner]                (fp32)
+ *       h0, h_last, h  : [batch][d_inner][d_state] (fp32)
+ *   - Every base pointer must be 16-byte aligned (MS_ERR_ALIGN otherwise).
+ *   - Validation is synchronous and host-only: on any error status nothing has
+ *     been launched.  Work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the default stream) and outputs are valid once the stream reaches it.
+ *     No call synchronises the host.
+ *   - Data problems (NaN/Inf inputs, A > 0 growth) are computed as written and
+ *     are not reported.  A NaN in one channel's inputs reaches only that
+ *     channel's outputs (and state), from that timestep on.
+ *   - Thread safety: calls may be made from several host threads; the last
+ *     error text is thread-local.  Two calls that share an output buffer or a
+ *     workspace and run concurrently (different streams) race.
+ */
+#ifndef MSSCAN_H
+#define MSSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MS_ABI_VERSION 1
+
+typedef enum {
+    MS_OK = 0,
+    MS_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    MS_ERR_SHAPE = 2,       /* a size is out of range                           */
+    MS_ERR_DTYPE = 3,       /* io is not MS_F32 or MS_BF16                      */
+    MS_ERR_FLAGS = 4,       /* unknown bits in flags                            */
+    MS_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned            */
+    MS_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required       */
+    MS_ERR_UNSUPPORTED = 7, /* valid request this build cannot serve            */
+    MS_ERR_HIP = 8          /* a HIP runtime call failed (text: ms_last_error)  */
+} ms_status;
+
+/* Element type of u, delta, z, B, C and y (x_t, delta_t, z_t, B_t, C_t, y_t). */
+typedef enum { MS_F32 = 0, MS_BF16 = 1 } ms_dtype;
+
+/* Flag bits. */
+#define MS_SOFTPLUS (1u << 0) /* dt = softplus(delta + bias); else dt = delta + bias */
+#define MS_ZOH (1u << 1)      /* zero-order hold B_bar; else Euler B_bar = dt * B     */
+
+typedef struct {
+    int32_t batch;   /* >= 1                                   */
+    int64_t seqlen;  /* L >= 1, any value (no power-of-two rule), <= 2^31 - 1 */
+    int32_t d_inner; /* >= 1, any value (tails are masked)     */
+    int32_t d_state; /* 1 .. 128                               */
+    int32_t io;      /* ms_dtype                               */
+} ms_dims;
+
+/*
+ * Bytes of device workspace ms_scan_fwd needs for these dims and flags
+ * (0 when the sequence is scanned in one piece).  Returns (size_t)-1 when the
+ * dims are invalid.  Pure function of its arguments; no device call.
+ */
+size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags);
+
+/*
+ * Full-sequence selective scan (the formula at the top of this file).
+ *
+ *   u, delta, A, B, C, y, dims : required.
+ *   D, z, delta_bias           : optional (NULL = term absent; a NULL bias is
+ *                                identical to a zero bias).
+ *   h0                         : optional initial state (NULL = zeros).
+ *   h_last                     : optional; receives the state after step L-1.
+ *                                h_last may equal h0 (h0 is read first).
+ *   workspace, workspace_bytes : device scratch of at least
+ *                                ms_scan_workspace_bytes(dims, flags) bytes,
+ *                                16-byte aligned; may be NULL when that is 0.
+ *                                Its contents need no initialisation and are
+ *                                undefined afterwards.
+ *   stream                     : hipStream_t (NULL = default stream).
+ *
+ * y must not overlap any input.  Results are deterministic: the same inputs on
+ * the same device give bit-identical outputs.
+ */
+ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z,
+                      const float* delta_bias, uint32_t flags, void* y,
+                      const float* h0, float* h_last, const ms_dims* dims,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for a batch of sequences (one timestep of
+ * ms_scan_fwd with the state kept by the caller between calls).
+ *
+ *   h          : in/out state [batch][d_inner][d_state] fp32, updated in place.
+ *   x_t, delta_t, z_t, y_t : [batch][d_inner] io dtype (z_t optional).
+ *   B_t, C_t   : [batch][d_state] io dtype.
+ *   A, D, delta_bias, flags : as for ms_scan_fwd (D, delta_bias optional).
+ *
+ * y_t must not overlap any input or h.
+ */
+ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const float* A,
+                          const void* B_t, const void* C_t, const float* D,
+                          const void* z_t, const float* delta_bias, uint32_t flags,
+                          void* y_t, int32_t batch, int32_t d_inner, int32_t d_state,
+                          int32_t io, void* stream);
+
+/* Static text for a status code. */
+const char* ms_status_string(ms_status s);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* ms_last_error(void);
+
+/* MS_ABI_VERSION of the loaded library. */
+int ms_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSCAN_H */

@@ -148,14 +148,17 @@ int oracle_step(double* h, const double* x, const double* delta_raw,
                 double* y) {
     if (!h || !x || !delta_raw || !A || !B || !C || !y) return -1;
     if (batch < 0 || Dn < 0 || N < 1) return -1;
-    for (int64_t b = 0; b < batch; ++b)
-        for (int64_t d = 0; d < Dn; ++d) {
-            int64_t e = b * Dn + d;
-            double dt = step_size(delta_raw[e], delta_bias, d, softplus);
-            y[e] = one_step(h + e * N, x[e], dt, A + d * N, B + b * N, C + b * N,
-                            N, D ? D[d] : 0.0, D != NULL, z ? z[e] : 0.0,
-                            z != NULL, zoh);
-        }
+    int64_t nch = batch * Dn;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t e = 0; e < nch; ++e) {
+        int64_t b = e / Dn, d = e % Dn;
+        double dt = step_size(delta_raw[e], delta_bias, d, softplus);
+        y[e] = one_step(h + e * N, x[e], dt, A + d * N, B + b * N, C + b * N,
+                        N, D ? D[d] : 0.0, D != NULL, z ? z[e] : 0.0,
+                        z != NULL, zoh);
+    }
     return 0;
 }
 

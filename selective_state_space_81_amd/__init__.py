@@ -1,0 +1,162 @@
+"""Python binding of libmsscan (selective scan, S6, on MI355X / gfx950).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libmsscan.so`` behind the C ABI declared in ``include/msscan.h``.  Torch is
+used for device memory and streams: tensors are passed as raw device pointers
+together with the current HIP stream.  There is no CPU fallback -- if the
+library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsscan.so")
+
+MS_OK = 0
+MS_F32 = 0
+MS_BF16 = 1
+MS_SOFTPLUS = 1
+MS_ZOH = 2
+
+STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
+          4: "MS_ERR_FLAGS", 5: "MS_ERR_ALIGN", 6: "MS_ERR_WORKSPACE",
+          7: "MS_ERR_UNSUPPORTED", 8: "MS_ERR_HIP"}
+
+EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
+           "ms_last_error", "ms_abi_version")
+
+
+class MsDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int64),
+                ("d_inner", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("io", ctypes.c_int32)]
+
+
+class MsError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libmsscan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with "
+                           "`python -m selective_state_space_81_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int32
+    lib.ms_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.ms_scan_workspace_bytes.argtypes = [ctypes.POINTER(MsDims), u32]
+    lib.ms_scan_fwd.restype = ctypes.c_int
+    lib.ms_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
+                                ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
+    lib.ms_state_update.restype = ctypes.c_int
+    lib.ms_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp,
+                                    i32, i32, i32, i32, vp]
+    lib.ms_status_string.restype = ctypes.c_char_p
+    lib.ms_status_string.argtypes = [ctypes.c_int]
+    lib.ms_last_error.restype = ctypes.c_char_p
+    lib.ms_last_error.argtypes = []
+    lib.ms_abi_version.restype = ctypes.c_int
+    lib.ms_abi_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _io(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MS_BF16
+    if t.dtype == torch.float32:
+        return MS_F32
+    raise TypeError(f"io tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != MS_OK:
+        raise MsError(rc, load().ms_last_error().decode())
+
+
+def flags(softplus: bool = True, zoh: bool = False) -> int:
+    return (MS_SOFTPLUS if softplus else 0) | (MS_ZOH if zoh else 0)
+
+
+def dims(batch: int, seqlen: int, d_inner: int, d_state: int, io: int) -> MsDims:
+    return MsDims(batch, seqlen, d_inner, d_state, io)
+
+
+def workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int, io: int,
+                    flag_bits: int = MS_SOFTPLUS) -> int:
+    d = dims(batch, seqlen, d_inner, d_state, io)
+    n = load().ms_scan_workspace_bytes(ctypes.byref(d), flag_bits)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsError(2, "invalid dims")
+    return int(n)
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=True, zoh=False,
+             y=None, h0=None, h_last=None, workspace=None, stream=None):
+    """ms_scan_fwd on torch device tensors.  Allocates y (and the workspace)
+    when not given -- that allocation is torch's, outside the library.
+    Returns y."""
+    import torch
+    batch, L, Dn = u.shape
+    N = A.shape[1]
+    io = _io(u)
+    fl = flags(softplus, zoh)
+    if y is None:
+        y = torch.empty_like(u)
+    ws_n = workspace_bytes(batch, L, Dn, N, io, fl)
+    if workspace is None and ws_n:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=u.device)
+    ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    d = dims(batch, L, Dn, N, io)
+    rc = load().ms_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), fl, _ptr(y), _ptr(h0), _ptr(h_last),
+                            ctypes.byref(d), _ptr(workspace), ws_size, _stream(stream))
+    _check(rc)
+    return y
+
+
+def state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None, *,
+                 softplus=True, zoh=False, y_t=None, stream=None):
+    """ms_state_update on torch device tensors; h is updated in place.
+    Returns y_t."""
+    import torch
+    batch, Dn = x_t.shape
+    N = A.shape[1]
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    rc = load().ms_state_update(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t),
+                                _ptr(C_t), _ptr(D), _ptr(z_t), _ptr(delta_bias),
+                                flags(softplus, zoh), _ptr(y_t), batch, Dn, N, _io(x_t),
+                                _stream(stream))
+    _check(rc)
+    return y_t

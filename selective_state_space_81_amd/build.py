@@ -1,0 +1,74 @@
+"""Build libmsscan.so in-tree with hipcc for gfx950.
+
+    python -m selective_state_space_81_amd.build        # or build() from Python
+
+Packed fp32 VALU instructions are disabled for all device code (the
+``-packed-fp32-ops`` target feature); hipcc's host pass warns that it does not
+know the feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmsscan.so")
+SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "api.cpp")]
+ARCH = os.environ.get("MSSCAN_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libmsscan)")
+
+
+def flags() -> list:
+    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument",
+            "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libmsscan.so (always rebuilds)."""
+    objs = []
+    bdir = os.path.join(HERE, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        lang = ["-x", "hip"]  # both files go through the HIP front end
+        cmd = [hipcc()] + flags() + lang + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def asm(out_dir: str) -> None:
+    """Write the gfx950 assembly of the kernels (for inspecting our own code)."""
+    os.makedirs(out_dir, exist_ok=True)
+    src = SOURCES[0]
+    out = os.path.join(out_dir, "scan_kernels.s")
+    cmd = [hipcc()] + flags() + ["-x", "hip", "--cuda-device-only", "-S", src, "-o", out]
+    subprocess.run(cmd, check=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,179 @@
+// api.cpp -- the C ABI of libmsscan: argument validation, work planning and
+// dispatch to the HIP kernels.  Declarations and the full contract are in
+// include/msscan.h.
+#include "../../include/msscan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "msscan_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ms_status fail(ms_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+constexpr int kMaxState = 128;
+constexpr int64_t kMaxLen = 0x7fffffffLL;
+// Target number of waves for one call.  The chip has 256 CUs x 4 SIMDs; a
+// few waves per SIMD hide memory latency.  Below this the sequence is cut.
+constexpr int64_t kTargetWaves = 2048;
+constexpr int64_t kMinChunk = 64;  // never cut pieces shorter than this
+
+ms_status check_dims(const ms_dims* d) {
+    if (!d) return fail(MS_ERR_NULL, "dims is NULL");
+    if (d->batch < 1) return fail(MS_ERR_SHAPE, "batch=%d must be >= 1", d->batch);
+    if (d->seqlen < 1 || d->seqlen > kMaxLen)
+        return fail(MS_ERR_SHAPE, "seqlen=%lld must be in [1, 2^31-1]", (long long)d->seqlen);
+    if (d->d_inner < 1) return fail(MS_ERR_SHAPE, "d_inner=%d must be >= 1", d->d_inner);
+    if (d->d_state < 1 || d->d_state > kMaxState)
+        return fail(MS_ERR_SHAPE, "d_state=%d must be in [1, %d]", d->d_state, kMaxState);
+    if (d->io != MS_F32 && d->io != MS_BF16)
+        return fail(MS_ERR_DTYPE, "io=%d is not MS_F32 (0) or MS_BF16 (1)", d->io);
+    // grid limits: tiles and batch go to grid y/z
+    if ((d->d_inner + 63) / 64 > 65535 || d->batch > 65535)
+        return fail(MS_ERR_UNSUPPORTED, "d_inner/64 and batch must be <= 65535");
+    return MS_OK;
+}
+
+ms_status check_flags(uint32_t flags) {
+    if (flags & ~(uint32_t)(MS_SOFTPLUS | MS_ZOH))
+        return fail(MS_ERR_FLAGS, "unknown flag bits 0x%x", flags & ~(uint32_t)(MS_SOFTPLUS | MS_ZOH));
+    return MS_OK;
+}
+
+msscan::Plan make_plan(const ms_dims& d) {
+    msscan::Plan p{};
+    const int N = d.d_state;
+    if (N <= 4) p.ns = 4;
+    else if (N <= 8) p.ns = 8;
+    else if (N <= 16) p.ns = 16;
+    else p.ns = 32;
+    p.waves = (N + p.ns - 1) / p.ns;
+    p.tiles = (d.d_inner + 63) / 64;
+    const int64_t per_chunk = (int64_t)d.batch * p.tiles * p.waves;
+    int64_t k = (kTargetWaves + per_chunk - 1) / per_chunk;
+    const int64_t kmax = (d.seqlen + kMinChunk - 1) / kMinChunk;
+    if (k > kmax) k = kmax;
+    if (k < 1) k = 1;
+    int64_t len = (d.seqlen + k - 1) / k;
+    len = (len + 15) / 16 * 16;  // whole LDS exchange blocks
+    if (len > d.seqlen) len = d.seqlen;
+    p.chunk_len = len;
+    p.chunks = (int)((d.seqlen + len - 1) / len);
+    if (p.chunks > 1) {
+        const size_t km1 = (size_t)(p.chunks - 1);
+        p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
+    } else {
+        p.ws_floats = 0;
+    }
+    return p;
+}
+
+size_t ws_bytes(const msscan::Plan& p) {
+    return p.ws_floats ? ((p.ws_floats * sizeof(float) + 255) / 256) * 256 + 256 : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ms_abi_version(void) { return MS_ABI_VERSION; }
+
+const char* ms_last_error(void) { return g_err; }
+
+const char* ms_status_string(ms_status s) {
+    switch (s) {
+        case MS_OK: return "ok";
+        case MS_ERR_NULL: return "required pointer is NULL";
+        case MS_ERR_SHAPE: return "size out of range";
+        case MS_ERR_DTYPE: return "unsupported io dtype";
+        case MS_ERR_FLAGS: return "unknown flag bits";
+        case MS_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case MS_ERR_WORKSPACE: return "workspace missing or too small";
+        case MS_ERR_UNSUPPORTED: return "unsupported request";
+        case MS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags) {
+    if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
+    return ws_bytes(make_plan(*dims));
+}
+
+ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      uint32_t flags, void* y, const float* h0, float* h_last,
+                      const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    g_err[0] = '\0';
+    ms_status st = check_dims(dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (!u || !delta || !A || !B || !C || !y)
+        return fail(MS_ERR_NULL, "u, delta, A, B, C and y are required");
+    const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    const msscan::Plan p = make_plan(*dims);
+    const size_t need = ws_bytes(p);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    msscan::ScanArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+    a.h0 = h0; a.h_last = h_last; a.y = y;
+    a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
+    a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    if (p.chunks > 1) {
+        float* ws = static_cast<float*>(workspace);
+        const size_t km1 = (size_t)(p.chunks - 1);
+        a.agg = ws;
+        const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
+        a.sdt = ws + ((agg_n + 63) / 64) * 64;
+    }
+    hipError_t e = msscan::launch_scan(p, a, dims->io == MS_BF16, (flags & MS_ZOH) != 0,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
+ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const float* A,
+                          const void* B_t, const void* C_t, const float* D, const void* z_t,
+                          const float* delta_bias, uint32_t flags, void* y_t, int32_t batch,
+                          int32_t d_inner, int32_t d_state, int32_t io, void* stream) {
+    g_err[0] = '\0';
+    ms_dims dims{batch, 1, d_inner, d_state, io};
+    ms_status st = check_dims(&dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (!h || !x_t || !delta_t || !A || !B_t || !C_t || !y_t)
+        return fail(MS_ERR_NULL, "h, x_t, delta_t, A, B_t, C_t and y_t are required");
+    const void* ptrs[] = {h, x_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, y_t};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    msscan::StepArgs a{};
+    a.h = h; a.x = x_t; a.delta = delta_t; a.A = A; a.B = B_t; a.C = C_t; a.D = D; a.z = z_t;
+    a.bias = delta_bias; a.y = y_t; a.batch = batch; a.Dn = d_inner; a.N = d_state;
+    a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    hipError_t e = msscan::launch_step(a, io == MS_BF16, (flags & MS_ZOH) != 0,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// msscan_internal.h -- launch interface between the C ABI (api.cpp) and the
+// HIP kernels (scan_kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msscan {
+
+// How one ms_scan_fwd call is cut into work.  Lanes of a wave own 64
+// consecutive channels; a workgroup holds `waves` waves that split the
+// d_state states (`ns` per lane); the sequence is cut into `chunks` pieces of
+// `chunk_len` steps each.  Pieces after the first start from a carried state
+// computed by a separate pass (chunk summaries + carry propagation).
+struct Plan {
+    int ns;             // states per lane (compile-time variant)
+    int waves;          // waves per workgroup = ceil(d_state / ns)
+    int chunks;         // pieces along L
+    int64_t chunk_len;  // steps per piece (last piece may be shorter)
+    int tiles;          // ceil(d_inner / 64)
+    size_t ws_floats;   // workspace floats (0 when chunks == 1)
+};
+
+struct ScanArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* bias;
+    const float* h0;
+    float* h_last;
+    void* y;
+    float* agg;   // [batch][chunks-1][N][Dn]: chunk summaries, then carries
+    float* sdt;   // [batch][chunks-1][Dn]: sum of dt over each chunk
+    int64_t L;
+    int64_t chunk_len;
+    int batch;
+    int Dn;
+    int N;
+    int chunks;
+    int softplus;
+};
+
+struct StepArgs {
+    float* h;
+    const void* x;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* bias;
+    void* y;
+    int batch;
+    int Dn;
+    int N;
+    int softplus;
+};
+
+// Each returns hipSuccess or the first launch error.
+hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
+hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
+
+}  // namespace msscan

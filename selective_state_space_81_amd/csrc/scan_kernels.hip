@@ -1,0 +1,378 @@
+// scan_kernels.hip -- HIP kernels of the selective scan (S6) for gfx950.
+//
+// Method (per batch b, channel d, state n; see include/msscan.h for the full
+// statement and the passages it follows):
+//   dt = softplus(delta + bias),  A_bar = exp(dt*A[d,n]),
+//   h  = A_bar*h + B_bar*u  with B_bar = dt*B (Euler) or expm1(dt*A)/A*B (ZOH),
+//   y  = sum_n C*h + D*u,  out = y*silu(z).
+//
+// Work mapping (CDNA4, wave64):
+//   * lane  = one channel d of a 64-channel tile: u/delta/z/y rows are read and
+//     written as 64 consecutive elements per wave (coalesced), and B_t/C_t --
+//     shared by every channel (lmnt page section 3.2 broadcasts them over
+//     channels) -- are wave-uniform, so they travel through scalar loads and
+//     SGPR operands instead of per-lane registers;
+//   * the lane's `NS` states live in VGPRs for the whole piece of sequence it
+//     scans; a workgroup of `waves` waves covers d_state = waves*NS states and
+//     sums their partial readouts through LDS;
+//   * the sequence is cut into pieces ("chunks").  The scan is a composition
+//     of affine maps h -> a*h + b (jsqmd page section 3.4), so a chunk is
+//     summarised by (a, b) = (exp(A * sum dt), state reached from 0).  Pass 1
+//     (scan_summary) computes every chunk's b and sum dt, pass 2
+//     (carry_propagate) composes them in order to get each chunk's starting
+//     state, pass 3 (scan_chunks) rescans every chunk from its true starting
+//     state and writes y.  No pass waits on another workgroup, so there is no
+//     spin-wait and the association order -- hence every output bit -- is
+//     fixed by the plan alone.
+//
+// Arithmetic: fp32 throughout; bf16 io is widened exactly (bits << 16) and
+// rounded back to nearest-even.  exp/log use the hardware base-2
+// instructions with log2(e) folded into A once per (d, n).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msscan_internal.h"
+
+namespace msscan {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTB = 16;  // timesteps per LDS exchange when waves > 1
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---- io -------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+    if constexpr (BF16)
+        return __uint_as_float((uint32_t)(static_cast<const uint16_t*>(p)[i]) << 16);
+    else
+        return static_cast<const float*>(p)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void st(void* p, int64_t i, float v) {
+    if constexpr (BF16)
+        static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
+    else
+        static_cast<float*>(p)[i] = v;
+}
+
+// ---- per-element activations ------------------------------------------------
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) for small
+// w by its alternating series (6 terms: relative error < w^6/7 < 1e-8 for
+// w < 1/16), else by the hardware log of 1 + w.
+__device__ __forceinline__ float softplus_f(float v) {
+    float w = hw_exp2(-fabsf(v) * kLog2e);
+    float ser = w * (1.f + w * (-0.5f + w * (1.f / 3.f + w * (-0.25f + w * (0.2f + w * (-1.f / 6.f))))));
+    float lg = hw_log2(1.f + w) * kLn2;
+    return fmaxf(v, 0.f) + (w < 0.0625f ? ser : lg);
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z).
+__device__ __forceinline__ float silu_f(float z) {
+    return z * hw_rcp(1.f + hw_exp2(-z * kLog2e));
+}
+
+__device__ __forceinline__ float step_size(float draw, float bias, int softplus) {
+    float v = draw + bias;
+    return softplus ? softplus_f(v) : v;
+}
+
+// ZOH input factor expm1(x)/A with x = dt*A.  For |x| < 1/16 the series
+// dt*(1 + x/2 + x^2/6 + x^3/24 + x^4/120) (relative error < 2e-9) avoids the
+// cancellation of exp(x) - 1; it is also the A == 0 limit dt.  Otherwise
+// (abar - 1) * (1/A), where abar = exp(x) is already computed.
+__device__ __forceinline__ float zoh_factor(float dt, float x, float abar, float invA) {
+    float ser = dt * (1.f + x * (0.5f + x * (1.f / 6.f + x * (1.f / 24.f + x * (1.f / 120.f)))));
+    float big = (abar - 1.f) * invA;
+    return fabsf(x) < 0.0625f ? ser : big;
+}
+
+// Load the lane's A row slice (pre-multiplied by log2 e) and, for ZOH, 1/A.
+template <int NS, bool ZOH>
+__device__ __forceinline__ void load_a(const float* A, int dd, int N, int n0, int nvalid,
+                                       float (&A2)[NS], float (&invA)[NS]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        float av = (j < nvalid) ? A[(int64_t)dd * N + n0 + j] : 0.f;
+        A2[j] = av * kLog2e;
+        if constexpr (ZOH) invA[j] = (av != 0.f) ? 1.f / av : 0.f;
+    }
+}
+
+// One timestep of the lane's NS states; returns the partial readout.
+template <int NS, bool BF16, bool ZOH, bool READOUT>
+__device__ __forceinline__ float advance(float (&h)[NS], const float (&A2)[NS],
+                                         const float (&invA)[NS], float dt, float uval,
+                                         const void* B, const void* C, int64_t row,
+                                         int nvalid) {
+    float y = 0.f;
+    const float x = dt * uval;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const bool ok = j < nvalid;
+        const float bn = ok ? ld<BF16>(B, row + j) : 0.f;
+        const float arg = dt * A2[j];
+        const float abar = hw_exp2(arg);
+        float bx;
+        if constexpr (ZOH)
+            bx = zoh_factor(dt, arg * kLn2, abar, invA[j]) * (bn * uval);
+        else
+            bx = x * bn;
+        h[j] = fmaf(abar, h[j], bx);
+        if constexpr (READOUT) {
+            const float cn = ok ? ld<BF16>(C, row + j) : 0.f;
+            y = fmaf(cn, h[j], y);
+        }
+    }
+    return y;
+}
+
+// ---- pass 1: chunk summaries --------------------------------------------------
+// For every chunk but the last: the state reached from h = 0 over the chunk
+// (the "b" of its affine summary) and the compensated sum of dt (the "a" is
+// exp(A * sum dt), formed in pass 2).
+template <int NS, bool BF16, bool ZOH>
+__global__ void __launch_bounds__(256) scan_summary(ScanArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = blockIdx.x;  // 0 .. chunks-2
+    const int b = blockIdx.z;
+    const int d = blockIdx.y * 64 + lane;
+    const bool dvalid = d < a.Dn;
+    const int dd = dvalid ? d : a.Dn - 1;
+    const int n0 = w * NS;
+    const int nvalid = min(NS, a.N - n0);
+
+    float A2[NS], invA[NS], h[NS];
+    load_a<NS, ZOH>(a.A, dd, a.N, n0, nvalid, A2, invA);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) h[j] = 0.f;
+    const float bias = a.bias ? a.bias[dd] : 0.f;
+
+    const int64_t t0 = (int64_t)c * a.chunk_len;
+    const int64_t t1 = min(a.L, t0 + a.chunk_len);
+    float s = 0.f, comp = 0.f;  // Kahan sum of dt
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t e = ((int64_t)b * a.L + t) * a.Dn + dd;
+        const float uval = ld<BF16>(a.u, e);
+        const float dt = step_size(ld<BF16>(a.delta, e), bias, a.softplus);
+        const float yk = dt - comp;
+        const float tk = s + yk;
+        comp = (tk - s) - yk;
+        s = tk;
+        advance<NS, BF16, ZOH, false>(h, A2, invA, dt, uval, a.B, nullptr,
+                                      ((int64_t)b * a.L + t) * a.N + n0, nvalid);
+    }
+    if (!dvalid) return;
+    const int km1 = a.chunks - 1;
+    const int64_t base = (int64_t)b * km1 + c;
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+        if (j < nvalid) a.agg[(base * a.N + n0 + j) * a.Dn + d] = h[j];
+    if (w == 0) a.sdt[base * a.Dn + d] = s;
+}
+
+// ---- pass 2: compose chunk summaries in order --------------------------------
+// One thread per (b, n, d).  Replaces each summary slot c by the state at the
+// start of chunk c+1: h_{c+1} = exp(A * sum dt_c) * h_c + b_c, h_0 = h0 or 0.
+__global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)a.batch * a.N * a.Dn;
+    if (idx >= total) return;
+    const int d = (int)(idx % a.Dn);
+    const int n = (int)((idx / a.Dn) % a.N);
+    const int b = (int)(idx / ((int64_t)a.Dn * a.N));
+    const float A2 = a.A[(int64_t)d * a.N + n] * kLog2e;
+    float h = a.h0 ? a.h0[((int64_t)b * a.Dn + d) * a.N + n] : 0.f;
+    const int km1 = a.chunks - 1;
+    for (int c = 0; c < km1; ++c) {
+        const int64_t base = (int64_t)b * km1 + c;
+        const float decay = hw_exp2(A2 * a.sdt[base * a.Dn + d]);
+        const int64_t i = (base * a.N + n) * a.Dn + d;
+        h = fmaf(decay, h, a.agg[i]);
+        a.agg[i] = h;
+    }
+}
+
+// ---- pass 3: rescan every chunk from its true start, write y -----------------
+template <int NS, bool BF16, bool ZOH, bool MULTI>
+__global__ void __launch_bounds__(256) scan_chunks(ScanArgs a) {
+    __shared__ float ypart[MULTI ? 4 : 1][MULTI ? kTB : 1][64];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int c = blockIdx.x;
+    const int b = blockIdx.z;
+    const int d = blockIdx.y * 64 + lane;
+    const bool dvalid = d < a.Dn;
+    const int dd = dvalid ? d : a.Dn - 1;
+    const int n0 = w * NS;
+    const int nvalid = min(NS, a.N - n0);
+
+    float A2[NS], invA[NS], h[NS];
+    load_a<NS, ZOH>(a.A, dd, a.N, n0, nvalid, A2, invA);
+    const int km1 = a.chunks - 1;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        float v = 0.f;
+        if (j < nvalid) {
+            if (c == 0) {
+                if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * a.N + n0 + j];
+            } else {
+                v = a.agg[(((int64_t)b * km1 + (c - 1)) * a.N + n0 + j) * a.Dn + dd];
+            }
+        }
+        h[j] = v;
+    }
+    const float bias = a.bias ? a.bias[dd] : 0.f;
+    const float Dd = a.D ? a.D[dd] : 0.f;
+
+    const int64_t t0 = (int64_t)c * a.chunk_len;
+    const int64_t t1 = min(a.L, t0 + a.chunk_len);
+    if constexpr (!MULTI) {
+        for (int64_t t = t0; t < t1; ++t) {
+            const int64_t e = ((int64_t)b * a.L + t) * a.Dn + dd;
+            const float uval = ld<BF16>(a.u, e);
+            const float dt = step_size(ld<BF16>(a.delta, e), bias, a.softplus);
+            float y = advance<NS, BF16, ZOH, true>(h, A2, invA, dt, uval, a.B, a.C,
+                                                   ((int64_t)b * a.L + t) * a.N + n0, nvalid);
+            y = fmaf(Dd, uval, y);
+            if (a.z) y *= silu_f(ld<BF16>(a.z, e));
+            if (dvalid) st<BF16>(a.y, e, y);
+        }
+    } else {
+        for (int64_t tb = t0; tb < t1; tb += kTB) {
+            const int cnt = (int)min((int64_t)kTB, t1 - tb);
+            for (int tt = 0; tt < cnt; ++tt) {
+                const int64_t t = tb + tt;
+                const int64_t e = ((int64_t)b * a.L + t) * a.Dn + dd;
+                const float uval = ld<BF16>(a.u, e);
+                const float dt = step_size(ld<BF16>(a.delta, e), bias, a.softplus);
+                ypart[w][tt][lane] = advance<NS, BF16, ZOH, true>(
+                    h, A2, invA, dt, uval, a.B, a.C, ((int64_t)b * a.L + t) * a.N + n0, nvalid);
+            }
+            __syncthreads();
+            for (int tt = w; tt < cnt; tt += nw) {
+                const int64_t e = ((int64_t)b * a.L + tb + tt) * a.Dn + dd;
+                float y = 0.f;
+                for (int s = 0; s < nw; ++s) y += ypart[s][tt][lane];
+                y = fmaf(Dd, ld<BF16>(a.u, e), y);
+                if (a.z) y *= silu_f(ld<BF16>(a.z, e));
+                if (dvalid) st<BF16>(a.y, e, y);
+            }
+            __syncthreads();
+        }
+    }
+    if (c == a.chunks - 1 && a.h_last && dvalid) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            if (j < nvalid) a.h_last[((int64_t)b * a.Dn + d) * a.N + n0 + j] = h[j];
+    }
+}
+
+// ---- decode step ---------------------------------------------------------------
+// One thread per (b, d): the channel's N-state row (contiguous in h) is read,
+// advanced one step and written back; B_t, C_t are uniform over the block's
+// channels (one batch row per block).
+template <bool BF16, bool ZOH>
+__global__ void __launch_bounds__(256) state_step(StepArgs a) {
+    const int d = blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = blockIdx.y;
+    if (d >= a.Dn) return;
+    const int64_t e = (int64_t)b * a.Dn + d;
+    const float xv = ld<BF16>(a.x, e);
+    const float dt = step_size(ld<BF16>(a.delta, e), a.bias ? a.bias[d] : 0.f, a.softplus);
+    const float dx = dt * xv;
+    float* hrow = a.h + e * a.N;
+    const float* arow = a.A + (int64_t)d * a.N;
+    const int64_t brow = (int64_t)b * a.N;
+    float y = 0.f;
+    for (int n = 0; n < a.N; ++n) {
+        const float an = arow[n];
+        const float arg = dt * (an * kLog2e);
+        const float abar = hw_exp2(arg);
+        const float bn = ld<BF16>(a.B, brow + n);
+        float bx;
+        if constexpr (ZOH)
+            bx = zoh_factor(dt, arg * kLn2, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
+        else
+            bx = dx * bn;
+        const float hn = fmaf(abar, hrow[n], bx);
+        hrow[n] = hn;
+        y = fmaf(ld<BF16>(a.C, brow + n), hn, y);
+    }
+    y = fmaf(a.D ? a.D[d] : 0.f, xv, y);
+    if (a.z) y *= silu_f(ld<BF16>(a.z, e));
+    st<BF16>(a.y, e, y);
+}
+
+template <int NS, bool BF16, bool ZOH>
+hipError_t launch_ns(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    const dim3 block(64 * p.waves);
+    if (p.chunks > 1) {
+        hipLaunchKernelGGL((scan_summary<NS, BF16, ZOH>), dim3(p.chunks - 1, p.tiles, a.batch),
+                           block, 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t total = (int64_t)a.batch * a.N * a.Dn;
+        hipLaunchKernelGGL(carry_propagate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                           s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (p.waves > 1) {
+        if constexpr (NS == 32)
+            hipLaunchKernelGGL((scan_chunks<NS, BF16, ZOH, true>),
+                               dim3(p.chunks, p.tiles, a.batch), block, 0, s, a);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((scan_chunks<NS, BF16, ZOH, false>), dim3(p.chunks, p.tiles, a.batch),
+                           block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16, bool ZOH>
+hipError_t launch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    switch (p.ns) {
+        case 4: return launch_ns<4, BF16, ZOH>(p, a, s);
+        case 8: return launch_ns<8, BF16, ZOH>(p, a, s);
+        case 16: return launch_ns<16, BF16, ZOH>(p, a, s);
+        case 32: return launch_ns<32, BF16, ZOH>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s) {
+    if (bf16) return zoh ? launch_io<true, true>(p, a, s) : launch_io<true, false>(p, a, s);
+    return zoh ? launch_io<false, true>(p, a, s) : launch_io<false, false>(p, a, s);
+}
+
+hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s) {
+    const dim3 grid((a.Dn + 255) / 256, a.batch), block(256);
+    if (bf16) {
+        if (zoh) hipLaunchKernelGGL((state_step<true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((state_step<true, false>), grid, block, 0, s, a);
+    } else {
+        if (zoh) hipLaunchKernelGGL((state_step<false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((state_step<false, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace msscan

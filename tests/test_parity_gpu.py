@@ -1,0 +1,221 @@
+"""GPU parity: ms_scan_fwd (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element, within the stated tolerances.
+
+Small cases compare every output; the full-size layer shapes compare sampled
+channels over the whole sequence (channels are independent, so the oracle on a
+channel subset is exactly the oracle's value there), in the same launch
+configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_within, oracle_on_channels, sample_channels
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(ms, x, softplus, zoh, **kw):
+    y = ms.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x.get("D"), z=x.get("z"),
+                    delta_bias=x.get("delta_bias"), softplus=softplus, zoh=zoh, **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+def _oracle_full(x, softplus, zoh, h0=None):
+    return oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x.get("D"), z=x.get("z"),
+                       delta_bias=x.get("delta_bias"), h0=h0, softplus=softplus, zoh=zoh)
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+def test_tiny_workload_full(gpu, zoh):
+    w = synth.workload("tiny")
+    x = synth.scan_inputs(w, device=DEV, seed=0)
+    h_last = torch.empty(w.batch, w.Dn, w.N, device=DEV)
+    y = _run(gpu, x, True, zoh, h_last=h_last)
+    yr, hr = _oracle_full(x, True, zoh)
+    assert_within(y, yr, "f32")
+    assert_within(h_last, hr, "f32", "h_last")
+
+
+EDGE = [
+    # batch, L, Dn, N, io
+    (1, 1, 64, 16, "f32"),
+    (1, 2, 1, 16, "f32"),
+    (2, 1009, 70, 16, "bf16"),
+    (3, 4099, 130, 8, "f32"),
+    (1, 777, 33, 1, "f32"),
+    (2, 300, 65, 3, "bf16"),
+    (1, 520, 64, 17, "f32"),
+    (1, 400, 96, 32, "bf16"),
+    (1, 333, 64, 33, "f32"),
+    (2, 2500, 64, 64, "bf16"),
+    (1, 260, 40, 100, "f32"),
+    (1, 1100, 128, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "B{}L{}D{}N{}{}".format(*s))
+def test_edge_shapes(gpu, shape, zoh):
+    batch, L, Dn, N, io = shape
+    w = synth.workload("tiny", batch=batch, L=L, Dn=Dn, N=N, io=io)
+    x = synth.scan_inputs(w, device=DEV, seed=11)
+    h_last = torch.empty(batch, Dn, N, device=DEV)
+    y = _run(gpu, x, True, zoh, h_last=h_last)
+    yr, hr = _oracle_full(x, True, zoh)
+    assert_within(y, yr, io)
+    assert_within(h_last, hr, "f32", "h_last")
+
+
+@pytest.mark.parametrize("variant", ["no_z", "no_D", "no_bias", "softplus_off", "none"])
+def test_optional_terms(gpu, variant):
+    w = synth.workload("m130m", batch=2, L=700, Dn=96)
+    x = synth.scan_inputs(w, device=DEV, seed=5)
+    softplus = True
+    if variant in ("no_z", "none"):
+        x["z"] = None
+    if variant in ("no_D", "none"):
+        x["D"] = None
+    if variant in ("no_bias", "none"):
+        x["delta_bias"] = None
+    if variant == "softplus_off":
+        # positive steps drawn directly, no softplus
+        x["delta"] = (torch.rand(x["delta"].shape, device=DEV) * 0.1 + 1e-3).to(torch.bfloat16)
+        softplus = False
+    y = _run(gpu, x, softplus, False)
+    yr, _ = _oracle_full(x, softplus, False)
+    assert_within(y, yr, "bf16")
+
+
+def test_zero_bias_equals_null_bias(gpu):
+    w = synth.workload("tiny", L=300)
+    x = synth.scan_inputs(w, device=DEV, seed=2)
+    assert torch.count_nonzero(x["delta_bias"]) == 0
+    y0 = _run(gpu, x, True, False).clone()
+    x2 = dict(x)
+    x2["delta_bias"] = None
+    y1 = _run(gpu, x2, True, False)
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+def test_special_cases_zero_A_and_zero_step(gpu, zoh):
+    w = synth.workload("tiny", batch=2, L=513, Dn=80, N=16)
+    x = synth.scan_inputs(w, device=DEV, seed=3)
+    xa = dict(x)
+    xa["A"] = torch.zeros_like(x["A"])          # prefix-sum regime
+    y = _run(gpu, xa, True, zoh)
+    yr, _ = _oracle_full(xa, True, zoh)
+    assert_within(y, yr, "f32")
+    xd = dict(x)
+    xd["delta"] = torch.zeros_like(x["delta"])  # dt = 0: state frozen at h0
+    xd["delta_bias"] = None
+    h0 = torch.randn(2, 80, 16, device=DEV)
+    hl = torch.empty_like(h0)
+    y = _run(gpu, xd, False, zoh, h0=h0, h_last=hl)
+    yr, hr = _oracle_full(xd, False, zoh, h0=h0)
+    assert_within(y, yr, "f32")
+    assert torch.equal(hl, h0)
+
+
+def test_split_resume_matches_single_scan(gpu):
+    w = synth.workload("m130m", batch=2, L=3000, Dn=128)
+    x = synth.scan_inputs(w, device=DEV, seed=4)
+    h0 = torch.randn(2, 128, 16, device=DEV) * 0.1
+    hl = torch.empty_like(h0)
+    y = _run(gpu, x, True, False, h0=h0, h_last=hl)
+    yr, hr = _oracle_full(x, True, False, h0=h0)
+    assert_within(y, yr, "bf16")
+    assert_within(hl, hr, "f32", "h_last")
+    L1 = 1234
+    first = {k: (v[:, :L1].contiguous() if k in ("u", "delta", "z", "B", "C") else v)
+             for k, v in x.items()}
+    second = {k: (v[:, L1:].contiguous() if k in ("u", "delta", "z", "B", "C") else v)
+              for k, v in x.items()}
+    hm = torch.empty_like(h0)
+    y1 = _run(gpu, first, True, False, h0=h0, h_last=hm)
+    h2 = torch.empty_like(h0)
+    y2 = _run(gpu, second, True, False, h0=hm, h_last=h2)
+    assert_within(torch.cat([y1, y2], dim=1), yr, "bf16", "split y")
+    assert_within(h2, hr, "f32", "split h_last")
+    # h0 may alias h_last
+    hh = h0.clone()
+    y3 = _run(gpu, x, True, False, h0=hh, h_last=hh)
+    assert torch.equal(y3, y)
+    assert torch.equal(hh, hl)
+
+
+def test_deterministic_and_workspace_reuse(gpu):
+    w = synth.workload("m130m", batch=3, L=4096, Dn=192)
+    x = synth.scan_inputs(w, device=DEV, seed=6)
+    n = gpu.workspace_bytes(3, 4096, 192, 16, gpu.MS_BF16)
+    assert n > 0
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN-filled scratch
+    y1 = _run(gpu, x, True, False, workspace=ws).clone()
+    y2 = _run(gpu, x, True, False, workspace=ws)
+    assert torch.equal(y1, y2)
+
+
+def test_outputs_stay_in_bounds(gpu):
+    """Tail channels and the last chunk must not write past y or h_last."""
+    batch, L, Dn, N = 2, 1500, 70, 16
+    w = synth.workload("m130m", batch=batch, L=L, Dn=Dn)
+    x = synth.scan_inputs(w, device=DEV, seed=7)
+    pad = 4096
+    ybuf = torch.full((batch * L * Dn + pad,), 12345.0, device=DEV).to(torch.bfloat16)
+    hbuf = torch.full((batch * Dn * N + pad,), 777.0, device=DEV)
+    y = ybuf[: batch * L * Dn].view(batch, L, Dn)
+    hl = hbuf[: batch * Dn * N].view(batch, Dn, N)
+    _run(gpu, x, True, False, y=y, h_last=hl)
+    assert torch.all(ybuf[batch * L * Dn:].float() == 12352.0)  # bf16(12345) = 12352
+    assert torch.all(hbuf[batch * Dn * N:] == 777.0)
+
+
+def test_nan_stays_in_its_channel(gpu):
+    w = synth.workload("m130m", batch=2, L=1024, Dn=128)
+    x = synth.scan_inputs(w, device=DEV, seed=8)
+    b0, t0, d0 = 1, 500, 77
+    x["u"][b0, t0, d0] = float("nan")
+    y = _run(gpu, x, True, False).float().cpu()
+    bad = torch.isnan(y)
+    assert bad[b0, t0:, d0].all()
+    bad[b0, t0:, d0] = False
+    assert not bad.any()
+
+
+# ---------------------------------------------------------------- full sizes ---
+@pytest.mark.parametrize("name,zoh,k", [("m130m", False, 48), ("m3b", False, 32),
+                                         ("m3b", True, 32)],
+                         ids=["m130m-euler", "m3b-euler", "m3b-zoh"])
+def test_layer_workloads_sampled(gpu, name, zoh, k):
+    w = synth.workload(name)
+    x = synth.scan_inputs(w, device=DEV, seed=0)
+    y = _run(gpu, x, w.softplus, zoh)
+    idx = sample_channels(w.Dn, k, seed=1)
+    yr, _ = oracle_on_channels(x, idx, w.softplus, zoh)
+    got = y.index_select(2, torch.as_tensor(idx, device=DEV))
+    assert_within(got, yr, w.io)
+    # Whole-tensor properties at full size: finite, and not all zero.
+    assert torch.isfinite(y.float()).all()
+    del x, y
+    torch.cuda.empty_cache()
+
+
+def test_long_context_sampled(gpu):
+    w = synth.workload("long")
+    x = synth.scan_inputs(w, device=DEV, seed=0)
+    hl = torch.empty(w.batch, w.Dn, w.N, device=DEV)
+    y = _run(gpu, x, w.softplus, False, h_last=hl)
+    idx = sample_channels(w.Dn, 6, seed=2)
+    yr, hr = oracle_on_channels(x, idx, w.softplus, False)
+    ii = torch.as_tensor(idx, device=DEV)
+    assert_within(y.index_select(2, ii), yr, w.io)
+    assert_within(hl.index_select(1, ii), hr, "f32", "h_last")
+    assert torch.isfinite(y.float()).all()
+    del x, y
+    torch.cuda.empty_cache()
