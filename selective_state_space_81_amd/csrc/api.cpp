@@ -54,9 +54,51 @@ ms_status check_flags(uint32_t flags) {
     return MS_OK;
 }
 
+// Tile path: one workgroup per (batch row, 64-channel tile, segment) with
+// four waves splitting d_state.  The sequence is cut into segments only when
+// the batch x tile count alone leaves most of the chip idle.
+#ifndef MSSCAN_TILE_WAVES
+#define MSSCAN_TILE_WAVES 4
+#endif
+constexpr int kTileWaves = MSSCAN_TILE_WAVES;
+constexpr int kTileTB = 16;
+constexpr int64_t kFullChip = 160;        // units that already fill the chip well
+constexpr int64_t kTargetUnits = 512;     // otherwise aim for about 2 per CU
+constexpr int64_t kMinSegment = 8 * kTileTB;
+
+bool tile_plan(const ms_dims& d, msscan::Plan& p) {
+    const int N = d.d_state;
+    if (N % kTileWaves) return false;
+    const int ns = N / kTileWaves;
+    if (!msscan::tile_variant_exists(ns, kTileWaves)) return false;
+    p.tile_path = 1;
+    p.ns = ns;
+    p.waves = kTileWaves;
+    p.tiles = (d.d_inner + 63) / 64;
+    const int64_t units = (int64_t)d.batch * p.tiles;
+    int64_t k = 1;
+    if (units < kFullChip) k = (kTargetUnits + units - 1) / units;
+    const int64_t kmax = (d.seqlen + kMinSegment - 1) / kMinSegment;
+    if (k > kmax) k = kmax;
+    if (k < 1) k = 1;
+    int64_t len = (d.seqlen + k - 1) / k;
+    len = (len + kTileTB - 1) / kTileTB * kTileTB;
+    p.chunk_len = len;
+    p.chunks = (int)((d.seqlen + len - 1) / len);
+    return true;
+}
+
 msscan::Plan make_plan(const ms_dims& d) {
     msscan::Plan p{};
     const int N = d.d_state;
+    if (tile_plan(d, p)) {
+        if (p.chunks > 1) {
+            const size_t km1 = (size_t)(p.chunks - 1);
+            p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
+        }
+        return p;
+    }
+    p.tile_path = 0;
     if (N <= 4) p.ns = 4;
     else if (N <= 8) p.ns = 8;
     else if (N <= 16) p.ns = 16;
@@ -146,8 +188,10 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
         const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
         a.sdt = ws + ((agg_n + 63) / 64) * 64;
     }
-    hipError_t e = msscan::launch_scan(p, a, dims->io == MS_BF16, (flags & MS_ZOH) != 0,
-                                       static_cast<hipStream_t>(stream));
+    const bool bf16 = dims->io == MS_BF16, zoh = (flags & MS_ZOH) != 0;
+    hipError_t e = p.tile_path
+                       ? msscan::launch_scan_tiles(p, a, bf16, zoh, static_cast<hipStream_t>(stream))
+                       : msscan::launch_scan(p, a, bf16, zoh, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

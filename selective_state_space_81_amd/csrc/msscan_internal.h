@@ -14,6 +14,7 @@ namespace msscan {
 // `chunk_len` steps each.  Pieces after the first start from a carried state
 // computed by a separate pass (chunk summaries + carry propagation).
 struct Plan {
+    int tile_path;      // 1: scan_tile kernels (d_state = 4*ns); 0: generic kernels
     int ns;             // states per lane (compile-time variant)
     int waves;          // waves per workgroup = ceil(d_state / ns)
     int chunks;         // pieces along L
@@ -64,6 +65,9 @@ struct StepArgs {
 
 // Each returns hipSuccess or the first launch error.
 hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
+hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
+hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
+bool tile_variant_exists(int ns, int waves);
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
 
 }  // namespace msscan

@@ -31,73 +31,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "msscan_internal.h"
 
 namespace msscan {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+using namespace dev;
+
 constexpr int kTB = 16;  // timesteps per LDS exchange when waves > 1
-
-__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
-__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-// ---- io -------------------------------------------------------------------
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-template <bool BF16>
-__device__ __forceinline__ float ld(const void* p, int64_t i) {
-    if constexpr (BF16)
-        return __uint_as_float((uint32_t)(static_cast<const uint16_t*>(p)[i]) << 16);
-    else
-        return static_cast<const float*>(p)[i];
-}
-
-template <bool BF16>
-__device__ __forceinline__ void st(void* p, int64_t i, float v) {
-    if constexpr (BF16)
-        static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
-    else
-        static_cast<float*>(p)[i] = v;
-}
-
-// ---- per-element activations ------------------------------------------------
-// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) for small
-// w by its alternating series (6 terms: relative error < w^6/7 < 1e-8 for
-// w < 1/16), else by the hardware log of 1 + w.
-__device__ __forceinline__ float softplus_f(float v) {
-    float w = hw_exp2(-fabsf(v) * kLog2e);
-    float ser = w * (1.f + w * (-0.5f + w * (1.f / 3.f + w * (-0.25f + w * (0.2f + w * (-1.f / 6.f))))));
-    float lg = hw_log2(1.f + w) * kLn2;
-    return fmaxf(v, 0.f) + (w < 0.0625f ? ser : lg);
-}
-
-// silu(z) = z * sigmoid(z) = z / (1 + e^-z).
-__device__ __forceinline__ float silu_f(float z) {
-    return z * hw_rcp(1.f + hw_exp2(-z * kLog2e));
-}
-
-__device__ __forceinline__ float step_size(float draw, float bias, int softplus) {
-    float v = draw + bias;
-    return softplus ? softplus_f(v) : v;
-}
-
-// ZOH input factor expm1(x)/A with x = dt*A.  For |x| < 1/16 the series
-// dt*(1 + x/2 + x^2/6 + x^3/24 + x^4/120) (relative error < 2e-9) avoids the
-// cancellation of exp(x) - 1; it is also the A == 0 limit dt.  Otherwise
-// (abar - 1) * (1/A), where abar = exp(x) is already computed.
-__device__ __forceinline__ float zoh_factor(float dt, float x, float abar, float invA) {
-    float ser = dt * (1.f + x * (0.5f + x * (1.f / 6.f + x * (1.f / 24.f + x * (1.f / 120.f)))));
-    float big = (abar - 1.f) * invA;
-    return fabsf(x) < 0.0625f ? ser : big;
-}
 
 // Load the lane's A row slice (pre-multiplied by log2 e) and, for ZOH, 1/A.
 template <int NS, bool ZOH>
@@ -326,10 +268,7 @@ hipError_t launch_ns(const Plan& p, const ScanArgs& a, hipStream_t s) {
                            block, 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const int64_t total = (int64_t)a.batch * a.N * a.Dn;
-        hipLaunchKernelGGL(carry_propagate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                           s, a);
-        e = hipGetLastError();
+        e = launch_carry(a, s);
         if (e != hipSuccess) return e;
     }
     if (p.waves > 1) {
@@ -361,6 +300,12 @@ hipError_t launch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
 hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s) {
     if (bf16) return zoh ? launch_io<true, true>(p, a, s) : launch_io<true, false>(p, a, s);
     return zoh ? launch_io<false, true>(p, a, s) : launch_io<false, false>(p, a, s);
+}
+
+hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
+    const int64_t total = (int64_t)a.batch * a.N * a.Dn;
+    hipLaunchKernelGGL(carry_propagate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s) {

@@ -75,8 +75,12 @@ def test_workspace_size_function():
     # Invalid dims -> (size_t)-1.
     bad = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 0, 64, 16, 1)), 1)
     assert bad == ctypes.c_size_t(-1).value
+    # A shape that fills the chip with batch x channel tiles runs in one piece.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 16, 1)), 1) == 0
     # Deterministic and independent of flags that do not change the plan.
-    d = ms.dims(8, 2048, 1536, 16, 1)
+    d = ms.dims(1, 65536, 256, 16, 1)
     a = lib.ms_scan_workspace_bytes(ctypes.byref(d), 1)
     assert a == lib.ms_scan_workspace_bytes(ctypes.byref(d), 3)
     assert a % 256 == 0 and a > 0
+    # Odd d_state takes the generic kernels, which also size their workspace.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 65536, 256, 17, 1)), 1) > 0

@@ -84,8 +84,9 @@ def test_optional_terms(gpu, variant):
     if variant in ("no_bias", "none"):
         x["delta_bias"] = None
     if variant == "softplus_off":
-        # positive steps drawn directly, no softplus
+        # positive steps drawn directly, no softplus and no bias
         x["delta"] = (torch.rand(x["delta"].shape, device=DEV) * 0.1 + 1e-3).to(torch.bfloat16)
+        x["delta_bias"] = None
         softplus = False
     y = _run(gpu, x, softplus, False)
     yr, _ = _oracle_full(x, softplus, False)
