@@ -54,48 +54,78 @@ ms_status check_flags(uint32_t flags) {
     return MS_OK;
 }
 
-// Tile path: one workgroup per (batch row, 64-channel tile, segment) with
-// four waves splitting d_state.  The sequence is cut into segments only when
-// the batch x tile count alone leaves most of the chip idle.
+// Fast paths.  Both map one 64-channel tile of one batch row to a
+// workgroup and cut the sequence into segments until about kTargetWaves
+// waves exist (many waves per CU keep the VALU issuing; a segment after the
+// first costs a summary pass over it, so segments are not cut shorter than
+// kMinSegment).
+//   lane path (d_state 8 or 16): one wave per workgroup, all states of a
+//     channel in one lane;
+//   tile path (d_state 32, 64, 128, or 8/16 when forced): several waves
+//     split d_state and share per-element work through LDS.
 #ifndef MSSCAN_TILE_WAVES
 #define MSSCAN_TILE_WAVES 4
 #endif
+#ifndef MSSCAN_TARGET_WAVES
+#define MSSCAN_TARGET_WAVES 3072
+#endif
+#ifndef MSSCAN_LANE_PATH
+#define MSSCAN_LANE_PATH 1
+#endif
 constexpr int kTileWaves = MSSCAN_TILE_WAVES;
-constexpr int kTileTB = 16;
-constexpr int64_t kFullChip = 160;        // units that already fill the chip well
-constexpr int64_t kTargetUnits = 512;     // otherwise aim for about 2 per CU
-constexpr int64_t kMinSegment = 8 * kTileTB;
+constexpr int64_t kTargetWaves2 = MSSCAN_TARGET_WAVES;
+constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
+constexpr int64_t kMinSegment = 128;
 
-bool tile_plan(const ms_dims& d, msscan::Plan& p) {
-    const int N = d.d_state;
-    if (N % kTileWaves) return false;
-    const int ns = N / kTileWaves;
-    if (!msscan::tile_variant_exists(ns, kTileWaves)) return false;
-    p.tile_path = 1;
-    p.ns = ns;
-    p.waves = kTileWaves;
-    p.tiles = (d.d_inner + 63) / 64;
-    const int64_t units = (int64_t)d.batch * p.tiles;
-    int64_t k = 1;
-    if (units < kFullChip) k = (kTargetUnits + units - 1) / units;
+void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) {
+    int64_t k = (kTargetWaves2 + waves_per_segment - 1) / waves_per_segment;
     const int64_t kmax = (d.seqlen + kMinSegment - 1) / kMinSegment;
     if (k > kmax) k = kmax;
     if (k < 1) k = 1;
     int64_t len = (d.seqlen + k - 1) / k;
-    len = (len + kTileTB - 1) / kTileTB * kTileTB;
+    len = (len + kSegmentQuantum - 1) / kSegmentQuantum * kSegmentQuantum;
     p.chunk_len = len;
     p.chunks = (int)((d.seqlen + len - 1) / len);
+}
+
+bool lane_plan(const ms_dims& d, msscan::Plan& p) {
+    if (!MSSCAN_LANE_PATH || !msscan::lane_variant_exists(d.d_state)) return false;
+    p.tile_path = 2;
+    p.ns = d.d_state;
+    p.waves = 1;
+    p.tiles = (d.d_inner + 63) / 64;
+    cut_sequence(d, (int64_t)d.batch * p.tiles, p);
+    return true;
+}
+
+bool tile_plan(const ms_dims& d, msscan::Plan& p) {
+    const int N = d.d_state;
+    int waves = kTileWaves;
+    if (N % waves) return false;
+    int ns = N / waves;
+    if (ns > 16 && N % 8 == 0) {  // a wave's states must fit one 16-lane DPP row
+        waves = 8;
+        ns = N / 8;
+    }
+    if (!msscan::tile_variant_exists(ns, waves)) return false;
+    p.tile_path = 1;
+    p.ns = ns;
+    p.waves = waves;
+    p.tiles = (d.d_inner + 63) / 64;
+    cut_sequence(d, (int64_t)d.batch * p.tiles * waves, p);
     return true;
 }
 
 msscan::Plan make_plan(const ms_dims& d) {
     msscan::Plan p{};
     const int N = d.d_state;
-    if (tile_plan(d, p)) {
+    if (lane_plan(d, p) || tile_plan(d, p)) {
         if (p.chunks > 1) {
             const size_t km1 = (size_t)(p.chunks - 1);
             p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
         }
+        // fp32 copy of B and C, rows [b][t][B_t | C_t], read as DPP operands.
+        p.bc_floats = (size_t)d.batch * (size_t)d.seqlen * 2 * (size_t)N;
         return p;
     }
     p.tile_path = 0;
@@ -124,8 +154,13 @@ msscan::Plan make_plan(const ms_dims& d) {
     return p;
 }
 
+size_t round256(size_t bytes) { return (bytes + 255) / 256 * 256; }
+
+// Workspace layout: [fp32 B/C slices][chunk summaries + carries][sum of dt].
 size_t ws_bytes(const msscan::Plan& p) {
-    return p.ws_floats ? ((p.ws_floats * sizeof(float) + 255) / 256) * 256 + 256 : 0;
+    size_t n = round256(p.bc_floats * sizeof(float));
+    if (p.ws_floats) n += round256(p.ws_floats * sizeof(float)) + 256;
+    return n;
 }
 
 }  // namespace
@@ -181,17 +216,23 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
     a.h0 = h0; a.h_last = h_last; a.y = y;
     a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
     a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    a.waves = p.waves;
+    float* ws = static_cast<float*>(workspace);
+    if (p.bc_floats) {
+        a.bcw = ws;
+        ws += round256(p.bc_floats * sizeof(float)) / sizeof(float);
+    }
     if (p.chunks > 1) {
-        float* ws = static_cast<float*>(workspace);
         const size_t km1 = (size_t)(p.chunks - 1);
         a.agg = ws;
         const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
         a.sdt = ws + ((agg_n + 63) / 64) * 64;
     }
     const bool bf16 = dims->io == MS_BF16, zoh = (flags & MS_ZOH) != 0;
-    hipError_t e = p.tile_path
-                       ? msscan::launch_scan_tiles(p, a, bf16, zoh, static_cast<hipStream_t>(stream))
-                       : msscan::launch_scan(p, a, bf16, zoh, static_cast<hipStream_t>(stream));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = p.tile_path == 2   ? msscan::launch_scan_lanes(p, a, bf16, zoh, hs)
+                   : p.tile_path == 1 ? msscan::launch_scan_tiles(p, a, bf16, zoh, hs)
+                                      : msscan::launch_scan(p, a, bf16, zoh, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

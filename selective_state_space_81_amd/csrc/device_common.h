@@ -41,14 +41,15 @@ __device__ __forceinline__ void st(void* p, int64_t i, float v) {
 }
 
 // ---- per-element activations ------------------------------------------------
-// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).  log1p(w) for small
-// w by its alternating series (6 terms: relative error < w^6/7 < 1e-8 for
-// w < 1/16), else by the hardware log of 1 + w.
+// softplus(v) = log(1 + e^v) with the hardware base-2 exp/log:
+// ln2 * log2(1 + 2^(v*log2 e)).  The exponent is clamped at 64 so 2^x stays
+// finite; for v > 44 the result is v itself to fp32 precision, and max(v, .)
+// returns it.  The rounding of 1 + w bounds the absolute error by about
+// 2^-24 * ln2, which is what the step size needs (it scales B*u and the
+// exponent dt*A).
 __device__ __forceinline__ float softplus_f(float v) {
-    float w = hw_exp2(-fabsf(v) * kLog2e);
-    float ser = w * (1.f + w * (-0.5f + w * (1.f / 3.f + w * (-0.25f + w * (0.2f + w * (-1.f / 6.f))))));
-    float lg = hw_log2(1.f + w) * kLn2;
-    return fmaxf(v, 0.f) + (w < 0.0625f ? ser : lg);
+    const float w = hw_exp2(fminf(v * kLog2e, 64.f));
+    return fmaxf(v, hw_log2(1.f + w) * kLn2);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).

@@ -14,13 +14,15 @@ namespace msscan {
 // `chunk_len` steps each.  Pieces after the first start from a carried state
 // computed by a separate pass (chunk summaries + carry propagation).
 struct Plan {
-    int tile_path;      // 1: scan_tile kernels (d_state = 4*ns); 0: generic kernels
+    int tile_path;      // 2: scan_lane kernels (all states in a lane);
+                        // 1: scan_tile kernels (waves split d_state); 0: generic
     int ns;             // states per lane (compile-time variant)
     int waves;          // waves per workgroup = ceil(d_state / ns)
     int chunks;         // pieces along L
     int64_t chunk_len;  // steps per piece (last piece may be shorter)
     int tiles;          // ceil(d_inner / 64)
     size_t ws_floats;   // workspace floats (0 when chunks == 1)
+    size_t bc_floats;   // tile path: fp32 B/C copy laid out per wave (0 if unused)
 };
 
 struct ScanArgs {
@@ -37,6 +39,7 @@ struct ScanArgs {
     void* y;
     float* agg;   // [batch][chunks-1][N][Dn]: chunk summaries, then carries
     float* sdt;   // [batch][chunks-1][Dn]: sum of dt over each chunk
+    float* bcw;   // tile path: [batch][waves][L][2*ns] fp32 B_t then C_t slices
     int64_t L;
     int64_t chunk_len;
     int batch;
@@ -44,6 +47,7 @@ struct ScanArgs {
     int N;
     int chunks;
     int softplus;
+    int waves;    // tile path: waves per workgroup
 };
 
 struct StepArgs {
@@ -68,6 +72,9 @@ hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hi
 hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
 bool tile_variant_exists(int ns, int waves);
+hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
+bool lane_variant_exists(int n);
+hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
 
 }  // namespace msscan

@@ -1,0 +1,236 @@
+// scan_lane.hip -- selective scan (S6) kernel with every state of a channel
+// in one lane, for d_state <= 16 on gfx950.
+//
+// A workgroup is a single wave: lane = one channel of a 64-channel tile, and
+// the lane keeps all N states of its channel in VGPRs.  The wave walks one
+// segment of the sequence timestep by timestep, doing the whole per-element
+// pipeline in registers:
+//   dt = softplus(delta + bias), x = dt*u                 (once per element)
+//   for n: A_bar = exp(dt*A), h = A_bar*h + B_bar*u         (N recurrences)
+//   y = sum_n C*h + D*u, times silu(z), rounded, stored    (once per element)
+// There is no LDS, no barrier and no cross-wave exchange, so many waves fit
+// a CU and the VALU stays busy; the sequence is cut into segments to supply
+// those waves (the batch x tile count alone is too small for the chip).  A
+// segment after the first starts from a carried state: a summary variant of
+// this kernel (SUMMARY = true, no readout) computes each segment's end state
+// from zero and its compensated sum of dt, and the carry pass composes them
+// in order -- the scan is a composition of affine maps (jsqmd page,
+// section 3.4).
+//
+// B_t and C_t (shared by all channels, lmnt page section 3.2) come from the
+// fp32 rows [b][t][B | C] written by the B/C prepass: lane l loads state
+// (l mod 16) and the DPP row_newbcast control hands state n to every lane as
+// the first operand of v_mul / v_fmac, so the broadcast costs no extra
+// instruction, no LDS traffic and no SGPRs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "dpp_common.h"
+#include "msscan_internal.h"
+
+namespace msscan {
+namespace {
+
+using namespace dev;
+
+template <int N, int TB, bool BF16, bool ZOH, bool SUMMARY>
+__global__ void __launch_bounds__(64) scan_lane(ScanArgs a) {
+    static_assert(N == 8 || N == 16, "one DPP row holds the states of a lane");
+    using R = Io<BF16>;
+    using RT = typename R::T;
+
+    const int lane = threadIdx.x;
+    const int b = blockIdx.z;
+    const int seg = blockIdx.y;
+    const int d = blockIdx.x * 64 + lane;
+    const bool dvalid = d < a.Dn;
+    const int dd = dvalid ? d : a.Dn - 1;
+
+    float A2[N], invA[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float av = a.A[(int64_t)dd * N + n];
+        A2[n] = av * kLog2e;
+        if constexpr (ZOH) invA[n] = (av != 0.f) ? 1.f / av : 0.f;
+    }
+    const int km1 = a.chunks - 1;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        float v = 0.f;
+        if constexpr (!SUMMARY) {
+            if (seg == 0) {
+                if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * N + n];
+            } else {
+                v = a.agg[(((int64_t)b * km1 + (seg - 1)) * N + n) * a.Dn + dd];
+            }
+        }
+        h[n] = v;
+    }
+    const float bias = a.bias ? a.bias[dd] : 0.f;
+    const float Dd = a.D ? a.D[dd] : 0.f;
+    const bool has_z = a.z != nullptr;
+    const bool use_sp = a.softplus != 0;
+
+    const int64_t t0 = (int64_t)seg * a.chunk_len;
+    const int64_t t1 = min(a.L, t0 + a.chunk_len);
+    const int nblocks = (int)((t1 - t0 + TB - 1) / TB);
+    const int64_t row0 = (int64_t)b * a.L;
+
+    const uint32_t rowb = (uint32_t)a.Dn * R::kSize;
+    const uint32_t off0 = dvalid ? (uint32_t)d * R::kSize : kOutOfRange;
+    auto block_rows = [&](int64_t tb) -> uint32_t {
+        return (uint32_t)max((int64_t)0, min((int64_t)TB, t1 - tb));
+    };
+    auto block_base = [&](const void* p, int64_t tb) -> const void* {
+        return static_cast<const char*>(p) + (row0 + tb) * (int64_t)rowb;
+    };
+    constexpr uint32_t kBCRow = 2u * N * 4u;
+    const uint32_t bcoff = (uint32_t)(lane & (N - 1)) * 4u;
+
+    // Register double buffer of one block's raw inputs.
+    RT ru[2][TB], rd[2][TB], rz[2][TB];
+    float vb[2][TB], vc[2][TB];
+    auto load_block = [&](int buf, int64_t tb) {
+        const uint32_t nr = block_rows(tb);
+        const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
+        const auto rD = make_rsrc(block_base(a.delta, tb), nr * rowb);
+        const auto rZ = make_rsrc(has_z ? block_base(a.z, tb) : a.u, has_z ? nr * rowb : 0u);
+        const auto rBC = make_rsrc(a.bcw + (row0 + tb) * (2 * N), nr * kBCRow);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) {
+            const uint32_t off = off0 + (uint32_t)tt * rowb;
+            ru[buf][tt] = R::load(rU, off);
+            rd[buf][tt] = R::load(rD, off);
+            if constexpr (!SUMMARY) rz[buf][tt] = R::load(rZ, off);
+            vb[buf][tt] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rBC, (uint32_t)tt * kBCRow + bcoff, 0, 0));
+            if constexpr (!SUMMARY)
+                vc[buf][tt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rBC, (uint32_t)tt * kBCRow + (uint32_t)N * 4u + bcoff, 0, 0));
+        }
+    };
+
+    float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (SUMMARY)
+
+    // One timestep: all N states of the lane's channel.
+    auto step = [&](RT raw_u, RT raw_d, RT raw_z, float vbt, float vct, float& y_out) {
+        const float uv = R::widen(raw_u);
+        const float v = R::widen(raw_d) + bias;
+        const float dt = use_sp ? softplus_f(v) : v;
+        const float xv = ZOH ? uv : dt * uv;
+        static_for(
+            [&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                const float arg = dt * A2[n];
+                const float abar = hw_exp2(arg);
+                const float bu = row_bcast<n>(vbt) * xv;  // B*x (Euler) or B*u (ZOH)
+                float bx;
+                if constexpr (ZOH)
+                    bx = zoh_factor(dt, arg * kLn2, abar, invA[n]) * bu;
+                else
+                    bx = bu;
+                h[n] = fmaf(abar, h[n], bx);
+            },
+            std::make_integer_sequence<int, N>{});
+        if constexpr (SUMMARY) {
+            const float yk = dt - s_comp;
+            const float tk = s_sum + yk;
+            s_comp = (tk - s_sum) - yk;
+            s_sum = tk;
+        } else {
+            float y = DppReadout<N>::run(vct, h);
+            y = fmaf(Dd, uv, y);
+            const float g = silu_f(R::widen(raw_z));
+            y_out = y * (has_z ? g : 1.f);
+        }
+    };
+
+    auto do_block = [&](auto cur_c, int blk) {
+        constexpr int cur = decltype(cur_c)::value;
+        const int64_t tb = t0 + (int64_t)blk * TB;
+        const int cnt = (int)min((int64_t)TB, t1 - tb);
+        load_block(cur ^ 1, tb + TB);  // past the end it reads zeros
+        const auto rY = make_rsrc(block_base(a.y, tb), (uint32_t)cnt * rowb);
+        if (cnt == TB) {
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt) {
+                float y = 0.f;
+                step(ru[cur][tt], rd[cur][tt], rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
+                if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt) {
+                if (tt < cnt) {
+                    float y = 0.f;
+                    step(ru[cur][tt], rd[cur][tt], rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
+                    if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
+                }
+            }
+        }
+    };
+
+    load_block(0, t0);
+    int blk = 0;
+    for (; blk + 1 < nblocks; blk += 2) {
+        do_block(std::integral_constant<int, 0>{}, blk);
+        do_block(std::integral_constant<int, 1>{}, blk + 1);
+    }
+    if (blk < nblocks) do_block(std::integral_constant<int, 0>{}, blk);
+
+    if (!dvalid) return;
+    if constexpr (SUMMARY) {
+        const int64_t base = (int64_t)b * km1 + seg;
+#pragma unroll
+        for (int n = 0; n < N; ++n) a.agg[(base * N + n) * a.Dn + d] = h[n];
+        a.sdt[base * a.Dn + d] = s_sum;
+    } else {
+        if (seg == a.chunks - 1 && a.h_last) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) a.h_last[((int64_t)b * a.Dn + d) * N + n] = h[n];
+        }
+    }
+}
+
+template <int N, bool BF16, bool ZOH>
+hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    constexpr int TB = 8;
+    hipError_t e = launch_bc_prepare(a, BF16, s);
+    if (e != hipSuccess) return e;
+    if (p.chunks > 1) {
+        hipLaunchKernelGGL((scan_lane<N, TB, BF16, ZOH, true>),
+                           dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_carry(a, s);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((scan_lane<N, TB, BF16, ZOH, false>), dim3(p.tiles, p.chunks, a.batch),
+                       dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool ZOH>
+hipError_t dispatch(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    switch (p.ns) {
+        case 8: return launch_lanes<8, BF16, ZOH>(p, a, s);
+        case 16: return launch_lanes<16, BF16, ZOH>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool lane_variant_exists(int n) { return n == 8 || n == 16; }
+
+hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool zoh,
+                             hipStream_t s) {
+    if (bf16) return zoh ? dispatch<true, true>(p, a, s) : dispatch<true, false>(p, a, s);
+    return zoh ? dispatch<false, true>(p, a, s) : dispatch<false, false>(p, a, s);
+}
+
+}  // namespace msscan

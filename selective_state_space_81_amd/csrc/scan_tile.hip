@@ -9,17 +9,23 @@
 //
 // The sequence is walked in blocks of TB timesteps, each in three phases:
 //   A  per element (t, channel), spread over all threads of the workgroup:
-//      widen u / delta (/ z), dt = softplus(delta + bias), x = dt*u, and the
-//      block's B_t / C_t rows widened to fp32 -- all into LDS.  Each element's
-//      activations are computed exactly once, not once per state.
+//      widen u / delta, dt = softplus(delta + bias), x = dt*u, into LDS.  Each
+//      element's activations are computed once, not once per state.
 //   B  per wave: for each timestep, its NS states advance and their partial
-//      readout sum_n C*h goes to LDS.  dt, x, B_t, C_t are read from LDS; the
-//      B/C reads are wave-uniform broadcasts.
+//      readout sum_n C*h goes to LDS.
 //   C  per element again: y = sum of the S partials + D*u, times silu(z),
 //      rounded to the io type and stored (coalesced rows).
 // The next block's global loads are issued before phase A of the current one
-// (register double buffering), and the LDS buffers alternate between blocks,
+// (register double buffering) and the LDS buffers alternate between blocks,
 // so each block needs two barriers.
+//
+// B_t and C_t are shared by every channel (the naive scan of the lmnt page,
+// section 3.2, broadcasts them over channels).  They reach the VALU as DPP
+// operands: a prepass widens them to fp32 rows [b][t][B row | C row]; each
+// lane loads the value of state n0 + (lane mod NS) and the row_newbcast DPP
+// control hands state n0 + j of the lane's 16-lane row to every lane as the
+// first operand of v_mul / v_fmac.  No LDS bandwidth, no SGPRs and no extra
+// instruction is spent per (state, timestep) on the broadcast.
 //
 // With several segments, a summary variant of the same kernel (no readout,
 // SUMMARY = true) computes each segment's end state from zero and its
@@ -30,8 +36,10 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
+#include "dpp_common.h"
 #include "msscan_internal.h"
 
 namespace msscan {
@@ -39,60 +47,16 @@ namespace {
 
 using namespace dev;
 
-// Buffer-resource io.  A block's rows of u / delta / z / y are addressed
-// through a buffer descriptor whose size ends at the block's last valid row,
-// so reads past it return 0 and writes past it are dropped by the hardware;
-// tail channels get an offset beyond any size.  No branch is needed for
-// ragged sequence ends or d_inner tails.
-constexpr uint32_t kBufFlags = 0x00020000u;  // raw (untyped) access, gfx9 family
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             (int)kBufFlags);
-}
-
-template <bool BF16>
-struct Io {
-    static constexpr int kSize = BF16 ? 2 : 4;
-    using T = typename std::conditional<BF16, uint16_t, float>::type;
-    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        if constexpr (BF16)
-            return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-        else
-            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-    }
-    static __device__ __forceinline__ float widen(T v) {
-        if constexpr (BF16)
-            return __uint_as_float((uint32_t)v << 16);
-        else
-            return v;
-    }
-    // Round to the io type (bf16: hardware round-to-nearest-even) and store.
-    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-        if constexpr (BF16)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off,
-                                                  0, 0);
-        else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-    }
-};
-
 template <int NS, int S, int TB, bool BF16, bool ZOH, bool SUMMARY>
 __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     constexpr int N = NS * S;
-    constexpr int NT = 64 * S;
-    constexpr int J = TB / S;                    // timesteps per thread in phases A/C
-    constexpr int BCN = (TB * N + NT - 1) / NT;  // B (and C) tile elements per thread
+    constexpr int J = TB / S;  // timesteps per thread in phases A/C
     static_assert(TB % S == 0, "TB must be a multiple of S");
-    static_assert(NS % 2 == 0, "the B/C slice of a wave is read in 16-byte pieces");
+    static_assert(NS == 2 || NS == 4 || NS == 8 || NS == 16, "a wave's states fit one DPP row");
     using R = Io<BF16>;
     using RT = typename R::T;
 
-    __shared__ float2 s_dx[2][TB][64];           // (dt, x) Euler; (dt, u) ZOH
-    // B_t / C_t of the block widened to fp32, grouped per wave: for timestep
-    // tt and wave w, the NS values of B then the NS values of C.
-    __shared__ __attribute__((aligned(16))) float s_bc[2][TB][S][2][NS];
+    __shared__ float2 s_dx[2][TB][64];  // (dt, x) Euler; (dt, u) ZOH
     __shared__ float s_y[SUMMARY ? 1 : 2][SUMMARY ? 1 : S][SUMMARY ? 1 : TB][64];
 
     const int tid = threadIdx.x;
@@ -139,32 +103,27 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     // (w*J + j), channel d.  Tail channels point past every buffer.
     const uint32_t rowb = (uint32_t)a.Dn * R::kSize;
     const uint32_t off0 = dvalid ? ((uint32_t)(w * J) * rowb + (uint32_t)d * R::kSize) : kOutOfRange;
-    auto block_bytes = [&](int64_t tb) -> uint32_t {
-        return (uint32_t)min((int64_t)TB, t1 - tb) * rowb;
+    // Valid rows of the block starting at tb (0 past the segment end, so a
+    // prefetch of a block that does not exist reads only zeros).
+    auto block_rows = [&](int64_t tb) -> uint32_t {
+        return (uint32_t)max((int64_t)0, min((int64_t)TB, t1 - tb));
     };
     auto block_base = [&](const void* p, int64_t tb) -> const void* {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)rowb;
     };
+    // Prepared B/C rows: 2N floats per timestep.  Lane l reads state
+    // n0 + (l mod NS) of B (and, N floats further, of C).
+    constexpr uint32_t kBCRow = 2u * N * 4u;
+    const uint32_t bcoff = (uint32_t)(n0 + (lane & (NS - 1))) * 4u;
 
     // Register double buffer of the raw inputs of one block.
-    RT ru[2][J], rd[2][J], rz[2][J], rb[2][BCN], rc[2][BCN];
+    RT ru[2][J], rd[2][J], rz[2][J];
+    float vb[2][TB], vc[2][TB];
     auto load_block = [&](int buf, int64_t tb) {
-        {
-            const uint32_t nbc = (uint32_t)min((int64_t)TB, t1 - tb) * (uint32_t)(N * R::kSize);
-            const auto rB = make_rsrc(static_cast<const char*>(a.B) + (row0 + tb) * N * R::kSize, nbc);
-            const auto rC = make_rsrc(static_cast<const char*>(a.C) + (row0 + tb) * N * R::kSize, nbc);
-#pragma unroll
-            for (int k = 0; k < BCN; ++k) {
-                const int i = tid + k * NT;
-                const uint32_t off = (i < TB * N) ? (uint32_t)i * R::kSize : kOutOfRange;
-                rb[buf][k] = R::load(rB, off);
-                if constexpr (!SUMMARY) rc[buf][k] = R::load(rC, off);
-            }
-        }
-        const uint32_t nb = block_bytes(tb);
-        const auto rU = make_rsrc(block_base(a.u, tb), nb);
-        const auto rD = make_rsrc(block_base(a.delta, tb), nb);
-        const auto rZ = make_rsrc(has_z ? block_base(a.z, tb) : a.u, has_z ? nb : 0u);
+        const uint32_t nr = block_rows(tb);
+        const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
+        const auto rD = make_rsrc(block_base(a.delta, tb), nr * rowb);
+        const auto rZ = make_rsrc(has_z ? block_base(a.z, tb) : a.u, has_z ? nr * rowb : 0u);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const uint32_t off = off0 + (uint32_t)j * rowb;
@@ -172,34 +131,39 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
             rd[buf][j] = R::load(rD, off);
             if constexpr (!SUMMARY) rz[buf][j] = R::load(rZ, off);
         }
+        const auto rBC = make_rsrc(a.bcw + (row0 + tb) * (2 * N), nr * kBCRow);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) {
+            vb[buf][tt] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rBC, (uint32_t)tt * kBCRow + bcoff, 0, 0));
+            if constexpr (!SUMMARY)
+                vc[buf][tt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rBC, (uint32_t)tt * kBCRow + (uint32_t)N * 4u + bcoff, 0, 0));
+        }
     };
 
     float uf[J];                      // widened u kept from phase A to phase C
     float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (wave 0, SUMMARY)
 
-    // One timestep of this wave's NS states; B and C come from LDS.
-    auto step = [&](int cur, int tt, float2 dx) {
-        float bc[2 * NS];
-#pragma unroll
-        for (int q = 0; q < 2 * NS; q += 4)
-            *reinterpret_cast<float4*>(&bc[q]) =
-                *reinterpret_cast<const float4*>(&s_bc[cur][tt][w][0][0] + q);
-        float y = 0.f;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const float arg = dx.x * A2[j];
-            const float abar = hw_exp2(arg);
-            const float bn = bc[j];
-            float bx;
-            if constexpr (ZOH)
-                bx = zoh_factor(dx.x, arg * kLn2, abar, invA[j]) * (dx.y * bn);
-            else
-                bx = dx.y * bn;
-            h[j] = fmaf(abar, h[j], bx);
-            if constexpr (!SUMMARY) y = fmaf(bc[NS + j], h[j], y);
-        }
-        if constexpr (!SUMMARY) s_y[cur][w][tt][lane] = y;
-        if constexpr (SUMMARY) {
+    // One timestep of this wave's NS states.
+    auto step = [&](int cur, int tt, float2 dx, float vbt, float vct) {
+        static_for(
+            [&](auto jc) {
+                constexpr int j = decltype(jc)::value;
+                const float arg = dx.x * A2[j];
+                const float abar = hw_exp2(arg);
+                const float bu = row_bcast<j>(vbt) * dx.y;  // B*x (Euler) or B*u (ZOH)
+                float bx;
+                if constexpr (ZOH)
+                    bx = zoh_factor(dx.x, arg * kLn2, abar, invA[j]) * bu;
+                else
+                    bx = bu;
+                h[j] = fmaf(abar, h[j], bx);
+            },
+            std::make_integer_sequence<int, NS>{});
+        if constexpr (!SUMMARY) {
+            s_y[cur][w][tt][lane] = DppReadout<NS>::run(vct, h);
+        } else {
             if (w == 0) {
                 const float yk = dx.x - s_comp;
                 const float tk = s_sum + yk;
@@ -215,7 +179,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
         constexpr int cur = decltype(cur_c)::value;
         const int64_t tb = t0 + (int64_t)blk * TB;
         const int cnt = (int)min((int64_t)TB, t1 - tb);
-        if (blk + 1 < nblocks) load_block(cur ^ 1, tb + TB);
+        load_block(cur ^ 1, tb + TB);  // unconditional: past the end it reads zeros
 
         // ---- phase A: per-element activations into LDS ----
 #pragma unroll
@@ -228,15 +192,6 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
             uf[j] = uv;
             s_dx[cur][tl][lane] = ZOH ? make_float2(dt, uv) : make_float2(dt, dt * uv);
         }
-#pragma unroll
-        for (int k = 0; k < BCN; ++k) {
-            const int i = tid + k * NT;
-            if (i < TB * N) {
-                const int tt = i / N, n = i % N;
-                s_bc[cur][tt][n / NS][0][n % NS] = R::widen(rb[cur][k]);
-                if constexpr (!SUMMARY) s_bc[cur][tt][n / NS][1][n % NS] = R::widen(rc[cur][k]);
-            }
-        }
         __syncthreads();
 
         // ---- phase B: the recurrences of this wave's states ----
@@ -245,9 +200,11 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
 #pragma unroll
             for (int tt = 0; tt < TB; ++tt) dxr[tt] = s_dx[cur][tt][lane];
 #pragma unroll
-            for (int tt = 0; tt < TB; ++tt) step(cur, tt, dxr[tt]);
+            for (int tt = 0; tt < TB; ++tt) step(cur, tt, dxr[tt], vb[cur][tt], vc[cur][tt]);
         } else {
-            for (int tt = 0; tt < cnt; ++tt) step(cur, tt, s_dx[cur][tt][lane]);
+#pragma unroll
+            for (int tt = 0; tt < TB; ++tt)
+                if (tt < cnt) step(cur, tt, s_dx[cur][tt][lane], vb[cur][tt], vc[cur][tt]);
         }
 
         // ---- phase C: combine partial readouts, skip term, gate, store ----
@@ -258,7 +215,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
             for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int s = 0; s < S; ++s) yp[j][s] = s_y[cur][s][w * J + j][lane];
-            const auto rY = make_rsrc(block_base(a.y, tb), block_bytes(tb));
+            const auto rY = make_rsrc(block_base(a.y, tb), (uint32_t)cnt * rowb);
 #pragma unroll
             for (int j = 0; j < J; ++j) {
                 float y = 0.f;
@@ -272,11 +229,13 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
         }
     };
 
-    if (nblocks > 0) load_block(0, t0);
-    for (int blk = 0; blk < nblocks; blk += 2) {
+    load_block(0, t0);
+    int blk = 0;
+    for (; blk + 1 < nblocks; blk += 2) {
         do_block(std::integral_constant<int, 0>{}, blk);
-        if (blk + 1 < nblocks) do_block(std::integral_constant<int, 1>{}, blk + 1);
+        do_block(std::integral_constant<int, 1>{}, blk + 1);
     }
+    if (blk < nblocks) do_block(std::integral_constant<int, 0>{}, blk);
 
     if (!dvalid) return;
     if constexpr (SUMMARY) {
@@ -292,13 +251,26 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     }
 }
 
+// Widen B and C to fp32 rows [b][t][B_t row | C_t row] for the DPP delivery.
+// One thread per output float: reads and writes are both contiguous.
+template <bool BF16>
+__global__ void __launch_bounds__(256) bc_prepare(ScanArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = i / (2 * a.N);
+    if (row >= (int64_t)a.batch * a.L) return;
+    const int k = (int)(i - row * 2 * a.N);
+    a.bcw[i] = k < a.N ? ld<BF16>(a.B, row * a.N + k) : ld<BF16>(a.C, row * a.N + k - a.N);
+}
+
 template <int NS, int S, int TB, bool BF16, bool ZOH>
 hipError_t launch_tiles(const Plan& p, const ScanArgs& a, hipStream_t s) {
     const dim3 block(64 * S);
+    hipError_t e = launch_bc_prepare(a, BF16, s);
+    if (e != hipSuccess) return e;
     if (p.chunks > 1) {
         hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, true>),
                            dim3(p.tiles, p.chunks - 1, a.batch), block, 0, s, a);
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_carry(a, s);
         if (e != hipSuccess) return e;
@@ -317,13 +289,13 @@ hipError_t dispatch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
             case 4: return launch_tiles<4, 4, TB, BF16, ZOH>(p, a, s);
             case 8: return launch_tiles<8, 4, TB, BF16, ZOH>(p, a, s);
             case 16: return launch_tiles<16, 4, TB, BF16, ZOH>(p, a, s);
-            case 32: return launch_tiles<32, 4, TB, BF16, ZOH>(p, a, s);
             default: break;
         }
     } else if (p.waves == 8) {
         switch (p.ns) {
             case 2: return launch_tiles<2, 8, TB, BF16, ZOH>(p, a, s);
             case 8: return launch_tiles<8, 8, TB, BF16, ZOH>(p, a, s);
+            case 16: return launch_tiles<16, 8, TB, BF16, ZOH>(p, a, s);
             default: break;
         }
     }
@@ -332,9 +304,19 @@ hipError_t dispatch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s) {
+    const int64_t total = (int64_t)a.batch * a.L * 2 * a.N;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    if (bf16)
+        hipLaunchKernelGGL((bc_prepare<true>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bc_prepare<false>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 bool tile_variant_exists(int ns, int waves) {
-    if (waves == 4) return ns == 2 || ns == 4 || ns == 8 || ns == 16 || ns == 32;
-    if (waves == 8) return ns == 2 || ns == 8;
+    if (waves == 4) return ns == 2 || ns == 4 || ns == 8 || ns == 16;
+    if (waves == 8) return ns == 2 || ns == 8 || ns == 16;
     return false;
 }
 
