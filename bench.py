@@ -5,20 +5,31 @@ One step = one ms_scan_fwd call over one batch of the Mamba-130M-layer
 workload (batch 8, L 2048, d_inner 1536, d_state 16, bf16 io, fp32 state,
 Euler, softplus + bias, z gate and D skip on), inputs resident in HBM.
 Several input/output buffer sets are rotated so that consecutive steps do
-not hit the 256 MB Infinity Cache with the previous step's data.
+not find the previous step's data in the 256 MB Infinity Cache.
 
-Prints ONE JSON line: elements/s (B*L*d_inner per second), the dominant
-kernel's roofline position, and the fp64 CPU oracle timed on this host's
-cores on the same workload.
+Prints ONE JSON line: elements/s (B*L*d_inner per second); the dominant
+kernel's roofline position, from its HIP-event kernel times recorded on the
+launch stream over the timed region (ms_profile_*); the whole call's HBM
+rate against the 8 TB/s peak; a Mamba-3B-layer line item; and the fp64 CPU
+oracle timed on this host's cores on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Profile helpers (used to write the summaries kept under profiles/):
+    python bench.py --steps 3 --warmup 1 --no-cpu --no-secondary --copy-calibration
+        (the command run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
+    python bench.py --rocprof-summary KTRACE_DIR [--fetch DIR --write DIR]
+        (no GPU: reads rocprofv3 CSV output and prints a markdown summary)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +38,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scan elem/s (B·L·D_inner) + achieved HBM GB/s vs peak, 130M & 3B layer shapes"
 HBM_PEAK_GBPS = 8000.0
+# Peak VALU issue of the chip for plain (non-packed) fp32 instructions:
+# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32e12 lane-ops/s (the 157.3
+# TFLOP/s fp32 vector figure counts a packed FMA, 2 lanes x 2 flops, per slot).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+COPY_MIB = 256  # size of the calibration copy (read and written)
+MAIN_KERNEL_RE = r"scan_lane<[^>]*false>|scan_tile<[^>]*false>|scan_chunks<"
+WORKLOAD_TITLE = {"m130m": "Mamba-130M-layer selective scan (S6) forward",
+                  "m3b": "Mamba-3B-layer selective scan (S6) forward"}
 
 
 def parse():
@@ -37,45 +56,49 @@ def parse():
     ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b"])
     ap.add_argument("--buffer-sets", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle sample")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 3B-layer line item")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help=f"also run a {COPY_MIB} MiB device copy (HBM counter calibration)")
+    ap.add_argument("--rocprof-summary", metavar="KTRACE_DIR",
+                    help="summarise rocprofv3 output instead of benchmarking")
+    ap.add_argument("--fetch", metavar="DIR", help="rocprofv3 --pmc FETCH_SIZE output dir")
+    ap.add_argument("--write", metavar="DIR", help="rocprofv3 --pmc WRITE_SIZE output dir")
     return ap.parse_args()
 
 
 def source_hash() -> str:
+    """Hash of everything that decides the kernels' code: sources, header,
+    build flags."""
     h = hashlib.sha256()
-    for f in ("scan_kernels.hip", "api.cpp", "msscan_internal.h"):
-        with open(os.path.join(ROOT, "selective_state_space_81_amd", "csrc", f), "rb") as fh:
+    files = sorted(glob.glob(os.path.join(ROOT, "selective_state_space_81_amd", "csrc", "*")))
+    files += [os.path.join(ROOT, "include", "msscan.h"),
+              os.path.join(ROOT, "selective_state_space_81_amd", "build.py")]
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def time_calls(ms, sets, w, steps, warmup, softplus=True, zoh=False):
-    """Average ms per ms_scan_fwd call, timed with HIP events recorded on the
-    stream the calls are enqueued on (torch's current stream)."""
-    import torch
-    stream = torch.cuda.current_stream()
-    ws_n = ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, ms.MS_BF16 if w.io == "bf16" else ms.MS_F32,
-                              ms.flags(softplus, zoh))
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-
-    def call(i):
-        x, y = sets[i % len(sets)]
-        ms.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
-                    delta_bias=x.get("delta_bias"), softplus=softplus, zoh=zoh, y=y,
-                    workspace=ws if ws_n else None, stream=stream)
-
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        call(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+# ---------------------------------------------------------------- counting --
+def valu_ops_per_element(n_state: int, zoh: bool, softplus: bool = True) -> int:
+    """fp32 VALU operations the method needs per element (b, t, d), counted
+    one per lane-instruction, an FMA as one:
+      per state: dt*A, exp, B*x (Euler x = dt*u), A_bar*h + .., C*h + ..  = 5
+                 ZOH adds (A_bar - 1)/A as one FMA with 1/A kept, and one
+                 more product with B*u                                   = 7
+      per element: delta + bias, softplus (exp, 1 +, log), dt*u (Euler),
+                 D*u + y, silu gate (exp, 1 +, reciprocal, z*r), y*gate.
+    Only the kernel that writes y is priced this way; the segment-summary
+    pass is work the parallel split adds, not work of the method."""
+    per_state = 7 if zoh else 5
+    per_elem = 1 + (3 if softplus else 0) + (0 if zoh else 1) + 1 + 4 + 1
+    return per_state * n_state + per_elem
 
 
+# ----------------------------------------------------------------- timing --
 def make_sets(w, n_sets):
     import torch
     import synth
@@ -87,23 +110,81 @@ def make_sets(w, n_sets):
     return sets
 
 
-def cpu_baseline(w, softplus=True, zoh=False):
-    """fp64 oracle on this host's cores, on the same workload: every channel
-    of batch element 0 over the full sequence (1/batch of the job), compute
-    time only, scaled to elements per second."""
-    import numpy as np
+def time_calls(ms, sets, w, steps, warmup, zoh=False):
+    """Two timed regions of `steps` ms_scan_fwd calls each, on the stream the
+    calls are enqueued on (torch's current stream):
+      1. plain calls, bracketed by torch events -> ms per call (the value);
+      2. the same calls with the library's kernel timing on (ms_profile_*):
+         HIP events recorded on that stream around each kernel launch give the
+         per-phase kernel times.  The event records add gaps between kernels,
+         so region 2 is not used for the per-call time."""
     import torch
+    stream = torch.cuda.current_stream()
+    io = ms.MS_BF16 if w.io == "bf16" else ms.MS_F32
+    ws_n = ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, io, ms.flags(w.softplus, zoh))
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        x, y = sets[i % len(sets)]
+        ms.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                    delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh, y=y,
+                    workspace=ws if ws_n else None, stream=stream)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_ms = start.elapsed_time(end) / steps
+    ms.profile_begin(steps)
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    phases = ms.profile_end()
+    return t_ms, phases
+
+
+def copy_calibration(reps=3):
+    """A plain device copy of COPY_MIB MiB (one read and one write of every
+    byte), so that a counter run can scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = COPY_MIB * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+# ------------------------------------------------------------ CPU oracle --
+def cpu_baseline(w, min_seconds):
+    """fp64 oracle on this host's cores on the same workload, compute time
+    only: whole batch rows (all channels, full sequence) are scanned one after
+    another, cycling over the batch, until at least min_seconds have passed."""
+    import numpy as np
     import oracle
     import synth
     x = synth.scan_inputs(w, device="cpu", seed=0)
-    sub = {k: (v[:1] if k in ("u", "delta", "z", "B", "C") else v) for k, v in x.items()}
-    f64 = {k: np.ascontiguousarray(v.double().numpy()) for k, v in sub.items()}
     threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.scan(f64["u"], f64["delta"], f64["A"], f64["B"], f64["C"], D=f64["D"], z=f64["z"],
-                delta_bias=f64.get("delta_bias"), softplus=softplus, zoh=zoh, nthreads=threads)
-    dt = time.perf_counter() - t0
-    elems = 1 * w.L * w.Dn
+    shared = {k: np.ascontiguousarray(x[k].double().numpy()) for k in ("A", "D", "delta_bias")
+              if x.get(k) is not None}
+    rows, elapsed, b = 0, 0.0, 0
+    while elapsed < min_seconds and rows < 64 * w.batch:
+        f = {k: np.ascontiguousarray(x[k][b:b + 1].double().numpy())
+             for k in ("u", "delta", "z", "B", "C")}
+        t0 = time.perf_counter()
+        oracle.scan(f["u"], f["delta"], shared["A"], f["B"], f["C"], D=shared.get("D"), z=f["z"],
+                    delta_bias=shared.get("delta_bias"), softplus=w.softplus, zoh=False,
+                    nthreads=threads)
+        elapsed += time.perf_counter() - t0
+        rows += 1
+        b = (b + 1) % w.batch
+    elems = rows * w.L * w.Dn
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -113,32 +194,117 @@ def cpu_baseline(w, softplus=True, zoh=False):
                     break
     except OSError:
         pass
-    return {"value": elems / dt, "unit": "elem/s", "cores": threads, "kind": "oracle",
-            "sample": f"batch element 0 of {w.batch} (all {w.Dn} channels, full L={w.L}); "
-                      f"fp64 C oracle, OpenMP over channels; {dt:.2f} s compute; host CPU: {cpu}"}
+    return {"value": elems / elapsed, "unit": "elem/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} batch rows of the {w.name} workload (each: all {w.Dn} channels "
+                      f"x L={w.L}, d_state {w.N}, Euler, softplus, z gate, D), cycling over "
+                      f"its {w.batch} rows; fp64 C oracle, OpenMP over channels, "
+                      f"{threads} threads; {elapsed:.1f} s compute; host CPU: {cpu}"}
 
 
+# --------------------------------------------------------- traffic record --
 def load_traffic(w_name: str, src: str):
-    """HBM bytes per call from rocprofv3 FETCH_SIZE/WRITE_SIZE runs recorded
-    in profiles/, if they were taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{w_name}.json")
+    """HBM bytes per launch of the dominant kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary in profiles/, if it was taken on the
+    current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"hbm_traffic_scan_main_{w_name}.md")
     if not os.path.exists(p):
         return None
-    try:
-        with open(p) as fh:
-            rec = json.load(fh)
-        if rec.get("source_hash") != src:
-            return None
-        return rec.get("bytes_per_call")
-    except (OSError, ValueError):
+    fields = {}
+    with open(p) as fh:
+        for line in fh:
+            m = re.match(r"^- (\w+): `?([^`\s]+)`?", line.strip())
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("source_hash") != src:
         return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------- rocprof tools --
+def _csv(dirname, suffix):
+    hits = sorted(glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {dirname}")
+    with open(hits[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name):
+    m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|scan_chunks<[^>]*>|scan_summary<[^>]*>|"
+                  r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|neg_kernel)", name)
+    return m.group(1) if m else name[:60]
+
+
+def _pmc_per_dispatch(dirname, counter):
+    """Mean counter value (KiB) per dispatch, by short kernel name."""
+    acc = {}
+    for r in _csv(dirname, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        k = _short(r["Kernel_Name"])
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def rocprof_summary(args):
+    rows = _csv(args.rocprof_summary, "kernel_stats.csv")
+    print("| kernel | calls | average us | min us | max us |")
+    print("|---|---|---|---|---|")
+    for r in rows:
+        n = r["Name"]
+        if "msscan" not in n:
+            continue
+        print(f"| `{_short(n)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    if args.fetch and args.write:
+        fetch = _pmc_per_dispatch(args.fetch, "FETCH_SIZE")
+        write = _pmc_per_dispatch(args.write, "WRITE_SIZE")
+        copy_kib = COPY_MIB * 1024.0
+        cf = [v for k, v in fetch.items() if k == "neg_kernel"]
+        cw = [v for k, v in write.items() if k == "neg_kernel"]
+        if not cf or not cw:
+            raise SystemExit("calibration copy (neg_kernel) not found in the counter runs")
+        f_fetch, f_write = copy_kib / cf[0], copy_kib / cw[0]
+        print()
+        print(f"- copy_fetch_kib: {cf[0]:.0f} (expected {copy_kib:.0f}; factor {f_fetch:.4f})")
+        print(f"- copy_write_kib: {cw[0]:.0f} (expected {copy_kib:.0f}; factor {f_write:.4f})")
+        print()
+        print("| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled MB/dispatch |")
+        print("|---|---|---|---|")
+        main = None
+        for k in sorted(fetch):
+            if k == "neg_kernel" or k not in write or not re.search(r"scan_|carry_|bc_prep|state_step", k):
+                continue
+            mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
+            print(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {mb:.2f} |")
+            if re.search(MAIN_KERNEL_RE, k):
+                main = (fetch[k] * f_fetch + write[k] * f_write) * 1024
+        if main is not None:
+            print()
+            print(f"- traffic_bytes_per_launch: {main:.0f}")
+
+
+# ------------------------------------------------------------------ main --
+def measure(ms, w_name, steps, warmup, n_sets, zoh=False):
+    import synth
+    w = synth.workload(w_name)
+    sets = make_sets(w, n_sets)
+    t_ms, ph = time_calls(ms, sets, w, steps, warmup, zoh=zoh)
+    del sets
+    return w, t_ms, ph
 
 
 def main():
     args = parse()
+    if args.rocprof_summary:
+        rocprof_summary(args)
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); "
-              f"got --gpus {args.gpus}", file=sys.stderr)
+        print(f"bench.py measures one GPU only: this scan has no multi-GPU path "
+              f"(got --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
     import selective_state_space_81_amd as ms
@@ -147,14 +313,17 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     ms.load()
-    w = synth.workload(args.workload)
-    sets = make_sets(w, args.buffer_sets)
-    t_ms = time_calls(ms, sets, w, args.steps, args.warmup)
+    if args.copy_calibration:
+        copy_calibration()
+    w, t_ms, ph = measure(ms, args.workload, args.steps, args.warmup, args.buffer_sets)
+    torch.cuda.empty_cache()
     elems = w.batch * w.L * w.Dn
     alg_bytes = synth.algorithmic_bytes(w)
-    gbps = alg_bytes / (t_ms * 1e-3) / 1e9
+    main_ms = ph["main"]["mean_ms"]
+    ops = valu_ops_per_element(w.N, zoh=False, softplus=w.softplus) * elems
+    achieved = ops / (main_ms * 1e-3) / 1e12
     src = source_hash()
-    traffic = load_traffic(args.workload, src)
+    gbps = alg_bytes / (t_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": elems / (t_ms * 1e-3),
@@ -168,33 +337,38 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{'Mamba-130M' if w.name == 'm130m' else 'Mamba-3B'}-layer "
-                               f"selective scan (S6) forward",
+        "config": {"workload": WORKLOAD_TITLE[w.name],
                    "batch": w.batch, "seq_len": w.L, "d_inner": w.Dn, "d_state": w.N,
-                   "io": w.io, "state": "fp32", "discretisation": "euler",
-                   "softplus_bias": True, "z_gate": True, "D_skip": True,
+                   "io": w.io, "state": "f32", "discretisation": "euler",
+                   "softplus_bias": w.softplus, "z_gate": True, "D_skip": True,
                    "buffer_sets": args.buffer_sets, "parallelism": "single-gpu"},
-        "hbm_gbps": gbps,
-        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "ms_scan_fwd call (all passes)",
-                     "algorithmic_bytes_per_call": alg_bytes},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS,
+                     "unit": "TOP/s", "frac": achieved / VALU_PEAK_TOPS,
+                     "traffic": load_traffic(w.name, src),
+                     "kernel": "scan main pass (writes y)",
+                     "kernel_mean_ms": main_ms,
+                     "ops_per_element": valu_ops_per_element(w.N, zoh=False,
+                                                             softplus=w.softplus),
+                     "ops_per_launch": ops,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS, "scope": "whole ms_scan_fwd call",
+                "algorithmic_bytes_per_call": alg_bytes},
+        "kernels_ms": {k: v["mean_ms"] for k, v in ph.items() if k != "calls" and v["launches"]},
         "source_hash": src,
     }
-    del sets
-    torch.cuda.empty_cache()
     if not args.no_secondary and args.workload == "m130m":
-        w3 = synth.workload("m3b")
-        s3 = make_sets(w3, 2)
-        t3 = time_calls(ms, s3, w3, max(3, args.steps // 4), 2)
+        w3, t3, ph3 = measure(ms, "m3b", max(3, args.steps // 4), 2, 2)
         e3 = w3.batch * w3.L * w3.Dn
-        out["secondary"] = {"workload": "Mamba-3B-layer (B4 L8192 D5120 N16 bf16, euler)",
+        out["secondary"] = {"workload": WORKLOAD_TITLE["m3b"] + " (B4 L8192 D5120 N16 bf16, "
+                                                                 "Euler)",
                             "ms_per_call": t3, "elem_per_s": e3 / (t3 * 1e-3),
-                            "hbm_gbps": synth.algorithmic_bytes(w3) / (t3 * 1e-3) / 1e9}
-        del s3
+                            "hbm_gbps": synth.algorithmic_bytes(w3) / (t3 * 1e-3) / 1e9,
+                            "kernels_ms": {k: v["mean_ms"] for k, v in ph3.items()
+                                           if k != "calls" and v["launches"]}}
         torch.cuda.empty_cache()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -89,9 +89,9 @@ typedef struct {
 } ms_dims;
 
 /*
- * Bytes of device workspace ms_scan_fwd needs for these dims and flags
- * (0 when the sequence is scanned in one piece).  Returns (size_t)-1 when the
- * dims are invalid.  Pure function of its arguments; no device call.
+ * Bytes of device workspace ms_scan_fwd needs for these dims and flags (may
+ * be 0).  Returns (size_t)-1 when the dims or flags are invalid.  Pure
+ * function of its arguments; no device call.
  */
 size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags);
 
@@ -145,6 +145,49 @@ const char* ms_last_error(void);
 
 /* MS_ABI_VERSION of the loaded library. */
 int ms_abi_version(void);
+
+/*
+ * Kernel timing, for benchmarks and profiling (not an operation of the
+ * method).  Between ms_profile_begin and ms_profile_end, each of the next
+ * `max_calls` successful calls of ms_scan_fwd / ms_state_update records a
+ * pair of HIP events on its own stream around every kernel it launches, and
+ * ms_profile_end waits for those events and returns the summed kernel times
+ * per phase:
+ *   MS_PHASE_PREP     B/C staging pass
+ *   MS_PHASE_SUMMARY  per-segment end states (sequence cut into segments)
+ *   MS_PHASE_CARRY    composition of segment summaries into start states
+ *   MS_PHASE_MAIN     the scan that writes y (and h_last)
+ *   MS_PHASE_STEP     ms_state_update's kernel
+ * A phase a call does not need records nothing.  Calls after the first
+ * max_calls are not timed (out->calls counts the timed ones).  The event
+ * records add a few microseconds per kernel to a call's wall time.
+ *
+ * ms_profile_begin: max_calls in [1, 4096]; creates the events on the current
+ *   device (MS_ERR_SHAPE for a bad count, MS_ERR_HIP on event creation
+ *   failure, MS_ERR_UNSUPPORTED when a profile is already open).
+ * ms_profile_end: out may be NULL (results dropped).  Synchronises on the
+ *   recorded events (blocks the host until they complete), frees them and
+ *   closes the profile.  MS_ERR_UNSUPPORTED when no profile is open.
+ * The profile is process-wide: open it, run the calls, close it from one
+ * host thread.
+ */
+typedef enum {
+    MS_PHASE_PREP = 0,
+    MS_PHASE_SUMMARY = 1,
+    MS_PHASE_CARRY = 2,
+    MS_PHASE_MAIN = 3,
+    MS_PHASE_STEP = 4,
+    MS_PHASE_COUNT = 5
+} ms_phase;
+
+typedef struct {
+    int32_t calls;                     /* calls timed                     */
+    int32_t launches[MS_PHASE_COUNT];  /* kernel launches timed per phase */
+    double total_ms[MS_PHASE_COUNT];   /* summed kernel time per phase    */
+} ms_profile;
+
+ms_status ms_profile_begin(int32_t max_calls);
+ms_status ms_profile_end(ms_profile* out);
 
 #ifdef __cplusplus
 }

@@ -26,13 +26,20 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
           7: "MS_ERR_UNSUPPORTED", 8: "MS_ERR_HIP"}
 
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
-           "ms_last_error", "ms_abi_version")
+           "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end")
+
+PHASES = ("prep", "summary", "carry", "main", "step")  # ms_phase order
 
 
 class MsDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int64),
                 ("d_inner", ctypes.c_int32), ("d_state", ctypes.c_int32),
                 ("io", ctypes.c_int32)]
+
+
+class MsProfile(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int32), ("launches", ctypes.c_int32 * len(PHASES)),
+                ("total_ms", ctypes.c_double * len(PHASES))]
 
 
 class MsError(RuntimeError):
@@ -70,6 +77,10 @@ def load(path: Optional[str] = None):
     lib.ms_last_error.argtypes = []
     lib.ms_abi_version.restype = ctypes.c_int
     lib.ms_abi_version.argtypes = []
+    lib.ms_profile_begin.restype = ctypes.c_int
+    lib.ms_profile_begin.argtypes = [i32]
+    lib.ms_profile_end.restype = ctypes.c_int
+    lib.ms_profile_end.argtypes = [ctypes.POINTER(MsProfile)]
     if path is None:
         _lib = lib
     return lib
@@ -160,3 +171,24 @@ def state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None
                                 _stream(stream))
     _check(rc)
     return y_t
+
+
+def profile_begin(max_calls: int) -> None:
+    """ms_profile_begin: time the kernels of the next max_calls calls."""
+    rc = load().ms_profile_begin(max_calls)
+    if rc != MS_OK:
+        raise MsError(rc, "ms_profile_begin failed")
+
+
+def profile_end() -> dict:
+    """ms_profile_end: wait for the recorded events and return, per phase,
+    the number of timed launches and their mean kernel time in ms."""
+    out = MsProfile()
+    rc = load().ms_profile_end(ctypes.byref(out))
+    if rc != MS_OK:
+        raise MsError(rc, "ms_profile_end failed")
+    res = {"calls": out.calls}
+    for i, name in enumerate(PHASES):
+        n = out.launches[i]
+        res[name] = {"launches": n, "mean_ms": (out.total_ms[i] / n) if n else None}
+    return res

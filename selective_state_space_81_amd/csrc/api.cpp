@@ -67,7 +67,7 @@ ms_status check_flags(uint32_t flags) {
 #define MSSCAN_TILE_WAVES 4
 #endif
 #ifndef MSSCAN_TARGET_WAVES
-#define MSSCAN_TARGET_WAVES 3072
+#define MSSCAN_TARGET_WAVES 8192
 #endif
 #ifndef MSSCAN_LANE_PATH
 #define MSSCAN_LANE_PATH 1
@@ -75,7 +75,10 @@ ms_status check_flags(uint32_t flags) {
 constexpr int kTileWaves = MSSCAN_TILE_WAVES;
 constexpr int64_t kTargetWaves2 = MSSCAN_TARGET_WAVES;
 constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
-constexpr int64_t kMinSegment = 128;
+#ifndef MSSCAN_MIN_SEGMENT
+#define MSSCAN_MIN_SEGMENT 128
+#endif
+constexpr int64_t kMinSegment = MSSCAN_MIN_SEGMENT;
 
 void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) {
     int64_t k = (kTargetWaves2 + waves_per_segment - 1) / waves_per_segment;
@@ -230,6 +233,7 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
     }
     const bool bf16 = dims->io == MS_BF16, zoh = (flags & MS_ZOH) != 0;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    msscan::prof_call();
     hipError_t e = p.tile_path == 2   ? msscan::launch_scan_lanes(p, a, bf16, zoh, hs)
                    : p.tile_path == 1 ? msscan::launch_scan_tiles(p, a, bf16, zoh, hs)
                                       : msscan::launch_scan(p, a, bf16, zoh, hs);
@@ -255,6 +259,7 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
     a.h = h; a.x = x_t; a.delta = delta_t; a.A = A; a.B = B_t; a.C = C_t; a.D = D; a.z = z_t;
     a.bias = delta_bias; a.y = y_t; a.batch = batch; a.Dn = d_inner; a.N = d_state;
     a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    msscan::prof_call();
     hipError_t e = msscan::launch_step(a, io == MS_BF16, (flags & MS_ZOH) != 0,
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -77,4 +77,20 @@ bool lane_variant_exists(int n);
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
 
+// Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
+// ProfScope records the phase's begin event at construction and its end
+// event at destruction, around one kernel launch.  Both do nothing unless a
+// profile is open.  Phase numbers are the ms_phase values of msscan.h.
+void prof_call();
+void prof_mark(hipStream_t s, int phase, int edge);
+enum : int { kPhasePrep = 0, kPhaseSummary = 1, kPhaseCarry = 2, kPhaseMain = 3, kPhaseStep = 4 };
+struct ProfScope {
+    hipStream_t s;
+    int phase;
+    ProfScope(hipStream_t s_, int phase_) : s(s_), phase(phase_) { prof_mark(s, phase, 0); }
+    ~ProfScope() { prof_mark(s, phase, 1); }
+    ProfScope(const ProfScope&) = delete;
+    ProfScope& operator=(const ProfScope&) = delete;
+};
+
 }  // namespace msscan

@@ -139,12 +139,29 @@ __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
     const float A2 = a.A[(int64_t)d * a.N + n] * kLog2e;
     float h = a.h0 ? a.h0[((int64_t)b * a.Dn + d) * a.N + n] : 0.f;
     const int km1 = a.chunks - 1;
-    for (int c = 0; c < km1; ++c) {
-        const int64_t base = (int64_t)b * km1 + c;
-        const float decay = hw_exp2(A2 * a.sdt[base * a.Dn + d]);
-        const int64_t i = (base * a.N + n) * a.Dn + d;
-        h = fmaf(decay, h, a.agg[i]);
-        a.agg[i] = h;
+    // Loads of a group are issued before its stores so that the chain waits
+    // on memory once per group, not once per chunk.
+    constexpr int G = 8;
+    for (int c0 = 0; c0 < km1; c0 += G) {
+        float s[G], g[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            s[j] = 0.f;
+            g[j] = 0.f;
+            if (c0 + j < km1) {
+                const int64_t base = (int64_t)b * km1 + c0 + j;
+                s[j] = a.sdt[base * a.Dn + d];
+                g[j] = a.agg[(base * a.N + n) * a.Dn + d];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (c0 + j < km1) {
+                const int64_t base = (int64_t)b * km1 + c0 + j;
+                h = fmaf(hw_exp2(A2 * s[j]), h, g[j]);
+                a.agg[(base * a.N + n) * a.Dn + d] = h;
+            }
+        }
     }
 }
 
@@ -264,13 +281,17 @@ template <int NS, bool BF16, bool ZOH>
 hipError_t launch_ns(const Plan& p, const ScanArgs& a, hipStream_t s) {
     const dim3 block(64 * p.waves);
     if (p.chunks > 1) {
-        hipLaunchKernelGGL((scan_summary<NS, BF16, ZOH>), dim3(p.chunks - 1, p.tiles, a.batch),
-                           block, 0, s, a);
+        {
+            ProfScope ps(s, kPhaseSummary);
+            hipLaunchKernelGGL((scan_summary<NS, BF16, ZOH>), dim3(p.chunks - 1, p.tiles, a.batch),
+                               block, 0, s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_carry(a, s);
         if (e != hipSuccess) return e;
     }
+    ProfScope ps(s, kPhaseMain);
     if (p.waves > 1) {
         if constexpr (NS == 32)
             hipLaunchKernelGGL((scan_chunks<NS, BF16, ZOH, true>),
@@ -304,12 +325,14 @@ hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hi
 
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
     const int64_t total = (int64_t)a.batch * a.N * a.Dn;
+    ProfScope ps(s, kPhaseCarry);
     hipLaunchKernelGGL(carry_propagate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s) {
     const dim3 grid((a.Dn + 255) / 256, a.batch), block(256);
+    ProfScope ps(s, kPhaseStep);
     if (bf16) {
         if (zoh) hipLaunchKernelGGL((state_step<true, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((state_step<true, false>), grid, block, 0, s, a);

@@ -37,8 +37,18 @@ namespace {
 
 using namespace dev;
 
-template <int N, int TB, bool BF16, bool ZOH, bool SUMMARY>
-__global__ void __launch_bounds__(64) scan_lane(ScanArgs a) {
+#ifndef MSSCAN_LANE_TB
+#define MSSCAN_LANE_TB 8
+#endif
+#ifndef MSSCAN_LANE_DB
+#define MSSCAN_LANE_DB 1
+#endif
+#ifndef MSSCAN_LANE_WPE
+#define MSSCAN_LANE_WPE 1
+#endif
+
+template <int N, int TB, bool DB, bool BF16, bool ZOH, bool SP, bool SUMMARY>
+__global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     static_assert(N == 8 || N == 16, "one DPP row holds the states of a lane");
     using R = Io<BF16>;
     using RT = typename R::T;
@@ -73,27 +83,27 @@ __global__ void __launch_bounds__(64) scan_lane(ScanArgs a) {
     const float bias = a.bias ? a.bias[dd] : 0.f;
     const float Dd = a.D ? a.D[dd] : 0.f;
     const bool has_z = a.z != nullptr;
-    const bool use_sp = a.softplus != 0;
 
     const int64_t t0 = (int64_t)seg * a.chunk_len;
     const int64_t t1 = min(a.L, t0 + a.chunk_len);
-    const int nblocks = (int)((t1 - t0 + TB - 1) / TB);
     const int64_t row0 = (int64_t)b * a.L;
 
     const uint32_t rowb = (uint32_t)a.Dn * R::kSize;
     const uint32_t off0 = dvalid ? (uint32_t)d * R::kSize : kOutOfRange;
     auto block_rows = [&](int64_t tb) -> uint32_t {
         return (uint32_t)max((int64_t)0, min((int64_t)TB, t1 - tb));
-    };
+    };  // rows of a block inside this segment (the prefetch past its end gets 0)
     auto block_base = [&](const void* p, int64_t tb) -> const void* {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)rowb;
     };
     constexpr uint32_t kBCRow = 2u * N * 4u;
     const uint32_t bcoff = (uint32_t)(lane & (N - 1)) * 4u;
 
-    // Register double buffer of one block's raw inputs.
-    RT ru[2][TB], rd[2][TB], rz[2][TB];
-    float vb[2][TB], vc[2][TB];
+    // Register buffers of one block's raw inputs (two when the next block is
+    // prefetched while this one is computed).
+    constexpr int NB = DB ? 2 : 1;
+    RT ru[NB][TB], rd[NB][TB], rz[NB][TB];
+    float vb[NB][TB], vc[NB][TB];
     auto load_block = [&](int buf, int64_t tb) {
         const uint32_t nr = block_rows(tb);
         const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
@@ -120,7 +130,7 @@ __global__ void __launch_bounds__(64) scan_lane(ScanArgs a) {
     auto step = [&](RT raw_u, RT raw_d, RT raw_z, float vbt, float vct, float& y_out) {
         const float uv = R::widen(raw_u);
         const float v = R::widen(raw_d) + bias;
-        const float dt = use_sp ? softplus_f(v) : v;
+        const float dt = SP ? softplus_f(v) : v;  // compile-time: no branch per step
         const float xv = ZOH ? uv : dt * uv;
         static_for(
             [&](auto nc) {
@@ -149,38 +159,55 @@ __global__ void __launch_bounds__(64) scan_lane(ScanArgs a) {
         }
     };
 
+    // A full block of TB timesteps, straight-line code.  The ragged end of
+    // the last segment is left to a one-step loop below: a shared body with a
+    // per-step guard would make every step a branch target and cost a copy of
+    // every state per step.
     auto do_block = [&](auto cur_c, int blk) {
         constexpr int cur = decltype(cur_c)::value;
         const int64_t tb = t0 + (int64_t)blk * TB;
-        const int cnt = (int)min((int64_t)TB, t1 - tb);
-        load_block(cur ^ 1, tb + TB);  // past the end it reads zeros
-        const auto rY = make_rsrc(block_base(a.y, tb), (uint32_t)cnt * rowb);
-        if (cnt == TB) {
+        if constexpr (DB)
+            load_block(cur ^ 1, tb + TB);  // past the end it reads zeros
+        else
+            load_block(cur, tb);
+        const auto rY = make_rsrc(block_base(a.y, tb), (uint32_t)TB * rowb);
 #pragma unroll
-            for (int tt = 0; tt < TB; ++tt) {
-                float y = 0.f;
-                step(ru[cur][tt], rd[cur][tt], rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
-                if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
-            }
-        } else {
-#pragma unroll
-            for (int tt = 0; tt < TB; ++tt) {
-                if (tt < cnt) {
-                    float y = 0.f;
-                    step(ru[cur][tt], rd[cur][tt], rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
-                    if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
-                }
-            }
+        for (int tt = 0; tt < TB; ++tt) {
+            float y = 0.f;
+            step(ru[cur][tt], rd[cur][tt], rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
+            if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
         }
     };
 
-    load_block(0, t0);
+    const int nfull = (int)((t1 - t0) / TB);
     int blk = 0;
-    for (; blk + 1 < nblocks; blk += 2) {
-        do_block(std::integral_constant<int, 0>{}, blk);
-        do_block(std::integral_constant<int, 1>{}, blk + 1);
+    if constexpr (DB) {
+        load_block(0, t0);
+        for (; blk + 1 < nfull; blk += 2) {
+            do_block(std::integral_constant<int, 0>{}, blk);
+            do_block(std::integral_constant<int, 1>{}, blk + 1);
+        }
+        if (blk < nfull) do_block(std::integral_constant<int, 0>{}, blk);
+    } else {
+        for (; blk < nfull; ++blk) do_block(std::integral_constant<int, 0>{}, blk);
     }
-    if (blk < nblocks) do_block(std::integral_constant<int, 0>{}, blk);
+    // Ragged end (only the last segment can have one): one timestep at a time.
+    for (int64_t t = t0 + (int64_t)nfull * TB; t < t1; ++t) {
+        const auto rU = make_rsrc(block_base(a.u, t), rowb);
+        const auto rD = make_rsrc(block_base(a.delta, t), rowb);
+        const auto rZ = make_rsrc(has_z ? block_base(a.z, t) : a.u, has_z ? rowb : 0u);
+        const auto rBC = make_rsrc(a.bcw + (row0 + t) * (2 * N), kBCRow);
+        const RT xu = R::load(rU, off0);
+        const RT xd = R::load(rD, off0);
+        const RT xz = SUMMARY ? RT{} : R::load(rZ, off0);
+        const float xb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rBC, bcoff, 0, 0));
+        const float xc = SUMMARY ? 0.f
+                                 : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                       rBC, (uint32_t)N * 4u + bcoff, 0, 0));
+        float y = 0.f;
+        step(xu, xd, xz, xb, xc, y);
+        if constexpr (!SUMMARY) R::store(make_rsrc(block_base(a.y, t), rowb), off0, y);
+    }
 
     if (!dvalid) return;
     if constexpr (SUMMARY) {
@@ -196,31 +223,43 @@ __global__ void __launch_bounds__(64) scan_lane(ScanArgs a) {
     }
 }
 
-template <int N, bool BF16, bool ZOH>
+template <int N, bool BF16, bool ZOH, bool SP>
 hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    constexpr int TB = 8;
+    constexpr int TB = MSSCAN_LANE_TB;
+    constexpr bool DB = MSSCAN_LANE_DB != 0;
     hipError_t e = launch_bc_prepare(a, BF16, s);
     if (e != hipSuccess) return e;
     if (p.chunks > 1) {
-        hipLaunchKernelGGL((scan_lane<N, TB, BF16, ZOH, true>),
-                           dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
+        {
+            ProfScope ps(s, kPhaseSummary);
+            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, ZOH, SP, true>),
+                               dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_carry(a, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((scan_lane<N, TB, BF16, ZOH, false>), dim3(p.tiles, p.chunks, a.batch),
-                       dim3(64), 0, s, a);
+    {
+        ProfScope ps(s, kPhaseMain);
+        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, ZOH, SP, false>),
+                           dim3(p.tiles, p.chunks, a.batch), dim3(64), 0, s, a);
+    }
     return hipGetLastError();
+}
+
+template <bool BF16, bool ZOH, bool SP>
+hipError_t dispatch_n(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    switch (p.ns) {
+        case 8: return launch_lanes<8, BF16, ZOH, SP>(p, a, s);
+        case 16: return launch_lanes<16, BF16, ZOH, SP>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool BF16, bool ZOH>
 hipError_t dispatch(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    switch (p.ns) {
-        case 8: return launch_lanes<8, BF16, ZOH>(p, a, s);
-        case 16: return launch_lanes<16, BF16, ZOH>(p, a, s);
-        default: return hipErrorInvalidValue;
-    }
+    return a.softplus ? dispatch_n<BF16, ZOH, true>(p, a, s) : dispatch_n<BF16, ZOH, false>(p, a, s);
 }
 
 }  // namespace

@@ -268,15 +268,21 @@ hipError_t launch_tiles(const Plan& p, const ScanArgs& a, hipStream_t s) {
     hipError_t e = launch_bc_prepare(a, BF16, s);
     if (e != hipSuccess) return e;
     if (p.chunks > 1) {
-        hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, true>),
-                           dim3(p.tiles, p.chunks - 1, a.batch), block, 0, s, a);
+        {
+            ProfScope ps(s, kPhaseSummary);
+            hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, true>),
+                               dim3(p.tiles, p.chunks - 1, a.batch), block, 0, s, a);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_carry(a, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, false>), dim3(p.tiles, p.chunks, a.batch),
-                       block, 0, s, a);
+    {
+        ProfScope ps(s, kPhaseMain);
+        hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, false>),
+                           dim3(p.tiles, p.chunks, a.batch), block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -307,6 +313,7 @@ hipError_t dispatch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s) {
     const int64_t total = (int64_t)a.batch * a.L * 2 * a.N;
     const dim3 grid((unsigned)((total + 255) / 256));
+    ProfScope ps(s, kPhasePrep);
     if (bf16)
         hipLaunchKernelGGL((bc_prepare<true>), grid, dim3(256), 0, s, a);
     else

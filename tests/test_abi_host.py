@@ -85,3 +85,11 @@ def test_workspace_size_function():
     assert a % 256 == 0 and a > 0
     # Odd d_state takes the generic kernels, which also size their workspace.
     assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 65536, 256, 17, 1)), 1) > 0
+
+
+def test_profile_errors_without_gpu_work():
+    lib = ms.load()
+    assert lib.ms_profile_end(None) == 7  # MS_ERR_UNSUPPORTED: no profile open
+    assert lib.ms_profile_begin(0) == 2  # MS_ERR_SHAPE
+    assert lib.ms_profile_begin(4097) == 2
+    assert ms.PHASES == ("prep", "summary", "carry", "main", "step")
