@@ -127,8 +127,9 @@ msscan::Plan make_plan(const ms_dims& d) {
             const size_t km1 = (size_t)(p.chunks - 1);
             p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
         }
-        // fp32 copy of B and C, rows [b][t][B_t | C_t], read as DPP operands.
-        p.bc_floats = (size_t)d.batch * (size_t)d.seqlen * 2 * (size_t)N;
+        // tile path: fp32 copy of B and C, rows [b][t][B_t | C_t], read as DPP
+        // operands (the lane path reads B and C in place).
+        if (p.tile_path == 1) p.bc_floats = (size_t)d.batch * (size_t)d.seqlen * 2 * (size_t)N;
         return p;
     }
     p.tile_path = 0;

@@ -62,14 +62,30 @@ __device__ __forceinline__ float step_size(float draw, float bias, int softplus)
     return softplus ? softplus_f(v) : v;
 }
 
-// ZOH input factor expm1(x)/A with x = dt*A.  For |x| < 1/16 the series
-// dt*(1 + x/2 + x^2/6 + x^3/24 + x^4/120) (relative error < 2e-9) avoids the
-// cancellation of exp(x) - 1; it is also the A == 0 limit dt.  Otherwise
-// (abar - 1) * (1/A), where abar = exp(x) is already computed.
-__device__ __forceinline__ float zoh_factor(float dt, float x, float abar, float invA) {
-    float ser = dt * (1.f + x * (0.5f + x * (1.f / 6.f + x * (1.f / 24.f + x * (1.f / 120.f)))));
-    float big = (abar - 1.f) * invA;
-    return fabsf(x) < 0.0625f ? ser : big;
+// ZOH input factor (exp(x) - 1)/A for x = dt*A, from t = x*log2(e) (the
+// argument already formed for abar = 2^t).  For |x| < 1/32 the series
+// dt*(1 + x/2 + x^2/6), written in t, avoids the cancellation of exp(x) - 1
+// (truncation < 1.3e-6 relative) and is the A == 0 limit dt.  Otherwise
+// abar*(1/A) - 1/A as one fma: only the rounding of abar is left, < 2e-6
+// relative at the switch point.
+constexpr float kZohT1 = 0.34657359027997264f;  // ln2 / 2
+constexpr float kZohT2 = 0.08007550231970023f;  // ln2^2 / 6
+constexpr float kZohSwitch = 0.045084220027780106f;  // (1/32) / ln2
+__device__ __forceinline__ float zoh_factor(float dt, float t, float abar, float invA) {
+    const float ser = dt * fmaf(t, fmaf(t, kZohT2, kZohT1), 1.f);
+    const float big = fmaf(abar, invA, -invA);
+    return fabsf(t) < kZohSwitch ? ser : big;
+}
+
+// The same factor with the series expanded in powers of dt, for kernels that
+// evaluate many states per dt:  dt + (c1 dt^2) a + (c2 dt^3) a^2  with
+// a = A*log2(e), q1 = c1*dt^2 and q2 = c2*dt^3 formed once per timestep and
+// a^2 once per channel (two fma per state instead of three operations).
+__device__ __forceinline__ float zoh_factor_q(float dt, float q1, float q2, float a, float a_sq,
+                                              float t, float abar, float invA) {
+    const float ser = fmaf(q2, a_sq, fmaf(q1, a, dt));
+    const float big = fmaf(abar, invA, -invA);
+    return fabsf(t) < kZohSwitch ? ser : big;
 }
 
 }  // namespace dev

@@ -69,7 +69,7 @@ __device__ __forceinline__ float advance(float (&h)[NS], const float (&A2)[NS],
         const float abar = hw_exp2(arg);
         float bx;
         if constexpr (ZOH)
-            bx = zoh_factor(dt, arg * kLn2, abar, invA[j]) * (bn * uval);
+            bx = zoh_factor(dt, arg, abar, invA[j]) * (bn * uval);
         else
             bx = x * bn;
         h[j] = fmaf(abar, h[j], bx);
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(256) state_step(StepArgs a) {
         const float bn = ld<BF16>(a.B, brow + n);
         float bx;
         if constexpr (ZOH)
-            bx = zoh_factor(dt, arg * kLn2, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
+            bx = zoh_factor(dt, arg, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
         else
             bx = dx * bn;
         const float hn = fmaf(abar, hrow[n], bx);

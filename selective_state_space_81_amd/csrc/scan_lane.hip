@@ -17,11 +17,11 @@
 // in order -- the scan is a composition of affine maps (jsqmd page,
 // section 3.4).
 //
-// B_t and C_t (shared by all channels, lmnt page section 3.2) come from the
-// fp32 rows [b][t][B | C] written by the B/C prepass: lane l loads state
-// (l mod 16) and the DPP row_newbcast control hands state n to every lane as
-// the first operand of v_mul / v_fmac, so the broadcast costs no extra
-// instruction, no LDS traffic and no SGPRs.
+// B_t and C_t (shared by all channels, lmnt page section 3.2) are read from
+// the caller's [batch][L][d_state] tensors: lane l loads state (l mod N) and
+// the DPP row_newbcast control hands state n to every lane as the first
+// operand of v_mul / v_fmac, so the broadcast costs no extra instruction, no
+// LDS traffic and no SGPRs (bf16 values are widened by one shift first).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,7 +38,7 @@ namespace {
 using namespace dev;
 
 #ifndef MSSCAN_LANE_TB
-#define MSSCAN_LANE_TB 8
+#define MSSCAN_LANE_TB 4
 #endif
 #ifndef MSSCAN_LANE_DB
 #define MSSCAN_LANE_DB 1
@@ -60,12 +60,15 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     const bool dvalid = d < a.Dn;
     const int dd = dvalid ? d : a.Dn - 1;
 
-    float A2[N], invA[N], h[N];
+    float A2[N], invA[N], A2sq[N], h[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         const float av = a.A[(int64_t)dd * N + n];
         A2[n] = av * kLog2e;
-        if constexpr (ZOH) invA[n] = (av != 0.f) ? 1.f / av : 0.f;
+        if constexpr (ZOH) {
+            invA[n] = (av != 0.f) ? 1.f / av : 0.f;
+            A2sq[n] = A2[n] * A2[n];
+        }
     }
     const int km1 = a.chunks - 1;
 #pragma unroll
@@ -96,42 +99,49 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     auto block_base = [&](const void* p, int64_t tb) -> const void* {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)rowb;
     };
-    constexpr uint32_t kBCRow = 2u * N * 4u;
-    const uint32_t bcoff = (uint32_t)(lane & (N - 1)) * 4u;
+    constexpr uint32_t kBRow = (uint32_t)N * R::kSize;  // one timestep of B or C
+    const uint32_t bcoff = (uint32_t)(lane & (N - 1)) * R::kSize;
+    auto bc_base = [&](const void* p, int64_t tb) -> const void* {
+        return static_cast<const char*>(p) + (row0 + tb) * (int64_t)kBRow;
+    };
 
     // Register buffers of one block's raw inputs (two when the next block is
     // prefetched while this one is computed).
     constexpr int NB = DB ? 2 : 1;
-    RT ru[NB][TB], rd[NB][TB], rz[NB][TB];
-    float vb[NB][TB], vc[NB][TB];
+    RT ru[NB][TB], rd[NB][TB], rz[NB][TB], vb[NB][TB], vc[NB][TB];
     auto load_block = [&](int buf, int64_t tb) {
         const uint32_t nr = block_rows(tb);
         const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
         const auto rD = make_rsrc(block_base(a.delta, tb), nr * rowb);
         const auto rZ = make_rsrc(has_z ? block_base(a.z, tb) : a.u, has_z ? nr * rowb : 0u);
-        const auto rBC = make_rsrc(a.bcw + (row0 + tb) * (2 * N), nr * kBCRow);
+        const auto rB = make_rsrc(bc_base(a.B, tb), nr * kBRow);
+        const auto rC = make_rsrc(bc_base(a.C, tb), SUMMARY ? 0u : nr * kBRow);
 #pragma unroll
         for (int tt = 0; tt < TB; ++tt) {
             const uint32_t off = off0 + (uint32_t)tt * rowb;
             ru[buf][tt] = R::load(rU, off);
             rd[buf][tt] = R::load(rD, off);
             if constexpr (!SUMMARY) rz[buf][tt] = R::load(rZ, off);
-            vb[buf][tt] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rBC, (uint32_t)tt * kBCRow + bcoff, 0, 0));
-            if constexpr (!SUMMARY)
-                vc[buf][tt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    rBC, (uint32_t)tt * kBCRow + (uint32_t)N * 4u + bcoff, 0, 0));
+            vb[buf][tt] = R::load(rB, (uint32_t)tt * kBRow + bcoff);
+            if constexpr (!SUMMARY) vc[buf][tt] = R::load(rC, (uint32_t)tt * kBRow + bcoff);
         }
     };
 
     float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (SUMMARY)
 
     // One timestep: all N states of the lane's channel.
-    auto step = [&](RT raw_u, RT raw_d, RT raw_z, float vbt, float vct, float& y_out) {
+    auto step = [&](RT raw_u, RT raw_d, RT raw_z, RT raw_b, RT raw_c, float& y_out) {
+        const float vbt = R::widen(raw_b);
         const float uv = R::widen(raw_u);
         const float v = R::widen(raw_d) + bias;
         const float dt = SP ? softplus_f(v) : v;  // compile-time: no branch per step
         const float xv = ZOH ? uv : dt * uv;
+        float q1 = 0.f, q2 = 0.f;  // ZOH series coefficients for this dt
+        if constexpr (ZOH) {
+            const float dt2 = dt * dt;
+            q1 = dt2 * kZohT1;
+            q2 = dt2 * dt * kZohT2;
+        }
         static_for(
             [&](auto nc) {
                 constexpr int n = decltype(nc)::value;
@@ -140,7 +150,7 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
                 const float bu = row_bcast<n>(vbt) * xv;  // B*x (Euler) or B*u (ZOH)
                 float bx;
                 if constexpr (ZOH)
-                    bx = zoh_factor(dt, arg * kLn2, abar, invA[n]) * bu;
+                    bx = zoh_factor_q(dt, q1, q2, A2[n], A2sq[n], arg, abar, invA[n]) * bu;
                 else
                     bx = bu;
                 h[n] = fmaf(abar, h[n], bx);
@@ -152,7 +162,7 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
             s_comp = (tk - s_sum) - yk;
             s_sum = tk;
         } else {
-            float y = DppReadout<N>::run(vct, h);
+            float y = DppReadout<N>::run(R::widen(raw_c), h);
             y = fmaf(Dd, uv, y);
             const float g = silu_f(R::widen(raw_z));
             y_out = y * (has_z ? g : 1.f);
@@ -196,14 +206,11 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
         const auto rU = make_rsrc(block_base(a.u, t), rowb);
         const auto rD = make_rsrc(block_base(a.delta, t), rowb);
         const auto rZ = make_rsrc(has_z ? block_base(a.z, t) : a.u, has_z ? rowb : 0u);
-        const auto rBC = make_rsrc(a.bcw + (row0 + t) * (2 * N), kBCRow);
         const RT xu = R::load(rU, off0);
         const RT xd = R::load(rD, off0);
         const RT xz = SUMMARY ? RT{} : R::load(rZ, off0);
-        const float xb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rBC, bcoff, 0, 0));
-        const float xc = SUMMARY ? 0.f
-                                 : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                       rBC, (uint32_t)N * 4u + bcoff, 0, 0));
+        const RT xb = R::load(make_rsrc(bc_base(a.B, t), kBRow), bcoff);
+        const RT xc = SUMMARY ? RT{} : R::load(make_rsrc(bc_base(a.C, t), kBRow), bcoff);
         float y = 0.f;
         step(xu, xd, xz, xb, xc, y);
         if constexpr (!SUMMARY) R::store(make_rsrc(block_base(a.y, t), rowb), off0, y);
@@ -227,8 +234,7 @@ template <int N, bool BF16, bool ZOH, bool SP>
 hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     constexpr int TB = MSSCAN_LANE_TB;
     constexpr bool DB = MSSCAN_LANE_DB != 0;
-    hipError_t e = launch_bc_prepare(a, BF16, s);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);

@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
                 const float bu = row_bcast<j>(vbt) * dx.y;  // B*x (Euler) or B*u (ZOH)
                 float bx;
                 if constexpr (ZOH)
-                    bx = zoh_factor(dx.x, arg * kLn2, abar, invA[j]) * bu;
+                    bx = zoh_factor(dx.x, arg, abar, invA[j]) * bu;
                 else
                     bx = bu;
                 h[j] = fmaf(abar, h[j], bx);

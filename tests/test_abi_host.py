@@ -75,9 +75,14 @@ def test_workspace_size_function():
     # Invalid dims -> (size_t)-1.
     bad = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 0, 64, 16, 1)), 1)
     assert bad == ctypes.c_size_t(-1).value
-    # The tile kernels stage fp32 B/C slices: at least batch*L*2*N floats.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 16, 1)), 1) >= \
-        8 * 2048 * 2 * 16 * 4
+    # The tile kernels (d_state 64 here) stage fp32 B/C rows: at least
+    # batch*L*2*N floats.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 1) >= \
+        2 * 2048 * 2 * 64 * 4
+    # The lane kernels (d_state 16) keep only segment summaries: N + 1 floats
+    # per (segment boundary, batch, channel).
+    n16 = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 16, 1)), 1)
+    assert n16 > 0 and n16 % (8 * 1536 * 17 * 4) < 1024
     # Deterministic and independent of flags that do not change the plan.
     d = ms.dims(1, 65536, 256, 16, 1)
     a = lib.ms_scan_workspace_bytes(ctypes.byref(d), 1)
