@@ -45,7 +45,8 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 COPY_MIB = 256  # size of the calibration copy (read and written)
 MAIN_KERNEL_RE = r"scan_lane<[^>]*false>|scan_tile<[^>]*false>|scan_chunks<"
 WORKLOAD_TITLE = {"m130m": "Mamba-130M-layer selective scan (S6) forward",
-                  "m3b": "Mamba-3B-layer selective scan (S6) forward"}
+                  "m3b": "Mamba-3B-layer selective scan (S6) forward",
+                  "long": "long-context selective scan (S6) forward, d_state 64"}
 
 
 def parse():
@@ -53,7 +54,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b"])
+    ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b", "long"])
+    ap.add_argument("--zoh", action="store_true", help="zero-order hold instead of Euler")
     ap.add_argument("--buffer-sets", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -65,6 +67,8 @@ def parse():
                     help="summarise rocprofv3 output instead of benchmarking")
     ap.add_argument("--fetch", metavar="DIR", help="rocprofv3 --pmc FETCH_SIZE output dir")
     ap.add_argument("--write", metavar="DIR", help="rocprofv3 --pmc WRITE_SIZE output dir")
+    ap.add_argument("--counters", metavar="DIR", action="append", default=[],
+                    help="other rocprofv3 --pmc output dirs: mean of every counter per kernel")
     return ap.parse_args()
 
 
@@ -161,30 +165,82 @@ def copy_calibration(reps=3):
     del src, dst
 
 
+def decode_bytes(w) -> int:
+    """Bytes one ms_state_update step must move: h read and written
+    ([batch, Dn, N] fp32), x, delta, z read and y written ([batch, Dn] io),
+    B_t and C_t read ([batch, N] io), A ([Dn, N]) and D, delta_bias ([Dn])."""
+    e = 2 if w.io == "bf16" else 4
+    return (2 * w.batch * w.Dn * w.N * 4 + 4 * w.batch * w.Dn * e + 2 * w.batch * w.N * e
+            + w.Dn * w.N * 4 + 2 * w.Dn * 4)
+
+
+def measure_decode(ms, reps=3):
+    """The decode workload: w.steps back-to-back ms_state_update calls on a
+    state resident in HBM; ms per step over `reps` timed runs, plus the
+    step kernel's HIP-event time."""
+    import torch
+    import synth
+    w = synth.workload("decode")
+    x = synth.decode_inputs(w, device="cuda", seed=0)
+    h = x["h0"].clone()
+    y = torch.empty_like(x["x"][0])
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for t in range(w.steps):
+            ms.state_update(h, x["x"][t], x["delta"][t], x["A"], x["B"][t], x["C"][t], D=x["D"],
+                            z_t=x["z"][t], delta_bias=x.get("delta_bias"), softplus=w.softplus,
+                            y_t=y, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        run()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_ms = start.elapsed_time(end) / (reps * w.steps)
+    ms.profile_begin(w.steps)
+    run()
+    torch.cuda.synchronize()
+    k_ms = ms.profile_end()["step"]["mean_ms"]
+    nb = decode_bytes(w)
+    return {"workload": f"recurrent decode, ms_state_update: batch {w.batch}, d_inner {w.Dn}, "
+                        f"d_state {w.N}, {w.io} io, fp32 state in HBM, {w.steps} steps",
+            "ms_per_step": t_ms, "kernel_ms": k_ms, "bytes_per_step": nb,
+            "hbm_gbps": nb / (t_ms * 1e-3) / 1e9,
+            "hbm_frac": nb / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9}
+
+
 # ------------------------------------------------------------ CPU oracle --
-def cpu_baseline(w, min_seconds):
+def cpu_baseline(w, min_seconds, zoh=False):
     """fp64 oracle on this host's cores on the same workload, compute time
-    only: whole batch rows (all channels, full sequence) are scanned one after
-    another, cycling over the batch, until at least min_seconds have passed."""
+    only: batch rows (full sequence; all channels, or the first `chans` when a
+    row is very large) are scanned one after another, cycling over the batch,
+    until at least min_seconds have passed."""
     import numpy as np
     import oracle
     import synth
     x = synth.scan_inputs(w, device="cpu", seed=0)
     threads = oracle.max_threads()
-    shared = {k: np.ascontiguousarray(x[k].double().numpy()) for k in ("A", "D", "delta_bias")
-              if x.get(k) is not None}
+    chans = w.Dn if w.L * w.Dn <= (1 << 25) else max(64, (1 << 25) // w.L)
+    shared = {k: np.ascontiguousarray(x[k][:chans].double().numpy())
+              for k in ("A", "D", "delta_bias") if x.get(k) is not None}
     rows, elapsed, b = 0, 0.0, 0
     while elapsed < min_seconds and rows < 64 * w.batch:
-        f = {k: np.ascontiguousarray(x[k][b:b + 1].double().numpy())
-             for k in ("u", "delta", "z", "B", "C")}
+        f = {k: np.ascontiguousarray(x[k][b:b + 1, :, :chans].double().numpy())
+             for k in ("u", "delta", "z")}
+        f.update({k: np.ascontiguousarray(x[k][b:b + 1].double().numpy()) for k in ("B", "C")})
         t0 = time.perf_counter()
         oracle.scan(f["u"], f["delta"], shared["A"], f["B"], f["C"], D=shared.get("D"), z=f["z"],
-                    delta_bias=shared.get("delta_bias"), softplus=w.softplus, zoh=False,
+                    delta_bias=shared.get("delta_bias"), softplus=w.softplus, zoh=zoh,
                     nthreads=threads)
         elapsed += time.perf_counter() - t0
         rows += 1
         b = (b + 1) % w.batch
-    elems = rows * w.L * w.Dn
+    elems = rows * w.L * chans
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -194,9 +250,11 @@ def cpu_baseline(w, min_seconds):
                     break
     except OSError:
         pass
+    what = f"all {w.Dn} channels" if chans == w.Dn else f"the first {chans} of {w.Dn} channels"
     return {"value": elems / elapsed, "unit": "elem/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} batch rows of the {w.name} workload (each: all {w.Dn} channels "
-                      f"x L={w.L}, d_state {w.N}, Euler, softplus, z gate, D), cycling over "
+            "sample": f"{rows} batch rows of the {w.name} workload (each: {what} "
+                      f"x L={w.L}, d_state {w.N}, {'ZOH' if zoh else 'Euler'}, "
+                      f"softplus {'on' if w.softplus else 'off'}, z gate, D), cycling over "
                       f"its {w.batch} rows; fp64 C oracle, OpenMP over channels, "
                       f"{threads} threads; {elapsed:.1f} s compute; host CPU: {cpu}"}
 
@@ -234,7 +292,8 @@ def _csv(dirname, suffix):
 
 def _short(name):
     m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|scan_chunks<[^>]*>|scan_summary<[^>]*>|"
-                  r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|neg_kernel)", name)
+                  r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|step_quads<[^>]*>|"
+                  r"neg_kernel)", name)
     return m.group(1) if m else name[:60]
 
 
@@ -276,7 +335,8 @@ def rocprof_summary(args):
         print("|---|---|---|---|")
         main = None
         for k in sorted(fetch):
-            if k == "neg_kernel" or k not in write or not re.search(r"scan_|carry_|bc_prep|state_step", k):
+            if k == "neg_kernel" or k not in write or not re.search(
+                    r"scan_|carry_|bc_prep|state_step|step_quads", k):
                 continue
             mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
             print(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {mb:.2f} |")
@@ -285,6 +345,22 @@ def rocprof_summary(args):
         if main is not None:
             print()
             print(f"- traffic_bytes_per_launch: {main:.0f}")
+    for dirname in args.counters:
+        acc = {}
+        for r in _csv(dirname, "counter_collection.csv"):
+            k = _short(r["Kernel_Name"])
+            if not re.search(r"scan_|carry_|bc_prep|state_step|step_quads", k):
+                continue
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        names = sorted({c for v in acc.values() for c in v})
+        print()
+        print("| kernel | " + " | ".join(names) + " |")
+        print("|---|" + "---|" * len(names))
+        for k in sorted(acc):
+            vals = [acc[k].get(c) for c in names]
+            print(f"| `{k}` | " + " | ".join(f"{sum(v) / len(v):.4g}" if v else "-"
+                                             for v in vals) + " |")
 
 
 # ------------------------------------------------------------------ main --
@@ -315,12 +391,13 @@ def main():
     ms.load()
     if args.copy_calibration:
         copy_calibration()
-    w, t_ms, ph = measure(ms, args.workload, args.steps, args.warmup, args.buffer_sets)
+    n_sets = args.buffer_sets if args.workload != "long" else 1  # long: 13 GB per set
+    w, t_ms, ph = measure(ms, args.workload, args.steps, args.warmup, n_sets, zoh=args.zoh)
     torch.cuda.empty_cache()
     elems = w.batch * w.L * w.Dn
     alg_bytes = synth.algorithmic_bytes(w)
     main_ms = ph["main"]["mean_ms"]
-    ops = valu_ops_per_element(w.N, zoh=False, softplus=w.softplus) * elems
+    ops = valu_ops_per_element(w.N, zoh=args.zoh, softplus=w.softplus) * elems
     achieved = ops / (main_ms * 1e-3) / 1e12
     src = source_hash()
     gbps = alg_bytes / (t_ms * 1e-3) / 1e9
@@ -339,15 +416,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TITLE[w.name],
                    "batch": w.batch, "seq_len": w.L, "d_inner": w.Dn, "d_state": w.N,
-                   "io": w.io, "state": "f32", "discretisation": "euler",
+                   "io": w.io, "state": "f32",
+                   "discretisation": "zoh" if args.zoh else "euler",
                    "softplus_bias": w.softplus, "z_gate": True, "D_skip": True,
-                   "buffer_sets": args.buffer_sets, "parallelism": "single-gpu"},
+                   "buffer_sets": n_sets, "parallelism": "single-gpu"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS,
                      "unit": "TOP/s", "frac": achieved / VALU_PEAK_TOPS,
                      "traffic": load_traffic(w.name, src),
                      "kernel": "scan main pass (writes y)",
                      "kernel_mean_ms": main_ms,
-                     "ops_per_element": valu_ops_per_element(w.N, zoh=False,
+                     "ops_per_element": valu_ops_per_element(w.N, zoh=args.zoh,
                                                              softplus=w.softplus),
                      "ops_per_launch": ops,
                      "algorithmic_bytes_per_launch": alg_bytes},
@@ -357,7 +435,7 @@ def main():
         "kernels_ms": {k: v["mean_ms"] for k, v in ph.items() if k != "calls" and v["launches"]},
         "source_hash": src,
     }
-    if not args.no_secondary and args.workload == "m130m":
+    if not args.no_secondary and args.workload == "m130m" and not args.zoh:
         w3, t3, ph3 = measure(ms, "m3b", max(3, args.steps // 4), 2, 2)
         e3 = w3.batch * w3.L * w3.Dn
         out["secondary"] = {"workload": WORKLOAD_TITLE["m3b"] + " (B4 L8192 D5120 N16 bf16, "
@@ -367,8 +445,11 @@ def main():
                             "kernels_ms": {k: v["mean_ms"] for k, v in ph3.items()
                                            if k != "calls" and v["launches"]}}
         torch.cuda.empty_cache()
+    if not args.no_secondary and args.workload == "m130m" and not args.zoh:
+        out["decode"] = measure_decode(ms)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, zoh=args.zoh)
     print(json.dumps(out), flush=True)
 
 

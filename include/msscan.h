@@ -13,11 +13,12 @@
  *   y     = sum_n C[b,t,n] * h[n]  +  D[d] * u[b,t,d]
  *   out[b,t,d] = y * z * sigmoid(z),  z = z[b,t,d]    (when z is given; else y)
  *
- * Passages followed (page titles as published; section numbers are the pages'):
+ * Passages followed (page titles as published, or the site where a page has
+ * no title; section numbers are the pages'):
  *   - the per-timestep loop of the naive selective scan, with B and C shared by
- *     all channels and D*u added before the silu(z) gate: "从RNN到Mamba：状态空间
- *     模型原理与长序列建模实战" (lmnt.cn), section 3.2; the block data flow in
- *     section 3.1;
+ *     all channels and D*u added before the silu(z) gate: the lmnt.cn page
+ *     (news/271401, untitled; opens with section 1 "从RNN到Mamba"), section
+ *     3.2; the block data flow in section 3.1;
  *   - dt = softplus(W x + b): "Mamba架构原理与工业级长文本处理实战指南"
  *     (jsqmd.com), section 2.2;
  *   - zero-order hold A_bar = exp(dt A), B_bar = (A_bar - I) A^-1 B: "Mamba模型

@@ -9,8 +9,9 @@
  * Every function below follows the pages' statement of the method:
  *
  *   * The recurrence and its readout are the per-timestep loop of the naive
- *     PyTorch selective scan on the page "从RNN到Mamba：状态空间模型原理与长序列
- *     建模实战" (lmnt.cn/news/271401), section 3.2: A_bar = exp(dt*A),
+ *     PyTorch selective scan on the lmnt.cn page (news/271401; its text
+ *     carries no title line and opens with section 1, "从RNN到Mamba"),
+ *     section 3.2: A_bar = exp(dt*A),
  *     B_bar = dt*B_t (broadcast over channels), h = A_bar*h + B_bar*x_t,
  *     y_t = sum_n h*C_t, then y += x*D, then y * silu(z).
  *   * The step size is softplus of a linear map plus bias: page "Mamba架构原理与

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsscan.so")
 SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "scan_tile.hip"),
-           os.path.join(CSRC, "scan_lane.hip"),
+           os.path.join(CSRC, "scan_lane.hip"), os.path.join(CSRC, "decode.hip"),
            os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "profile.cpp")]
 ARCH = os.environ.get("MSSCAN_ARCH", "gfx950")
 
@@ -66,7 +66,7 @@ def build(verbose: bool = False) -> str:
 def asm(out_dir: str) -> None:
     """Write the gfx950 assembly of the kernels (for inspecting our own code)."""
     os.makedirs(out_dir, exist_ok=True)
-    for src in SOURCES[:3]:
+    for src in [x for x in SOURCES if x.endswith(".hip")]:
         out = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".s"))
         cmd = [hipcc()] + flags() + ["-x", "hip", "--cuda-device-only", "-S", src, "-o", out]
         subprocess.run(cmd, check=True)

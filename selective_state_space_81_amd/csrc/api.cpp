@@ -261,8 +261,11 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
     a.bias = delta_bias; a.y = y_t; a.batch = batch; a.Dn = d_inner; a.N = d_state;
     a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
     msscan::prof_call();
-    hipError_t e = msscan::launch_step(a, io == MS_BF16, (flags & MS_ZOH) != 0,
-                                       static_cast<hipStream_t>(stream));
+    const bool bf16 = io == MS_BF16, zoh = (flags & MS_ZOH) != 0;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = msscan::step_quads_supported(batch, d_inner, d_state)
+                       ? msscan::launch_step_quads(a, bf16, zoh, hs)
+                       : msscan::launch_step(a, bf16, zoh, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

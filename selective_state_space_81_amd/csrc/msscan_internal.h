@@ -76,6 +76,9 @@ hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool z
 bool lane_variant_exists(int n);
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
+// Decode step with 4 states per lane (d_state in {4, 8, ..., 128}).
+bool step_quads_supported(int batch, int d_inner, int n);
+hipError_t launch_step_quads(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
 
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
 // ProfScope records the phase's begin event at construction and its end
