@@ -59,10 +59,11 @@ ms_status check_flags(uint32_t flags) {
 // waves exist (many waves per CU keep the VALU issuing; a segment after the
 // first costs a summary pass over it, so segments are not cut shorter than
 // kMinSegment).
-//   lane path (d_state 8 or 16): one wave per workgroup, all states of a
-//     channel in one lane;
-//   tile path (d_state 32, 64, 128, or 8/16 when forced): several waves
-//     split d_state and share per-element work through LDS.
+//   lane path (d_state 8, 16, 32; 64 with Euler): one wave per workgroup,
+//     all states of a channel in one lane;
+//   tile path (d_state 128, 64 with ZOH, or the others when the lane path is
+//     compiled out): several waves split d_state and share per-element work
+//     through LDS.
 #ifndef MSSCAN_TILE_WAVES
 #define MSSCAN_TILE_WAVES 4
 #endif
@@ -91,8 +92,8 @@ void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) 
     p.chunks = (int)((d.seqlen + len - 1) / len);
 }
 
-bool lane_plan(const ms_dims& d, msscan::Plan& p) {
-    if (!MSSCAN_LANE_PATH || !msscan::lane_variant_exists(d.d_state)) return false;
+bool lane_plan(const ms_dims& d, bool zoh, msscan::Plan& p) {
+    if (!MSSCAN_LANE_PATH || !msscan::lane_variant_exists(d.d_state, zoh)) return false;
     p.tile_path = 2;
     p.ns = d.d_state;
     p.waves = 1;
@@ -119,10 +120,10 @@ bool tile_plan(const ms_dims& d, msscan::Plan& p) {
     return true;
 }
 
-msscan::Plan make_plan(const ms_dims& d) {
+msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
     msscan::Plan p{};
     const int N = d.d_state;
-    if (lane_plan(d, p) || tile_plan(d, p)) {
+    if (lane_plan(d, (flags & MS_ZOH) != 0, p) || tile_plan(d, p)) {
         if (p.chunks > 1) {
             const size_t km1 = (size_t)(p.chunks - 1);
             p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
@@ -192,7 +193,7 @@ const char* ms_status_string(ms_status s) {
 
 size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags) {
     if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
-    return ws_bytes(make_plan(*dims));
+    return ws_bytes(make_plan(*dims, flags));
 }
 
 ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
@@ -209,7 +210,7 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
     const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
     for (const void* p : ptrs)
         if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
-    const msscan::Plan p = make_plan(*dims);
+    const msscan::Plan p = make_plan(*dims, flags);
     const size_t need = ws_bytes(p);
     if (need && (!workspace || workspace_bytes < need))
         return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,

@@ -124,6 +124,28 @@ struct DppReadout<16> {
         return y;
     }
 };
+// y + sum_j C[n0 + j] * h[j] for 16 states: the continuation of a readout
+// chain for the second and later groups of 16 states of a lane.
+struct DppReadoutAcc16 {
+    static __device__ __forceinline__ float run(float y, float vc, const float* h) {
+        asm("s_nop 1\n" MS_DPP_("v_fmac_f32_dpp", 0, "%2") MS_DPP_("v_fmac_f32_dpp", 1, "%3")
+                MS_DPP_("v_fmac_f32_dpp", 2, "%4") MS_DPP_("v_fmac_f32_dpp", 3, "%5")
+                    MS_DPP_("v_fmac_f32_dpp", 4, "%6") MS_DPP_("v_fmac_f32_dpp", 5, "%7")
+                        MS_DPP_("v_fmac_f32_dpp", 6, "%8") MS_DPP_("v_fmac_f32_dpp", 7, "%9")
+                            MS_DPP_("v_fmac_f32_dpp", 8, "%10") MS_DPP_("v_fmac_f32_dpp", 9, "%11")
+                                MS_DPP_("v_fmac_f32_dpp", 10, "%12")
+                                    MS_DPP_("v_fmac_f32_dpp", 11, "%13")
+                                        MS_DPP_("v_fmac_f32_dpp", 12, "%14")
+                                            MS_DPP_("v_fmac_f32_dpp", 13, "%15")
+                                                MS_DPP_("v_fmac_f32_dpp", 14, "%16")
+                                                    MS_DPP_("v_fmac_f32_dpp", 15, "%17")
+            : "+&v"(y)
+            : "v"(vc), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]),
+              "v"(h[6]), "v"(h[7]), "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]),
+              "v"(h[13]), "v"(h[14]), "v"(h[15]));
+        return y;
+    }
+};
 #undef MS_DPP_
 
 template <typename F, int... Js>

@@ -73,7 +73,7 @@ hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, bool z
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
 bool tile_variant_exists(int ns, int waves);
 hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
-bool lane_variant_exists(int n);
+bool lane_variant_exists(int n, bool zoh);
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
 // Decode step with 4 states per lane (d_state in {4, 8, ..., 128}).

@@ -43,13 +43,23 @@ using namespace dev;
 #ifndef MSSCAN_LANE_DB
 #define MSSCAN_LANE_DB 1
 #endif
+#ifndef MSSCAN_LANE_TB64
+#define MSSCAN_LANE_TB64 4
+#endif
+#ifndef MSSCAN_LANE_DB64
+#define MSSCAN_LANE_DB64 0
+#endif
 #ifndef MSSCAN_LANE_WPE
 #define MSSCAN_LANE_WPE 1
 #endif
 
 template <int N, int TB, bool DB, bool BF16, bool ZOH, bool SP, bool SUMMARY>
-__global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
-    static_assert(N == 8 || N == 16, "one DPP row holds the states of a lane");
+__global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "states per lane");
+    // B_t and C_t reach the lanes in groups of RW states, one DPP row each:
+    // lane l holds state 16k + (l mod RW) of group k.
+    constexpr int RW = N < 16 ? N : 16;
+    constexpr int KB = N / RW;
     using R = Io<BF16>;
     using RT = typename R::T;
 
@@ -100,7 +110,7 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)rowb;
     };
     constexpr uint32_t kBRow = (uint32_t)N * R::kSize;  // one timestep of B or C
-    const uint32_t bcoff = (uint32_t)(lane & (N - 1)) * R::kSize;
+    const uint32_t bcoff = (uint32_t)(lane & (RW - 1)) * R::kSize;
     auto bc_base = [&](const void* p, int64_t tb) -> const void* {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)kBRow;
     };
@@ -108,7 +118,7 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     // Register buffers of one block's raw inputs (two when the next block is
     // prefetched while this one is computed).
     constexpr int NB = DB ? 2 : 1;
-    RT ru[NB][TB], rd[NB][TB], rz[NB][TB], vb[NB][TB], vc[NB][TB];
+    RT ru[NB][TB], rd[NB][TB], rz[NB][TB], vb[NB][TB][KB], vc[NB][TB][KB];
     auto load_block = [&](int buf, int64_t tb) {
         const uint32_t nr = block_rows(tb);
         const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
@@ -122,16 +132,23 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
             ru[buf][tt] = R::load(rU, off);
             rd[buf][tt] = R::load(rD, off);
             if constexpr (!SUMMARY) rz[buf][tt] = R::load(rZ, off);
-            vb[buf][tt] = R::load(rB, (uint32_t)tt * kBRow + bcoff);
-            if constexpr (!SUMMARY) vc[buf][tt] = R::load(rC, (uint32_t)tt * kBRow + bcoff);
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const uint32_t o = (uint32_t)tt * kBRow + (uint32_t)(16 * k) * R::kSize + bcoff;
+                vb[buf][tt][k] = R::load(rB, o);
+                if constexpr (!SUMMARY) vc[buf][tt][k] = R::load(rC, o);
+            }
         }
     };
 
     float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (SUMMARY)
 
     // One timestep: all N states of the lane's channel.
-    auto step = [&](RT raw_u, RT raw_d, RT raw_z, RT raw_b, RT raw_c, float& y_out) {
-        const float vbt = R::widen(raw_b);
+    auto step = [&](RT raw_u, RT raw_d, RT raw_z, const RT (&raw_b)[KB], const RT (&raw_c)[KB],
+                    float& y_out) {
+        float vbt[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) vbt[k] = R::widen(raw_b[k]);
         const float uv = R::widen(raw_u);
         const float v = R::widen(raw_d) + bias;
         const float dt = SP ? softplus_f(v) : v;  // compile-time: no branch per step
@@ -147,13 +164,16 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
                 constexpr int n = decltype(nc)::value;
                 const float arg = dt * A2[n];
                 const float abar = hw_exp2(arg);
-                const float bu = row_bcast<n>(vbt) * xv;  // B*x (Euler) or B*u (ZOH)
+                const float bu = row_bcast<n % RW>(vbt[n / RW]) * xv;  // B*x (Euler) or B*u (ZOH)
                 float bx;
                 if constexpr (ZOH)
                     bx = zoh_factor_q(dt, q1, q2, A2[n], A2sq[n], arg, abar, invA[n]) * bu;
                 else
                     bx = bu;
                 h[n] = fmaf(abar, h[n], bx);
+                // With 32+ states the scheduler would otherwise start every
+                // exponential before the first update and run out of VGPRs.
+                if constexpr (N >= 32 && n % 8 == 7) __builtin_amdgcn_sched_barrier(0);
             },
             std::make_integer_sequence<int, N>{});
         if constexpr (SUMMARY) {
@@ -162,7 +182,9 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
             s_comp = (tk - s_sum) - yk;
             s_sum = tk;
         } else {
-            float y = DppReadout<N>::run(R::widen(raw_c), h);
+            float y = DppReadout<RW>::run(R::widen(raw_c[0]), *reinterpret_cast<const float(*)[RW]>(h));
+#pragma unroll
+            for (int k = 1; k < KB; ++k) y = DppReadoutAcc16::run(y, R::widen(raw_c[k]), h + 16 * k);
             y = fmaf(Dd, uv, y);
             const float g = silu_f(R::widen(raw_z));
             y_out = y * (has_z ? g : 1.f);
@@ -209,8 +231,13 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
         const RT xu = R::load(rU, off0);
         const RT xd = R::load(rD, off0);
         const RT xz = SUMMARY ? RT{} : R::load(rZ, off0);
-        const RT xb = R::load(make_rsrc(bc_base(a.B, t), kBRow), bcoff);
-        const RT xc = SUMMARY ? RT{} : R::load(make_rsrc(bc_base(a.C, t), kBRow), bcoff);
+        RT xb[KB], xc[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const uint32_t o = (uint32_t)(16 * k) * R::kSize + bcoff;
+            xb[k] = R::load(make_rsrc(bc_base(a.B, t), kBRow), o);
+            xc[k] = SUMMARY ? RT{} : R::load(make_rsrc(bc_base(a.C, t), kBRow), o);
+        }
         float y = 0.f;
         step(xu, xd, xz, xb, xc, y);
         if constexpr (!SUMMARY) R::store(make_rsrc(block_base(a.y, t), rowb), off0, y);
@@ -232,8 +259,11 @@ __global__ void __launch_bounds__(64, MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
 
 template <int N, bool BF16, bool ZOH, bool SP>
 hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    constexpr int TB = MSSCAN_LANE_TB;
-    constexpr bool DB = MSSCAN_LANE_DB != 0;
+    // 64 states (32 with ZOH's extra per-state constants) leave room for one
+    // register block only: no prefetch of the next block.
+    constexpr bool kBig = N >= 64 || (N >= 32 && ZOH);
+    constexpr int TB = kBig ? MSSCAN_LANE_TB64 : MSSCAN_LANE_TB;
+    constexpr bool DB = kBig ? MSSCAN_LANE_DB64 != 0 : MSSCAN_LANE_DB != 0;
     hipError_t e = hipSuccess;
     if (p.chunks > 1) {
         {
@@ -259,6 +289,10 @@ hipError_t dispatch_n(const Plan& p, const ScanArgs& a, hipStream_t s) {
     switch (p.ns) {
         case 8: return launch_lanes<8, BF16, ZOH, SP>(p, a, s);
         case 16: return launch_lanes<16, BF16, ZOH, SP>(p, a, s);
+        case 32: return launch_lanes<32, BF16, ZOH, SP>(p, a, s);
+        case 64:
+            if constexpr (!ZOH) return launch_lanes<64, BF16, ZOH, SP>(p, a, s);
+            return hipErrorInvalidValue;  // 64 ZOH states do not fit a lane's registers
         default: return hipErrorInvalidValue;
     }
 }
@@ -270,7 +304,9 @@ hipError_t dispatch(const Plan& p, const ScanArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool lane_variant_exists(int n) { return n == 8 || n == 16; }
+bool lane_variant_exists(int n, bool zoh) {
+    return n == 8 || n == 16 || n == 32 || (n == 64 && !zoh);
+}
 
 hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool zoh,
                              hipStream_t s) {

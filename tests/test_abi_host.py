@@ -75,10 +75,16 @@ def test_workspace_size_function():
     # Invalid dims -> (size_t)-1.
     bad = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 0, 64, 16, 1)), 1)
     assert bad == ctypes.c_size_t(-1).value
-    # The tile kernels (d_state 64 here) stage fp32 B/C rows: at least
-    # batch*L*2*N floats.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 1) >= \
+    # The tile kernels (d_state 128, or 64 with ZOH) stage fp32 B/C rows: at
+    # least batch*L*2*N floats.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 128, 1)), 1) >= \
+        2 * 2048 * 2 * 128 * 4
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 3) >= \
         2 * 2048 * 2 * 64 * 4
+    # d_state 64 with Euler takes the lane kernels (summaries only, no staged
+    # B/C rows), so it needs less than the same shape with ZOH.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 1) < \
+        lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 3)
     # The lane kernels (d_state 16) keep only segment summaries: N + 1 floats
     # per (segment boundary, batch, channel).
     n16 = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 16, 1)), 1)
