@@ -5,14 +5,13 @@
 // calls (lmnt.cn page, section 5.3; the state cache of the jsqmd page,
 // section 5.3): per (b, d) read x_t, delta_t, z_t, per n read and rewrite
 // h[b, d, n].  Its bytes are dominated by the fp32 state (read and written
-// once per step), so the kernel is laid out for that stream: lane g of a
-// channel owns states 4g .. 4g+3 and moves them as one 16-byte load and one
-// 16-byte store, so a wave covers 1 KiB of consecutive state.  The G = N/4
-// lanes of a channel sit in one wave (G divides 64) and sum their partial
-// readouts with cross-lane shuffles; the per-element work (softplus, gate) is
-// repeated by each of them, which costs little next to the state traffic.
+// once per step), so the kernel is laid out for that stream (see
+// step_quads); the per-element work (softplus, gate) is repeated by the G
+// lanes of a channel, which costs little next to the state traffic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "msscan_internal.h"
@@ -34,86 +33,140 @@ __device__ __forceinline__ float4 ld4(const void* p, int64_t i) {
     }
 }
 
-template <int G, bool BF16, bool ZOH>
+#ifndef MSSCAN_STEP_ROWS
+#define MSSCAN_STEP_ROWS 4
+#endif
+
+// Lane l of a wave owns one quad (4 consecutive states) of the d_inner * G
+// quads of a batch row -- a wave's 16-byte state moves are one contiguous
+// 1 KiB access -- and applies the step to that quad in BR batch rows: A's
+// quad is loaded once for all of them and the BR state loads are in flight
+// together.  A channel's G quads sit on G neighbouring lanes (G divides 64),
+// which sum their partial readouts with shuffles.
+// Sum of v over each aligned group of G lanes (G a power of two, <= 64),
+// left in every lane of the group.  Within a 16-lane row the partners come
+// through DPP (quad_perm for xor 1 and 2; row_half_mirror and row_mirror
+// pair each lane with one of the other half once its half holds one value);
+// wider groups use shuffles.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    auto dpp = [](float x, auto ctrl) {
+        return __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, true));
+    };
+    if constexpr (G >= 2) v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+    if constexpr (G >= 4) v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+    if constexpr (G >= 8) v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+    if constexpr (G >= 16) v += dpp(v, std::integral_constant<int, 0x140>{}); // row_mirror
+    if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int G, int BR, bool BF16, bool ZOH>
 __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
     constexpr int N = 4 * G;
-    const int64_t total = (int64_t)a.batch * a.Dn * G;
-    const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // Lanes past the end stay alive (clamped to the last lane) so that every
-    // shuffle has all its partners; they store nothing.
-    const bool valid = gl < total;
-    const int64_t gc = valid ? gl : total - 1;
-    const int q = (int)(gc % G);
-    const int64_t e = gc / G;  // b * Dn + d
-    const int d = (int)(e % a.Dn);
-    const int b = (int)(e / a.Dn);
+    const int quads = a.Dn * G;
+    const int qi = blockIdx.x * blockDim.x + threadIdx.x;
+    // Quads past the row's end are clamped to its last quad (so every
+    // shuffle has its partners) and store nothing; so are rows past the batch.
+    const bool qvalid = qi < quads;
+    const int qc = qvalid ? qi : quads - 1;
+    const int d = qc / G;  // G is a power of two: a shift
+    const int j = qc & (G - 1);
+    const int n0 = 4 * j;
+    const int b0 = blockIdx.y * BR;
 
-    const float xv = ld<BF16>(a.x, e);
-    const float dt = step_size(ld<BF16>(a.delta, e), a.bias ? a.bias[d] : 0.f, a.softplus);
-    const float dx = dt * xv;
-    float* hp = a.h + e * N + 4 * q;
-    float4 hv = *reinterpret_cast<const float4*>(hp);
-    const float4 av = *reinterpret_cast<const float4*>(a.A + (int64_t)d * N + 4 * q);
-    const float4 bv = ld4<BF16>(a.B, (int64_t)b * N + 4 * q);
-    const float4 cv = ld4<BF16>(a.C, (int64_t)b * N + 4 * q);
-
-    auto one = [&](float an, float bn, float cn, float& h, float& y) {
-        const float arg = dt * (an * kLog2e);
-        const float abar = hw_exp2(arg);
-        float bx;
-        if constexpr (ZOH)
-            bx = zoh_factor(dt, arg, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
-        else
-            bx = dx * bn;
-        h = fmaf(abar, h, bx);
-        y = fmaf(cn, h, y);
-    };
-    float y = 0.f;
-    one(av.x, bv.x, cv.x, hv.x, y);
-    one(av.y, bv.y, cv.y, hv.y, y);
-    one(av.z, bv.z, cv.z, hv.z, y);
-    one(av.w, bv.w, cv.w, hv.w, y);
+    // Every load is issued here, before any arithmetic, so that a wave waits
+    // on memory once.
+    const float4 av = *reinterpret_cast<const float4*>(a.A + (int64_t)d * N + n0);
+    const float bias = a.bias ? a.bias[d] : 0.f;
+    const float Dd = a.D ? a.D[d] : 0.f;
+    float4 hv[BR], bv[BR], cv[BR];
+    float xv[BR], dr[BR], zv[BR];
 #pragma unroll
-    for (int off = G / 2; off >= 1; off /= 2) y += __shfl_xor(y, off, 64);
+    for (int r = 0; r < BR; ++r) {
+        const int b = min(b0 + r, a.batch - 1);
+        const int64_t e = (int64_t)b * a.Dn + d;
+        hv[r] = *reinterpret_cast<const float4*>(a.h + e * N + n0);
+        bv[r] = ld4<BF16>(a.B, (int64_t)b * N + n0);
+        cv[r] = ld4<BF16>(a.C, (int64_t)b * N + n0);
+        xv[r] = ld<BF16>(a.x, e);
+        dr[r] = ld<BF16>(a.delta, e);
+        zv[r] = a.z ? ld<BF16>(a.z, e) : 0.f;
+    }
+    const float A2[4] = {av.x * kLog2e, av.y * kLog2e, av.z * kLog2e, av.w * kLog2e};
+    const float an[4] = {av.x, av.y, av.z, av.w};
 
-    if (!valid) return;
-    *reinterpret_cast<float4*>(hp) = hv;
-    if (q == 0) {
-        y = fmaf(a.D ? a.D[d] : 0.f, xv, y);
-        if (a.z) y *= silu_f(ld<BF16>(a.z, e));
-        st<BF16>(a.y, e, y);
+#pragma unroll
+    for (int r = 0; r < BR; ++r) {
+        const float dt = step_size(dr[r], bias, a.softplus);
+        const float dx = dt * xv[r];
+        float hs[4] = {hv[r].x, hv[r].y, hv[r].z, hv[r].w};
+        const float bs[4] = {bv[r].x, bv[r].y, bv[r].z, bv[r].w};
+        const float cs[4] = {cv[r].x, cv[r].y, cv[r].z, cv[r].w};
+        float y = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float arg = dt * A2[k];
+            const float abar = hw_exp2(arg);
+            float bx;
+            if constexpr (ZOH)
+                bx = zoh_factor(dt, arg, abar, an[k] != 0.f ? 1.f / an[k] : 0.f) * (bs[k] * xv[r]);
+            else
+                bx = dx * bs[k];
+            hs[k] = fmaf(abar, hs[k], bx);
+            y = fmaf(cs[k], hs[k], y);
+        }
+        y = group_sum<G>(y);
+        const int b = b0 + r;
+        if (!qvalid || b >= a.batch) continue;
+        const int64_t e = (int64_t)b * a.Dn + d;
+        *reinterpret_cast<float4*>(a.h + e * N + n0) = make_float4(hs[0], hs[1], hs[2], hs[3]);
+        if (j == 0) {
+            y = fmaf(Dd, xv[r], y);
+            if (a.z) y *= silu_f(zv[r]);
+            st<BF16>(a.y, e, y);
+        }
     }
 }
 
-template <bool BF16, bool ZOH>
+template <int BR, bool BF16, bool ZOH>
 hipError_t launch_g(const StepArgs& a, hipStream_t s) {
     const int G = a.N / 4;
-    const int64_t lanes = (int64_t)a.batch * a.Dn * G;
-    const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+    const int64_t quads = (int64_t)a.Dn * G;
+    const dim3 grid((unsigned)((quads + 255) / 256), (unsigned)((a.batch + BR - 1) / BR)),
+        block(256);
     switch (G) {
-        case 1: hipLaunchKernelGGL((step_quads<1, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((step_quads<2, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((step_quads<4, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((step_quads<8, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((step_quads<16, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((step_quads<32, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((step_quads<1, BR, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((step_quads<2, BR, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((step_quads<4, BR, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((step_quads<8, BR, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((step_quads<16, BR, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((step_quads<32, BR, BF16, ZOH>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <bool BF16, bool ZOH>
+hipError_t launch_p(const StepArgs& a, hipStream_t s) {
+    return launch_g<MSSCAN_STEP_ROWS, BF16, ZOH>(a, s);
+}
+
 }  // namespace
 
 bool step_quads_supported(int batch, int d_inner, int n) {
+    (void)batch;  // batch rows go to grid.y (<= 65535, checked by the caller)
     if (n % 4 != 0 || n < 4 || n > 128 || ((n / 4) & (n / 4 - 1)) != 0) return false;
-    return (int64_t)batch * d_inner * (n / 4) / 256 < 0x7fffffffLL;  // grid.x limit
+    return (int64_t)d_inner * (n / 4) < (1LL << 30);  // quad index of a row fits int
 }
 
 hipError_t launch_step_quads(const StepArgs& a, bool bf16, bool zoh, hipStream_t s) {
     if (!step_quads_supported(a.batch, a.Dn, a.N)) return hipErrorInvalidValue;
     ProfScope ps(s, kPhaseStep);
-    if (bf16) return zoh ? launch_g<true, true>(a, s) : launch_g<true, false>(a, s);
-    return zoh ? launch_g<false, true>(a, s) : launch_g<false, false>(a, s);
+    if (bf16) return zoh ? launch_p<true, true>(a, s) : launch_p<true, false>(a, s);
+    return zoh ? launch_p<false, true>(a, s) : launch_p<false, false>(a, s);
 }
 
 }  // namespace msscan
