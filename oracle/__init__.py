@@ -48,6 +48,9 @@ def _load():
                                                dp, dp, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_step.argtypes = [dp] * 9 + [ctypes.c_int, ctypes.c_int, i64, i64, i64, dp]
+        lib.oracle_conv1d.restype = ctypes.c_int
+        lib.oracle_conv1d.argtypes = [dp] * 4 + [i64, ctypes.c_int, i64, i64, i64, dp,
+                                                 ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         _lib = lib
@@ -119,3 +122,25 @@ def step(h, x, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise RuntimeError(f"oracle_step failed with code {rc}")
     return y, h
+
+
+def conv1d(x, w, bias=None, x_prev=None, silu: bool = True, nthreads: int = 0) -> np.ndarray:
+    """Causal depthwise conv1d (+ silu) in fp64.
+
+    x: [batch, L, Dn]; w: [Dn, width]; bias: [Dn]; x_prev: [batch, width-1, Dn]
+    (the inputs before t = 0, oldest first; None = zeros).  Returns u
+    [batch, L, Dn] as float64."""
+    xf, wf, bf, pf = _f64(x), _f64(w), _f64(bias), _f64(x_prev)
+    batch, L, Dn = xf.shape
+    width = wf.shape[1]
+    assert wf.shape == (Dn, width)
+    if bf is not None:
+        assert bf.shape == (Dn,)
+    if pf is not None:
+        assert pf.shape == (batch, width - 1, Dn)
+    u = np.empty((batch, L, Dn), dtype=np.float64)
+    rc = _load().oracle_conv1d(_ptr(xf), _ptr(wf), _ptr(bf), _ptr(pf), width, int(silu),
+                               batch, L, Dn, _ptr(u), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d failed ({rc})")
+    return u

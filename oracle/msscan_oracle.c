@@ -164,6 +164,45 @@ int oracle_step(double* h, const double* x, const double* delta_raw,
 }
 
 /* Number of threads OpenMP would use (for reporting the CPU baseline). */
+/* Causal depthwise conv1d, optionally followed by silu: the step that turns
+ * the x branch of the block input into the scan input u (lmnt page,
+ * section 3.1: a depthwise 1D convolution of width about 4 on x_ssm before
+ * the SSM; section 3.2: groups = d_inner, padding = width - 1, output cut to
+ * the first L steps, then silu).  For every (b, t, d):
+ *   pre = bias[d] + sum_{k=0}^{width-1} w[d][k] * x[b, t - (width-1) + k, d]
+ * where a time index below 0 reads x_prev[b][width-1 + index][d] when x_prev
+ * is given (the width-1 inputs before t = 0, oldest first) and 0 otherwise;
+ * u = silu(pre) when silu is set, else pre.
+ * Layouts: x, u [batch][L][Dn]; w [Dn][width]; bias [Dn];
+ * x_prev [batch][width-1][Dn]. */
+int oracle_conv1d(const double* x, const double* w, const double* bias, const double* x_prev,
+                  int64_t width, int silu, int64_t batch, int64_t L, int64_t Dn, double* u,
+                  int nthreads) {
+    if (width < 1 || batch < 0 || L < 0 || Dn < 0) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for collapse(2) schedule(static)
+#endif
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < Dn; ++d) {
+            for (int64_t t = 0; t < L; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < width; ++k) {
+                    const int64_t ti = t - (width - 1) + k;
+                    double xv = 0.0;
+                    if (ti >= 0)
+                        xv = x[(b * L + ti) * Dn + d];
+                    else if (x_prev)
+                        xv = x_prev[(b * (width - 1) + (width - 1) + ti) * Dn + d];
+                    pre += w[d * width + k] * xv;
+                }
+                u[(b * L + t) * Dn + d] = silu ? sp_silu(pre) : pre;
+            }
+        }
+    }
+    return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
     const int km1 = a.chunks - 1;
     // Loads of a group are issued before its stores so that the chain waits
     // on memory once per group, not once per chunk.
-    constexpr int G = 8;
+    constexpr int G = 16;
     for (int c0 = 0; c0 < km1; c0 += G) {
         float s[G], g[G];
 #pragma unroll
