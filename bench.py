@@ -214,6 +214,48 @@ def measure_decode(ms, reps=3):
             "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9}
 
 
+def measure_conv(ms, reps=20, width=4):
+    """ms_conv1d_silu on the 130M-layer shape (B8 L2048 D1536, bf16, width
+    4, bias, silu): ms per call over rotated buffers, kernel time from HIP
+    events, and the HBM rate of its algorithmic bytes (x read, u written,
+    weight and bias read)."""
+    import torch
+    import synth
+    w = synth.workload("m130m")
+    sets = []
+    for i in range(4):
+        c = synth.conv_inputs(w, width, device="cuda", seed=i)
+        sets.append((c, torch.empty_like(c["x"])))
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        c, u = sets[i % len(sets)]
+        ms.conv1d_silu(c["x"], c["weight"], c["bias"], None, u=u, stream=stream)
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(reps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_ms = start.elapsed_time(end) / reps
+    ms.profile_begin(reps)
+    for i in range(reps):
+        call(i)
+    torch.cuda.synchronize()
+    k_ms = ms.profile_end()["conv"]["mean_ms"]
+    e = 2 if w.io == "bf16" else 4
+    nb = 2 * w.batch * w.L * w.Dn * e + w.Dn * (width + 1) * 4
+    return {"workload": f"causal depthwise conv1d + silu (ms_conv1d_silu): batch {w.batch}, "
+                        f"L {w.L}, d_inner {w.Dn}, width {width}, {w.io}",
+            "ms_per_call": t_ms, "kernel_ms": k_ms, "bytes_per_call": nb,
+            "hbm_gbps": nb / (t_ms * 1e-3) / 1e9, "hbm_frac": nb / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9}
+
+
 # ------------------------------------------------------------ CPU oracle --
 def cpu_baseline(w, min_seconds, zoh=False):
     """fp64 oracle on this host's cores on the same workload, compute time
@@ -292,7 +334,7 @@ def _csv(dirname, suffix):
 
 def _short(name):
     m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|scan_chunks<[^>]*>|scan_summary<[^>]*>|"
-                  r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|step_quads<[^>]*>|"
+                  r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
                   r"neg_kernel)", name)
     return m.group(1) if m else name[:60]
 
@@ -447,6 +489,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_secondary and args.workload == "m130m" and not args.zoh:
         out["decode"] = measure_decode(ms)
+        torch.cuda.empty_cache()
+        out["conv1d"] = measure_conv(ms)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, zoh=args.zoh)

@@ -138,6 +138,37 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
                           void* y_t, int32_t batch, int32_t d_inner, int32_t d_state,
                           int32_t io, void* stream);
 
+/*
+ * Causal depthwise conv1d over the sequence, optionally followed by silu: the
+ * step of the block that turns the x branch into the scan input u (the
+ * lmnt.cn page, section 3.1, puts a depthwise 1D convolution of width about 4
+ * ahead of the SSM; its section 3.2 code uses groups = d_inner, width-1 zeros
+ * of left padding, keeps the first L outputs and applies silu):
+ *
+ *   pre[b,t,d] = bias[d] + sum_{k<width} weight[d][k] * x[b, t-(width-1)+k, d]
+ *   u[b,t,d]   = silu(pre) = pre * sigmoid(pre)   (silu != 0; else pre)
+ *
+ * where x at a time before 0 is x_prev[b][width-1 + time][d] when x_prev is
+ * given (the width-1 inputs that precede this piece, oldest first, so a long
+ * sequence can be processed in pieces or continued after a prefill) and 0
+ * otherwise.
+ *
+ *   x      : [batch][L][d_inner] io dtype            (required)
+ *   weight : [d_inner][width] fp32, width in 1..8    (required)
+ *   bias   : [d_inner] fp32                          (NULL = no bias)
+ *   x_prev : [batch][width-1][d_inner] io dtype      (NULL = zeros; ignored
+ *            when width == 1)
+ *   u      : [batch][L][d_inner] io dtype; must not overlap x or x_prev.
+ *   batch, seqlen, d_inner, io : as in ms_dims (batch, d_inner/256 and the
+ *            grid limits of ms_scan_fwd apply).
+ * Statuses as for ms_scan_fwd (MS_ERR_SHAPE for a width outside 1..8).  All
+ * pointers 16-byte aligned.  Deterministic.
+ */
+ms_status ms_conv1d_silu(const void* x, const float* weight, const float* bias,
+                         const void* x_prev, int32_t width, int32_t silu, void* u,
+                         int32_t batch, int64_t seqlen, int32_t d_inner, int32_t io,
+                         void* stream);
+
 /* Static text for a status code. */
 const char* ms_status_string(ms_status s);
 
@@ -150,7 +181,8 @@ int ms_abi_version(void);
 /*
  * Kernel timing, for benchmarks and profiling (not an operation of the
  * method).  Between ms_profile_begin and ms_profile_end, each of the next
- * `max_calls` successful calls of ms_scan_fwd / ms_state_update records a
+ * `max_calls` successful calls of ms_scan_fwd / ms_state_update /
+ * ms_conv1d_silu records a
  * pair of HIP events on its own stream around every kernel it launches, and
  * ms_profile_end waits for those events and returns the summed kernel times
  * per phase:
@@ -159,6 +191,7 @@ int ms_abi_version(void);
  *   MS_PHASE_CARRY    composition of segment summaries into start states
  *   MS_PHASE_MAIN     the scan that writes y (and h_last)
  *   MS_PHASE_STEP     ms_state_update's kernel
+ *   MS_PHASE_CONV     ms_conv1d_silu's kernel
  * A phase a call does not need records nothing.  Calls after the first
  * max_calls are not timed (out->calls counts the timed ones).  The event
  * records add a few microseconds per kernel to a call's wall time.
@@ -178,7 +211,8 @@ typedef enum {
     MS_PHASE_CARRY = 2,
     MS_PHASE_MAIN = 3,
     MS_PHASE_STEP = 4,
-    MS_PHASE_COUNT = 5
+    MS_PHASE_CONV = 5,
+    MS_PHASE_COUNT = 6
 } ms_phase;
 
 typedef struct {

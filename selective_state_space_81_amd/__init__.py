@@ -26,9 +26,10 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
           7: "MS_ERR_UNSUPPORTED", 8: "MS_ERR_HIP"}
 
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
-           "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end")
+           "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end",
+           "ms_conv1d_silu")
 
-PHASES = ("prep", "summary", "carry", "main", "step")  # ms_phase order
+PHASES = ("prep", "summary", "carry", "main", "step", "conv")  # ms_phase order
 
 
 class MsDims(ctypes.Structure):
@@ -77,6 +78,9 @@ def load(path: Optional[str] = None):
     lib.ms_last_error.argtypes = []
     lib.ms_abi_version.restype = ctypes.c_int
     lib.ms_abi_version.argtypes = []
+    lib.ms_conv1d_silu.restype = ctypes.c_int
+    lib.ms_conv1d_silu.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, ctypes.c_int64, i32, i32,
+                                   vp]
     lib.ms_profile_begin.restype = ctypes.c_int
     lib.ms_profile_begin.argtypes = [i32]
     lib.ms_profile_end.restype = ctypes.c_int
@@ -192,3 +196,19 @@ def profile_end() -> dict:
         n = out.launches[i]
         res[name] = {"launches": n, "mean_ms": (out.total_ms[i] / n) if n else None}
     return res
+
+
+def conv1d_silu(x, weight, bias=None, x_prev=None, *, silu=True, u=None, stream=None):
+    """ms_conv1d_silu on torch device tensors: causal depthwise conv1d of x
+    ([batch, L, d_inner]) with weight [d_inner, width] (+ bias), then silu.
+    x_prev: [batch, width-1, d_inner] inputs before t = 0 (None = zeros).
+    Returns u."""
+    import torch
+    batch, L, Dn = x.shape
+    width = weight.shape[1]
+    if u is None:
+        u = torch.empty_like(x)
+    rc = load().ms_conv1d_silu(_ptr(x), _ptr(weight), _ptr(bias), _ptr(x_prev), width,
+                               1 if silu else 0, _ptr(u), batch, L, Dn, _io(x), _stream(stream))
+    _check(rc)
+    return u

@@ -271,4 +271,27 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
     return MS_OK;
 }
 
+ms_status ms_conv1d_silu(const void* x, const float* weight, const float* bias,
+                         const void* x_prev, int32_t width, int32_t silu, void* u,
+                         int32_t batch, int64_t seqlen, int32_t d_inner, int32_t io,
+                         void* stream) {
+    g_err[0] = '\0';
+    ms_dims dims{batch, seqlen, d_inner, 1, io};
+    ms_status st = check_dims(&dims);
+    if (st != MS_OK) return st;
+    if (width < 1 || width > 8) return fail(MS_ERR_SHAPE, "width=%d must be in [1, 8]", width);
+    if (!x || !weight || !u) return fail(MS_ERR_NULL, "x, weight and u are required");
+    const void* ptrs[] = {x, weight, bias, x_prev, u};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    msscan::ConvArgs a{};
+    a.x = x; a.w = weight; a.bias = bias; a.x_prev = width > 1 ? x_prev : nullptr; a.u = u;
+    a.L = seqlen; a.batch = batch; a.Dn = d_inner; a.width = width;
+    msscan::prof_call();
+    hipError_t e = msscan::launch_conv1d(a, io == MS_BF16, silu != 0,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
 }  // extern "C"

@@ -50,6 +50,18 @@ struct ScanArgs {
     int waves;    // tile path: waves per workgroup
 };
 
+struct ConvArgs {
+    const void* x;
+    const float* w;      // [Dn][width]
+    const float* bias;   // [Dn] or null
+    const void* x_prev;  // [batch][width-1][Dn] or null
+    void* u;
+    int64_t L;
+    int batch;
+    int Dn;
+    int width;
+};
+
 struct StepArgs {
     float* h;
     const void* x;
@@ -76,6 +88,8 @@ hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool z
 bool lane_variant_exists(int n, bool zoh);
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
+// Causal depthwise conv1d (+ silu), width 1..8.
+hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s);
 // Decode step with 4 states per lane (d_state in {4, 8, ..., 128}).
 bool step_quads_supported(int batch, int d_inner, int n);
 hipError_t launch_step_quads(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
@@ -86,7 +100,14 @@ hipError_t launch_step_quads(const StepArgs& a, bool bf16, bool zoh, hipStream_t
 // profile is open.  Phase numbers are the ms_phase values of msscan.h.
 void prof_call();
 void prof_mark(hipStream_t s, int phase, int edge);
-enum : int { kPhasePrep = 0, kPhaseSummary = 1, kPhaseCarry = 2, kPhaseMain = 3, kPhaseStep = 4 };
+enum : int {
+    kPhasePrep = 0,
+    kPhaseSummary = 1,
+    kPhaseCarry = 2,
+    kPhaseMain = 3,
+    kPhaseStep = 4,
+    kPhaseConv = 5
+};
 struct ProfScope {
     hipStream_t s;
     int phase;

@@ -186,6 +186,27 @@ def decode_inputs(w: Workload, device="cpu", seed: int = 0) -> Dict[str, torch.T
     return out
 
 
+def conv_inputs(w: Workload, width: int = 4, device="cpu", seed: int = 0,
+                history: bool = False) -> Dict[str, torch.Tensor]:
+    """Inputs of the causal depthwise conv1d that produces the scan input:
+    x [batch, L, Dn] ~ N(0,1) (io dtype), weight [Dn, width] ~ N(0, 0.5^2),
+    bias [Dn] ~ N(0, 0.1^2) (fp32), and with history=True x_prev
+    [batch, width-1, Dn] ~ N(0,1) (io dtype)."""
+    dt = io_dtype(w.io)
+
+    def g(name):
+        return _gen(seed, w.name, "conv_" + name, device)
+
+    out = {
+        "x": _normal((w.batch, w.L, w.Dn), g("x"), device).to(dt),
+        "weight": _normal((w.Dn, width), g("weight"), device, std=0.5),
+        "bias": _normal((w.Dn,), g("bias"), device, std=0.1),
+    }
+    if history and width > 1:
+        out["x_prev"] = _normal((w.batch, width - 1, w.Dn), g("x_prev"), device).to(dt)
+    return out
+
+
 def algorithmic_bytes(w: Workload) -> int:
     """Bytes the scan must move once: u, delta, z read and y written
     ([batch, L, Dn] each, io dtype), B and C read ([batch, L, N]), A read

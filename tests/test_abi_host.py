@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "msscan.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ms_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(ms_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -103,4 +103,18 @@ def test_profile_errors_without_gpu_work():
     assert lib.ms_profile_end(None) == 7  # MS_ERR_UNSUPPORTED: no profile open
     assert lib.ms_profile_begin(0) == 2  # MS_ERR_SHAPE
     assert lib.ms_profile_begin(4097) == 2
-    assert ms.PHASES == ("prep", "summary", "carry", "main", "step")
+    assert ms.PHASES == ("prep", "summary", "carry", "main", "step", "conv")
+
+
+def test_conv_validation_host_only():
+    lib = ms.load()
+    p = 16
+
+    def call(width=4, silu=1, x=p, w=p, u=p, batch=2, L=10, Dn=8, io=1):
+        return lib.ms_conv1d_silu(x, w, None, None, width, silu, u, batch, L, Dn, io, None)
+
+    assert call(width=0) == 2 and call(width=9) == 2  # MS_ERR_SHAPE
+    assert call(x=None) == 1 and call(w=None) == 1 and call(u=None) == 1  # MS_ERR_NULL
+    assert call(io=5) == 3  # MS_ERR_DTYPE
+    assert call(L=0) == 2 and call(batch=0) == 2
+    assert call(u=24) == 5  # MS_ERR_ALIGN
