@@ -73,10 +73,17 @@ def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
 
+def _disc(zoh: bool, bilinear: bool) -> int:
+    if zoh and bilinear:
+        raise ValueError("zoh and bilinear are exclusive")
+    return 2 if bilinear else (1 if zoh else 0)
+
+
 def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
-         softplus: bool = True, zoh: bool = False, nthreads: int = 0
+         softplus: bool = True, zoh: bool = False, nthreads: int = 0, bilinear: bool = False
          ) -> Tuple[np.ndarray, np.ndarray]:
-    """Selective scan in fp64.
+    """Selective scan in fp64 (Euler by default; zoh or bilinear pick the
+    other discretisations).
 
     u, delta, z: [batch, L, Dn]; B, C: [batch, L, N]; A: [Dn, N];
     D, delta_bias: [Dn]; h0: [batch, Dn, N].  Returns (y [batch, L, Dn],
@@ -96,7 +103,7 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     y = np.empty((batch, L, Dn), dtype=np.float64)
     h_last = np.empty((batch, Dn, N), dtype=np.float64)
     rc = lib.oracle_scan(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                         _ptr(delta_bias), _ptr(h0), int(bool(softplus)), int(bool(zoh)),
+                         _ptr(delta_bias), _ptr(h0), int(bool(softplus)), _disc(zoh, bilinear),
                          batch, L, Dn, N, _ptr(y), _ptr(h_last), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_scan failed with code {rc}")
@@ -104,7 +111,8 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
 
 
 def step(h, x, delta, A, B, C, D=None, z=None, delta_bias=None,
-         softplus: bool = True, zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+         softplus: bool = True, zoh: bool = False, bilinear: bool = False
+         ) -> Tuple[np.ndarray, np.ndarray]:
     """One decode step in fp64.  h: [batch, Dn, N] (not modified; the updated
     state is returned); x, delta, z: [batch, Dn]; B, C: [batch, N].
     Returns (y [batch, Dn], h_new [batch, Dn, N])."""
@@ -117,7 +125,7 @@ def step(h, x, delta, A, B, C, D=None, z=None, delta_bias=None,
     assert h.shape == (batch, Dn, N) and B.shape == (batch, N) and C.shape == (batch, N)
     y = np.empty((batch, Dn), dtype=np.float64)
     rc = lib.oracle_step(_ptr(h), _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                         _ptr(z), _ptr(delta_bias), int(bool(softplus)), int(bool(zoh)),
+                         _ptr(z), _ptr(delta_bias), int(bool(softplus)), _disc(zoh, bilinear),
                          batch, Dn, N, _ptr(y))
     if rc != 0:
         raise RuntimeError(f"oracle_step failed with code {rc}")

@@ -67,20 +67,33 @@ static double step_size(double draw, const double* delta_bias, int64_t d, int so
 }
 
 /* One timestep of one channel: updates h[0..N) in place, returns the gated
- * output.  The body is the loop body of the lmnt page section 3.2, with the
- * ZOH factor of the intelliparadigm page section 3.2 when zoh != 0. */
+ * output.  The body is the loop body of the lmnt page section 3.2.  The
+ * discretisation `disc` picks A_bar and the factor of B*u:
+ *   0 Euler     A_bar = exp(dt*A),  dt
+ *   1 ZOH       A_bar = exp(dt*A),  (exp(dt*A) - 1)/A  (dt at A == 0)
+ *               (intelliparadigm page, section 3.2)
+ *   2 bilinear  A_bar = (1 + dt*A/2)/(1 - dt*A/2),  dt/(1 - dt*A/2)
+ *               (the bilinear transform the intelliparadigm page's section 3.2
+ *               code names; its printed code is garbled, so this is the
+ *               textbook form for a diagonal A). */
 static double one_step(double* h, double ut, double dt, const double* Arow,
                        const double* Bt, const double* Ct, int64_t N,
-                       double Dd, int has_D, double zt, int has_z, int zoh) {
+                       double Dd, int has_D, double zt, int has_z, int disc) {
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
         double a = Arow[n];
-        double abar = exp(dt * a);
-        double bfac;
-        if (zoh)
-            bfac = (a == 0.0) ? dt : expm1(dt * a) / a;
-        else
-            bfac = dt;
+        double abar, bfac;
+        if (disc == 2) {
+            const double half = 0.5 * dt * a;
+            abar = (1.0 + half) / (1.0 - half);
+            bfac = dt / (1.0 - half);
+        } else {
+            abar = exp(dt * a);
+            if (disc == 1)
+                bfac = (a == 0.0) ? dt : expm1(dt * a) / a;
+            else
+                bfac = dt;
+        }
         h[n] = abar * h[n] + bfac * Bt[n] * ut;
         acc += Ct[n] * h[n];
     }
@@ -95,7 +108,7 @@ static double one_step(double* h, double ut, double dt, const double* Arow,
 int oracle_scan(const double* u, const double* delta_raw, const double* A,
                 const double* B, const double* C, const double* D,
                 const double* z, const double* delta_bias, const double* h0,
-                int softplus, int zoh, int64_t batch, int64_t L, int64_t Dn,
+                int softplus, int disc, int64_t batch, int64_t L, int64_t Dn,
                 int64_t N, double* y, double* h_last, int nthreads) {
     if (!u || !delta_raw || !A || !B || !C || !y) return -1;
     if (batch < 0 || L < 0 || Dn < 0 || N < 1) return -1;
@@ -128,7 +141,7 @@ int oracle_scan(const double* u, const double* delta_raw, const double* A,
                 double dt = step_size(delta_raw[e], delta_bias, d, softplus);
                 y[e] = one_step(h, u[e], dt, A + d * N, Bt, Ct, N,
                                 D ? D[d] : 0.0, D != NULL, z ? z[e] : 0.0,
-                                z != NULL, zoh);
+                                z != NULL, disc);
             }
             if (h_last)
                 for (int64_t n = 0; n < N; ++n) h_last[(b * Dn + d) * N + n] = h[n];
@@ -145,7 +158,7 @@ int oracle_scan(const double* u, const double* delta_raw, const double* A,
 int oracle_step(double* h, const double* x, const double* delta_raw,
                 const double* A, const double* B, const double* C,
                 const double* D, const double* z, const double* delta_bias,
-                int softplus, int zoh, int64_t batch, int64_t Dn, int64_t N,
+                int softplus, int disc, int64_t batch, int64_t Dn, int64_t N,
                 double* y) {
     if (!h || !x || !delta_raw || !A || !B || !C || !y) return -1;
     if (batch < 0 || Dn < 0 || N < 1) return -1;
@@ -158,12 +171,11 @@ int oracle_step(double* h, const double* x, const double* delta_raw,
         double dt = step_size(delta_raw[e], delta_bias, d, softplus);
         y[e] = one_step(h + e * N, x[e], dt, A + d * N, B + b * N, C + b * N,
                         N, D ? D[d] : 0.0, D != NULL, z ? z[e] : 0.0,
-                        z != NULL, zoh);
+                        z != NULL, disc);
     }
     return 0;
 }
 
-/* Number of threads OpenMP would use (for reporting the CPU baseline). */
 /* Causal depthwise conv1d, optionally followed by silu: the step that turns
  * the x branch of the block input into the scan input u (lmnt page,
  * section 3.1: a depthwise 1D convolution of width about 4 on x_ssm before
@@ -203,6 +215,7 @@ int oracle_conv1d(const double* x, const double* w, const double* bias, const do
     return 0;
 }
 
+/* Number of threads OpenMP would use (for reporting the CPU baseline). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
