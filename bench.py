@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b", "long"])
     ap.add_argument("--zoh", action="store_true", help="zero-order hold instead of Euler")
+    ap.add_argument("--bilinear", action="store_true", help="bilinear instead of Euler")
     ap.add_argument("--buffer-sets", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -87,18 +88,20 @@ def source_hash() -> str:
 
 
 # ---------------------------------------------------------------- counting --
-def valu_ops_per_element(n_state: int, zoh: bool, softplus: bool = True) -> int:
+def valu_ops_per_element(n_state: int, disc: str, softplus: bool = True) -> int:
     """fp32 VALU operations the method needs per element (b, t, d), counted
     one per lane-instruction, an FMA as one:
       per state: dt*A, exp, B*x (Euler x = dt*u), A_bar*h + .., C*h + ..  = 5
                  ZOH adds (A_bar - 1)/A as one FMA with 1/A kept, and one
                  more product with B*u                                   = 7
+                 bilinear: dt*A, 1 - ../2, reciprocal r, A_bar = 2r - 1,
+                 x*r, B*.., A_bar*h + .., C*h + ..                        = 8
       per element: delta + bias, softplus (exp, 1 +, log), dt*u (Euler),
                  D*u + y, silu gate (exp, 1 +, reciprocal, z*r), y*gate.
     Only the kernel that writes y is priced this way; the segment-summary
     pass is work the parallel split adds, not work of the method."""
-    per_state = 7 if zoh else 5
-    per_elem = 1 + (3 if softplus else 0) + (0 if zoh else 1) + 1 + 4 + 1
+    per_state = {"euler": 5, "zoh": 7, "bilinear": 8}[disc]
+    per_elem = 1 + (3 if softplus else 0) + (0 if disc == "zoh" else 1) + 1 + 4 + 1
     return per_state * n_state + per_elem
 
 
@@ -114,7 +117,7 @@ def make_sets(w, n_sets):
     return sets
 
 
-def time_calls(ms, sets, w, steps, warmup, zoh=False):
+def time_calls(ms, sets, w, steps, warmup, zoh=False, bilinear=False):
     """Two timed regions of `steps` ms_scan_fwd calls each, on the stream the
     calls are enqueued on (torch's current stream):
       1. plain calls, bracketed by torch events -> ms per call (the value);
@@ -125,14 +128,14 @@ def time_calls(ms, sets, w, steps, warmup, zoh=False):
     import torch
     stream = torch.cuda.current_stream()
     io = ms.MS_BF16 if w.io == "bf16" else ms.MS_F32
-    ws_n = ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, io, ms.flags(w.softplus, zoh))
+    ws_n = ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, io, ms.flags(w.softplus, zoh, bilinear))
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
     def call(i):
         x, y = sets[i % len(sets)]
         ms.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
-                    delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh, y=y,
-                    workspace=ws if ws_n else None, stream=stream)
+                    delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh,
+                    bilinear=bilinear, y=y, workspace=ws if ws_n else None, stream=stream)
 
     for i in range(warmup):
         call(i)
@@ -257,7 +260,7 @@ def measure_conv(ms, reps=20, width=4):
 
 
 # ------------------------------------------------------------ CPU oracle --
-def cpu_baseline(w, min_seconds, zoh=False):
+def cpu_baseline(w, min_seconds, disc="euler"):
     """fp64 oracle on this host's cores on the same workload, compute time
     only: batch rows (full sequence; all channels, or the first `chans` when a
     row is very large) are scanned one after another, cycling over the batch,
@@ -277,7 +280,8 @@ def cpu_baseline(w, min_seconds, zoh=False):
         f.update({k: np.ascontiguousarray(x[k][b:b + 1].double().numpy()) for k in ("B", "C")})
         t0 = time.perf_counter()
         oracle.scan(f["u"], f["delta"], shared["A"], f["B"], f["C"], D=shared.get("D"), z=f["z"],
-                    delta_bias=shared.get("delta_bias"), softplus=w.softplus, zoh=zoh,
+                    delta_bias=shared.get("delta_bias"), softplus=w.softplus,
+                    zoh=disc == "zoh", bilinear=disc == "bilinear",
                     nthreads=threads)
         elapsed += time.perf_counter() - t0
         rows += 1
@@ -295,7 +299,7 @@ def cpu_baseline(w, min_seconds, zoh=False):
     what = f"all {w.Dn} channels" if chans == w.Dn else f"the first {chans} of {w.Dn} channels"
     return {"value": elems / elapsed, "unit": "elem/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} batch rows of the {w.name} workload (each: {what} "
-                      f"x L={w.L}, d_state {w.N}, {'ZOH' if zoh else 'Euler'}, "
+                      f"x L={w.L}, d_state {w.N}, {disc}, "
                       f"softplus {'on' if w.softplus else 'off'}, z gate, D), cycling over "
                       f"its {w.batch} rows; fp64 C oracle, OpenMP over channels, "
                       f"{threads} threads; {elapsed:.1f} s compute; host CPU: {cpu}"}
@@ -406,11 +410,11 @@ def rocprof_summary(args):
 
 
 # ------------------------------------------------------------------ main --
-def measure(ms, w_name, steps, warmup, n_sets, zoh=False):
+def measure(ms, w_name, steps, warmup, n_sets, zoh=False, bilinear=False):
     import synth
     w = synth.workload(w_name)
     sets = make_sets(w, n_sets)
-    t_ms, ph = time_calls(ms, sets, w, steps, warmup, zoh=zoh)
+    t_ms, ph = time_calls(ms, sets, w, steps, warmup, zoh=zoh, bilinear=bilinear)
     del sets
     return w, t_ms, ph
 
@@ -434,12 +438,17 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     n_sets = args.buffer_sets if args.workload != "long" else 1  # long: 13 GB per set
-    w, t_ms, ph = measure(ms, args.workload, args.steps, args.warmup, n_sets, zoh=args.zoh)
+    if args.zoh and args.bilinear:
+        print("--zoh and --bilinear are exclusive", file=sys.stderr)
+        sys.exit(2)
+    w, t_ms, ph = measure(ms, args.workload, args.steps, args.warmup, n_sets, zoh=args.zoh,
+                          bilinear=args.bilinear)
+    disc = "zoh" if args.zoh else ("bilinear" if args.bilinear else "euler")
     torch.cuda.empty_cache()
     elems = w.batch * w.L * w.Dn
     alg_bytes = synth.algorithmic_bytes(w)
     main_ms = ph["main"]["mean_ms"]
-    ops = valu_ops_per_element(w.N, zoh=args.zoh, softplus=w.softplus) * elems
+    ops = valu_ops_per_element(w.N, disc, softplus=w.softplus) * elems
     achieved = ops / (main_ms * 1e-3) / 1e12
     src = source_hash()
     gbps = alg_bytes / (t_ms * 1e-3) / 1e9
@@ -459,7 +468,7 @@ def main():
         "config": {"workload": WORKLOAD_TITLE[w.name],
                    "batch": w.batch, "seq_len": w.L, "d_inner": w.Dn, "d_state": w.N,
                    "io": w.io, "state": "f32",
-                   "discretisation": "zoh" if args.zoh else "euler",
+                   "discretisation": disc,
                    "softplus_bias": w.softplus, "z_gate": True, "D_skip": True,
                    "buffer_sets": n_sets, "parallelism": "single-gpu"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_TOPS,
@@ -467,7 +476,7 @@ def main():
                      "traffic": load_traffic(w.name, src),
                      "kernel": "scan main pass (writes y)",
                      "kernel_mean_ms": main_ms,
-                     "ops_per_element": valu_ops_per_element(w.N, zoh=args.zoh,
+                     "ops_per_element": valu_ops_per_element(w.N, disc,
                                                              softplus=w.softplus),
                      "ops_per_launch": ops,
                      "algorithmic_bytes_per_launch": alg_bytes},
@@ -477,7 +486,7 @@ def main():
         "kernels_ms": {k: v["mean_ms"] for k, v in ph.items() if k != "calls" and v["launches"]},
         "source_hash": src,
     }
-    if not args.no_secondary and args.workload == "m130m" and not args.zoh:
+    if not args.no_secondary and args.workload == "m130m" and disc == "euler":
         w3, t3, ph3 = measure(ms, "m3b", max(3, args.steps // 4), 2, 2)
         e3 = w3.batch * w3.L * w3.Dn
         out["secondary"] = {"workload": WORKLOAD_TITLE["m3b"] + " (B4 L8192 D5120 N16 bf16, "
@@ -487,13 +496,13 @@ def main():
                             "kernels_ms": {k: v["mean_ms"] for k, v in ph3.items()
                                            if k != "calls" and v["launches"]}}
         torch.cuda.empty_cache()
-    if not args.no_secondary and args.workload == "m130m" and not args.zoh:
+    if not args.no_secondary and args.workload == "m130m" and disc == "euler":
         out["decode"] = measure_decode(ms)
         torch.cuda.empty_cache()
         out["conv1d"] = measure_conv(ms)
         torch.cuda.empty_cache()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, zoh=args.zoh)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, disc)
     print(json.dumps(out), flush=True)
 
 

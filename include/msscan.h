@@ -6,9 +6,11 @@
  *
  *   dt    = softplus(delta[b,t,d] + delta_bias[d])    (MS_SOFTPLUS set)
  *         =          delta[b,t,d] + delta_bias[d]     (otherwise)
- *   A_bar = exp(dt * A[d,n])
+ *   A_bar = exp(dt * A[d,n])                           (Euler, MS_ZOH)
+ *         = (1 + dt*A[d,n]/2) / (1 - dt*A[d,n]/2)      (MS_BILINEAR)
  *   B_bar = dt * B[b,t,n]                             (Euler, default)
  *         = (exp(dt*A[d,n]) - 1) / A[d,n] * B[b,t,n]  (MS_ZOH; dt*B when A == 0)
+ *         = dt / (1 - dt*A[d,n]/2) * B[b,t,n]          (MS_BILINEAR)
  *   h[n]  = A_bar * h[n] + B_bar * u[b,t,d]           (h starts at h0, else 0)
  *   y     = sum_n C[b,t,n] * h[n]  +  D[d] * u[b,t,d]
  *   out[b,t,d] = y * z * sigmoid(z),  z = z[b,t,d]    (when z is given; else y)
@@ -24,6 +26,8 @@
  *   - zero-order hold A_bar = exp(dt A), B_bar = (A_bar - I) A^-1 B: "Mamba模型
  *     解析：从状态空间到序列建模实践" (intelliparadigm.com), section 3.2, and the
  *     integral form on the jsqmd page, section 2.3;
+ *   - the bilinear transform named by the same page's section 3.2 code (printed
+ *     garbled; the textbook form for a diagonal A is taken);
  *   - the scan as a composition of per-step affine maps, evaluated in parallel:
  *     jsqmd page section 3.4, lmnt page section 2.2;
  *   - single-token recurrent inference with one kept fp32 state: lmnt page,
@@ -67,7 +71,7 @@ typedef enum {
     MS_ERR_NULL = 1,        /* a required pointer is NULL                       */
     MS_ERR_SHAPE = 2,       /* a size is out of range                           */
     MS_ERR_DTYPE = 3,       /* io is not MS_F32 or MS_BF16                      */
-    MS_ERR_FLAGS = 4,       /* unknown bits in flags                            */
+    MS_ERR_FLAGS = 4,       /* unknown flag bits, or MS_ZOH with MS_BILINEAR    */
     MS_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned            */
     MS_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required       */
     MS_ERR_UNSUPPORTED = 7, /* valid request this build cannot serve            */
@@ -80,6 +84,7 @@ typedef enum { MS_F32 = 0, MS_BF16 = 1 } ms_dtype;
 /* Flag bits. */
 #define MS_SOFTPLUS (1u << 0) /* dt = softplus(delta + bias); else dt = delta + bias */
 #define MS_ZOH (1u << 1)      /* zero-order hold B_bar; else Euler B_bar = dt * B     */
+#define MS_BILINEAR (1u << 2) /* bilinear A_bar, B_bar (exclusive with MS_ZOH)        */
 
 typedef struct {
     int32_t batch;   /* >= 1                                   */

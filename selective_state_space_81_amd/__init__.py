@@ -20,6 +20,7 @@ MS_F32 = 0
 MS_BF16 = 1
 MS_SOFTPLUS = 1
 MS_ZOH = 2
+MS_BILINEAR = 4
 
 STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
           4: "MS_ERR_FLAGS", 5: "MS_ERR_ALIGN", 6: "MS_ERR_WORKSPACE",
@@ -119,8 +120,9 @@ def _check(rc: int):
         raise MsError(rc, load().ms_last_error().decode())
 
 
-def flags(softplus: bool = True, zoh: bool = False) -> int:
-    return (MS_SOFTPLUS if softplus else 0) | (MS_ZOH if zoh else 0)
+def flags(softplus: bool = True, zoh: bool = False, bilinear: bool = False) -> int:
+    return (MS_SOFTPLUS if softplus else 0) | (MS_ZOH if zoh else 0) | \
+        (MS_BILINEAR if bilinear else 0)
 
 
 def dims(batch: int, seqlen: int, d_inner: int, d_state: int, io: int) -> MsDims:
@@ -137,7 +139,7 @@ def workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int, io: int
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=True, zoh=False,
-             y=None, h0=None, h_last=None, workspace=None, stream=None):
+             y=None, h0=None, h_last=None, workspace=None, stream=None, bilinear=False):
     """ms_scan_fwd on torch device tensors.  Allocates y (and the workspace)
     when not given -- that allocation is torch's, outside the library.
     Returns y."""
@@ -145,7 +147,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=Tru
     batch, L, Dn = u.shape
     N = A.shape[1]
     io = _io(u)
-    fl = flags(softplus, zoh)
+    fl = flags(softplus, zoh, bilinear)
     if y is None:
         y = torch.empty_like(u)
     ws_n = workspace_bytes(batch, L, Dn, N, io, fl)
@@ -161,7 +163,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=Tru
 
 
 def state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None, *,
-                 softplus=True, zoh=False, y_t=None, stream=None):
+                 softplus=True, zoh=False, y_t=None, stream=None, bilinear=False):
     """ms_state_update on torch device tensors; h is updated in place.
     Returns y_t."""
     import torch
@@ -171,7 +173,7 @@ def state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None
         y_t = torch.empty_like(x_t)
     rc = load().ms_state_update(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t),
                                 _ptr(C_t), _ptr(D), _ptr(z_t), _ptr(delta_bias),
-                                flags(softplus, zoh), _ptr(y_t), batch, Dn, N, _io(x_t),
+                                flags(softplus, zoh, bilinear), _ptr(y_t), batch, Dn, N, _io(x_t),
                                 _stream(stream))
     _check(rc)
     return y_t

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "device_common.h"
 #include "msscan_internal.h"
 
 namespace {
@@ -48,10 +49,20 @@ ms_status check_dims(const ms_dims* d) {
     return MS_OK;
 }
 
+constexpr uint32_t kKnownFlags = MS_SOFTPLUS | MS_ZOH | MS_BILINEAR;
+
 ms_status check_flags(uint32_t flags) {
-    if (flags & ~(uint32_t)(MS_SOFTPLUS | MS_ZOH))
-        return fail(MS_ERR_FLAGS, "unknown flag bits 0x%x", flags & ~(uint32_t)(MS_SOFTPLUS | MS_ZOH));
+    if (flags & ~kKnownFlags)
+        return fail(MS_ERR_FLAGS, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+    if ((flags & MS_ZOH) && (flags & MS_BILINEAR))
+        return fail(MS_ERR_FLAGS, "MS_ZOH and MS_BILINEAR are exclusive");
     return MS_OK;
+}
+
+// Discretisation of the flags (kEuler / kZoh / kBilinear of the kernels).
+int disc_of(uint32_t flags) {
+    return (flags & MS_BILINEAR) ? msscan::dev::kBilinear
+                                 : ((flags & MS_ZOH) ? msscan::dev::kZoh : msscan::dev::kEuler);
 }
 
 // Fast paths.  Both map one 64-channel tile of one batch row to a
@@ -61,7 +72,7 @@ ms_status check_flags(uint32_t flags) {
 // kMinSegment).
 //   lane path (d_state 8, 16, 32; 64 with Euler): one wave per workgroup,
 //     all states of a channel in one lane;
-//   tile path (d_state 128, 64 with ZOH, or the others when the lane path is
+//   tile path (d_state 128, 64 with ZOH or bilinear, or the others when the lane path is
 //     compiled out): several waves split d_state and share per-element work
 //     through LDS.
 #ifndef MSSCAN_TILE_WAVES
@@ -92,8 +103,8 @@ void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) 
     p.chunks = (int)((d.seqlen + len - 1) / len);
 }
 
-bool lane_plan(const ms_dims& d, bool zoh, msscan::Plan& p) {
-    if (!MSSCAN_LANE_PATH || !msscan::lane_variant_exists(d.d_state, zoh)) return false;
+bool lane_plan(const ms_dims& d, int disc, msscan::Plan& p) {
+    if (!MSSCAN_LANE_PATH || !msscan::lane_variant_exists(d.d_state, disc)) return false;
     p.tile_path = 2;
     p.ns = d.d_state;
     p.waves = 1;
@@ -123,10 +134,13 @@ bool tile_plan(const ms_dims& d, msscan::Plan& p) {
 msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
     msscan::Plan p{};
     const int N = d.d_state;
-    if (lane_plan(d, (flags & MS_ZOH) != 0, p) || tile_plan(d, p)) {
+    // Per segment boundary and channel: N summary states, plus the segment
+    // decay -- one sum of dt, or N products of A_bar for the bilinear form.
+    const size_t per_channel = (size_t)N + ((flags & MS_BILINEAR) ? (size_t)N : 1);
+    if (lane_plan(d, disc_of(flags), p) || tile_plan(d, p)) {
         if (p.chunks > 1) {
             const size_t km1 = (size_t)(p.chunks - 1);
-            p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
+            p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * per_channel;
         }
         // tile path: fp32 copy of B and C, rows [b][t][B_t | C_t], read as DPP
         // operands (the lane path reads B and C in place).
@@ -152,7 +166,7 @@ msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
     p.chunks = (int)((d.seqlen + len - 1) / len);
     if (p.chunks > 1) {
         const size_t km1 = (size_t)(p.chunks - 1);
-        p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * ((size_t)N + 1);
+        p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * per_channel;
     } else {
         p.ws_floats = 0;
     }
@@ -231,14 +245,19 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
         const size_t km1 = (size_t)(p.chunks - 1);
         a.agg = ws;
         const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
-        a.sdt = ws + ((agg_n + 63) / 64) * 64;
+        float* after = ws + ((agg_n + 63) / 64) * 64;
+        if (flags & MS_BILINEAR)
+            a.prod = after;  // [batch][chunks-1][N][Dn], like the summaries
+        else
+            a.sdt = after;
     }
-    const bool bf16 = dims->io == MS_BF16, zoh = (flags & MS_ZOH) != 0;
+    const bool bf16 = dims->io == MS_BF16;
+    const int disc = disc_of(flags);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     msscan::prof_call();
-    hipError_t e = p.tile_path == 2   ? msscan::launch_scan_lanes(p, a, bf16, zoh, hs)
-                   : p.tile_path == 1 ? msscan::launch_scan_tiles(p, a, bf16, zoh, hs)
-                                      : msscan::launch_scan(p, a, bf16, zoh, hs);
+    hipError_t e = p.tile_path == 2   ? msscan::launch_scan_lanes(p, a, bf16, disc, hs)
+                   : p.tile_path == 1 ? msscan::launch_scan_tiles(p, a, bf16, disc, hs)
+                                      : msscan::launch_scan(p, a, bf16, disc, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }
@@ -262,11 +281,12 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
     a.bias = delta_bias; a.y = y_t; a.batch = batch; a.Dn = d_inner; a.N = d_state;
     a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
     msscan::prof_call();
-    const bool bf16 = io == MS_BF16, zoh = (flags & MS_ZOH) != 0;
+    const bool bf16 = io == MS_BF16;
+    const int disc = disc_of(flags);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e = msscan::step_quads_supported(batch, d_inner, d_state)
-                       ? msscan::launch_step_quads(a, bf16, zoh, hs)
-                       : msscan::launch_step(a, bf16, zoh, hs);
+                       ? msscan::launch_step_quads(a, bf16, disc, hs)
+                       : msscan::launch_step(a, bf16, disc, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

@@ -63,7 +63,7 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-template <int G, int BR, bool BF16, bool ZOH>
+template <int G, int BR, bool BF16, int DISC>
 __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
     constexpr int N = 4 * G;
     const int quads = a.Dn * G;
@@ -109,12 +109,19 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float arg = dt * A2[k];
-            const float abar = hw_exp2(arg);
-            float bx;
-            if constexpr (ZOH)
-                bx = zoh_factor(dt, arg, abar, an[k] != 0.f ? 1.f / an[k] : 0.f) * (bs[k] * xv[r]);
-            else
-                bx = dx * bs[k];
+            float abar, bx;
+            if constexpr (DISC == kBilinear) {
+                const float rb = bilinear_r(arg);
+                abar = fmaf(2.f, rb, -1.f);
+                bx = (dx * rb) * bs[k];
+            } else {
+                abar = hw_exp2(arg);
+                if constexpr (DISC == kZoh)
+                    bx = zoh_factor(dt, arg, abar, an[k] != 0.f ? 1.f / an[k] : 0.f) *
+                         (bs[k] * xv[r]);
+                else
+                    bx = dx * bs[k];
+            }
             hs[k] = fmaf(abar, hs[k], bx);
             y = fmaf(cs[k], hs[k], y);
         }
@@ -131,27 +138,32 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
     }
 }
 
-template <int BR, bool BF16, bool ZOH>
+template <int BR, bool BF16, int DISC>
 hipError_t launch_g(const StepArgs& a, hipStream_t s) {
     const int G = a.N / 4;
     const int64_t quads = (int64_t)a.Dn * G;
     const dim3 grid((unsigned)((quads + 255) / 256), (unsigned)((a.batch + BR - 1) / BR)),
         block(256);
     switch (G) {
-        case 1: hipLaunchKernelGGL((step_quads<1, BR, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((step_quads<2, BR, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((step_quads<4, BR, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((step_quads<8, BR, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((step_quads<16, BR, BF16, ZOH>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((step_quads<32, BR, BF16, ZOH>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((step_quads<1, BR, BF16, DISC>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((step_quads<2, BR, BF16, DISC>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((step_quads<4, BR, BF16, DISC>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((step_quads<8, BR, BF16, DISC>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((step_quads<16, BR, BF16, DISC>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((step_quads<32, BR, BF16, DISC>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <bool BF16, bool ZOH>
-hipError_t launch_p(const StepArgs& a, hipStream_t s) {
-    return launch_g<MSSCAN_STEP_ROWS, BF16, ZOH>(a, s);
+template <bool BF16>
+hipError_t launch_p(const StepArgs& a, int disc, hipStream_t s) {
+    switch (disc) {
+        case kEuler: return launch_g<MSSCAN_STEP_ROWS, BF16, kEuler>(a, s);
+        case kZoh: return launch_g<MSSCAN_STEP_ROWS, BF16, kZoh>(a, s);
+        case kBilinear: return launch_g<MSSCAN_STEP_ROWS, BF16, kBilinear>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -162,11 +174,10 @@ bool step_quads_supported(int batch, int d_inner, int n) {
     return (int64_t)d_inner * (n / 4) < (1LL << 30);  // quad index of a row fits int
 }
 
-hipError_t launch_step_quads(const StepArgs& a, bool bf16, bool zoh, hipStream_t s) {
+hipError_t launch_step_quads(const StepArgs& a, bool bf16, int disc, hipStream_t s) {
     if (!step_quads_supported(a.batch, a.Dn, a.N)) return hipErrorInvalidValue;
     ProfScope ps(s, kPhaseStep);
-    if (bf16) return zoh ? launch_p<true, true>(a, s) : launch_p<true, false>(a, s);
-    return zoh ? launch_p<false, true>(a, s) : launch_p<false, false>(a, s);
+    return bf16 ? launch_p<true>(a, disc, s) : launch_p<false>(a, disc, s);
 }
 
 }  // namespace msscan

@@ -62,6 +62,17 @@ __device__ __forceinline__ float step_size(float draw, float bias, int softplus)
     return softplus ? softplus_f(v) : v;
 }
 
+// Discretisations (ms_scan_fwd flags): Euler (A_bar = exp(dt A), B_bar =
+// dt B), zero-order hold (B_bar = (exp(dt A) - 1)/A B) and bilinear
+// (A_bar = (1 + dt A/2)/(1 - dt A/2), B_bar = dt/(1 - dt A/2) B).
+enum : int { kEuler = 0, kZoh = 1, kBilinear = 2 };
+
+// Bilinear factor r = 1/(1 - dt*A/2) from t = dt*A*log2(e) (the argument the
+// other discretisations feed to exp2): A_bar = 2r - 1 and B_bar = dt*r*B.
+__device__ __forceinline__ float bilinear_r(float t) {
+    return hw_rcp(fmaf(t, -0.5f * kLn2, 1.f));
+}
+
 // ZOH input factor (exp(x) - 1)/A for x = dt*A, from t = x*log2(e) (the
 // argument already formed for abar = 2^t).  For |x| < 1/32 the series
 // dt*(1 + x/2 + x^2/6), written in t, avoids the cancellation of exp(x) - 1

@@ -38,7 +38,8 @@ struct ScanArgs {
     float* h_last;
     void* y;
     float* agg;   // [batch][chunks-1][N][Dn]: chunk summaries, then carries
-    float* sdt;   // [batch][chunks-1][Dn]: sum of dt over each chunk
+    float* sdt;   // [batch][chunks-1][Dn]: sum of dt over each chunk (exp-based A_bar)
+    float* prod;  // [batch][chunks-1][N][Dn]: product of A_bar over each chunk (bilinear)
     float* bcw;   // tile path: [batch][waves][L][2*ns] fp32 B_t then C_t slices
     int64_t L;
     int64_t chunk_len;
@@ -80,19 +81,20 @@ struct StepArgs {
 };
 
 // Each returns hipSuccess or the first launch error.
-hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
-hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
+// disc: 0 Euler, 1 zero-order hold, 2 bilinear (kEuler / kZoh / kBilinear).
+hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
+hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
 bool tile_variant_exists(int ns, int waves);
-hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s);
-bool lane_variant_exists(int n, bool zoh);
+hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
+bool lane_variant_exists(int n, int disc);
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
+hipError_t launch_step(const StepArgs& a, bool bf16, int disc, hipStream_t s);
 // Causal depthwise conv1d (+ silu), width 1..8.
 hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s);
 // Decode step with 4 states per lane (d_state in {4, 8, ..., 128}).
 bool step_quads_supported(int batch, int d_inner, int n);
-hipError_t launch_step_quads(const StepArgs& a, bool bf16, bool zoh, hipStream_t s);
+hipError_t launch_step_quads(const StepArgs& a, bool bf16, int disc, hipStream_t s);
 
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
 // ProfScope records the phase's begin event at construction and its end

@@ -53,9 +53,10 @@ __device__ __forceinline__ void load_a(const float* A, int dd, int N, int n0, in
     }
 }
 
-// One timestep of the lane's NS states; returns the partial readout.
-template <int NS, bool BF16, bool ZOH, bool READOUT>
-__device__ __forceinline__ float advance(float (&h)[NS], const float (&A2)[NS],
+// One timestep of the lane's NS states; returns the partial readout.  PROD
+// multiplies each state's A_bar into P (the bilinear segment decay).
+template <int NS, bool BF16, int DISC, bool READOUT, bool PROD = false>
+__device__ __forceinline__ float advance(float (&h)[NS], float (&P)[NS], const float (&A2)[NS],
                                          const float (&invA)[NS], float dt, float uval,
                                          const void* B, const void* C, int64_t row,
                                          int nvalid) {
@@ -66,12 +67,19 @@ __device__ __forceinline__ float advance(float (&h)[NS], const float (&A2)[NS],
         const bool ok = j < nvalid;
         const float bn = ok ? ld<BF16>(B, row + j) : 0.f;
         const float arg = dt * A2[j];
-        const float abar = hw_exp2(arg);
-        float bx;
-        if constexpr (ZOH)
-            bx = zoh_factor(dt, arg, abar, invA[j]) * (bn * uval);
-        else
-            bx = x * bn;
+        float abar, bx;
+        if constexpr (DISC == kBilinear) {
+            const float r = bilinear_r(arg);
+            abar = fmaf(2.f, r, -1.f);
+            bx = (x * r) * bn;
+        } else {
+            abar = hw_exp2(arg);
+            if constexpr (DISC == kZoh)
+                bx = zoh_factor(dt, arg, abar, invA[j]) * (bn * uval);
+            else
+                bx = x * bn;
+        }
+        if constexpr (PROD) P[j] *= abar;
         h[j] = fmaf(abar, h[j], bx);
         if constexpr (READOUT) {
             const float cn = ok ? ld<BF16>(C, row + j) : 0.f;
@@ -84,9 +92,12 @@ __device__ __forceinline__ float advance(float (&h)[NS], const float (&A2)[NS],
 // ---- pass 1: chunk summaries --------------------------------------------------
 // For every chunk but the last: the state reached from h = 0 over the chunk
 // (the "b" of its affine summary) and the compensated sum of dt (the "a" is
-// exp(A * sum dt), formed in pass 2).
-template <int NS, bool BF16, bool ZOH>
+// exp(A * sum dt), formed in pass 2) -- or, for the bilinear form, whose
+// decay is not an exponential of sum dt, the product of A_bar per state.
+template <int NS, bool BF16, int DISC>
 __global__ void __launch_bounds__(256) scan_summary(ScanArgs a) {
+    constexpr bool ZOH = DISC == kZoh;
+    constexpr bool PROD = DISC == kBilinear;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = blockIdx.x;  // 0 .. chunks-2
@@ -97,10 +108,13 @@ __global__ void __launch_bounds__(256) scan_summary(ScanArgs a) {
     const int n0 = w * NS;
     const int nvalid = min(NS, a.N - n0);
 
-    float A2[NS], invA[NS], h[NS];
+    float A2[NS], invA[NS], h[NS], P[NS];
     load_a<NS, ZOH>(a.A, dd, a.N, n0, nvalid, A2, invA);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) h[j] = 0.f;
+    for (int j = 0; j < NS; ++j) {
+        h[j] = 0.f;
+        P[j] = 1.f;
+    }
     const float bias = a.bias ? a.bias[dd] : 0.f;
 
     const int64_t t0 = (int64_t)c * a.chunk_len;
@@ -114,8 +128,8 @@ __global__ void __launch_bounds__(256) scan_summary(ScanArgs a) {
         const float tk = s + yk;
         comp = (tk - s) - yk;
         s = tk;
-        advance<NS, BF16, ZOH, false>(h, A2, invA, dt, uval, a.B, nullptr,
-                                      ((int64_t)b * a.L + t) * a.N + n0, nvalid);
+        advance<NS, BF16, DISC, false, PROD>(h, P, A2, invA, dt, uval, a.B, nullptr,
+                                             ((int64_t)b * a.L + t) * a.N + n0, nvalid);
     }
     if (!dvalid) return;
     const int km1 = a.chunks - 1;
@@ -123,12 +137,20 @@ __global__ void __launch_bounds__(256) scan_summary(ScanArgs a) {
 #pragma unroll
     for (int j = 0; j < NS; ++j)
         if (j < nvalid) a.agg[(base * a.N + n0 + j) * a.Dn + d] = h[j];
-    if (w == 0) a.sdt[base * a.Dn + d] = s;
+    if constexpr (PROD) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            if (j < nvalid) a.prod[(base * a.N + n0 + j) * a.Dn + d] = P[j];
+    } else {
+        if (w == 0) a.sdt[base * a.Dn + d] = s;
+    }
 }
 
 // ---- pass 2: compose chunk summaries in order --------------------------------
 // One thread per (b, n, d).  Replaces each summary slot c by the state at the
-// start of chunk c+1: h_{c+1} = exp(A * sum dt_c) * h_c + b_c, h_0 = h0 or 0.
+// start of chunk c+1: h_{c+1} = a_c * h_c + b_c, h_0 = h0 or 0, where the
+// decay a_c is exp(A * sum dt_c) or, when the summaries hold products of
+// A_bar (bilinear), that product.
 __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = (int64_t)a.batch * a.N * a.Dn;
@@ -141,7 +163,9 @@ __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
     const int km1 = a.chunks - 1;
     // Loads of a group are issued before its stores so that the chain waits
     // on memory once per group, not once per chunk.
-    constexpr int G = 16;
+    // (Raw values are loaded; the decays are formed in the chain loop.)
+    const bool prod = a.prod != nullptr;
+    constexpr int G = 8;
     for (int c0 = 0; c0 < km1; c0 += G) {
         float s[G], g[G];
 #pragma unroll
@@ -150,7 +174,7 @@ __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
             g[j] = 0.f;
             if (c0 + j < km1) {
                 const int64_t base = (int64_t)b * km1 + c0 + j;
-                s[j] = a.sdt[base * a.Dn + d];
+                s[j] = prod ? a.prod[(base * a.N + n) * a.Dn + d] : a.sdt[base * a.Dn + d];
                 g[j] = a.agg[(base * a.N + n) * a.Dn + d];
             }
         }
@@ -158,7 +182,8 @@ __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
         for (int j = 0; j < G; ++j) {
             if (c0 + j < km1) {
                 const int64_t base = (int64_t)b * km1 + c0 + j;
-                h = fmaf(hw_exp2(A2 * s[j]), h, g[j]);
+                const float decay = prod ? s[j] : hw_exp2(A2 * s[j]);
+                h = fmaf(decay, h, g[j]);
                 a.agg[(base * a.N + n) * a.Dn + d] = h;
             }
         }
@@ -166,8 +191,9 @@ __global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
 }
 
 // ---- pass 3: rescan every chunk from its true start, write y -----------------
-template <int NS, bool BF16, bool ZOH, bool MULTI>
+template <int NS, bool BF16, int DISC, bool MULTI>
 __global__ void __launch_bounds__(256) scan_chunks(ScanArgs a) {
+    constexpr bool ZOH = DISC == kZoh;
     __shared__ float ypart[MULTI ? 4 : 1][MULTI ? kTB : 1][64];
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -180,7 +206,7 @@ __global__ void __launch_bounds__(256) scan_chunks(ScanArgs a) {
     const int n0 = w * NS;
     const int nvalid = min(NS, a.N - n0);
 
-    float A2[NS], invA[NS], h[NS];
+    float A2[NS], invA[NS], h[NS], P[NS];
     load_a<NS, ZOH>(a.A, dd, a.N, n0, nvalid, A2, invA);
     const int km1 = a.chunks - 1;
 #pragma unroll
@@ -205,7 +231,7 @@ __global__ void __launch_bounds__(256) scan_chunks(ScanArgs a) {
             const int64_t e = ((int64_t)b * a.L + t) * a.Dn + dd;
             const float uval = ld<BF16>(a.u, e);
             const float dt = step_size(ld<BF16>(a.delta, e), bias, a.softplus);
-            float y = advance<NS, BF16, ZOH, true>(h, A2, invA, dt, uval, a.B, a.C,
+            float y = advance<NS, BF16, DISC, true>(h, P, A2, invA, dt, uval, a.B, a.C,
                                                    ((int64_t)b * a.L + t) * a.N + n0, nvalid);
             y = fmaf(Dd, uval, y);
             if (a.z) y *= silu_f(ld<BF16>(a.z, e));
@@ -219,8 +245,8 @@ __global__ void __launch_bounds__(256) scan_chunks(ScanArgs a) {
                 const int64_t e = ((int64_t)b * a.L + t) * a.Dn + dd;
                 const float uval = ld<BF16>(a.u, e);
                 const float dt = step_size(ld<BF16>(a.delta, e), bias, a.softplus);
-                ypart[w][tt][lane] = advance<NS, BF16, ZOH, true>(
-                    h, A2, invA, dt, uval, a.B, a.C, ((int64_t)b * a.L + t) * a.N + n0, nvalid);
+                ypart[w][tt][lane] = advance<NS, BF16, DISC, true>(
+                    h, P, A2, invA, dt, uval, a.B, a.C, ((int64_t)b * a.L + t) * a.N + n0, nvalid);
             }
             __syncthreads();
             for (int tt = w; tt < cnt; tt += nw) {
@@ -245,7 +271,7 @@ __global__ void __launch_bounds__(256) scan_chunks(ScanArgs a) {
 // One thread per (b, d): the channel's N-state row (contiguous in h) is read,
 // advanced one step and written back; B_t, C_t are uniform over the block's
 // channels (one batch row per block).
-template <bool BF16, bool ZOH>
+template <bool BF16, int DISC>
 __global__ void __launch_bounds__(256) state_step(StepArgs a) {
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
     const int b = blockIdx.y;
@@ -261,13 +287,19 @@ __global__ void __launch_bounds__(256) state_step(StepArgs a) {
     for (int n = 0; n < a.N; ++n) {
         const float an = arow[n];
         const float arg = dt * (an * kLog2e);
-        const float abar = hw_exp2(arg);
         const float bn = ld<BF16>(a.B, brow + n);
-        float bx;
-        if constexpr (ZOH)
-            bx = zoh_factor(dt, arg, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
-        else
-            bx = dx * bn;
+        float abar, bx;
+        if constexpr (DISC == kBilinear) {
+            const float r = bilinear_r(arg);
+            abar = fmaf(2.f, r, -1.f);
+            bx = (dx * r) * bn;
+        } else {
+            abar = hw_exp2(arg);
+            if constexpr (DISC == kZoh)
+                bx = zoh_factor(dt, arg, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
+            else
+                bx = dx * bn;
+        }
         const float hn = fmaf(abar, hrow[n], bx);
         hrow[n] = hn;
         y = fmaf(ld<BF16>(a.C, brow + n), hn, y);
@@ -277,13 +309,13 @@ __global__ void __launch_bounds__(256) state_step(StepArgs a) {
     st<BF16>(a.y, e, y);
 }
 
-template <int NS, bool BF16, bool ZOH>
+template <int NS, bool BF16, int DISC>
 hipError_t launch_ns(const Plan& p, const ScanArgs& a, hipStream_t s) {
     const dim3 block(64 * p.waves);
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((scan_summary<NS, BF16, ZOH>), dim3(p.chunks - 1, p.tiles, a.batch),
+            hipLaunchKernelGGL((scan_summary<NS, BF16, DISC>), dim3(p.chunks - 1, p.tiles, a.batch),
                                block, 0, s, a);
         }
         hipError_t e = hipGetLastError();
@@ -294,33 +326,42 @@ hipError_t launch_ns(const Plan& p, const ScanArgs& a, hipStream_t s) {
     ProfScope ps(s, kPhaseMain);
     if (p.waves > 1) {
         if constexpr (NS == 32)
-            hipLaunchKernelGGL((scan_chunks<NS, BF16, ZOH, true>),
+            hipLaunchKernelGGL((scan_chunks<NS, BF16, DISC, true>),
                                dim3(p.chunks, p.tiles, a.batch), block, 0, s, a);
         else
             return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((scan_chunks<NS, BF16, ZOH, false>), dim3(p.chunks, p.tiles, a.batch),
+        hipLaunchKernelGGL((scan_chunks<NS, BF16, DISC, false>), dim3(p.chunks, p.tiles, a.batch),
                            block, 0, s, a);
     }
     return hipGetLastError();
 }
 
-template <bool BF16, bool ZOH>
+template <bool BF16, int DISC>
 hipError_t launch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
     switch (p.ns) {
-        case 4: return launch_ns<4, BF16, ZOH>(p, a, s);
-        case 8: return launch_ns<8, BF16, ZOH>(p, a, s);
-        case 16: return launch_ns<16, BF16, ZOH>(p, a, s);
-        case 32: return launch_ns<32, BF16, ZOH>(p, a, s);
+        case 4: return launch_ns<4, BF16, DISC>(p, a, s);
+        case 8: return launch_ns<8, BF16, DISC>(p, a, s);
+        case 16: return launch_ns<16, BF16, DISC>(p, a, s);
+        case 32: return launch_ns<32, BF16, DISC>(p, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, bool zoh, hipStream_t s) {
-    if (bf16) return zoh ? launch_io<true, true>(p, a, s) : launch_io<true, false>(p, a, s);
-    return zoh ? launch_io<false, true>(p, a, s) : launch_io<false, false>(p, a, s);
+template <bool BF16>
+hipError_t launch_disc(const Plan& p, const ScanArgs& a, int disc, hipStream_t s) {
+    switch (disc) {
+        case kEuler: return launch_io<BF16, kEuler>(p, a, s);
+        case kZoh: return launch_io<BF16, kZoh>(p, a, s);
+        case kBilinear: return launch_io<BF16, kBilinear>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s) {
+    return bf16 ? launch_disc<true>(p, a, disc, s) : launch_disc<false>(p, a, disc, s);
 }
 
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
@@ -330,16 +371,21 @@ hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs& a, bool bf16, bool zoh, hipStream_t s) {
+hipError_t launch_step(const StepArgs& a, bool bf16, int disc, hipStream_t s) {
     const dim3 grid((a.Dn + 255) / 256, a.batch), block(256);
     ProfScope ps(s, kPhaseStep);
-    if (bf16) {
-        if (zoh) hipLaunchKernelGGL((state_step<true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((state_step<true, false>), grid, block, 0, s, a);
-    } else {
-        if (zoh) hipLaunchKernelGGL((state_step<false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((state_step<false, false>), grid, block, 0, s, a);
+#define MS_STEP_(DI)                                                           \
+    if (bf16)                                                                  \
+        hipLaunchKernelGGL((state_step<true, DI>), grid, block, 0, s, a);      \
+    else                                                                       \
+        hipLaunchKernelGGL((state_step<false, DI>), grid, block, 0, s, a);
+    switch (disc) {
+        case kEuler: MS_STEP_(kEuler) break;
+        case kZoh: MS_STEP_(kZoh) break;
+        case kBilinear: MS_STEP_(kBilinear) break;
+        default: return hipErrorInvalidValue;
     }
+#undef MS_STEP_
     return hipGetLastError();
 }
 

@@ -53,9 +53,14 @@ using namespace dev;
 #define MSSCAN_LANE_WPE 1
 #endif
 
-template <int N, int TB, bool DB, bool BF16, bool ZOH, bool SP, bool SUMMARY>
+template <int N, int TB, bool DB, bool BF16, int DISC, bool SP, bool SUMMARY>
 __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     static_assert(N == 8 || N == 16 || N == 32 || N == 64, "states per lane");
+    constexpr bool ZOH = DISC == kZoh;
+    constexpr bool BIL = DISC == kBilinear;
+    // A bilinear summary keeps the product of A_bar per state (its segment
+    // decay is not exp(A * sum dt)).
+    constexpr bool PROD = SUMMARY && BIL;
     // B_t and C_t reach the lanes in groups of RW states, one DPP row each:
     // lane l holds state 16k + (l mod RW) of group k.
     constexpr int RW = N < 16 ? N : 16;
@@ -70,7 +75,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     const bool dvalid = d < a.Dn;
     const int dd = dvalid ? d : a.Dn - 1;
 
-    float A2[N], invA[N], A2sq[N], h[N];
+    float A2[N], invA[N], A2sq[N], h[N], P[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         const float av = a.A[(int64_t)dd * N + n];
@@ -92,6 +97,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             }
         }
         h[n] = v;
+        P[n] = 1.f;
     }
     const float bias = a.bias ? a.bias[dd] : 0.f;
     const float Dd = a.D ? a.D[dd] : 0.f;
@@ -152,7 +158,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         const float uv = R::widen(raw_u);
         const float v = R::widen(raw_d) + bias;
         const float dt = SP ? softplus_f(v) : v;  // compile-time: no branch per step
-        const float xv = ZOH ? uv : dt * uv;
+        const float xv = ZOH ? uv : dt * uv;  // B is multiplied by u (ZOH) or dt*u
         float q1 = 0.f, q2 = 0.f;  // ZOH series coefficients for this dt
         if constexpr (ZOH) {
             const float dt2 = dt * dt;
@@ -163,25 +169,32 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             [&](auto nc) {
                 constexpr int n = decltype(nc)::value;
                 const float arg = dt * A2[n];
-                const float abar = hw_exp2(arg);
-                const float bu = row_bcast<n % RW>(vbt[n / RW]) * xv;  // B*x (Euler) or B*u (ZOH)
-                float bx;
-                if constexpr (ZOH)
-                    bx = zoh_factor_q(dt, q1, q2, A2[n], A2sq[n], arg, abar, invA[n]) * bu;
-                else
-                    bx = bu;
+                float abar, bx;
+                if constexpr (BIL) {
+                    const float r = bilinear_r(arg);
+                    abar = fmaf(2.f, r, -1.f);
+                    bx = row_bcast<n % RW>(vbt[n / RW]) * (xv * r);  // B * dt*r*u
+                } else {
+                    abar = hw_exp2(arg);
+                    const float bu = row_bcast<n % RW>(vbt[n / RW]) * xv;  // B*x (Euler) or B*u (ZOH)
+                    if constexpr (ZOH)
+                        bx = zoh_factor_q(dt, q1, q2, A2[n], A2sq[n], arg, abar, invA[n]) * bu;
+                    else
+                        bx = bu;
+                }
                 h[n] = fmaf(abar, h[n], bx);
+                if constexpr (PROD) P[n] *= abar;
                 // With 32+ states the scheduler would otherwise start every
                 // exponential before the first update and run out of VGPRs.
                 if constexpr (N >= 32 && n % 8 == 7) __builtin_amdgcn_sched_barrier(0);
             },
             std::make_integer_sequence<int, N>{});
-        if constexpr (SUMMARY) {
+        if constexpr (SUMMARY && !PROD) {
             const float yk = dt - s_comp;
             const float tk = s_sum + yk;
             s_comp = (tk - s_sum) - yk;
             s_sum = tk;
-        } else {
+        } else if constexpr (!SUMMARY) {
             float y = DppReadout<RW>::run(R::widen(raw_c[0]), *reinterpret_cast<const float(*)[RW]>(h));
 #pragma unroll
             for (int k = 1; k < KB; ++k) y = DppReadoutAcc16::run(y, R::widen(raw_c[k]), h + 16 * k);
@@ -248,7 +261,12 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         const int64_t base = (int64_t)b * km1 + seg;
 #pragma unroll
         for (int n = 0; n < N; ++n) a.agg[(base * N + n) * a.Dn + d] = h[n];
-        a.sdt[base * a.Dn + d] = s_sum;
+        if constexpr (PROD) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) a.prod[(base * N + n) * a.Dn + d] = P[n];
+        } else {
+            a.sdt[base * a.Dn + d] = s_sum;
+        }
     } else {
         if (seg == a.chunks - 1 && a.h_last) {
 #pragma unroll
@@ -257,18 +275,18 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     }
 }
 
-template <int N, bool BF16, bool ZOH, bool SP>
+template <int N, bool BF16, int DISC, bool SP>
 hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    // 64 states (32 with ZOH's extra per-state constants) leave room for one
-    // register block only: no prefetch of the next block.
-    constexpr bool kBig = N >= 64 || (N >= 32 && ZOH);
+    // 64 states (32 with the extra per-state values of ZOH or the bilinear
+    // summary) leave room for one register block only: no prefetch.
+    constexpr bool kBig = N >= 64 || (N >= 32 && DISC != kEuler);
     constexpr int TB = kBig ? MSSCAN_LANE_TB64 : MSSCAN_LANE_TB;
     constexpr bool DB = kBig ? MSSCAN_LANE_DB64 != 0 : MSSCAN_LANE_DB != 0;
     hipError_t e = hipSuccess;
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, ZOH, SP, true>),
+            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, true>),
                                dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
         }
         e = hipGetLastError();
@@ -278,40 +296,49 @@ hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     }
     {
         ProfScope ps(s, kPhaseMain);
-        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, ZOH, SP, false>),
+        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, false>),
                            dim3(p.tiles, p.chunks, a.batch), dim3(64), 0, s, a);
     }
     return hipGetLastError();
 }
 
-template <bool BF16, bool ZOH, bool SP>
+template <bool BF16, int DISC, bool SP>
 hipError_t dispatch_n(const Plan& p, const ScanArgs& a, hipStream_t s) {
     switch (p.ns) {
-        case 8: return launch_lanes<8, BF16, ZOH, SP>(p, a, s);
-        case 16: return launch_lanes<16, BF16, ZOH, SP>(p, a, s);
-        case 32: return launch_lanes<32, BF16, ZOH, SP>(p, a, s);
+        case 8: return launch_lanes<8, BF16, DISC, SP>(p, a, s);
+        case 16: return launch_lanes<16, BF16, DISC, SP>(p, a, s);
+        case 32: return launch_lanes<32, BF16, DISC, SP>(p, a, s);
         case 64:
-            if constexpr (!ZOH) return launch_lanes<64, BF16, ZOH, SP>(p, a, s);
-            return hipErrorInvalidValue;  // 64 ZOH states do not fit a lane's registers
+            if constexpr (DISC == kEuler) return launch_lanes<64, BF16, DISC, SP>(p, a, s);
+            return hipErrorInvalidValue;  // 64 ZOH/bilinear states do not fit a lane
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool BF16, bool ZOH>
+template <bool BF16, int DISC>
 hipError_t dispatch(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    return a.softplus ? dispatch_n<BF16, ZOH, true>(p, a, s) : dispatch_n<BF16, ZOH, false>(p, a, s);
+    return a.softplus ? dispatch_n<BF16, DISC, true>(p, a, s) : dispatch_n<BF16, DISC, false>(p, a, s);
+}
+
+template <bool BF16>
+hipError_t dispatch_disc(const Plan& p, const ScanArgs& a, int disc, hipStream_t s) {
+    switch (disc) {
+        case kEuler: return dispatch<BF16, kEuler>(p, a, s);
+        case kZoh: return dispatch<BF16, kZoh>(p, a, s);
+        case kBilinear: return dispatch<BF16, kBilinear>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-bool lane_variant_exists(int n, bool zoh) {
-    return n == 8 || n == 16 || n == 32 || (n == 64 && !zoh);
+bool lane_variant_exists(int n, int disc) {
+    return n == 8 || n == 16 || n == 32 || (n == 64 && disc == kEuler);
 }
 
-hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, bool zoh,
+hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                              hipStream_t s) {
-    if (bf16) return zoh ? dispatch<true, true>(p, a, s) : dispatch<true, false>(p, a, s);
-    return zoh ? dispatch<false, true>(p, a, s) : dispatch<false, false>(p, a, s);
+    return bf16 ? dispatch_disc<true>(p, a, disc, s) : dispatch_disc<false>(p, a, disc, s);
 }
 
 }  // namespace msscan

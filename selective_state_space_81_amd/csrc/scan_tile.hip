@@ -47,8 +47,11 @@ namespace {
 
 using namespace dev;
 
-template <int NS, int S, int TB, bool BF16, bool ZOH, bool SUMMARY>
+template <int NS, int S, int TB, bool BF16, int DISC, bool SUMMARY>
 __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
+    constexpr bool ZOH = DISC == kZoh;
+    constexpr bool BIL = DISC == kBilinear;
+    constexpr bool PROD = SUMMARY && BIL;  // bilinear: keep the product of A_bar
     constexpr int N = NS * S;
     constexpr int J = TB / S;  // timesteps per thread in phases A/C
     static_assert(TB % S == 0, "TB must be a multiple of S");
@@ -56,7 +59,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     using R = Io<BF16>;
     using RT = typename R::T;
 
-    __shared__ float2 s_dx[2][TB][64];  // (dt, x) Euler; (dt, u) ZOH
+    __shared__ float2 s_dx[2][TB][64];  // (dt, x) Euler and bilinear; (dt, u) ZOH
     __shared__ float s_y[SUMMARY ? 1 : 2][SUMMARY ? 1 : S][SUMMARY ? 1 : TB][64];
 
     const int tid = threadIdx.x;
@@ -69,9 +72,10 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     const int dd = dvalid ? d : a.Dn - 1;
     const int n0 = w * NS;
 
-    float A2[NS], invA[NS], h[NS];
+    float A2[NS], invA[NS], h[NS], P[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
+        P[j] = 1.f;
         const float av = a.A[(int64_t)dd * N + n0 + j];
         A2[j] = av * kLog2e;
         if constexpr (ZOH) invA[j] = (av != 0.f) ? 1.f / av : 0.f;
@@ -151,19 +155,26 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
             [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const float arg = dx.x * A2[j];
-                const float abar = hw_exp2(arg);
-                const float bu = row_bcast<j>(vbt) * dx.y;  // B*x (Euler) or B*u (ZOH)
-                float bx;
-                if constexpr (ZOH)
-                    bx = zoh_factor(dx.x, arg, abar, invA[j]) * bu;
-                else
-                    bx = bu;
+                float abar, bx;
+                if constexpr (BIL) {
+                    const float r = bilinear_r(arg);
+                    abar = fmaf(2.f, r, -1.f);
+                    bx = row_bcast<j>(vbt) * (dx.y * r);  // B * dt*r*u
+                } else {
+                    abar = hw_exp2(arg);
+                    const float bu = row_bcast<j>(vbt) * dx.y;  // B*x (Euler) or B*u (ZOH)
+                    if constexpr (ZOH)
+                        bx = zoh_factor(dx.x, arg, abar, invA[j]) * bu;
+                    else
+                        bx = bu;
+                }
                 h[j] = fmaf(abar, h[j], bx);
+                if constexpr (PROD) P[j] *= abar;
             },
             std::make_integer_sequence<int, NS>{});
         if constexpr (!SUMMARY) {
             s_y[cur][w][tt][lane] = DppReadout<NS>::run(vct, h);
-        } else {
+        } else if constexpr (!PROD) {
             if (w == 0) {
                 const float yk = dx.x - s_comp;
                 const float tk = s_sum + yk;
@@ -242,7 +253,12 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
         const int64_t base = (int64_t)b * km1 + seg;
 #pragma unroll
         for (int j = 0; j < NS; ++j) a.agg[(base * N + n0 + j) * a.Dn + d] = h[j];
-        if (w == 0) a.sdt[base * a.Dn + d] = s_sum;
+        if constexpr (PROD) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j) a.prod[(base * N + n0 + j) * a.Dn + d] = P[j];
+        } else {
+            if (w == 0) a.sdt[base * a.Dn + d] = s_sum;
+        }
     } else {
         if (seg == a.chunks - 1 && a.h_last) {
 #pragma unroll
@@ -262,7 +278,7 @@ __global__ void __launch_bounds__(256) bc_prepare(ScanArgs a) {
     a.bcw[i] = k < a.N ? ld<BF16>(a.B, row * a.N + k) : ld<BF16>(a.C, row * a.N + k - a.N);
 }
 
-template <int NS, int S, int TB, bool BF16, bool ZOH>
+template <int NS, int S, int TB, bool BF16, int DISC>
 hipError_t launch_tiles(const Plan& p, const ScanArgs& a, hipStream_t s) {
     const dim3 block(64 * S);
     hipError_t e = launch_bc_prepare(a, BF16, s);
@@ -270,7 +286,7 @@ hipError_t launch_tiles(const Plan& p, const ScanArgs& a, hipStream_t s) {
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, true>),
+            hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, DISC, true>),
                                dim3(p.tiles, p.chunks - 1, a.batch), block, 0, s, a);
         }
         e = hipGetLastError();
@@ -280,28 +296,28 @@ hipError_t launch_tiles(const Plan& p, const ScanArgs& a, hipStream_t s) {
     }
     {
         ProfScope ps(s, kPhaseMain);
-        hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, ZOH, false>),
+        hipLaunchKernelGGL((scan_tile<NS, S, TB, BF16, DISC, false>),
                            dim3(p.tiles, p.chunks, a.batch), block, 0, s, a);
     }
     return hipGetLastError();
 }
 
-template <bool BF16, bool ZOH>
+template <bool BF16, int DISC>
 hipError_t dispatch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
     constexpr int TB = 16;
     if (p.waves == 4) {
         switch (p.ns) {
-            case 2: return launch_tiles<2, 4, TB, BF16, ZOH>(p, a, s);
-            case 4: return launch_tiles<4, 4, TB, BF16, ZOH>(p, a, s);
-            case 8: return launch_tiles<8, 4, TB, BF16, ZOH>(p, a, s);
-            case 16: return launch_tiles<16, 4, TB, BF16, ZOH>(p, a, s);
+            case 2: return launch_tiles<2, 4, TB, BF16, DISC>(p, a, s);
+            case 4: return launch_tiles<4, 4, TB, BF16, DISC>(p, a, s);
+            case 8: return launch_tiles<8, 4, TB, BF16, DISC>(p, a, s);
+            case 16: return launch_tiles<16, 4, TB, BF16, DISC>(p, a, s);
             default: break;
         }
     } else if (p.waves == 8) {
         switch (p.ns) {
-            case 2: return launch_tiles<2, 8, TB, BF16, ZOH>(p, a, s);
-            case 8: return launch_tiles<8, 8, TB, BF16, ZOH>(p, a, s);
-            case 16: return launch_tiles<16, 8, TB, BF16, ZOH>(p, a, s);
+            case 2: return launch_tiles<2, 8, TB, BF16, DISC>(p, a, s);
+            case 8: return launch_tiles<8, 8, TB, BF16, DISC>(p, a, s);
+            case 16: return launch_tiles<16, 8, TB, BF16, DISC>(p, a, s);
             default: break;
         }
     }
@@ -327,10 +343,19 @@ bool tile_variant_exists(int ns, int waves) {
     return false;
 }
 
-hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, bool zoh,
+template <bool BF16>
+hipError_t dispatch_disc(const Plan& p, const ScanArgs& a, int disc, hipStream_t s) {
+    switch (disc) {
+        case kEuler: return dispatch_io<BF16, kEuler>(p, a, s);
+        case kZoh: return dispatch_io<BF16, kZoh>(p, a, s);
+        case kBilinear: return dispatch_io<BF16, kBilinear>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                              hipStream_t s) {
-    if (bf16) return zoh ? dispatch_io<true, true>(p, a, s) : dispatch_io<true, false>(p, a, s);
-    return zoh ? dispatch_io<false, true>(p, a, s) : dispatch_io<false, false>(p, a, s);
+    return bf16 ? dispatch_disc<true>(p, a, disc, s) : dispatch_disc<false>(p, a, disc, s);
 }
 
 }  // namespace msscan

@@ -51,8 +51,17 @@ def sample_channels(Dn: int, k: int, seed: int = 0) -> np.ndarray:
     return np.array(sorted(idx), dtype=np.int64)
 
 
+def disc_kw(disc: str) -> dict:
+    """Keyword arguments of scan_fwd / oracle.scan for a discretisation name."""
+    assert disc in ("euler", "zoh", "bilinear"), disc
+    return {"zoh": disc == "zoh", "bilinear": disc == "bilinear"}
+
+
+DISCS = ["euler", "zoh", "bilinear"]
+
+
 def oracle_on_channels(x: dict, idx: np.ndarray, softplus: bool, zoh: bool,
-                       h0: torch.Tensor | None = None):
+                       h0: torch.Tensor | None = None, bilinear: bool = False):
     """Run the oracle on a subset of channels (all batches, full L).  Channels
     are independent, so this is exactly the full oracle restricted to them."""
     ii = torch.as_tensor(idx, device=x["u"].device)
@@ -68,4 +77,4 @@ def oracle_on_channels(x: dict, idx: np.ndarray, softplus: bool, zoh: bool,
     h0s = h0.index_select(1, ii) if h0 is not None else None
     return oracle.scan(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"],
                        z=sub["z"], delta_bias=sub["delta_bias"], h0=h0s, softplus=softplus,
-                       zoh=zoh)
+                       zoh=zoh, bilinear=bilinear)

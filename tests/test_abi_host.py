@@ -52,6 +52,7 @@ def test_validation_statuses_host_only():
     assert b"d_state" in lib.ms_last_error()
     assert _call_scan(lib, ms.dims(1, 10, 64, 16, 7)) == 3              # bad io
     assert _call_scan(lib, good, flags=8) == 4                          # unknown flag
+    assert _call_scan(lib, good, flags=2 | 4) == 4                      # ZOH with bilinear
     assert _call_scan(lib, good, u=24) == 5                             # misaligned
     assert _call_scan(lib, good, h_last=8) == 5
     # workspace: this shape needs one (several chunks); none given
@@ -64,8 +65,10 @@ def test_validation_statuses_host_only():
     assert r == 2
     r = lib.ms_state_update(None, 16, 16, 16, 16, 16, None, None, None, 1, 16, 1, 64, 16, 1, None)
     assert r == 1
-    r = lib.ms_state_update(16, 16, 16, 16, 16, 16, None, None, None, 4, 16, 1, 64, 16, 1, None)
-    assert r == 4
+    r = lib.ms_state_update(16, 16, 16, 16, 16, 16, None, None, None, 8, 16, 1, 64, 16, 1, None)
+    assert r == 4  # unknown flag
+    r = lib.ms_state_update(16, 16, 16, 16, 16, 16, None, None, None, 6, 16, 1, 64, 16, 1, None)
+    assert r == 4  # ZOH with bilinear
 
 
 def test_workspace_size_function():
@@ -94,6 +97,12 @@ def test_workspace_size_function():
     a = lib.ms_scan_workspace_bytes(ctypes.byref(d), 1)
     assert a == lib.ms_scan_workspace_bytes(ctypes.byref(d), 3)
     assert a % 256 == 0 and a > 0
+    # The bilinear form keeps N products of A_bar per segment boundary instead
+    # of one sum of dt, so its summaries take more room.
+    d16 = ms.dims(8, 2048, 1536, 16, 1)
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(d16), 1 | 4) > \
+        lib.ms_scan_workspace_bytes(ctypes.byref(d16), 1)
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(d16), 2 | 4) == ctypes.c_size_t(-1).value
     # Odd d_state takes the generic kernels, which also size their workspace.
     assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 65536, 256, 17, 1)), 1) > 0
 

@@ -12,26 +12,31 @@ import torch
 
 import oracle
 import synth
-from helpers import assert_within, oracle_on_channels, sample_channels
+from helpers import DISCS, assert_within, disc_kw, oracle_on_channels, sample_channels
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 
 
+def _kw(zoh):
+    """zoh: a bool (Euler / ZOH) or a discretisation name."""
+    return disc_kw(zoh) if isinstance(zoh, str) else {"zoh": bool(zoh)}
+
+
 def _run(ms, x, softplus, zoh, **kw):
     y = ms.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x.get("D"), z=x.get("z"),
-                    delta_bias=x.get("delta_bias"), softplus=softplus, zoh=zoh, **kw)
+                    delta_bias=x.get("delta_bias"), softplus=softplus, **_kw(zoh), **kw)
     torch.cuda.synchronize()
     return y
 
 
 def _oracle_full(x, softplus, zoh, h0=None):
     return oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x.get("D"), z=x.get("z"),
-                       delta_bias=x.get("delta_bias"), h0=h0, softplus=softplus, zoh=zoh)
+                       delta_bias=x.get("delta_bias"), h0=h0, softplus=softplus, **_kw(zoh))
 
 
-@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("zoh", DISCS)
 def test_tiny_workload_full(gpu, zoh):
     w = synth.workload("tiny")
     x = synth.scan_inputs(w, device=DEV, seed=0)
@@ -59,7 +64,7 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("zoh", DISCS)
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "B{}L{}D{}N{}{}".format(*s))
 def test_edge_shapes(gpu, shape, zoh):
     batch, L, Dn, N, io = shape
@@ -104,7 +109,7 @@ def test_zero_bias_equals_null_bias(gpu):
     assert torch.equal(y0, y1)
 
 
-@pytest.mark.parametrize("zoh", [False, True], ids=["euler", "zoh"])
+@pytest.mark.parametrize("zoh", DISCS)
 def test_special_cases_zero_A_and_zero_step(gpu, zoh):
     w = synth.workload("tiny", batch=2, L=513, Dn=80, N=16)
     x = synth.scan_inputs(w, device=DEV, seed=3)
@@ -190,15 +195,15 @@ def test_nan_stays_in_its_channel(gpu):
 
 
 # ---------------------------------------------------------------- full sizes ---
-@pytest.mark.parametrize("name,zoh,k", [("m130m", False, 48), ("m3b", False, 32),
-                                         ("m3b", True, 32)],
-                         ids=["m130m-euler", "m3b-euler", "m3b-zoh"])
+@pytest.mark.parametrize("name,zoh,k", [("m130m", "euler", 48), ("m3b", "euler", 32),
+                                         ("m3b", "zoh", 32), ("m3b", "bilinear", 16)],
+                         ids=["m130m-euler", "m3b-euler", "m3b-zoh", "m3b-bilinear"])
 def test_layer_workloads_sampled(gpu, name, zoh, k):
     w = synth.workload(name)
     x = synth.scan_inputs(w, device=DEV, seed=0)
     y = _run(gpu, x, w.softplus, zoh)
     idx = sample_channels(w.Dn, k, seed=1)
-    yr, _ = oracle_on_channels(x, idx, w.softplus, zoh)
+    yr, _ = oracle_on_channels(x, idx, w.softplus, **_kw(zoh))
     got = y.index_select(2, torch.as_tensor(idx, device=DEV))
     assert_within(got, yr, w.io)
     # Whole-tensor properties at full size: finite, and not all zero.
