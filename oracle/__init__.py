@@ -48,6 +48,9 @@ def _load():
                                                dp, dp, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_step.argtypes = [dp] * 9 + [ctypes.c_int, ctypes.c_int, i64, i64, i64, dp]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [dp] * 9 + [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64] \
+            + [dp] * 11 + [ctypes.c_int]
         lib.oracle_conv1d.restype = ctypes.c_int
         lib.oracle_conv1d.argtypes = [dp] * 4 + [i64, ctypes.c_int, i64, i64, i64, dp,
                                                  ctypes.c_int]
@@ -152,3 +155,32 @@ def conv1d(x, w, bias=None, x_prev=None, silu: bool = True, nthreads: int = 0) -
     if rc != 0:
         raise ValueError(f"oracle_conv1d failed ({rc})")
     return u
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None, dh_last=None,
+             softplus: bool = True, zoh: bool = False, bilinear: bool = False,
+             nthreads: int = 0) -> dict:
+    """Gradients of scan() in fp64: given dy [batch, L, Dn] (and optionally
+    dh_last [batch, Dn, N]), returns a dict with du, ddelta (w.r.t. the raw
+    delta), dA, dB, dC, and dz / dD / dbias / dh0 (dbias and dh0 always; dz
+    and dD when z and D are given)."""
+    lib = _load()
+    u, delta, A, B, C, dy = (_f64(t) for t in (u, delta, A, B, C, dy))
+    D, z, delta_bias, h0, dh_last = (_f64(t) for t in (D, z, delta_bias, h0, dh_last))
+    batch, L, Dn = u.shape
+    N = A.shape[1]
+    assert dy.shape == u.shape
+    out = {"du": np.empty_like(u), "ddelta": np.empty_like(u), "dA": np.empty((Dn, N)),
+           "dB": np.empty((batch, L, N)), "dC": np.empty((batch, L, N)),
+           "dbias": np.empty(Dn), "dh0": np.empty((batch, Dn, N))}
+    out["dz"] = np.empty_like(u) if z is not None else None
+    out["dD"] = np.empty(Dn) if D is not None else None
+    rc = lib.oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                             _ptr(delta_bias), _ptr(h0), int(bool(softplus)),
+                             _disc(zoh, bilinear), batch, L, Dn, N, _ptr(dy), _ptr(dh_last),
+                             _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                             _ptr(out["dbias"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_scan_bwd failed with code {rc}")
+    return out

@@ -176,6 +176,194 @@ int oracle_step(double* h, const double* x, const double* delta_raw,
     return 0;
 }
 
+/* Derivatives of A_bar and of the B*u factor with respect to dt and to a,
+ * for the three discretisations of one_step:
+ *   Euler:    A_bar = e^{dt a}, f = dt
+ *   ZOH:      A_bar = e^{dt a}, f = (e^{dt a} - 1)/a  (dt at a = 0)
+ *   bilinear: A_bar = (1 + dt a/2)/(1 - dt a/2), f = dt/(1 - dt a/2)      */
+static void disc_parts(double dt, double a, int disc, double* abar, double* f, double* dabar_ddt,
+                       double* dabar_da, double* df_ddt, double* df_da) {
+    if (disc == 2) {
+        const double q = 1.0 - 0.5 * dt * a;
+        *abar = (1.0 + 0.5 * dt * a) / q;
+        *f = dt / q;
+        *dabar_ddt = a / (q * q);
+        *dabar_da = dt / (q * q);
+        *df_ddt = 1.0 / (q * q);
+        *df_da = 0.5 * dt * dt / (q * q);
+        return;
+    }
+    const double e = exp(dt * a);
+    *abar = e;
+    *dabar_ddt = a * e;
+    *dabar_da = dt * e;
+    if (disc == 1) {
+        if (a == 0.0) {
+            *f = dt;
+            *df_ddt = 1.0;
+            *df_da = 0.5 * dt * dt;
+        } else {
+            *f = expm1(dt * a) / a;
+            *df_ddt = e;
+            *df_da = (dt * e - *f) / a;
+        }
+    } else {
+        *f = dt;
+        *df_ddt = 1.0;
+        *df_da = 0.0;
+    }
+}
+
+/* Gradients of the scan (the reverse-mode derivative of oracle_scan), for
+ * training.  Given dy = dL/dy (and dh_last = dL/dh_last, or none), returns
+ * dL/d of every input: du, ddelta (w.r.t. delta_raw), dz, dA, dB, dC, dD,
+ * dbias, dh0.  The pages train the model end to end by gradient descent
+ * (jsqmd page, section 4.2; the lmnt page's training loop in section 4.2) but
+ * print no derivative, so this is the chain rule applied to one_step, run
+ * backwards in time: with lambda_t = dL/dh_t,
+ *   lambda_t = C_t g_t + A_bar_{t+1} lambda_{t+1}   (g_t = dL/dy_pre_t),
+ * and every input's gradient collects its terms from each step.  The forward
+ * states are recomputed per channel first.
+ * Layouts as oracle_scan; dA, dB, dC, dD, dbias accumulate sums over the
+ * channels / batch rows / timesteps that share the parameter.  Outputs dz,
+ * dD, dbias, dh0 may be NULL (dz and dD must be given when z and D are).
+ * Runs channels of one batch row in parallel with per-thread partial sums of
+ * dB and dC, reduced in thread order (deterministic for a fixed thread count). */
+int oracle_scan_bwd(const double* u, const double* delta_raw, const double* A, const double* B,
+                    const double* C, const double* D, const double* z, const double* delta_bias,
+                    const double* h0, int softplus, int disc, int64_t batch, int64_t L,
+                    int64_t Dn, int64_t N, const double* dy, const double* dh_last, double* du,
+                    double* ddelta, double* dA, double* dB, double* dC, double* dD, double* dz,
+                    double* dbias, double* dh0, int nthreads) {
+    if (!u || !delta_raw || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
+        return -1;
+    if ((z && !dz) || (D && !dD)) return -1;
+    if (batch < 0 || L < 0 || Dn < 0 || N < 1) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    const int nt = omp_get_max_threads();
+#else
+    const int nt = 1;
+#endif
+    for (int64_t i = 0; i < Dn * N; ++i) dA[i] = 0.0;
+    for (int64_t i = 0; i < batch * L * N; ++i) dB[i] = dC[i] = 0.0;
+    if (dD)
+        for (int64_t i = 0; i < Dn; ++i) dD[i] = 0.0;
+    if (dbias)
+        for (int64_t i = 0; i < Dn; ++i) dbias[i] = 0.0;
+    /* per-thread partial sums: dB, dC of the current batch row; dA, dD, dbias */
+    double* part = (double*)calloc((size_t)nt * (size_t)(2 * L * N + Dn * N + 2 * Dn),
+                                   sizeof(double));
+    if (!part) return -2;
+    int failed = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+        {
+#ifdef _OPENMP
+            const int tid = omp_get_thread_num();
+#else
+            const int tid = 0;
+#endif
+            double* pB = part + (size_t)tid * (size_t)(2 * L * N + Dn * N + 2 * Dn);
+            double* pC = pB + L * N;
+            double* pA = pC + L * N;
+            double* pD = pA + Dn * N;
+            double* pbias = pD + Dn;
+            for (int64_t i = 0; i < 2 * L * N; ++i) pB[i] = 0.0;
+            double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+            double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+            if (!hs || !lam) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+                failed = 1;
+            }
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+            for (int64_t d = 0; d < Dn; ++d) {
+                if (!hs || !lam) continue;
+                const double* Arow = A + d * N;
+                /* forward: hs[(t+1)*N + n] = h_t, hs[n] = h_{-1} */
+                for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * Dn + d) * N + n] : 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    const int64_t e = (b * L + t) * Dn + d;
+                    const double dt = step_size(delta_raw[e], delta_bias, d, softplus);
+                    for (int64_t n = 0; n < N; ++n) {
+                        double abar, f, x1, x2, x3, x4;
+                        disc_parts(dt, Arow[n], disc, &abar, &f, &x1, &x2, &x3, &x4);
+                        hs[(t + 1) * N + n] =
+                            abar * hs[t * N + n] + f * B[(b * L + t) * N + n] * u[e];
+                    }
+                }
+                /* backward */
+                for (int64_t n = 0; n < N; ++n) lam[n] = dh_last ? dh_last[(b * Dn + d) * N + n] : 0.0;
+                for (int64_t t = L - 1; t >= 0; --t) {
+                    const int64_t e = (b * L + t) * Dn + d;
+                    const double v = delta_raw[e] + (delta_bias ? delta_bias[d] : 0.0);
+                    const double dt = softplus ? sp_softplus(v) : v;
+                    const double* Bt = B + (b * L + t) * N;
+                    const double* Ct = C + (b * L + t) * N;
+                    const double* ht = hs + (t + 1) * N;
+                    const double* hp = hs + t * N;
+                    double ypre = D ? D[d] * u[e] : 0.0;
+                    for (int64_t n = 0; n < N; ++n) ypre += Ct[n] * ht[n];
+                    double g = dy[e];
+                    if (z) {
+                        const double sg = 1.0 / (1.0 + exp(-z[e]));
+                        g = dy[e] * z[e] * sg;
+                        dz[e] = dy[e] * ypre * sg * (1.0 + z[e] * (1.0 - sg));
+                    }
+                    double du_e = D ? g * D[d] : 0.0;
+                    if (D) pD[d] += g * u[e];
+                    double ddt = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        double abar, f, dab_dt, dab_da, df_dt, df_da;
+                        disc_parts(dt, Arow[n], disc, &abar, &f, &dab_dt, &dab_da, &df_dt, &df_da);
+                        const double l = Ct[n] * g + lam[n];      /* lambda_t */
+                        pC[t * N + n] += g * ht[n];
+                        const double dab = l * hp[n];               /* dL/dA_bar */
+                        const double dfac = l * Bt[n] * u[e];       /* dL/df */
+                        pB[t * N + n] += l * f * u[e];
+                        du_e += l * f * Bt[n];
+                        ddt += dab * dab_dt + dfac * df_dt;
+                        pA[d * N + n] += dab * dab_da + dfac * df_da;
+                        lam[n] = abar * l;                          /* to step t-1 */
+                    }
+                    du[e] = du_e;
+                    const double dv = softplus ? ddt / (1.0 + exp(-v)) : ddt;
+                    ddelta[e] = dv;
+                    pbias[d] += dv;
+                }
+                if (dh0)
+                    for (int64_t n = 0; n < N; ++n) dh0[(b * Dn + d) * N + n] = lam[n];
+            }
+            free(hs);
+            free(lam);
+        }
+        /* reduce the row's dB, dC partials in thread order */
+        for (int th = 0; th < nt; ++th) {
+            double* pB = part + (size_t)th * (size_t)(2 * L * N + Dn * N + 2 * Dn);
+            for (int64_t i = 0; i < L * N; ++i) {
+                dB[b * L * N + i] += pB[i];
+                dC[b * L * N + i] += pB[L * N + i];
+            }
+        }
+    }
+    for (int th = 0; th < nt; ++th) {
+        double* pA = part + (size_t)th * (size_t)(2 * L * N + Dn * N + 2 * Dn) + 2 * L * N;
+        for (int64_t i = 0; i < Dn * N; ++i) dA[i] += pA[i];
+        for (int64_t i = 0; i < Dn; ++i) {
+            if (dD) dD[i] += pA[Dn * N + i];
+            if (dbias) dbias[i] += pA[Dn * N + Dn + i];
+        }
+    }
+    free(part);
+    return failed ? -2 : 0;
+}
+
 /* Causal depthwise conv1d, optionally followed by silu: the step that turns
  * the x branch of the block input into the scan input u (lmnt page,
  * section 3.1: a depthwise 1D convolution of width about 4 on x_ssm before
