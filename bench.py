@@ -259,6 +259,50 @@ def measure_conv(ms, reps=20, width=4):
             "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9}
 
 
+def measure_bwd(ms, reps=5):
+    """ms_scan_bwd (gradients of every input) on the 130M-layer workload:
+    ms per call (forward recompute included) and the main backward kernel's
+    HIP-event time."""
+    import torch
+    import synth
+    w = synth.workload("m130m")
+    x = synth.scan_inputs(w, device="cuda", seed=0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dy = torch.randn(w.batch, w.L, w.Dn, generator=g, device="cuda").to(x["u"].dtype)
+    io = ms.MS_BF16 if w.io == "bf16" else ms.MS_F32
+    ws = torch.empty(ms.scan_bwd_workspace_bytes(w.batch, w.L, w.Dn, w.N, io,
+                                                 ms.flags(w.softplus)),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        ms.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                    delta_bias=x.get("delta_bias"), softplus=w.softplus, workspace=ws,
+                    stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_ms = start.elapsed_time(end) / reps
+    ms.profile_begin(reps)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    ph = ms.profile_end()
+    elems = w.batch * w.L * w.Dn
+    return {"workload": "gradients of the Mamba-130M-layer scan (ms_scan_bwd: du, ddelta, dz, "
+                        "dA, dB, dC, dD, dbias, dh0), Euler, bf16",
+            "ms_per_call": t_ms, "elem_per_s": elems / (t_ms * 1e-3),
+            "kernels_ms": {k: v["mean_ms"] for k, v in ph.items()
+                           if k != "calls" and v["launches"]}}
+
+
 # ------------------------------------------------------------ CPU oracle --
 def cpu_baseline(w, min_seconds, disc="euler"):
     """fp64 oracle on this host's cores on the same workload, compute time
@@ -339,6 +383,7 @@ def _csv(dirname, suffix):
 def _short(name):
     m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|scan_chunks<[^>]*>|scan_summary<[^>]*>|"
                   r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
+                  r"bwd_main<[^>]*>|bwd_summary<[^>]*>|carry_reverse|reduce_bc|reduce_params|"
                   r"neg_kernel)", name)
     return m.group(1) if m else name[:60]
 
@@ -500,6 +545,8 @@ def main():
         out["decode"] = measure_decode(ms)
         torch.cuda.empty_cache()
         out["conv1d"] = measure_conv(ms)
+        torch.cuda.empty_cache()
+        out["backward"] = measure_bwd(ms)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, disc)

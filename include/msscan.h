@@ -144,6 +144,41 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
                           int32_t io, void* stream);
 
 /*
+ * Gradients of ms_scan_fwd, for training (reverse mode; d_state <= 16).
+ * Given dy = dL/dy ([batch][L][d_inner], io dtype) and optionally dh_last =
+ * dL/dh_last ([batch][d_inner][d_state] fp32), returns dL/d of the inputs:
+ *   du, ddelta, dz : [batch][L][d_inner] io dtype (ddelta is w.r.t. the raw
+ *                    delta, i.e. through the softplus and bias)
+ *   dA             : [d_inner][d_state] fp32
+ *   dB, dC         : [batch][L][d_state] fp32 (sums over the channels)
+ *   dD, dbias      : [d_inner] fp32 (sums over batch and time)
+ *   dh0            : [batch][d_inner][d_state] fp32 (w.r.t. h0, or the zero
+ *                    initial state when h0 is NULL)
+ * The forward inputs, flags and dims are those of the ms_scan_fwd call being
+ * differentiated (the forward states are recomputed, nothing is kept from
+ * it).  The pages train the model end to end by gradient descent (jsqmd
+ * page, section 4.2; lmnt page, section 4.2) and print no derivative: these
+ * are the chain rule of the recurrence at the top of this file, run back in
+ * time with lambda_t = dL/dh_t = C_t g_t + A_bar_{t+1} lambda_{t+1}.
+ *
+ *   required: u, delta, A, B, C, dy, du, ddelta, dA, dB, dC, dims, workspace;
+ *   dz required when z is given, dD when D is given; dbias, dh0, dh_last,
+ *   h0, D, z, delta_bias optional (NULL).  Outputs must not overlap inputs.
+ *   workspace: ms_scan_bwd_workspace_bytes(dims, flags) bytes (never 0),
+ *   16-byte aligned, no initialisation needed.
+ * Statuses as for ms_scan_fwd; MS_ERR_UNSUPPORTED for d_state > 16.
+ * Deterministic: partial sums are added in a fixed order.
+ */
+size_t ms_scan_bwd_workspace_bytes(const ms_dims* dims, uint32_t flags);
+ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z,
+                      const float* delta_bias, uint32_t flags, const float* h0,
+                      const void* dy, const float* dh_last, void* du, void* ddelta,
+                      float* dA, float* dB, float* dC, float* dD, void* dz, float* dbias,
+                      float* dh0, const ms_dims* dims, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
  * Causal depthwise conv1d over the sequence, optionally followed by silu: the
  * step of the block that turns the x branch into the scan input u (the
  * lmnt.cn page, section 3.1, puts a depthwise 1D convolution of width about 4

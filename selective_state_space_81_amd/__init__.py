@@ -28,7 +28,7 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
 
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
            "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end",
-           "ms_conv1d_silu")
+           "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd")
 
 PHASES = ("prep", "summary", "carry", "main", "step", "conv")  # ms_phase order
 
@@ -79,6 +79,11 @@ def load(path: Optional[str] = None):
     lib.ms_last_error.argtypes = []
     lib.ms_abi_version.restype = ctypes.c_int
     lib.ms_abi_version.argtypes = []
+    lib.ms_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ms_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(MsDims), u32]
+    lib.ms_scan_bwd.restype = ctypes.c_int
+    lib.ms_scan_bwd.argtypes = [vp] * 8 + [u32] + [vp] * 12 + [ctypes.POINTER(MsDims), vp,
+                                                                ctypes.c_size_t, vp]
     lib.ms_conv1d_silu.restype = ctypes.c_int
     lib.ms_conv1d_silu.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, ctypes.c_int64, i32, i32,
                                    vp]
@@ -214,3 +219,49 @@ def conv1d_silu(x, weight, bias=None, x_prev=None, *, silu=True, u=None, stream=
                                1 if silu else 0, _ptr(u), batch, L, Dn, _io(x), _stream(stream))
     _check(rc)
     return u
+
+
+def scan_bwd_workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int, io: int,
+                             flag_bits: int = MS_SOFTPLUS) -> int:
+    d = dims(batch, seqlen, d_inner, d_state, io)
+    n = load().ms_scan_bwd_workspace_bytes(ctypes.byref(d), flag_bits)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsError(2, "invalid dims for ms_scan_bwd")
+    return int(n)
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, *, softplus=True,
+             zoh=False, bilinear=False, h0=None, dh_last=None, workspace=None, stream=None,
+             want_dh0=True):
+    """ms_scan_bwd on torch device tensors: gradients of scan_fwd for the
+    output gradient dy (and optionally dh_last).  Allocates the outputs (and
+    the workspace when not given).  Returns a dict: du, ddelta, dz (io dtype),
+    dA, dB, dC, dD, dbias, dh0 (fp32); dz / dD are None when z / D are."""
+    import torch
+    batch, L, Dn = u.shape
+    N = A.shape[1]
+    io = _io(u)
+    fl = flags(softplus, zoh, bilinear)
+    dev = u.device
+    f32 = torch.float32
+    out = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+           "dz": torch.empty_like(u) if z is not None else None,
+           "dA": torch.empty(Dn, N, dtype=f32, device=dev),
+           "dB": torch.empty(batch, L, N, dtype=f32, device=dev),
+           "dC": torch.empty(batch, L, N, dtype=f32, device=dev),
+           "dD": torch.empty(Dn, dtype=f32, device=dev) if D is not None else None,
+           "dbias": torch.empty(Dn, dtype=f32, device=dev),
+           "dh0": torch.empty(batch, Dn, N, dtype=f32, device=dev) if want_dh0 else None}
+    ws_n = scan_bwd_workspace_bytes(batch, L, Dn, N, io, fl)
+    if workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = workspace.numel() * workspace.element_size()
+    d = dims(batch, L, Dn, N, io)
+    rc = load().ms_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), fl, _ptr(h0), _ptr(dy), _ptr(dh_last),
+                            _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+                            _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                            _ptr(out["dbias"]), _ptr(out["dh0"]), ctypes.byref(d),
+                            _ptr(workspace), ws_size, _stream(stream))
+    _check(rc)
+    return out

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsscan.so")
 SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "scan_tile.hip"),
            os.path.join(CSRC, "scan_lane.hip"), os.path.join(CSRC, "decode.hip"),
-           os.path.join(CSRC, "conv.hip"),
+           os.path.join(CSRC, "conv.hip"), os.path.join(CSRC, "scan_bwd.hip"),
            os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "profile.cpp")]
 ARCH = os.environ.get("MSSCAN_ARCH", "gfx950")
 

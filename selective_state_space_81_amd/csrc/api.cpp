@@ -291,6 +291,112 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
     return MS_OK;
 }
 
+namespace {
+// Backward plan: segments of bwd_segment_len() steps, all states of a channel
+// in one lane (d_state <= 16).
+struct BwdPlan {
+    msscan::Plan fwd;
+    int64_t K, tiles;
+    size_t agg, fdecay, mu, bdecay, pbc, pparam;  // floats of each region
+};
+
+size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
+
+BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
+    BwdPlan q{};
+    const int64_t seg = msscan::bwd_segment_len();
+    q.K = (d.seqlen + seg - 1) / seg;
+    q.tiles = (d.d_inner + 63) / 64;
+    const size_t B = (size_t)d.batch, D = (size_t)d.d_inner, N = (size_t)d.d_state;
+    const size_t km1 = (size_t)(q.K - 1);
+    const bool bil = (flags & MS_BILINEAR) != 0;
+    q.agg = km1 * B * N * D;
+    q.fdecay = km1 * B * D * (bil ? N : 1);
+    q.mu = q.agg;
+    q.bdecay = q.fdecay;
+    q.pbc = (size_t)q.tiles * B * (size_t)d.seqlen * 2 * N;
+    q.pparam = B * (size_t)q.K * D * (N + 2);
+    msscan::Plan& p = q.fwd;
+    p.tile_path = 0;
+    p.ns = d.d_state <= 4 ? 4 : (d.d_state <= 8 ? 8 : 16);
+    p.waves = 1;
+    p.tiles = (int)q.tiles;
+    p.chunks = (int)q.K;
+    p.chunk_len = seg;
+    return q;
+}
+
+size_t bwd_ws_floats(const BwdPlan& q) {
+    return pad64(q.agg) + pad64(q.fdecay) + pad64(q.mu) + pad64(q.bdecay) + pad64(q.pbc) +
+           pad64(q.pparam);
+}
+}  // namespace
+
+size_t ms_scan_bwd_workspace_bytes(const ms_dims* dims, uint32_t flags) {
+    if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
+    if (dims->d_state > 16) return (size_t)-1;
+    return bwd_ws_floats(bwd_plan(*dims, flags)) * sizeof(float);
+}
+
+ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const void* B,
+                      const void* C, const float* D, const void* z, const float* delta_bias,
+                      uint32_t flags, const float* h0, const void* dy, const float* dh_last,
+                      void* du, void* ddelta, float* dA, float* dB, float* dC, float* dD,
+                      void* dz, float* dbias, float* dh0, const ms_dims* dims, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    ms_status st = check_dims(dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (dims->d_state > 16)
+        return fail(MS_ERR_UNSUPPORTED, "ms_scan_bwd supports d_state <= 16 (got %d)",
+                    dims->d_state);
+    if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
+        return fail(MS_ERR_NULL, "u, delta, A, B, C, dy, du, ddelta, dA, dB and dC are required");
+    if ((z && !dz) || (D && !dD))
+        return fail(MS_ERR_NULL, "dz (dD) is required when z (D) is given");
+    const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_last, du,
+                          ddelta, dA, dB, dC, dD, dz, dbias, dh0, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    const BwdPlan q = bwd_plan(*dims, flags);
+    const size_t need = bwd_ws_floats(q) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+        return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    msscan::ScanArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+    a.h0 = h0; a.L = dims->seqlen; a.chunk_len = q.fwd.chunk_len; a.batch = dims->batch;
+    a.Dn = dims->d_inner; a.N = dims->d_state; a.chunks = q.fwd.chunks;
+    a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0; a.waves = 1;
+    const bool bil = (flags & MS_BILINEAR) != 0;
+    float* ws = static_cast<float*>(workspace);
+    a.agg = ws;
+    ws += pad64(q.agg);
+    if (bil) a.prod = ws; else a.sdt = ws;
+    ws += pad64(q.fdecay);
+    msscan::BwdLaunch L{};
+    L.mu = ws;
+    ws += pad64(q.mu);
+    if (bil) L.prod_b = ws; else L.sdt_b = ws;
+    ws += pad64(q.bdecay);
+    L.pbc = ws;
+    ws += pad64(q.pbc);
+    L.pparam = ws;
+    L.f = a;
+    L.dy = dy; L.dh_last = dh_last; L.du = du; L.ddelta = ddelta; L.dz = z ? dz : nullptr;
+    L.dh0 = dh0; L.dA = dA; L.dB = dB; L.dC = dC; L.dD = D ? dD : nullptr; L.dbias = dbias;
+    L.bf16 = dims->io == MS_BF16;
+    L.disc = disc_of(flags);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    msscan::prof_call();
+    hipError_t e = msscan::launch_summary_carry(q.fwd, a, L.bf16, L.disc, hs);
+    if (e == hipSuccess) e = msscan::launch_scan_bwd(L, hs);
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
 ms_status ms_conv1d_silu(const void* x, const float* weight, const float* bias,
                          const void* x_prev, int32_t width, int32_t silu, void* u,
                          int32_t batch, int64_t seqlen, int32_t d_inner, int32_t io,

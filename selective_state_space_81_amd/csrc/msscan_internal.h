@@ -96,6 +96,37 @@ hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s)
 bool step_quads_supported(int batch, int d_inner, int n);
 hipError_t launch_step_quads(const StepArgs& a, bool bf16, int disc, hipStream_t s);
 
+// Gradients (scan_bwd.hip).  f carries the forward inputs, with f.agg and
+// f.sdt / f.prod holding the forward segment starts of a plan whose segments
+// are bwd_segment_len() steps (computed first by launch_summary_carry).
+struct BwdLaunch {
+    ScanArgs f;
+    const void* dy;
+    const float* dh_last;
+    void* du;
+    void* ddelta;
+    void* dz;
+    float* dh0;
+    float* dA;
+    float* dB;
+    float* dC;
+    float* dD;
+    float* dbias;
+    float* mu;
+    float* sdt_b;
+    float* prod_b;
+    float* pbc;
+    float* pparam;
+    bool bf16;
+    int disc;
+};
+int bwd_segment_len();
+hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s);
+// The forward's segment summaries and carry only (no main pass), generic
+// kernels with p.ns states per lane.
+hipError_t launch_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                hipStream_t s);
+
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
 // ProfScope records the phase's begin event at construction and its end
 // event at destruction, around one kernel launch.  Both do nothing unless a

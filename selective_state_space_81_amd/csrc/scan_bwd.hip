@@ -1,0 +1,480 @@
+// scan_bwd.hip -- gradients of the selective scan (ms_scan_bwd), for
+// training, d_state <= 16.
+//
+// The reverse-mode derivative of the forward scan.  With lambda_t = dL/dh_t
+// and g_t = dL/dy_pre_t (y_pre = sum_n C h + D u, before the gate),
+//
+//   lambda_t = C_t g_t + mu_t,   mu_t = A_bar_{t+1} lambda_{t+1}
+//
+// runs backwards in time, and every input collects its terms per step:
+//   dC_t += g_t h_t          dB_t += lambda_t f_t u_t        du_t += lambda_t f_t B_t + g_t D
+//   d(A_bar) = lambda_t h_{t-1},  d(f) = lambda_t B_t u_t  ->  ddt, dA
+// (f is the B*u factor of the discretisation: dt, (e^{dt A}-1)/A or
+// dt/(1-dt A/2)).  The pages train the model end to end (jsqmd page, section
+// 4.2; lmnt page, section 4.2) but print no derivative; this is the chain rule
+// applied to the forward recurrence.
+//
+// Parallel plan, mirroring the forward: the sequence is cut into segments of
+// kSeg steps.
+//   1. forward summaries + carry (the forward's own kernels) give every
+//      segment's starting state h;
+//   2. bwd_summary: from mu = 0 at a segment's end, the adjoint run over the
+//      segment gives the mu it passes left (beta) and the segment decay;
+//   3. carry_reverse composes them from the last segment to the first, giving
+//      each segment the mu that enters it from the right;
+//   4. bwd_main: per segment, the forward states are recomputed from its
+//      starting state (checkpoints every kSub steps kept in registers, the
+//      kSub states of a sub-block recomputed from its checkpoint), and the
+//      adjoint runs back over the segment producing every gradient.  The
+//      per-step sums over channels of dB and dC are reduced across the wave
+//      through LDS and stored per 64-channel tile; the sums over time and batch
+//      of dA, dD and dbias are stored per segment;
+//   5. two small passes add those partials in a fixed order.
+// No pass waits on another workgroup: the results are deterministic.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "dpp_common.h"
+#include "msscan_internal.h"
+
+namespace msscan {
+namespace {
+
+using namespace dev;
+
+constexpr int kSeg = 16;  // timesteps per backward segment
+constexpr int kSub = 4;   // timesteps per recomputed sub-block
+constexpr int kNumCk = kSeg / kSub;
+
+// Per-state derivatives of the discretisation: A_bar, the B*u factor f, and
+// their partial derivatives w.r.t. dt and a (the continuous A), from
+// t = dt*a*log2(e), invA = 1/a (0 at a = 0), a2 = a*log2(e).
+template <int DISC>
+struct Disc {
+    float abar, f, dab_dt, dab_da, df_dt, df_da;
+    __device__ __forceinline__ Disc(float dt, float t, float a2, float invA) {
+        const float a = a2 * kLn2;
+        if constexpr (DISC == kBilinear) {
+            const float r = bilinear_r(t);
+            const float r2 = r * r;
+            abar = fmaf(2.f, r, -1.f);
+            f = dt * r;
+            dab_dt = a * r2;
+            dab_da = dt * r2;
+            df_dt = r2;
+            df_da = 0.5f * dt * dt * r2;
+        } else {
+            abar = hw_exp2(t);
+            dab_dt = a * abar;
+            dab_da = dt * abar;
+            if constexpr (DISC == kZoh) {
+                f = zoh_factor(dt, t, abar, invA);
+                df_dt = abar;
+                // (dt A_bar - f)/a, or near a = 0 its series dt^2 (1/2 + x/3 + x^2/8)
+                const float x = t * kLn2;
+                const float ser = dt * dt * fmaf(x, fmaf(x, 0.125f, 1.f / 3.f), 0.5f);
+                df_da = fabsf(t) < kZohSwitch ? ser : (dt * abar - f) * invA;
+            } else {
+                f = dt;
+                df_dt = 1.f;
+                df_da = 0.f;
+            }
+        }
+    }
+};
+
+// Kernel arguments beyond the forward's.
+struct BwdArgs {
+    ScanArgs f;          // forward inputs; f.agg/f.sdt/f.prod: forward segment starts
+    const void* dy;      // [batch][L][Dn] io
+    const float* dh_last;
+    void* du;            // [batch][L][Dn] io
+    void* ddelta;        // [batch][L][Dn] io
+    void* dz;            // [batch][L][Dn] io or null
+    float* dh0;          // [batch][Dn][N] or null
+    float* mu;           // [batch][K-1][N][Dn]: beta, then the mu entering each segment
+    float* sdt_b;        // [batch][K-1][Dn] decay sums of segments 1..K-1 (exp-based)
+    float* prod_b;       // [batch][K-1][N][Dn] decay products (bilinear)
+    float* pbc;          // [tiles][batch][L][2N]: per-tile partial dB | dC
+    float* pparam;       // [batch][K][Dn][N+2]: per-segment partial dA | dD | dbias
+};
+
+template <bool BF16>
+__device__ __forceinline__ float ldio(const void* p, int64_t i) {
+    return ld<BF16>(p, i);
+}
+
+// ---- 2. backward summaries ----------------------------------------------------
+template <int NS, bool BF16, int DISC>
+__global__ void __launch_bounds__(64) bwd_summary(BwdArgs a) {
+    const ScanArgs& f = a.f;
+    const int lane = threadIdx.x;
+    const int b = blockIdx.z;
+    const int s = blockIdx.y + 1;  // segments 1 .. K-1
+    const int d = blockIdx.x * 64 + lane;
+    const bool dvalid = d < f.Dn;
+    const int dd = dvalid ? d : f.Dn - 1;
+    const int N = f.N;
+    float A2[NS], mu[NS], P[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        A2[n] = n < N ? f.A[(int64_t)dd * N + n] * kLog2e : 0.f;
+        mu[n] = 0.f;
+        P[n] = 1.f;
+    }
+    const float bias = f.bias ? f.bias[dd] : 0.f;
+    const int64_t t0 = (int64_t)s * kSeg;
+    const int64_t t1 = min(f.L, t0 + kSeg);
+    const int jn = lane & (NS - 1);
+    float ssum = 0.f, scomp = 0.f;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        const int64_t e = ((int64_t)b * f.L + t) * f.Dn + dd;
+        const float dt = step_size(ldio<BF16>(f.delta, e), bias, f.softplus);
+        float g = ldio<BF16>(a.dy, e);
+        if (f.z) g *= silu_f(ldio<BF16>(f.z, e));
+        const float cl = jn < N ? ldio<BF16>(f.C, ((int64_t)b * f.L + t) * N + jn) : 0.f;
+        static_for(
+            [&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                const float t2 = dt * A2[n];
+                float abar;
+                if constexpr (DISC == kBilinear)
+                    abar = fmaf(2.f, bilinear_r(t2), -1.f);
+                else
+                    abar = hw_exp2(t2);
+                mu[n] = abar * l;
+                if constexpr (DISC == kBilinear) P[n] *= abar;
+            },
+            std::make_integer_sequence<int, NS>{});
+        const float yk = dt - scomp;
+        const float tk = ssum + yk;
+        scomp = (tk - ssum) - yk;
+        ssum = tk;
+    }
+    if (!dvalid) return;
+    const int km1 = f.chunks - 1;
+    const int64_t base = (int64_t)b * km1 + (s - 1);
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+        if (n < N) a.mu[(base * N + n) * f.Dn + d] = mu[n];
+    if constexpr (DISC == kBilinear) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+            if (n < N) a.prod_b[(base * N + n) * f.Dn + d] = P[n];
+    } else {
+        a.sdt_b[base * f.Dn + d] = ssum;
+    }
+}
+
+// ---- 3. reverse carry ---------------------------------------------------------
+// One thread per (b, n, d).  Slot s-1 of mu holds beta_s (from segment s,
+// s = 1..K-1); it is replaced by the mu entering segment s-1 from the right:
+//   mu_in(K-1) = dh_last (or 0),  mu_in(s-1) = decay_s mu_in(s) + beta_s.
+__global__ void __launch_bounds__(256) carry_reverse(BwdArgs a) {
+    const ScanArgs& f = a.f;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = (int64_t)f.batch * f.N * f.Dn;
+    if (idx >= total) return;
+    const int d = (int)(idx % f.Dn);
+    const int n = (int)((idx / f.Dn) % f.N);
+    const int b = (int)(idx / ((int64_t)f.Dn * f.N));
+    const float A2 = f.A[(int64_t)d * f.N + n] * kLog2e;
+    float m = a.dh_last ? a.dh_last[((int64_t)b * f.Dn + d) * f.N + n] : 0.f;
+    const int km1 = f.chunks - 1;
+    for (int s = km1; s >= 1; --s) {  // slot s-1 <- mu entering segment s-1
+        const int64_t base = (int64_t)b * km1 + (s - 1);
+        const float decay = a.prod_b ? a.prod_b[(base * f.N + n) * f.Dn + d]
+                                     : hw_exp2(A2 * a.sdt_b[base * f.Dn + d]);
+        const int64_t i = (base * f.N + n) * f.Dn + d;
+        m = fmaf(decay, m, a.mu[i]);
+        a.mu[i] = m;
+    }
+}
+
+// ---- 4. per-segment gradients ---------------------------------------------------
+template <int NS, bool BF16, int DISC>
+__global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
+    const ScanArgs& f = a.f;
+    // Per-step dB | dC contributions, [value][lane]; rows padded to 65 floats
+    // so that the column sums below read distinct banks.
+    __shared__ float red[2 * NS][65];
+    const int lane = threadIdx.x;
+    const int b = blockIdx.z;
+    const int s = blockIdx.y;
+    const int tile = blockIdx.x;
+    const int d = tile * 64 + lane;
+    const bool dvalid = d < f.Dn;
+    const int dd = dvalid ? d : f.Dn - 1;
+    const int N = f.N;
+    const int km1 = f.chunks - 1;
+    const int jn = lane & (NS - 1);
+    const float live = dvalid ? 1.f : 0.f;  // tail lanes repeat a channel: count it once
+
+    float A2[NS], invA[NS], mu[NS], ck[kNumCk][NS], dA[NS];
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        const float av = n < N ? f.A[(int64_t)dd * N + n] : 0.f;
+        A2[n] = av * kLog2e;
+        invA[n] = av != 0.f ? 1.f / av : 0.f;
+        dA[n] = 0.f;
+        float h = 0.f, m = 0.f;
+        if (n < N) {
+            if (s == 0) {
+                if (f.h0) h = f.h0[((int64_t)b * f.Dn + dd) * N + n];
+            } else {
+                h = f.agg[(((int64_t)b * km1 + (s - 1)) * N + n) * f.Dn + dd];
+            }
+            if (s == f.chunks - 1) {
+                if (a.dh_last) m = a.dh_last[((int64_t)b * f.Dn + dd) * N + n];
+            } else {
+                m = a.mu[(((int64_t)b * km1 + s) * N + n) * f.Dn + dd];
+            }
+        }
+        ck[0][n] = h;
+        mu[n] = m;
+    }
+    const float bias = f.bias ? f.bias[dd] : 0.f;
+    const float Dd = f.D ? f.D[dd] : 0.f;
+    const int64_t t0 = (int64_t)s * kSeg;
+    const int64_t t1 = min(f.L, t0 + kSeg);
+    const int64_t row0 = (int64_t)b * f.L;
+
+    auto elem = [&](int64_t t) { return (row0 + t) * f.Dn + dd; };
+    auto bc_at = [&](const void* p, int64_t t) {
+        return jn < N ? ldio<BF16>(p, (row0 + t) * N + jn) : 0.f;
+    };
+    auto dt_at = [&](int64_t t) { return step_size(ldio<BF16>(f.delta, elem(t)), bias, f.softplus); };
+    // One forward step of all states from h (in place).
+    auto fwd = [&](float (&h)[NS], int64_t t) {
+        const float dt = dt_at(t);
+        const float uv = ldio<BF16>(f.u, elem(t));
+        const float bl = bc_at(f.B, t);
+        static_for(
+            [&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
+                h[n] = fmaf(q.abar, h[n], q.f * row_bcast<n>(bl) * uv);
+            },
+            std::make_integer_sequence<int, NS>{});
+    };
+
+    // Checkpoints: the state before each sub-block.
+#pragma unroll
+    for (int k = 1; k < kNumCk; ++k) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) ck[k][n] = ck[k - 1][n];
+        for (int j = 0; j < kSub; ++j) {
+            const int64_t t = t0 + (k - 1) * kSub + j;
+            if (t < t1) fwd(ck[k], t);
+        }
+    }
+
+    float dbias = 0.f, dD = 0.f;
+    float* pbc_row = a.pbc + ((int64_t)tile * f.batch + b) * f.L * (2 * N);
+#pragma unroll
+    for (int k = kNumCk - 1; k >= 0; --k) {
+        const int64_t tk = t0 + (int64_t)k * kSub;
+        if (tk >= t1) continue;
+        // states of this sub-block: hs[j] = h after step tk + j
+        float hs[kSub][NS];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) hs[j][n] = j == 0 ? ck[k][n] : hs[j - 1][n];
+            if (tk + j < t1) fwd(hs[j], tk + j);
+        }
+#pragma unroll
+        for (int j = kSub - 1; j >= 0; --j) {
+            const int64_t t = tk + j;
+            if (t >= t1) continue;
+            const int64_t e = elem(t);
+            const float v = ldio<BF16>(f.delta, e) + bias;
+            const float dt = f.softplus ? softplus_f(v) : v;
+            const float uv = ldio<BF16>(f.u, e);
+            const float bl = bc_at(f.B, t);
+            const float cl = bc_at(f.C, t);
+            const float dyv = ldio<BF16>(a.dy, e);
+            // y_pre from the recomputed state, for the gate's derivative
+            float ypre = Dd * uv;
+            static_for([&](auto nc) { ypre = fmaf(row_bcast<decltype(nc)::value>(cl), hs[j][decltype(nc)::value], ypre); },
+                       std::make_integer_sequence<int, NS>{});
+            float g = dyv;
+            if (f.z) {
+                const float zv = ldio<BF16>(f.z, e);
+                const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
+                g = dyv * zv * sg;
+                if (dvalid) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
+            }
+            float du = g * Dd;
+            dD = fmaf(g, uv, dD);
+            float ddt = 0.f;
+            static_for(
+                [&](auto nc) {
+                    constexpr int n = decltype(nc)::value;
+                    const float hp = j == 0 ? ck[k][n] : hs[j - 1][n];
+                    const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
+                    const float bn = row_bcast<n>(bl);
+                    const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                    red[NS + n][lane] = live * g * hs[j][n];    // dC contribution
+                    red[n][lane] = live * l * q.f * uv;         // dB contribution
+                    du = fmaf(l * q.f, bn, du);
+                    const float dab = l * hp;
+                    const float dfac = l * bn * uv;
+                    ddt = fmaf(dab, q.dab_dt, fmaf(dfac, q.df_dt, ddt));
+                    dA[n] = fmaf(dab, q.dab_da, fmaf(dfac, q.df_da, dA[n]));
+                    mu[n] = q.abar * l;
+                },
+                std::make_integer_sequence<int, NS>{});
+            const float dv = f.softplus ? ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e)) : ddt;
+            dbias += dv;
+            if (dvalid) {
+                st<BF16>(a.du, e, du);
+                st<BF16>(a.ddelta, e, dv);
+            }
+            // Sum the 2N contributions of this step over the wave's channels
+            // and store the tile's partial.
+            __syncthreads();
+            if (lane < 2 * NS) {
+                float acc = 0.f;
+                for (int i = 0; i < 64; ++i) acc += red[lane][i];
+                const int n = lane < NS ? lane : lane - NS;
+                if (n < N) pbc_row[t * (2 * N) + (lane < NS ? 0 : N) + n] = acc;
+            }
+            __syncthreads();
+        }
+    }
+    if (!dvalid) return;
+    // per-segment partials of dA, dD, dbias
+    float* pp = a.pparam + (((int64_t)b * f.chunks + s) * f.Dn + d) * (N + 2);
+#pragma unroll
+    for (int n = 0; n < NS; ++n)
+        if (n < N) pp[n] = dA[n];
+    pp[N] = dD;
+    pp[N + 1] = dbias;
+    if (s == 0 && a.dh0) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+            if (n < N) a.dh0[((int64_t)b * f.Dn + d) * N + n] = mu[n];
+    }
+}
+
+// ---- 5. fixed-order sums of the partials -----------------------------------------
+__global__ void __launch_bounds__(256) reduce_bc(BwdArgs a, float* dB, float* dC, int tiles) {
+    const ScanArgs& f = a.f;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, t, k), k < 2N
+    const int64_t per = (int64_t)f.batch * f.L * 2 * f.N;
+    if (idx >= per) return;
+    float acc = 0.f;
+    for (int tl = 0; tl < tiles; ++tl) acc += a.pbc[(int64_t)tl * per + idx];
+    const int k = (int)(idx % (2 * f.N));
+    const int64_t row = idx / (2 * f.N);
+    if (k < f.N)
+        dB[row * f.N + k] = acc;
+    else
+        dC[row * f.N + k - f.N] = acc;
+}
+
+__global__ void __launch_bounds__(256) reduce_params(BwdArgs a, float* dA, float* dD,
+                                                     float* dbias) {
+    const ScanArgs& f = a.f;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (d, k), k < N+2
+    const int64_t per = (int64_t)f.Dn * (f.N + 2);
+    if (idx >= per) return;
+    float acc = 0.f;
+    const int64_t rows = (int64_t)f.batch * f.chunks;
+    for (int64_t r = 0; r < rows; ++r) acc += a.pparam[r * per + idx];
+    const int k = (int)(idx % (f.N + 2));
+    const int64_t d = idx / (f.N + 2);
+    if (k < f.N)
+        dA[d * f.N + k] = acc;
+    else if (k == f.N) {
+        if (dD) dD[d] = acc;
+    } else if (dbias) {
+        dbias[d] = acc;
+    }
+}
+
+template <int NS, bool BF16, int DISC>
+hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* dD,
+                      float* dbias, hipStream_t s) {
+    const ScanArgs& f = a.f;
+    const int tiles = (f.Dn + 63) / 64;
+    const int K = f.chunks;
+    hipError_t e;
+    if (K > 1) {
+        {
+            ProfScope ps(s, kPhaseSummary);
+            hipLaunchKernelGGL((bwd_summary<NS, BF16, DISC>), dim3(tiles, K - 1, f.batch),
+                               dim3(64), 0, s, a);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int64_t total = (int64_t)f.batch * f.N * f.Dn;
+        {
+            ProfScope ps(s, kPhaseCarry);
+            hipLaunchKernelGGL(carry_reverse, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                               s, a);
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    {
+        ProfScope ps(s, kPhaseMain);
+        hipLaunchKernelGGL((bwd_main<NS, BF16, DISC>), dim3(tiles, K, f.batch), dim3(64), 0, s, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t nbc = (int64_t)f.batch * f.L * 2 * f.N;
+    hipLaunchKernelGGL(reduce_bc, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a, dB, dC,
+                       tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t npar = (int64_t)f.Dn * (f.N + 2);
+    hipLaunchKernelGGL(reduce_params, dim3((unsigned)((npar + 255) / 256)), dim3(256), 0, s, a,
+                       dA, dD, dbias);
+    return hipGetLastError();
+}
+
+template <bool BF16, int DISC>
+hipError_t launch_ns(const BwdArgs& a, float* dA, float* dB, float* dC, float* dD, float* dbias,
+                     hipStream_t s) {
+    const int N = a.f.N;
+    if (N <= 4) return launch_bwd<4, BF16, DISC>(a, dA, dB, dC, dD, dbias, s);
+    if (N <= 8) return launch_bwd<8, BF16, DISC>(a, dA, dB, dC, dD, dbias, s);
+    if (N <= 16) return launch_bwd<16, BF16, DISC>(a, dA, dB, dC, dD, dbias, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int bwd_segment_len() { return kSeg; }
+
+hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s) {
+    BwdArgs a{};
+    a.f = L.f;
+    a.dy = L.dy;
+    a.dh_last = L.dh_last;
+    a.du = L.du;
+    a.ddelta = L.ddelta;
+    a.dz = L.dz;
+    a.dh0 = L.dh0;
+    a.mu = L.mu;
+    a.sdt_b = L.sdt_b;
+    a.prod_b = L.prod_b;
+    a.pbc = L.pbc;
+    a.pparam = L.pparam;
+    switch (L.disc) {
+#define MS_BWD_(DI)                                                                     \
+    case DI:                                                                            \
+        return L.bf16 ? launch_ns<true, DI>(a, L.dA, L.dB, L.dC, L.dD, L.dbias, s)      \
+                      : launch_ns<false, DI>(a, L.dA, L.dB, L.dC, L.dD, L.dbias, s);
+        MS_BWD_(kEuler)
+        MS_BWD_(kZoh)
+        MS_BWD_(kBilinear)
+#undef MS_BWD_
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace msscan

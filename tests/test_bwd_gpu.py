@@ -1,0 +1,130 @@
+"""GPU parity of ms_scan_bwd (gradients of the scan) against the fp64 oracle's
+backward (itself pinned to finite differences of the forward oracle), through
+the C ABI, on the same seeded inputs.
+
+Bound.  Several gradients are sums of many terms of both signs (dA, dD and
+dbias over batch and time; dB and dC over channels), so their fp32 rounding
+scales with the size of the terms, not of the sum.  Every gradient tensor g is
+therefore checked as |g_gpu - g_ref| <= rtol * (|g_ref| + rms(g_ref)), with
+rtol = 2e-4 for fp32 io and, for the bf16 io outputs du / ddelta / dz, the
+bf16 rounding of the stored value added (2 bf16 ulp).  A wrong term or index
+gives O(1) relative errors and fails it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import DISCS, disc_kw
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check(got, ref, io, what, rtol=2e-4):
+    got = got.detach().to("cpu").double().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    lim = rtol * (np.abs(ref) + rms) + 1e-30
+    if io == "bf16":
+        a = np.abs(ref)
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+        lim = lim + 2.0 * np.where(a > 0, np.exp2(e - 7.0), 0.0)
+    err = np.abs(got - ref)
+    bad = ~(err <= lim)
+    if bad.any():
+        i = np.argwhere(bad)[:4].tolist()
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} outside bound; worst "
+                             f"err/lim {float(np.max(err / lim)):.3g}; at {i} got "
+                             f"{[float(got[tuple(k)]) for k in i]} ref "
+                             f"{[float(ref[tuple(k)]) for k in i]}")
+
+
+def _inputs(batch, L, Dn, N, io, seed, optional=True):
+    w = synth.workload("tiny", batch=batch, L=L, Dn=Dn, N=N, io=io)
+    x = synth.scan_inputs(w, device=DEV, seed=seed)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed + 1000)
+    x["dy"] = torch.randn(batch, L, Dn, generator=g, device=DEV).to(x["u"].dtype)
+    if optional:
+        x["h0"] = torch.randn(batch, Dn, N, generator=g, device=DEV)
+        x["dh_last"] = torch.randn(batch, Dn, N, generator=g, device=DEV)
+        x["delta_bias"] = torch.randn(Dn, generator=g, device=DEV) * 0.3
+    else:
+        x["z"] = None
+        x["D"] = None
+        x["delta_bias"] = None
+    return x
+
+
+def _compare(ms, x, io, disc, softplus=True):
+    kw = disc_kw(disc)
+    got = ms.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x.get("D"),
+                      z=x.get("z"), delta_bias=x.get("delta_bias"), softplus=softplus,
+                      h0=x.get("h0"), dh_last=x.get("dh_last"), **kw)
+    torch.cuda.synchronize()
+    ref = oracle.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x.get("D"),
+                          z=x.get("z"), delta_bias=x.get("delta_bias"), h0=x.get("h0"),
+                          dh_last=x.get("dh_last"), softplus=softplus, **kw)
+    for k in ("du", "ddelta", "dz"):
+        if ref[k] is not None:
+            _check(got[k], ref[k], io, k)
+    for k in ("dA", "dB", "dC", "dD", "dbias", "dh0"):
+        if ref[k] is not None:
+            _check(got[k], ref[k], "f32", k)
+
+
+SHAPES = [
+    # batch, L, Dn, N, io
+    (1, 1, 4, 4, "f32"),
+    (2, 37, 70, 16, "f32"),    # L not a multiple of the segment, a tail tile
+    (1, 100, 64, 8, "bf16"),
+    (2, 257, 130, 16, "bf16"),
+    (1, 48, 33, 5, "f32"),     # d_state 5: masked states
+    (3, 16, 64, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}L{}D{}N{}{}".format(*s))
+def test_bwd_shapes(gpu, shape, disc):
+    batch, L, Dn, N, io = shape
+    x = _inputs(batch, L, Dn, N, io, seed=31)
+    _compare(gpu, x, io, disc)
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_without_optional_terms(gpu, disc):
+    x = _inputs(2, 70, 64, 16, "f32", seed=32, optional=False)
+    _compare(gpu, x, "f32", disc)
+
+
+def test_bwd_softplus_off(gpu):
+    x = _inputs(1, 90, 64, 16, "f32", seed=33)
+    x["delta"] = x["delta"].abs() * 0.05 + 0.01
+    x["delta_bias"] = x["delta_bias"].abs() * 0.01
+    _compare(gpu, x, "f32", "euler", softplus=False)
+
+
+def test_bwd_deterministic(gpu):
+    x = _inputs(2, 300, 192, 16, "bf16", seed=34)
+    g1 = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
+                      delta_bias=x["delta_bias"], h0=x["h0"])
+    g2 = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
+                      delta_bias=x["delta_bias"], h0=x["h0"])
+    torch.cuda.synchronize()
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
+
+
+def test_bwd_130m_layer(gpu):
+    """The 130M-layer shape (B8 L2048 D1536 N16, bf16), every gradient."""
+    w = synth.workload("m130m")
+    x = synth.scan_inputs(w, device=DEV, seed=0)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    x["dy"] = torch.randn(w.batch, w.L, w.Dn, generator=g, device=DEV).to(x["u"].dtype)
+    _compare(gpu, x, "bf16", "euler")
