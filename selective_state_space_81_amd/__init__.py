@@ -60,6 +60,13 @@ def load(path: Optional[str] = None):
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
+    # torch ships its own HIP runtime; importing it first makes this library
+    # bind to that same runtime (one device context per process) rather than
+    # loading a second copy from the ROCm install.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with "
                            "`python -m selective_state_space_81_amd.build`")

@@ -391,7 +391,16 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
     L.disc = disc_of(flags);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     msscan::prof_call();
-    hipError_t e = msscan::launch_summary_carry(q.fwd, a, L.bf16, L.disc, hs);
+    // Forward segment starts: the lane kernels' summary where d_state is 8 or
+    // 16 (all states of a channel in one lane, B/C by DPP), else the generic one.
+    hipError_t e;
+    if (dims->d_state == 8 || dims->d_state == 16) {
+        msscan::Plan lp = q.fwd;
+        lp.ns = dims->d_state;
+        e = msscan::launch_lane_summary_carry(lp, a, L.bf16, L.disc, hs);
+    } else {
+        e = msscan::launch_summary_carry(q.fwd, a, L.bf16, L.disc, hs);
+    }
     if (e == hipSuccess) e = msscan::launch_scan_bwd(L, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;

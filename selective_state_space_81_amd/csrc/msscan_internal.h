@@ -126,6 +126,10 @@ hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s);
 // kernels with p.ns states per lane.
 hipError_t launch_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                                 hipStream_t s);
+// The same with the lane kernels' summary (p.ns = 8 or 16, one state set per
+// lane; segment length a multiple of 16).
+hipError_t launch_lane_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                     hipStream_t s);
 
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
 // ProfScope records the phase's begin event at construction and its end

@@ -23,9 +23,9 @@
 //   3. carry_reverse composes them from the last segment to the first, giving
 //      each segment the mu that enters it from the right;
 //   4. bwd_main: per segment, the forward states are recomputed from its
-//      starting state (checkpoints every kSub steps kept in registers, the
-//      kSub states of a sub-block recomputed from its checkpoint), and the
-//      adjoint runs back over the segment producing every gradient.  The
+//      starting state (the start and the state half way kept in registers,
+//      each sub-block's states recomputed from them), and the adjoint runs
+//      back over the segment producing every gradient.  The
 //      per-step sums over channels of dB and dC are reduced across the wave
 //      through LDS and stored per 64-channel tile; the sums over time and batch
 //      of dA, dD and dbias are stored per segment;
@@ -48,7 +48,6 @@ using namespace dev;
 
 constexpr int kSeg = 16;  // timesteps per backward segment
 constexpr int kSub = 4;   // timesteps per recomputed sub-block
-constexpr int kNumCk = kSeg / kSub;
 
 // Per-state derivatives of the discretisation: A_bar, the B*u factor f, and
 // their partial derivatives w.r.t. dt and a (the continuous A), from
@@ -131,12 +130,25 @@ __global__ void __launch_bounds__(64) bwd_summary(BwdArgs a) {
     const int64_t t1 = min(f.L, t0 + kSeg);
     const int jn = lane & (NS - 1);
     float ssum = 0.f, scomp = 0.f;
-    for (int64_t t = t1 - 1; t >= t0; --t) {
+    // All loads of the segment first (indices clamped into it), then the
+    // backward walk.
+    float rdl[kSeg], rdy[kSeg], rz[kSeg], rc[kSeg];
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+        const int64_t t = min(t0 + j, t1 - 1);
         const int64_t e = ((int64_t)b * f.L + t) * f.Dn + dd;
-        const float dt = step_size(ldio<BF16>(f.delta, e), bias, f.softplus);
-        float g = ldio<BF16>(a.dy, e);
-        if (f.z) g *= silu_f(ldio<BF16>(f.z, e));
-        const float cl = jn < N ? ldio<BF16>(f.C, ((int64_t)b * f.L + t) * N + jn) : 0.f;
+        rdl[j] = ldio<BF16>(f.delta, e);
+        rdy[j] = ldio<BF16>(a.dy, e);
+        rz[j] = f.z ? ldio<BF16>(f.z, e) : 0.f;
+        rc[j] = jn < N ? ldio<BF16>(f.C, ((int64_t)b * f.L + t) * N + jn) : 0.f;
+    }
+#pragma unroll
+    for (int j = kSeg - 1; j >= 0; --j) {
+        if (t0 + j >= t1) continue;
+        const float dt = step_size(rdl[j], bias, f.softplus);
+        float g = rdy[j];
+        if (f.z) g *= silu_f(rz[j]);
+        const float cl = rc[j];
         static_for(
             [&](auto nc) {
                 constexpr int n = decltype(nc)::value;
@@ -186,19 +198,44 @@ __global__ void __launch_bounds__(256) carry_reverse(BwdArgs a) {
     const float A2 = f.A[(int64_t)d * f.N + n] * kLog2e;
     float m = a.dh_last ? a.dh_last[((int64_t)b * f.Dn + d) * f.N + n] : 0.f;
     const int km1 = f.chunks - 1;
-    for (int s = km1; s >= 1; --s) {  // slot s-1 <- mu entering segment s-1
-        const int64_t base = (int64_t)b * km1 + (s - 1);
-        const float decay = a.prod_b ? a.prod_b[(base * f.N + n) * f.Dn + d]
-                                     : hw_exp2(A2 * a.sdt_b[base * f.Dn + d]);
-        const int64_t i = (base * f.N + n) * f.Dn + d;
-        m = fmaf(decay, m, a.mu[i]);
-        a.mu[i] = m;
+    const bool prod = a.prod_b != nullptr;
+    // Loads of a group of slots are issued before its chain of updates, so
+    // the chain waits on memory once per group.
+    constexpr int G = 8;
+    for (int s1 = km1; s1 >= 1; s1 -= G) {  // slots s-1 for s = s1, s1-1, ...
+        float dv[G], bv[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            dv[j] = 0.f;
+            bv[j] = 0.f;
+            const int s = s1 - j;
+            if (s >= 1) {
+                const int64_t base = (int64_t)b * km1 + (s - 1);
+                dv[j] = prod ? a.prod_b[(base * f.N + n) * f.Dn + d] : a.sdt_b[base * f.Dn + d];
+                bv[j] = a.mu[(base * f.N + n) * f.Dn + d];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int s = s1 - j;
+            if (s >= 1) {
+                const int64_t base = (int64_t)b * km1 + (s - 1);
+                const float decay = prod ? dv[j] : hw_exp2(A2 * dv[j]);
+                m = fmaf(decay, m, bv[j]);
+                a.mu[(base * f.N + n) * f.Dn + d] = m;
+            }
+        }
     }
 }
 
 // ---- 4. per-segment gradients ---------------------------------------------------
+// The segment's kSeg = 16 steps are walked back in sub-blocks of kSub = 4.
+// Forward states come from two kept states, the segment start and the state
+// after 8 steps (32 recomputed steps per segment), and each sub-block's
+// inputs are loaded in one batch before its arithmetic.
 template <int NS, bool BF16, int DISC>
 __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
+    static_assert(kSeg == 16 && kSub == 4, "the walk below is written for 4 x 4 steps");
     const ScanArgs& f = a.f;
     // Per-step dB | dC contributions, [value][lane]; rows padded to 65 floats
     // so that the column sums below read distinct banks.
@@ -215,7 +252,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     const int jn = lane & (NS - 1);
     const float live = dvalid ? 1.f : 0.f;  // tail lanes repeat a channel: count it once
 
-    float A2[NS], invA[NS], mu[NS], ck[kNumCk][NS], dA[NS];
+    float A2[NS], invA[NS], mu[NS], h0s[NS], dA[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         const float av = n < N ? f.A[(int64_t)dd * N + n] : 0.f;
@@ -235,7 +272,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                 m = a.mu[(((int64_t)b * km1 + s) * N + n) * f.Dn + dd];
             }
         }
-        ck[0][n] = h;
+        h0s[n] = h;
         mu[n] = m;
     }
     const float bias = f.bias ? f.bias[dd] : 0.f;
@@ -244,16 +281,28 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     const int64_t t1 = min(f.L, t0 + kSeg);
     const int64_t row0 = (int64_t)b * f.L;
 
-    auto elem = [&](int64_t t) { return (row0 + t) * f.Dn + dd; };
-    auto bc_at = [&](const void* p, int64_t t) {
-        return jn < N ? ldio<BF16>(p, (row0 + t) * N + jn) : 0.f;
+    // Raw inputs of the 4 steps from tb (indices clamped into the segment).
+    struct Rows {
+        float u[kSub], dl[kSub], z[kSub], dy[kSub], bl[kSub], cl[kSub];
     };
-    auto dt_at = [&](int64_t t) { return step_size(ldio<BF16>(f.delta, elem(t)), bias, f.softplus); };
-    // One forward step of all states from h (in place).
-    auto fwd = [&](float (&h)[NS], int64_t t) {
-        const float dt = dt_at(t);
-        const float uv = ldio<BF16>(f.u, elem(t));
-        const float bl = bc_at(f.B, t);
+    auto load_rows = [&](Rows& r, int64_t tb, bool full) {
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            const int64_t t = min(tb + j, t1 - 1);
+            const int64_t e = (row0 + t) * f.Dn + dd;
+            r.u[j] = ldio<BF16>(f.u, e);
+            r.dl[j] = ldio<BF16>(f.delta, e);
+            r.bl[j] = jn < N ? ldio<BF16>(f.B, (row0 + t) * N + jn) : 0.f;
+            if (full) {
+                r.z[j] = f.z ? ldio<BF16>(f.z, e) : 0.f;
+                r.dy[j] = ldio<BF16>(a.dy, e);
+                r.cl[j] = jn < N ? ldio<BF16>(f.C, (row0 + t) * N + jn) : 0.f;
+            }
+        }
+    };
+    // One forward step of all states (in place).
+    auto fwd = [&](float (&h)[NS], float dl, float uv, float bl) {
+        const float dt = step_size(dl, bias, f.softplus);
         static_for(
             [&](auto nc) {
                 constexpr int n = decltype(nc)::value;
@@ -262,50 +311,52 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             },
             std::make_integer_sequence<int, NS>{});
     };
-
-    // Checkpoints: the state before each sub-block.
+    // Advance h over the 4 steps from tb.
+    auto advance4 = [&](float (&h)[NS], int64_t tb) {
+        Rows r;
+        load_rows(r, tb, false);
 #pragma unroll
-    for (int k = 1; k < kNumCk; ++k) {
-#pragma unroll
-        for (int n = 0; n < NS; ++n) ck[k][n] = ck[k - 1][n];
-        for (int j = 0; j < kSub; ++j) {
-            const int64_t t = t0 + (k - 1) * kSub + j;
-            if (t < t1) fwd(ck[k], t);
-        }
-    }
+        for (int j = 0; j < kSub; ++j)
+            if (tb + j < t1) fwd(h, r.dl[j], r.u[j], r.bl[j]);
+    };
 
     float dbias = 0.f, dD = 0.f;
     float* pbc_row = a.pbc + ((int64_t)tile * f.batch + b) * f.L * (2 * N);
-#pragma unroll
-    for (int k = kNumCk - 1; k >= 0; --k) {
-        const int64_t tk = t0 + (int64_t)k * kSub;
-        if (tk >= t1) continue;
-        // states of this sub-block: hs[j] = h after step tk + j
-        float hs[kSub][NS];
+
+    // Gradients of the sub-block of 4 steps from tb, whose starting state is hb.
+    auto sub_block = [&](int64_t tb, const float (&hb)[NS]) {
+        if (tb >= t1) return;
+        Rows r;
+        load_rows(r, tb, true);
+        float hs[kSub][NS];  // hs[j] = state after step tb + j
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
 #pragma unroll
-            for (int n = 0; n < NS; ++n) hs[j][n] = j == 0 ? ck[k][n] : hs[j - 1][n];
-            if (tk + j < t1) fwd(hs[j], tk + j);
+            for (int n = 0; n < NS; ++n) hs[j][n] = j == 0 ? hb[n] : hs[j - 1][n];
+            if (tb + j < t1) fwd(hs[j], r.dl[j], r.u[j], r.bl[j]);
         }
 #pragma unroll
         for (int j = kSub - 1; j >= 0; --j) {
-            const int64_t t = tk + j;
+            const int64_t t = tb + j;
             if (t >= t1) continue;
-            const int64_t e = elem(t);
-            const float v = ldio<BF16>(f.delta, e) + bias;
+            const int64_t e = (row0 + t) * f.Dn + dd;
+            const float v = r.dl[j] + bias;
             const float dt = f.softplus ? softplus_f(v) : v;
-            const float uv = ldio<BF16>(f.u, e);
-            const float bl = bc_at(f.B, t);
-            const float cl = bc_at(f.C, t);
-            const float dyv = ldio<BF16>(a.dy, e);
+            const float uv = r.u[j];
+            const float bl = r.bl[j];
+            const float cl = r.cl[j];
+            const float dyv = r.dy[j];
             // y_pre from the recomputed state, for the gate's derivative
             float ypre = Dd * uv;
-            static_for([&](auto nc) { ypre = fmaf(row_bcast<decltype(nc)::value>(cl), hs[j][decltype(nc)::value], ypre); },
-                       std::make_integer_sequence<int, NS>{});
+            static_for(
+                [&](auto nc) {
+                    constexpr int n = decltype(nc)::value;
+                    ypre = fmaf(row_bcast<n>(cl), hs[j][n], ypre);
+                },
+                std::make_integer_sequence<int, NS>{});
             float g = dyv;
             if (f.z) {
-                const float zv = ldio<BF16>(f.z, e);
+                const float zv = r.z[j];
                 const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
                 g = dyv * zv * sg;
                 if (dvalid) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
@@ -316,12 +367,12 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             static_for(
                 [&](auto nc) {
                     constexpr int n = decltype(nc)::value;
-                    const float hp = j == 0 ? ck[k][n] : hs[j - 1][n];
+                    const float hp = j == 0 ? hb[n] : hs[j - 1][n];
                     const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
                     const float bn = row_bcast<n>(bl);
                     const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
-                    red[NS + n][lane] = live * g * hs[j][n];    // dC contribution
-                    red[n][lane] = live * l * q.f * uv;         // dB contribution
+                    red[NS + n][lane] = live * g * hs[j][n];  // dC contribution
+                    red[n][lane] = live * l * q.f * uv;       // dB contribution
                     du = fmaf(l * q.f, bn, du);
                     const float dab = l * hp;
                     const float dfac = l * bn * uv;
@@ -336,18 +387,46 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                 st<BF16>(a.du, e, du);
                 st<BF16>(a.ddelta, e, dv);
             }
-            // Sum the 2N contributions of this step over the wave's channels
-            // and store the tile's partial.
+            // Sum the 2N contributions of this step over the wave's channels:
+            // lane l adds half (l & 1) of row l >> 1, the pair is combined
+            // with a DPP add, and the even lane stores the tile's partial.
             __syncthreads();
-            if (lane < 2 * NS) {
+            {
+                const int row = lane >> 1;
+                const int half = lane & 1;
                 float acc = 0.f;
-                for (int i = 0; i < 64; ++i) acc += red[lane][i];
-                const int n = lane < NS ? lane : lane - NS;
-                if (n < N) pbc_row[t * (2 * N) + (lane < NS ? 0 : N) + n] = acc;
+                if (row < 2 * NS) {
+#pragma unroll 8
+                    for (int i = 0; i < 32; ++i) acc += red[row][32 * half + i];
+                }
+                acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf,
+                                                               0xf, true));  // quad_perm 1,0,3,2
+                const int n = row < NS ? row : row - NS;
+                if (half == 0 && row < 2 * NS && n < N)
+                    pbc_row[t * (2 * N) + (row < NS ? 0 : N) + n] = acc;
             }
             __syncthreads();
         }
+    };
+
+    float hm[NS];  // state after 8 steps (the start of sub-block 2)
+#pragma unroll
+    for (int n = 0; n < NS; ++n) hm[n] = h0s[n];
+    advance4(hm, t0);
+    advance4(hm, t0 + 4);
+    // Sub-blocks 3, 2, 1, 0: start from the kept state below them (the
+    // half-way state for 3 and 2, the segment start for 1 and 0) and, for
+    // the odd ones, advance 4 steps.  One loop body keeps one sub-block's
+    // registers live at a time.
+#pragma unroll 1
+    for (int k = 3; k >= 0; --k) {
+        float hb[NS];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) hb[n] = k >= 2 ? hm[n] : h0s[n];
+        if (k & 1) advance4(hb, t0 + 4 * (k - 1));
+        sub_block(t0 + 4 * k, hb);
     }
+
     if (!dvalid) return;
     // per-segment partials of dA, dD, dbias
     float* pp = a.pparam + (((int64_t)b * f.chunks + s) * f.Dn + d) * (N + 2);
@@ -385,9 +464,22 @@ __global__ void __launch_bounds__(256) reduce_params(BwdArgs a, float* dA, float
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (d, k), k < N+2
     const int64_t per = (int64_t)f.Dn * (f.N + 2);
     if (idx >= per) return;
-    float acc = 0.f;
+    // Eight independent partial sums keep eight loads in flight; they are
+    // combined in a fixed order, so the result does not depend on timing.
+    constexpr int P = 8;
+    float acc8[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) acc8[i] = 0.f;
     const int64_t rows = (int64_t)f.batch * f.chunks;
-    for (int64_t r = 0; r < rows; ++r) acc += a.pparam[r * per + idx];
+    int64_t r = 0;
+    for (; r + P <= rows; r += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) acc8[i] += a.pparam[(r + i) * per + idx];
+    }
+    for (; r < rows; ++r) acc8[0] += a.pparam[r * per + idx];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < P; ++i) acc += acc8[i];
     const int k = (int)(idx % (f.N + 2));
     const int64_t d = idx / (f.N + 2);
     if (k < f.N)
