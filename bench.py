@@ -303,6 +303,75 @@ def measure_bwd(ms, reps=5):
                            if k != "calls" and v["launches"]}}
 
 
+def measure_dtproj(ms, rank=16, reps=20):
+    """ms_scan_fwd_dtproj on the 130M-layer workload with a rank-`rank` step
+    projection (dt_low [8, 2048, rank] and W_dt [1536, rank], bf16): ms per
+    call over rotated buffers and the kernels' HIP-event times.  Beside it,
+    the same result computed in two steps -- torch's matmul writing the raw
+    step in bf16, then ms_scan_fwd -- for comparison."""
+    import torch
+    import synth
+    w = synth.workload("m130m")
+    base = synth.scan_inputs(w, device="cuda", seed=0)
+    sets = []
+    for i in range(4):
+        x = dict(base)
+        x.update(synth.dtproj_inputs(w, rank, device="cuda", seed=i))
+        sets.append((x, torch.empty_like(base["u"])))
+    io = ms.MS_BF16 if w.io == "bf16" else ms.MS_F32
+    ws = torch.empty(max(1, ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, io,
+                                               ms.flags(w.softplus))),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        x, y = sets[i % len(sets)]
+        ms.scan_fwd_dtproj(x["u"], x["dt_low"], x["W_dt"], x["A"], x["B"], x["C"], D=x["D"],
+                           z=x["z"], delta_bias=x.get("delta_bias"), softplus=w.softplus, y=y,
+                           workspace=ws, stream=stream)
+
+    delta = torch.empty_like(base["u"])
+
+    def two_step(i):
+        x, y = sets[i % len(sets)]
+        torch.matmul(x["dt_low"], x["W_dt"].t(), out=delta)
+        ms.scan_fwd(x["u"], delta, x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                    delta_bias=x.get("delta_bias"), softplus=w.softplus, y=y, workspace=ws,
+                    stream=stream)
+
+    def timed(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(reps):
+            fn(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    t_fused = timed(fused)
+    t_two = timed(two_step)
+    ms.profile_begin(reps)
+    for i in range(reps):
+        fused(i)
+    torch.cuda.synchronize()
+    ph = ms.profile_end()
+    elems = w.batch * w.L * w.Dn
+    main_ms = ph["main"]["mean_ms"]
+    ops = valu_ops_per_element(w.N, "euler", softplus=w.softplus) * elems
+    return {"workload": f"Mamba-130M-layer scan with the rank-{rank} step projection fused "
+                        f"(ms_scan_fwd_dtproj), Euler, bf16",
+            "ms_per_call": t_fused, "elem_per_s": elems / (t_fused * 1e-3),
+            "two_step_ms_per_call": t_two,
+            "two_step": "torch.matmul (raw step written in bf16) + ms_scan_fwd",
+            "main_valu_frac": ops / (main_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
+            "projection_flops_per_call": 2 * rank * elems,
+            "kernels_ms": {k: v["mean_ms"] for k, v in ph.items()
+                           if k != "calls" and v["launches"]}}
+
+
 # ------------------------------------------------------------ CPU oracle --
 def cpu_baseline(w, min_seconds, disc="euler"):
     """fp64 oracle on this host's cores on the same workload, compute time
@@ -547,6 +616,8 @@ def main():
         out["conv1d"] = measure_conv(ms)
         torch.cuda.empty_cache()
         out["backward"] = measure_bwd(ms)
+        torch.cuda.empty_cache()
+        out["dtproj"] = measure_dtproj(ms)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, disc)

@@ -127,6 +127,36 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ms_scan_fwd with the step size's low-rank projection fused into the scan.
+ * The step size is softplus of a linear map of the input plus a bias (jsqmd
+ * page, section 2.2); in the block that map is low-rank: x_proj yields a
+ * narrow dt slice per timestep and dt_proj lifts it to d_inner (lmnt page,
+ * section 3.2).  Here the raw step is
+ *
+ *   delta[b,t,d] = sum_{r < dt_rank} W_dt[d][r] * dt_low[b,t,r]
+ *
+ * accumulated in fp32 from the io values (exact products for bf16), never
+ * rounded to the io type, and the scan then runs exactly as ms_scan_fwd with
+ * that delta (bias, softplus flag, discretisation and outputs unchanged).
+ *
+ *   dt_low : [batch][seqlen][dt_rank] io dtype    (required)
+ *   W_dt   : [d_inner][dt_rank] io dtype          (required; the layout of a
+ *            linear layer's weight, out x in)
+ *   dt_rank: 1 .. 64
+ *   all other arguments as for ms_scan_fwd (the workspace is
+ *   ms_scan_workspace_bytes(dims, flags) bytes).
+ *
+ * Statuses as for ms_scan_fwd; MS_ERR_SHAPE for dt_rank outside 1..64;
+ * MS_ERR_UNSUPPORTED for d_state other than 8 or 16.  Deterministic.
+ */
+ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt,
+                             int32_t dt_rank, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias,
+                             uint32_t flags, void* y, const float* h0, float* h_last,
+                             const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * One recurrent decode step for a batch of sequences (one timestep of
  * ms_scan_fwd with the state kept by the caller between calls).
  *

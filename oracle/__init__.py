@@ -113,6 +113,27 @@ def scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     return y, h_last
 
 
+def scan_dtproj(u, dt_low, W_dt, A, B, C, D=None, z=None, delta_bias=None, h0=None,
+                softplus: bool = True, zoh: bool = False, nthreads: int = 0,
+                bilinear: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """The scan with its raw step given as a low-rank projection, in fp64.
+
+    The step size is softplus of a linear map of the input plus a bias (jsqmd
+    page, section 2.2); in the block, x_proj yields a narrow dt slice per
+    timestep that dt_proj lifts to d_inner (lmnt page, section 3.2).  So
+        delta[b, t, d] = sum_r W_dt[d, r] * dt_low[b, t, r]
+    (a matrix product, numpy's, in fp64 with no rounding to the io type), and
+    then exactly ``scan`` with that delta.
+
+    dt_low: [batch, L, rank]; W_dt: [Dn, rank] (a linear layer's out x in
+    weight); the rest as for ``scan``.  Returns (y, h_last)."""
+    dt_low, W_dt = _f64(dt_low), _f64(W_dt)
+    assert dt_low.ndim == 3 and W_dt.ndim == 2 and dt_low.shape[2] == W_dt.shape[1]
+    delta = np.matmul(dt_low, W_dt.T)
+    return scan(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias, h0=h0, softplus=softplus,
+                zoh=zoh, nthreads=nthreads, bilinear=bilinear)
+
+
 def step(h, x, delta, A, B, C, D=None, z=None, delta_bias=None,
          softplus: bool = True, zoh: bool = False, bilinear: bool = False
          ) -> Tuple[np.ndarray, np.ndarray]:

@@ -28,7 +28,8 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
 
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
            "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end",
-           "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd")
+           "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd",
+           "ms_scan_fwd_dtproj")
 
 PHASES = ("prep", "summary", "carry", "main", "step", "conv")  # ms_phase order
 
@@ -77,6 +78,9 @@ def load(path: Optional[str] = None):
     lib.ms_scan_fwd.restype = ctypes.c_int
     lib.ms_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
                                 ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
+    lib.ms_scan_fwd_dtproj.restype = ctypes.c_int
+    lib.ms_scan_fwd_dtproj.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
+                                       ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
     lib.ms_state_update.restype = ctypes.c_int
     lib.ms_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, u32, vp,
                                     i32, i32, i32, i32, vp]
@@ -170,6 +174,33 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=Tru
     rc = load().ms_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(delta_bias), fl, _ptr(y), _ptr(h0), _ptr(h_last),
                             ctypes.byref(d), _ptr(workspace), ws_size, _stream(stream))
+    _check(rc)
+    return y
+
+
+def scan_fwd_dtproj(u, dt_low, W_dt, A, B, C, D=None, z=None, delta_bias=None, *,
+                    softplus=True, zoh=False, bilinear=False, y=None, h0=None, h_last=None,
+                    workspace=None, stream=None):
+    """ms_scan_fwd_dtproj on torch device tensors: the scan with its raw step
+    projected from dt_low [batch][L][rank] by W_dt [d_inner][rank] inside the
+    kernel.  Allocates y (and the workspace) when not given.  Returns y."""
+    import torch
+    batch, L, Dn = u.shape
+    N = A.shape[1]
+    rank = int(W_dt.shape[1])
+    io = _io(u)
+    fl = flags(softplus, zoh, bilinear)
+    if y is None:
+        y = torch.empty_like(u)
+    ws_n = workspace_bytes(batch, L, Dn, N, io, fl)
+    if workspace is None and ws_n:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=u.device)
+    ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    d = dims(batch, L, Dn, N, io)
+    rc = load().ms_scan_fwd_dtproj(_ptr(u), _ptr(dt_low), _ptr(W_dt), rank, _ptr(A), _ptr(B),
+                                   _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), fl, _ptr(y),
+                                   _ptr(h0), _ptr(h_last), ctypes.byref(d), _ptr(workspace),
+                                   ws_size, _stream(stream))
     _check(rc)
     return y
 

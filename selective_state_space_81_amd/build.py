@@ -38,12 +38,22 @@ def flags() -> list:
             "-I", os.path.join(ROOT, "include")]
 
 
+def _jobs() -> int:
+    """Parallel compiles: the MAX_JOBS setting if any, else the CPU count,
+    at most 8 (one per source)."""
+    n = os.environ.get("MAX_JOBS")
+    n = int(n) if n and n.isdigit() else (os.cpu_count() or 1)
+    return max(1, min(n, 8, len(SOURCES)))
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libmsscan.so (always rebuilds)."""
-    objs = []
+    """Compile every source (in parallel) and link libmsscan.so (always
+    rebuilds)."""
+    from concurrent.futures import ThreadPoolExecutor
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(bdir, os.path.basename(src) + ".o")
         lang = ["-x", "hip"]  # both files go through the HIP front end
         cmd = [hipcc()] + flags() + lang + ["-c", src, "-o", obj]
@@ -52,7 +62,10 @@ def build(verbose: bool = False) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-        objs.append(obj)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     if verbose:

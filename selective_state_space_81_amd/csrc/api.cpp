@@ -262,6 +262,58 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
     return MS_OK;
 }
 
+ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt,
+                             int32_t dt_rank, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias,
+                             uint32_t flags, void* y, const float* h0, float* h_last,
+                             const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    g_err[0] = '\0';
+    ms_status st = check_dims(dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (!u || !dt_low || !W_dt || !A || !B || !C || !y)
+        return fail(MS_ERR_NULL, "u, dt_low, W_dt, A, B, C and y are required");
+    if (dt_rank < 1 || dt_rank > 64)
+        return fail(MS_ERR_SHAPE, "dt_rank=%d must be in [1, 64]", dt_rank);
+    const void* ptrs[] = {u, dt_low, W_dt, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    const msscan::Plan p = make_plan(*dims, flags);
+    if (p.tile_path != 2 || !msscan::dtproj_variant_exists(dims->d_state))
+        return fail(MS_ERR_UNSUPPORTED, "the fused dt projection needs d_state 8 or 16 (got %d)",
+                    dims->d_state);
+    const size_t need = ws_bytes(p);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    msscan::ScanArgs a{};
+    a.u = u; a.delta = nullptr; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+    a.h0 = h0; a.h_last = h_last; a.y = y;
+    a.dtx = dt_low; a.wdt = W_dt; a.rank = dt_rank;
+    a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
+    a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    a.waves = p.waves;
+    if (p.chunks > 1) {
+        const size_t km1 = (size_t)(p.chunks - 1);
+        float* ws = static_cast<float*>(workspace);
+        a.agg = ws;
+        const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
+        float* after = ws + ((agg_n + 63) / 64) * 64;
+        if (flags & MS_BILINEAR)
+            a.prod = after;
+        else
+            a.sdt = after;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    msscan::prof_call();
+    const hipError_t e =
+        msscan::launch_scan_lanes_dtproj(p, a, dims->io == MS_BF16, disc_of(flags), hs);
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
 ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const float* A,
                           const void* B_t, const void* C_t, const float* D, const void* z_t,
                           const float* delta_bias, uint32_t flags, void* y_t, int32_t batch,

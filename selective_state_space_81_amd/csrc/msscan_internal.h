@@ -41,6 +41,9 @@ struct ScanArgs {
     float* sdt;   // [batch][chunks-1][Dn]: sum of dt over each chunk (exp-based A_bar)
     float* prod;  // [batch][chunks-1][N][Dn]: product of A_bar over each chunk (bilinear)
     float* bcw;   // tile path: [batch][waves][L][2*ns] fp32 B_t then C_t slices
+    const void* dtx;  // fused dt projection: [batch][L][rank] low-rank input, io dtype
+    const void* wdt;  // fused dt projection: [Dn][rank] weight, io dtype
+    int rank;         // fused dt projection: columns of dtx and wdt (0: delta is given)
     int64_t L;
     int64_t chunk_len;
     int batch;
@@ -88,6 +91,10 @@ hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
 bool tile_variant_exists(int ns, int waves);
 hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 bool lane_variant_exists(int n, int disc);
+// Lane path with the low-rank dt projection fused in (a.dtx, a.wdt, a.rank).
+hipError_t launch_scan_lanes_dtproj(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                    hipStream_t s);
+bool dtproj_variant_exists(int n);
 hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_step(const StepArgs& a, bool bf16, int disc, hipStream_t s);
 // Causal depthwise conv1d (+ silu), width 1..8.

@@ -22,6 +22,15 @@
 // the DPP row_newbcast control hands state n to every lane as the first
 // operand of v_mul / v_fmac, so the broadcast costs no extra instruction, no
 // LDS traffic and no SGPRs (bf16 values are widened by one shift first).
+//
+// With DTP the raw step size is not read from HBM but projected from a
+// low-rank input (the step is softplus of a linear map of the input plus a
+// bias, jsqmd page section 2.2; the map is low-rank, a narrow slice of x_proj
+// lifted to d_inner by dt_proj, lmnt page section 3.2):
+//   delta[t][d] = sum_r W[d][r] * x[t][r],   r < rank <= 64.
+// Every 16 timesteps the wave forms the 16 x 64 tile of delta on the matrix
+// cores (one 16x16 output per 16 channels, K = rank in slices of 32) and turns
+// it through LDS so that each lane holds its own channel's 16 values.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,7 +62,74 @@ using namespace dev;
 #define MSSCAN_LANE_WPE 1
 #endif
 
-template <int N, int TB, bool DB, bool BF16, int DISC, bool SP, bool SUMMARY>
+constexpr int kPT = 16;   // timesteps per projected delta tile
+constexpr int kPTS = 20;  // LDS row stride of the turned tile (floats; 16-byte rows)
+constexpr int kMaxRank = 64;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Eight consecutive io values k0 .. k0+7 of one row (row byte offset `row`,
+// row length `rank`), zero at k >= rank and outside the resource.  `vec`:
+// rows are 16-byte multiples, so whole 16-byte loads apply.
+template <bool BF16>
+struct Frag8;
+template <>
+struct Frag8<true> {
+    u4 v;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row, int k0, int rank,
+                                         bool vec) {
+        if (vec) {
+            v = __builtin_amdgcn_raw_buffer_load_b128(r, k0 < rank ? row + 2u * k0 : kOutOfRange,
+                                                      0, 0);
+        } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                e[j] = __builtin_amdgcn_raw_buffer_load_b16(
+                    r, k0 + j < rank ? row + 2u * (k0 + j) : kOutOfRange, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = e[2 * j] | (e[2 * j + 1] << 16);
+            __builtin_amdgcn_sched_barrier(0);  // one fragment's loads in flight at a time
+        }
+    }
+    __device__ __forceinline__ void mma(const Frag8& w, f4& acc) const {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v),
+                                                      __builtin_bit_cast(bf16x8, w.v), acc, 0, 0, 0);
+    }
+};
+template <>
+struct Frag8<false> {
+    float v[8];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row, int k0, int rank,
+                                         bool vec) {
+        if (vec) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = k0 + 4 * h;
+                const u4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, k < rank ? row + 4u * k : kOutOfRange, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * h + j] = __uint_as_float(w[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    r, k0 + j < rank ? row + 4u * (k0 + j) : kOutOfRange, 0, 0));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // Eight K=4 products; lane group q supplies element j as its k, on both
+    // operands alike, so the pairing of x and W along r is exact.
+    __device__ __forceinline__ void mma(const Frag8& w, f4& acc) const {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], w.v[j], acc, 0, 0, 0);
+    }
+};
+
+template <int N, int TB, bool DB, bool BF16, int DISC, bool SP, bool SUMMARY, bool DTP = false>
 __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     static_assert(N == 8 || N == 16 || N == 32 || N == 64, "states per lane");
     constexpr bool ZOH = DISC == kZoh;
@@ -128,7 +204,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     auto load_block = [&](int buf, int64_t tb) {
         const uint32_t nr = block_rows(tb);
         const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
-        const auto rD = make_rsrc(block_base(a.delta, tb), nr * rowb);
+        const auto rD = make_rsrc(DTP ? a.u : block_base(a.delta, tb), DTP ? 0u : nr * rowb);
         const auto rZ = make_rsrc(has_z ? block_base(a.z, tb) : a.u, has_z ? nr * rowb : 0u);
         const auto rB = make_rsrc(bc_base(a.B, tb), nr * kBRow);
         const auto rC = make_rsrc(bc_base(a.C, tb), SUMMARY ? 0u : nr * kBRow);
@@ -136,7 +212,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         for (int tt = 0; tt < TB; ++tt) {
             const uint32_t off = off0 + (uint32_t)tt * rowb;
             ru[buf][tt] = R::load(rU, off);
-            rd[buf][tt] = R::load(rD, off);
+            if constexpr (!DTP) rd[buf][tt] = R::load(rD, off);
             if constexpr (!SUMMARY) rz[buf][tt] = R::load(rZ, off);
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
@@ -150,13 +226,13 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (SUMMARY)
 
     // One timestep: all N states of the lane's channel.
-    auto step = [&](RT raw_u, RT raw_d, RT raw_z, const RT (&raw_b)[KB], const RT (&raw_c)[KB],
+    auto step = [&](RT raw_u, float raw_d, RT raw_z, const RT (&raw_b)[KB], const RT (&raw_c)[KB],
                     float& y_out) {
         float vbt[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) vbt[k] = R::widen(raw_b[k]);
         const float uv = R::widen(raw_u);
-        const float v = R::widen(raw_d) + bias;
+        const float v = raw_d + bias;
         const float dt = SP ? softplus_f(v) : v;  // compile-time: no branch per step
         const float xv = ZOH ? uv : dt * uv;  // B is multiplied by u (ZOH) or dt*u
         float q1 = 0.f, q2 = 0.f;  // ZOH series coefficients for this dt
@@ -204,6 +280,53 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         }
     };
 
+    // DTP: the delta tile of timesteps [tp, tp + kPT), turned so that lane l
+    // finds its channel's values at s_dt[l * kPTS + i].
+    __shared__ __attribute__((aligned(16))) float s_dt[DTP ? 64 * kPTS : 4];
+    auto project_tile = [&](int64_t tp) {
+        if constexpr (DTP) {
+            static_assert(kPT % TB == 0, "blocks inside a projected tile");
+            const uint32_t xrow = (uint32_t)a.rank * R::kSize;
+            const uint32_t nr = (uint32_t)max((int64_t)0, min((int64_t)kPT, a.L - tp));
+            const auto rX = make_rsrc(static_cast<const char*>(a.dtx) + (row0 + tp) * (int64_t)xrow,
+                                      nr * xrow);  // rows past L read 0
+            const auto rW = make_rsrc(a.wdt, (uint32_t)a.Dn * xrow);  // channels past Dn read 0
+            const bool vec = (a.rank % (BF16 ? 8 : 4)) == 0;
+            const int m = lane & 15, q = lane >> 4;
+            const uint32_t d0 = blockIdx.x * 64u;
+            __syncthreads();  // the previous tile has been read
+            f4 acc[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[g] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int kc = 0; kc < kMaxRank / 32; ++kc) {
+                if (kc * 32 < a.rank) {  // uniform
+                    const int k0 = kc * 32 + 8 * q;
+                    Frag8<BF16> xf, wf[4];
+                    // A operand: row m = timestep tp + m; B operand: column m
+                    // of group g = channel d0 + 16 g + m; both take k0 .. k0+7.
+                    xf.load(rX, (uint32_t)m * xrow, k0, a.rank, vec);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        wf[g].load(rW, (d0 + 16u * g + (uint32_t)m) * xrow, k0, a.rank, vec);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) xf.mma(wf[g], acc[g]);
+                }
+            }
+            // acc[g][i] is delta at timestep 4q + i, channel 16g + m.
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f4*>(&s_dt[(16 * g + m) * kPTS + 4 * q]) = acc[g];
+            __syncthreads();
+        }
+    };
+    auto block_delta = [&](int cur, int64_t tb, int tt) -> float {
+        if constexpr (DTP)
+            return s_dt[lane * kPTS + (int)((tb - t0) & (kPT - 1)) + tt];
+        else
+            return R::widen(rd[cur][tt]);
+    };
+
     // A full block of TB timesteps, straight-line code.  The ragged end of
     // the last segment is left to a one-step loop below: a shared body with a
     // per-step guard would make every step a branch target and cost a copy of
@@ -215,11 +338,14 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             load_block(cur ^ 1, tb + TB);  // past the end it reads zeros
         else
             load_block(cur, tb);
+        if constexpr (DTP) {
+            if (((tb - t0) & (kPT - 1)) == 0) project_tile(tb);
+        }
         const auto rY = make_rsrc(block_base(a.y, tb), (uint32_t)TB * rowb);
 #pragma unroll
         for (int tt = 0; tt < TB; ++tt) {
             float y = 0.f;
-            step(ru[cur][tt], rd[cur][tt], rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
+            step(ru[cur][tt], block_delta(cur, tb, tt), rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
             if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
         }
     };
@@ -239,10 +365,16 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     // Ragged end (only the last segment can have one): one timestep at a time.
     for (int64_t t = t0 + (int64_t)nfull * TB; t < t1; ++t) {
         const auto rU = make_rsrc(block_base(a.u, t), rowb);
-        const auto rD = make_rsrc(block_base(a.delta, t), rowb);
+        const auto rD = make_rsrc(DTP ? a.u : block_base(a.delta, t), DTP ? 0u : rowb);
         const auto rZ = make_rsrc(has_z ? block_base(a.z, t) : a.u, has_z ? rowb : 0u);
         const RT xu = R::load(rU, off0);
-        const RT xd = R::load(rD, off0);
+        float xd;
+        if constexpr (DTP) {
+            if (((t - t0) & (kPT - 1)) == 0) project_tile(t);
+            xd = s_dt[lane * kPTS + (int)((t - t0) & (kPT - 1))];
+        } else {
+            xd = R::widen(R::load(rD, off0));
+        }
         const RT xz = SUMMARY ? RT{} : R::load(rZ, off0);
         RT xb[KB], xc[KB];
 #pragma unroll
@@ -275,7 +407,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     }
 }
 
-template <int N, bool BF16, int DISC, bool SP>
+template <int N, bool BF16, int DISC, bool SP, bool DTP = false>
 hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     // 64 states (32 with the extra per-state values of ZOH or the bilinear
     // summary) leave room for one register block only: no prefetch.
@@ -286,7 +418,7 @@ hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, true>),
+            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, true, DTP>),
                                dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
         }
         e = hipGetLastError();
@@ -296,10 +428,21 @@ hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     }
     {
         ProfScope ps(s, kPhaseMain);
-        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, false>),
+        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, false, DTP>),
                            dim3(p.tiles, p.chunks, a.batch), dim3(64), 0, s, a);
     }
     return hipGetLastError();
+}
+
+template <bool BF16, int DISC>
+hipError_t dispatch_dtp(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    switch (p.ns) {
+        case 8: return a.softplus ? launch_lanes<8, BF16, DISC, true, true>(p, a, s)
+                                  : launch_lanes<8, BF16, DISC, false, true>(p, a, s);
+        case 16: return a.softplus ? launch_lanes<16, BF16, DISC, true, true>(p, a, s)
+                                   : launch_lanes<16, BF16, DISC, false, true>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <bool BF16, int DISC, bool SP>
@@ -371,6 +514,20 @@ hipError_t launch_lane_summary_carry(const Plan& p, const ScanArgs& a, bool bf16
         default: return hipErrorInvalidValue;
     }
 }
+
+hipError_t launch_scan_lanes_dtproj(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                    hipStream_t s) {
+    if (a.rank < 1 || a.rank > kMaxRank) return hipErrorInvalidValue;
+    switch (disc) {
+        case kEuler: return bf16 ? dispatch_dtp<true, kEuler>(p, a, s) : dispatch_dtp<false, kEuler>(p, a, s);
+        case kZoh: return bf16 ? dispatch_dtp<true, kZoh>(p, a, s) : dispatch_dtp<false, kZoh>(p, a, s);
+        case kBilinear: return bf16 ? dispatch_dtp<true, kBilinear>(p, a, s)
+                                    : dispatch_dtp<false, kBilinear>(p, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool dtproj_variant_exists(int n) { return n == 8 || n == 16; }
 
 bool lane_variant_exists(int n, int disc) {
     return n == 8 || n == 16 || n == 32 || (n == 64 && disc == kEuler);

@@ -207,6 +207,22 @@ def conv_inputs(w: Workload, width: int = 4, device="cpu", seed: int = 0,
     return out
 
 
+def dtproj_inputs(w: Workload, rank: int, device="cpu", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of the fused low-rank step projection: dt_low [batch, L, rank]
+    ~ N(0,1) and W_dt [Dn, rank] ~ N(0, 0.5^2 / rank), both in the io dtype,
+    so the projected raw step has standard deviation about 0.5 (the spread of
+    the 130M-layer workload's raw step)."""
+    dt = io_dtype(w.io)
+
+    def g(name):
+        return _gen(seed, w.name, "dtproj_" + name, device)
+
+    return {
+        "dt_low": _normal((w.batch, w.L, rank), g("dt_low"), device).to(dt),
+        "W_dt": _normal((w.Dn, rank), g("W_dt"), device, std=0.5 / rank ** 0.5).to(dt),
+    }
+
+
 def algorithmic_bytes(w: Workload) -> int:
     """Bytes the scan must move once: u, delta, z read and y written
     ([batch, L, Dn] each, io dtype), B and C read ([batch, L, N]), A read

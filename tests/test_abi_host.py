@@ -127,3 +127,22 @@ def test_conv_validation_host_only():
     assert call(io=5) == 3  # MS_ERR_DTYPE
     assert call(L=0) == 2 and call(batch=0) == 2
     assert call(u=24) == 5  # MS_ERR_ALIGN
+
+
+def test_dtproj_validation_host_only():
+    lib = ms.load()
+    p = 16
+
+    def call(rank=16, N=16, x=p, w=p, u=p, y=p, flags=1, L=100, ws=None, ws_bytes=0):
+        d = ms.dims(2, L, 64, N, ms.MS_BF16)
+        return lib.ms_scan_fwd_dtproj(u, x, w, rank, p, p, p, None, None, None, flags, y, None,
+                                      None, ctypes.byref(d), ws, ws_bytes, None)
+
+    assert call(rank=0) == 2 and call(rank=65) == 2         # MS_ERR_SHAPE
+    assert b"dt_rank" in lib.ms_last_error()
+    assert call(x=None) == 1 and call(w=None) == 1 and call(u=None) == 1 and call(y=None) == 1
+    assert call(flags=8) == 4                                # unknown flag
+    assert call(x=24) == 5 and call(w=40) == 5               # misaligned
+    assert call(N=32) == 7 and call(N=4) == 7                # only d_state 8 and 16
+    assert b"d_state" in lib.ms_last_error()
+    assert call(L=4096) == 6                                 # several segments, no workspace
