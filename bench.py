@@ -43,7 +43,9 @@ HBM_PEAK_GBPS = 8000.0
 # TFLOP/s fp32 vector figure counts a packed FMA, 2 lanes x 2 flops, per slot).
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 COPY_MIB = 256  # size of the calibration copy (read and written)
-MAIN_KERNEL_RE = r"scan_lane<[^>]*false>|scan_tile<[^>]*false>|scan_chunks<"
+# the pass that writes y: scan_lane with SUMMARY (its 7th argument) false,
+# scan_tile with SUMMARY (its last) false, or the generic scan_chunks
+MAIN_KERNEL_RE = r"scan_lane<(?:[^,>]*, ){6}false[,>]|scan_tile<[^>]*false>|scan_chunks<"
 WORKLOAD_TITLE = {"m130m": "Mamba-130M-layer selective scan (S6) forward",
                   "m3b": "Mamba-3B-layer selective scan (S6) forward",
                   "long": "long-context selective scan (S6) forward, d_state 64"}
