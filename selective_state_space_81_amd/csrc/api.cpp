@@ -79,7 +79,7 @@ int disc_of(uint32_t flags) {
 #define MSSCAN_TILE_WAVES 4
 #endif
 #ifndef MSSCAN_TARGET_WAVES
-#define MSSCAN_TARGET_WAVES 8192
+#define MSSCAN_TARGET_WAVES 16384
 #endif
 #ifndef MSSCAN_LANE_PATH
 #define MSSCAN_LANE_PATH 1
@@ -88,7 +88,7 @@ constexpr int kTileWaves = MSSCAN_TILE_WAVES;
 constexpr int64_t kTargetWaves2 = MSSCAN_TARGET_WAVES;
 constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
 #ifndef MSSCAN_MIN_SEGMENT
-#define MSSCAN_MIN_SEGMENT 128
+#define MSSCAN_MIN_SEGMENT 64  // 6144 waves (6 per SIMD) at the 130M layer
 #endif
 constexpr int64_t kMinSegment = MSSCAN_MIN_SEGMENT;
 
