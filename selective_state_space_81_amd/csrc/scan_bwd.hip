@@ -303,13 +303,23 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     // One forward step of all states (in place).
     auto fwd = [&](float (&h)[NS], float dl, float uv, float bl) {
         const float dt = step_size(dl, bias, f.softplus);
-        static_for(
-            [&](auto nc) {
-                constexpr int n = decltype(nc)::value;
-                const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
-                h[n] = fmaf(q.abar, h[n], q.f * row_bcast<n>(bl) * uv);
-            },
-            std::make_integer_sequence<int, NS>{});
+        if constexpr (DISC == kEuler) {
+            const float xv = dt * uv;  // B_bar u = B * (dt u)
+            static_for(
+                [&](auto nc) {
+                    constexpr int n = decltype(nc)::value;
+                    h[n] = fmaf(hw_exp2(dt * A2[n]), h[n], row_bcast<n>(bl) * xv);
+                },
+                std::make_integer_sequence<int, NS>{});
+        } else {
+            static_for(
+                [&](auto nc) {
+                    constexpr int n = decltype(nc)::value;
+                    const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
+                    h[n] = fmaf(q.abar, h[n], q.f * row_bcast<n>(bl) * uv);
+                },
+                std::make_integer_sequence<int, NS>{});
+        }
     };
     // Advance h over the 4 steps from tb.
     auto advance4 = [&](float (&h)[NS], int64_t tb) {
@@ -364,23 +374,49 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             float du = g * Dd;
             dD = fmaf(g, uv, dD);
             float ddt = 0.f;
-            static_for(
-                [&](auto nc) {
-                    constexpr int n = decltype(nc)::value;
-                    const float hp = j == 0 ? hb[n] : hs[j - 1][n];
-                    const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
-                    const float bn = row_bcast<n>(bl);
-                    const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
-                    red[NS + n][lane] = live * g * hs[j][n];  // dC contribution
-                    red[n][lane] = live * l * q.f * uv;       // dB contribution
-                    du = fmaf(l * q.f, bn, du);
-                    const float dab = l * hp;
-                    const float dfac = l * bn * uv;
-                    ddt = fmaf(dab, q.dab_dt, fmaf(dfac, q.df_dt, ddt));
-                    dA[n] = fmaf(dab, q.dab_da, fmaf(dfac, q.df_da, dA[n]));
-                    mu[n] = q.abar * l;
-                },
-                std::make_integer_sequence<int, NS>{});
+            if constexpr (DISC == kEuler) {
+                // f = dt for every state, so with s = sum_n l_n B_n:
+                //   du   = g D + dt s,   d(dt) = sum_n l_n h_{n,t-1} A_bar_n a_n + u s,
+                //   dA_n += l_n h_{n,t-1} A_bar_n dt,   dB_n = l_n dt u,  dC_n = g h_n.
+                const float lg = live * g;
+                const float fuv = live * dt * uv;
+                float sb = 0.f, dta = 0.f;  // dta: sum_n (l h A_bar) A2_n
+                static_for(
+                    [&](auto nc) {
+                        constexpr int n = decltype(nc)::value;
+                        const float hp = j == 0 ? hb[n] : hs[j - 1][n];
+                        const float abar = hw_exp2(dt * A2[n]);
+                        const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                        red[NS + n][lane] = lg * hs[j][n];  // dC contribution
+                        red[n][lane] = l * fuv;             // dB contribution
+                        sb = fmaf(l, row_bcast<n>(bl), sb);
+                        const float w = l * hp * abar;
+                        dta = fmaf(w, A2[n], dta);
+                        dA[n] = fmaf(w, dt, dA[n]);
+                        mu[n] = abar * l;
+                    },
+                    std::make_integer_sequence<int, NS>{});
+                du = fmaf(dt, sb, du);
+                ddt = fmaf(dta, kLn2, uv * sb);
+            } else {
+                static_for(
+                    [&](auto nc) {
+                        constexpr int n = decltype(nc)::value;
+                        const float hp = j == 0 ? hb[n] : hs[j - 1][n];
+                        const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
+                        const float bn = row_bcast<n>(bl);
+                        const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                        red[NS + n][lane] = live * g * hs[j][n];  // dC contribution
+                        red[n][lane] = live * l * q.f * uv;       // dB contribution
+                        du = fmaf(l * q.f, bn, du);
+                        const float dab = l * hp;
+                        const float dfac = l * bn * uv;
+                        ddt = fmaf(dab, q.dab_dt, fmaf(dfac, q.df_dt, ddt));
+                        dA[n] = fmaf(dab, q.dab_da, fmaf(dfac, q.df_da, dA[n]));
+                        mu[n] = q.abar * l;
+                    },
+                    std::make_integer_sequence<int, NS>{});
+            }
             const float dv = f.softplus ? ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e)) : ddt;
             dbias += dv;
             if (dvalid) {
