@@ -281,7 +281,61 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     const int64_t t1 = min(f.L, t0 + kSeg);
     const int64_t row0 = (int64_t)b * f.L;
 
-    // Raw inputs of the 4 steps from tb (indices clamped into the segment).
+    // bf16 io: the segment's inputs are staged in LDS by one batch of loads
+    // at the start (raw 16-bit values: u, delta, z, dy per lane; B, C per
+    // state), so the walk below never waits on HBM.  fp32 io reads them
+    // from memory per sub-block.
+    constexpr bool STAGE = BF16;
+    __shared__ uint16_t s_io[STAGE ? 4 * kSeg * 64 : 1];  // [u|delta|z|dy][step][lane]
+    __shared__ uint16_t s_bc[STAGE ? 2 * kSeg * 16 : 1];  // [B|C][step][state]
+    if constexpr (STAGE) {
+        using R = Io<true>;
+        const uint32_t rowb = (uint32_t)f.Dn * 2u;
+        const uint32_t nrows = (uint32_t)(t1 - t0);
+        auto seg = [&](const void* p, uint32_t rb) {
+            return make_rsrc(static_cast<const char*>(p) + (row0 + t0) * (int64_t)rb, nrows * rb);
+        };
+        const auto rU = seg(f.u, rowb), rD = seg(f.delta, rowb), rY = seg(a.dy, rowb);
+        const auto rZ = f.z ? seg(f.z, rowb) : make_rsrc(f.u, 0u);
+        const uint32_t off = (uint32_t)dd * 2u;
+        uint16_t vu[kSeg], vd[kSeg], vz[kSeg], vy[kSeg];
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) {  // rows past the segment read 0 (never used)
+            const uint32_t o = off + (uint32_t)j * rowb;
+            vu[j] = R::load(rU, o);
+            vd[j] = R::load(rD, o);
+            vz[j] = R::load(rZ, o);
+            vy[j] = R::load(rY, o);
+        }
+        // B and C: lane l takes state l & 15 of step 4k + (l >> 4); states
+        // past N are zero.
+        const uint32_t bcrow = (uint32_t)N * 2u;
+        const auto rB = seg(f.B, bcrow), rC = seg(f.C, bcrow);
+        const int st = lane & 15, sr = lane >> 4;
+        uint16_t vb[kSeg / 4], vc[kSeg / 4];
+#pragma unroll
+        for (int k = 0; k < kSeg / 4; ++k) {
+            const uint32_t o = st < N ? (uint32_t)(4 * k + sr) * bcrow + (uint32_t)st * 2u : kOutOfRange;
+            vb[k] = R::load(rB, o);
+            vc[k] = R::load(rC, o);
+        }
+#pragma unroll
+        for (int j = 0; j < kSeg; ++j) {
+            s_io[(0 * kSeg + j) * 64 + lane] = vu[j];
+            s_io[(1 * kSeg + j) * 64 + lane] = vd[j];
+            s_io[(2 * kSeg + j) * 64 + lane] = vz[j];
+            s_io[(3 * kSeg + j) * 64 + lane] = vy[j];
+        }
+#pragma unroll
+        for (int k = 0; k < kSeg / 4; ++k) {
+            s_bc[(0 * kSeg + 4 * k + sr) * 16 + st] = vb[k];
+            s_bc[(1 * kSeg + 4 * k + sr) * 16 + st] = vc[k];
+        }
+        __syncthreads();
+    }
+    auto wid = [](uint16_t v) { return __uint_as_float((uint32_t)v << 16); };
+
+    // Inputs of the 4 steps from tb (indices clamped into the segment).
     struct Rows {
         float u[kSub], dl[kSub], z[kSub], dy[kSub], bl[kSub], cl[kSub];
     };
@@ -289,14 +343,26 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
             const int64_t t = min(tb + j, t1 - 1);
-            const int64_t e = (row0 + t) * f.Dn + dd;
-            r.u[j] = ldio<BF16>(f.u, e);
-            r.dl[j] = ldio<BF16>(f.delta, e);
-            r.bl[j] = jn < N ? ldio<BF16>(f.B, (row0 + t) * N + jn) : 0.f;
-            if (full) {
-                r.z[j] = f.z ? ldio<BF16>(f.z, e) : 0.f;
-                r.dy[j] = ldio<BF16>(a.dy, e);
-                r.cl[j] = jn < N ? ldio<BF16>(f.C, (row0 + t) * N + jn) : 0.f;
+            if constexpr (STAGE) {
+                const int jj = (int)(t - t0);
+                r.u[j] = wid(s_io[(0 * kSeg + jj) * 64 + lane]);
+                r.dl[j] = wid(s_io[(1 * kSeg + jj) * 64 + lane]);
+                r.bl[j] = wid(s_bc[(0 * kSeg + jj) * 16 + jn]);
+                if (full) {
+                    r.z[j] = wid(s_io[(2 * kSeg + jj) * 64 + lane]);
+                    r.dy[j] = wid(s_io[(3 * kSeg + jj) * 64 + lane]);
+                    r.cl[j] = wid(s_bc[(1 * kSeg + jj) * 16 + jn]);
+                }
+            } else {
+                const int64_t e = (row0 + t) * f.Dn + dd;
+                r.u[j] = ldio<BF16>(f.u, e);
+                r.dl[j] = ldio<BF16>(f.delta, e);
+                r.bl[j] = jn < N ? ldio<BF16>(f.B, (row0 + t) * N + jn) : 0.f;
+                if (full) {
+                    r.z[j] = f.z ? ldio<BF16>(f.z, e) : 0.f;
+                    r.dy[j] = ldio<BF16>(a.dy, e);
+                    r.cl[j] = jn < N ? ldio<BF16>(f.C, (row0 + t) * N + jn) : 0.f;
+                }
             }
         }
     };
