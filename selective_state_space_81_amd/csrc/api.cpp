@@ -349,7 +349,7 @@ namespace {
 struct BwdPlan {
     msscan::Plan fwd;
     int64_t K, tiles;
-    size_t agg, fdecay, mu, bdecay, pbc, pparam;  // floats of each region
+    size_t agg, fdecay, mu, bdecay, pbc, pparam, pgroup;  // floats of each region
 };
 
 size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
@@ -368,6 +368,7 @@ BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
     q.bdecay = q.fdecay;
     q.pbc = (size_t)q.tiles * B * (size_t)d.seqlen * 2 * N;
     q.pparam = B * (size_t)q.K * D * (N + 2);
+    q.pgroup = (size_t)msscan::kParamGroups * D * (N + 2);
     msscan::Plan& p = q.fwd;
     p.tile_path = 0;
     p.ns = d.d_state <= 4 ? 4 : (d.d_state <= 8 ? 8 : 16);
@@ -380,7 +381,7 @@ BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
 
 size_t bwd_ws_floats(const BwdPlan& q) {
     return pad64(q.agg) + pad64(q.fdecay) + pad64(q.mu) + pad64(q.bdecay) + pad64(q.pbc) +
-           pad64(q.pparam);
+           pad64(q.pparam) + pad64(q.pgroup);
 }
 }  // namespace
 
@@ -436,6 +437,7 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
     L.pbc = ws;
     ws += pad64(q.pbc);
     L.pparam = ws;
+    L.pgroup = ws + pad64(q.pparam);
     L.f = a;
     L.dy = dy; L.dh_last = dh_last; L.du = du; L.ddelta = ddelta; L.dz = z ? dz : nullptr;
     L.dh0 = dh0; L.dA = dA; L.dB = dB; L.dC = dC; L.dD = D ? dD : nullptr; L.dbias = dbias;
@@ -443,17 +445,9 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
     L.disc = disc_of(flags);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     msscan::prof_call();
-    // Forward segment starts: the lane kernels' summary where d_state is 8 or
-    // 16 (all states of a channel in one lane, B/C by DPP), else the generic one.
-    hipError_t e;
-    if (dims->d_state == 8 || dims->d_state == 16) {
-        msscan::Plan lp = q.fwd;
-        lp.ns = dims->d_state;
-        e = msscan::launch_lane_summary_carry(lp, a, L.bf16, L.disc, hs);
-    } else {
-        e = msscan::launch_summary_carry(q.fwd, a, L.bf16, L.disc, hs);
-    }
-    if (e == hipSuccess) e = msscan::launch_scan_bwd(L, hs);
+    // Segment summaries (forward and adjoint), both carries, the per-segment
+    // gradients and the fixed-order sums.
+    const hipError_t e = msscan::launch_scan_bwd(L, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

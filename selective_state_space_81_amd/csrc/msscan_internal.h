@@ -124,19 +124,13 @@ struct BwdLaunch {
     float* prod_b;
     float* pbc;
     float* pparam;
+    float* pgroup;  // [kParamGroups][Dn][N+2]: first-level sums of pparam
     bool bf16;
     int disc;
 };
 int bwd_segment_len();
+constexpr int kParamGroups = 16;  // first-level groups of the parameter sums
 hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s);
-// The forward's segment summaries and carry only (no main pass), generic
-// kernels with p.ns states per lane.
-hipError_t launch_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
-                                hipStream_t s);
-// The same with the lane kernels' summary (p.ns = 8 or 16, one state set per
-// lane; segment length a multiple of 16).
-hipError_t launch_lane_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
-                                     hipStream_t s);
 
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
 // ProfScope records the phase's begin event at construction and its end

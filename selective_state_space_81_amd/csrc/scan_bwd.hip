@@ -16,20 +16,20 @@
 //
 // Parallel plan, mirroring the forward: the sequence is cut into segments of
 // kSeg steps.
-//   1. forward summaries + carry (the forward's own kernels) give every
-//      segment's starting state h;
-//   2. bwd_summary: from mu = 0 at a segment's end, the adjoint run over the
-//      segment gives the mu it passes left (beta) and the segment decay;
-//   3. carry_reverse composes them from the last segment to the first, giving
-//      each segment the mu that enters it from the right;
-//   4. bwd_main: per segment, the forward states are recomputed from its
+//   1. seg_summaries: per segment, from a zero state its forward end state
+//      and, from mu = 0 at its end, the mu the adjoint passes left (beta),
+//      with the segment decay; bf16 inputs are staged in LDS first;
+//   2. carry_propagate composes the forward ones into every segment's
+//      starting state, carry_reverse the adjoint ones (last segment first)
+//      into the mu entering each segment from the right;
+//   3. bwd_main: per segment, the forward states are recomputed from its
 //      starting state (the start and the state half way kept in registers,
 //      each sub-block's states recomputed from them), and the adjoint runs
 //      back over the segment producing every gradient.  The
 //      per-step sums over channels of dB and dC are reduced across the wave
 //      through LDS and stored per 64-channel tile; the sums over time and batch
 //      of dA, dD and dbias are stored per segment;
-//   5. two small passes add those partials in a fixed order.
+//   4. small passes add those partials in a fixed order.
 // No pass waits on another workgroup: the results are deterministic.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,6 +46,9 @@ namespace {
 
 using namespace dev;
 
+#ifndef MSSCAN_SEGSUM_UNROLL
+#define MSSCAN_SEGSUM_UNROLL 4  // steps per unrolled body of the summary walks
+#endif
 constexpr int kSeg = 16;  // timesteps per backward segment
 constexpr int kSub = 4;   // timesteps per recomputed sub-block
 
@@ -100,6 +103,7 @@ struct BwdArgs {
     float* prod_b;       // [batch][K-1][N][Dn] decay products (bilinear)
     float* pbc;          // [tiles][batch][L][2N]: per-tile partial dB | dC
     float* pparam;       // [batch][K][Dn][N+2]: per-segment partial dA | dD | dbias
+    float* pgroup;       // [kParamGroups][Dn][N+2]: first-level sums of pparam
 };
 
 template <bool BF16>
@@ -107,79 +111,210 @@ __device__ __forceinline__ float ldio(const void* p, int64_t i) {
     return ld<BF16>(p, i);
 }
 
-// ---- 2. backward summaries ----------------------------------------------------
+// The raw bf16 inputs of steps [t0, t1) of one 64-channel tile, staged in
+// LDS by one batch of loads: s_io[k][j][lane] for k = u, delta, z, dy and
+// s_bc[k][j][state] for k = B, C (states past N zero; rows past t1 zero).
+__device__ __forceinline__ void stage_segment(const BwdArgs& a, int64_t row0, int64_t t0,
+                                              int64_t t1, int dd, int lane, uint16_t* s_io,
+                                              uint16_t* s_bc) {
+    const ScanArgs& f = a.f;
+    using R = Io<true>;
+    const int N = f.N;
+    const uint32_t rowb = (uint32_t)f.Dn * 2u;
+    const uint32_t nrows = (uint32_t)(t1 - t0);
+    auto seg = [&](const void* p, uint32_t rb) {
+        return make_rsrc(static_cast<const char*>(p) + (row0 + t0) * (int64_t)rb, nrows * rb);
+    };
+    const auto rU = seg(f.u, rowb), rD = seg(f.delta, rowb), rY = seg(a.dy, rowb);
+    const auto rZ = f.z ? seg(f.z, rowb) : make_rsrc(f.u, 0u);
+    const uint32_t off = (uint32_t)dd * 2u;
+    uint16_t vu[kSeg], vd[kSeg], vz[kSeg], vy[kSeg];
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+        const uint32_t o = off + (uint32_t)j * rowb;
+        vu[j] = R::load(rU, o);
+        vd[j] = R::load(rD, o);
+        vz[j] = R::load(rZ, o);
+        vy[j] = R::load(rY, o);
+    }
+    // lane l takes state l & 15 of step 4k + (l >> 4)
+    const uint32_t bcrow = (uint32_t)N * 2u;
+    const auto rB = seg(f.B, bcrow), rC = seg(f.C, bcrow);
+    const int st = lane & 15, sr = lane >> 4;
+    uint16_t vb[kSeg / 4], vc[kSeg / 4];
+#pragma unroll
+    for (int k = 0; k < kSeg / 4; ++k) {
+        const uint32_t o = st < N ? (uint32_t)(4 * k + sr) * bcrow + (uint32_t)st * 2u : kOutOfRange;
+        vb[k] = R::load(rB, o);
+        vc[k] = R::load(rC, o);
+    }
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+        s_io[(0 * kSeg + j) * 64 + lane] = vu[j];
+        s_io[(1 * kSeg + j) * 64 + lane] = vd[j];
+        s_io[(2 * kSeg + j) * 64 + lane] = vz[j];
+        s_io[(3 * kSeg + j) * 64 + lane] = vy[j];
+    }
+#pragma unroll
+    for (int k = 0; k < kSeg / 4; ++k) {
+        s_bc[(0 * kSeg + 4 * k + sr) * 16 + st] = vb[k];
+        s_bc[(1 * kSeg + 4 * k + sr) * 16 + st] = vc[k];
+    }
+    __syncthreads();
+}
+
+// ---- 1+2. segment summaries, forward and adjoint, in one pass -----------------
+// Per 16-step segment s (blockIdx.y) of one 64-channel tile:
+//   s < K-1 : the forward state at its end from a zero start (f.agg slot s)
+//             and its decay (sum of dt, or the product of A_bar per state);
+//   s >= 1  : from mu = 0 at its end, the adjoint run back over it gives the
+//             mu passed left (beta, a.mu slot s-1) and the same decay.
+// The carries then compose them (forward: carry_propagate; adjoint:
+// carry_reverse).
 template <int NS, bool BF16, int DISC>
-__global__ void __launch_bounds__(64) bwd_summary(BwdArgs a) {
+__global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
     const ScanArgs& f = a.f;
     const int lane = threadIdx.x;
     const int b = blockIdx.z;
-    const int s = blockIdx.y + 1;  // segments 1 .. K-1
+    const int s = blockIdx.y;
     const int d = blockIdx.x * 64 + lane;
     const bool dvalid = d < f.Dn;
     const int dd = dvalid ? d : f.Dn - 1;
     const int N = f.N;
-    float A2[NS], mu[NS], P[NS];
+    const int km1 = f.chunks - 1;
+    const bool do_fwd = s < km1, do_bwd = s >= 1;
+    const int jn = lane & (NS - 1);
+    constexpr bool BIL = DISC == kBilinear;
+    float A2[NS], invA[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-        A2[n] = n < N ? f.A[(int64_t)dd * N + n] * kLog2e : 0.f;
-        mu[n] = 0.f;
-        P[n] = 1.f;
+        const float av = n < N ? f.A[(int64_t)dd * N + n] : 0.f;
+        A2[n] = av * kLog2e;
+        invA[n] = av != 0.f ? 1.f / av : 0.f;
     }
     const float bias = f.bias ? f.bias[dd] : 0.f;
     const int64_t t0 = (int64_t)s * kSeg;
     const int64_t t1 = min(f.L, t0 + kSeg);
-    const int jn = lane & (NS - 1);
-    float ssum = 0.f, scomp = 0.f;
-    // All loads of the segment first (indices clamped into it), then the
-    // backward walk.
-    float rdl[kSeg], rdy[kSeg], rz[kSeg], rc[kSeg];
-#pragma unroll
-    for (int j = 0; j < kSeg; ++j) {
+    const int64_t row0 = (int64_t)b * f.L;
+    constexpr bool STAGE = BF16;
+    __shared__ uint16_t s_io[STAGE ? 4 * kSeg * 64 : 1];
+    __shared__ uint16_t s_bc[STAGE ? 2 * kSeg * 16 : 1];
+    if constexpr (STAGE) stage_segment(a, row0, t0, t1, dd, lane, s_io, s_bc);
+    // input k (0 u, 1 delta, 2 z, 3 dy) and B (0) / C (1) of step j
+    auto in = [&](int k, int j) -> float {
         const int64_t t = min(t0 + j, t1 - 1);
-        const int64_t e = ((int64_t)b * f.L + t) * f.Dn + dd;
-        rdl[j] = ldio<BF16>(f.delta, e);
-        rdy[j] = ldio<BF16>(a.dy, e);
-        rz[j] = f.z ? ldio<BF16>(f.z, e) : 0.f;
-        rc[j] = jn < N ? ldio<BF16>(f.C, ((int64_t)b * f.L + t) * N + jn) : 0.f;
-    }
-#pragma unroll
-    for (int j = kSeg - 1; j >= 0; --j) {
-        if (t0 + j >= t1) continue;
-        const float dt = step_size(rdl[j], bias, f.softplus);
-        float g = rdy[j];
-        if (f.z) g *= silu_f(rz[j]);
-        const float cl = rc[j];
-        static_for(
-            [&](auto nc) {
-                constexpr int n = decltype(nc)::value;
-                const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
-                const float t2 = dt * A2[n];
-                float abar;
-                if constexpr (DISC == kBilinear)
-                    abar = fmaf(2.f, bilinear_r(t2), -1.f);
-                else
-                    abar = hw_exp2(t2);
-                mu[n] = abar * l;
-                if constexpr (DISC == kBilinear) P[n] *= abar;
-            },
-            std::make_integer_sequence<int, NS>{});
-        const float yk = dt - scomp;
+        if constexpr (STAGE)
+            return __uint_as_float((uint32_t)s_io[(k * kSeg + (int)(t - t0)) * 64 + lane] << 16);
+        const void* p = k == 0 ? f.u : k == 1 ? f.delta : k == 2 ? f.z : a.dy;
+        return ldio<BF16>(p, (row0 + t) * f.Dn + dd);
+    };
+    auto bc = [&](int k, int j) -> float {
+        const int64_t t = min(t0 + j, t1 - 1);
+        if constexpr (STAGE)
+            return __uint_as_float((uint32_t)s_bc[(k * kSeg + (int)(t - t0)) * 16 + jn] << 16);
+        return jn < N ? ldio<BF16>(k == 0 ? f.B : f.C, (row0 + t) * N + jn) : 0.f;
+    };
+
+    // The compensated sum of dt over the segment (its decay for the
+    // exp-based forms), accumulated in whichever walk runs first.
+    float ssum = 0.f, scomp = 0.f;
+    auto kahan = [&](float v) {
+        const float yk = v - scomp;
         const float tk = ssum + yk;
         scomp = (tk - ssum) - yk;
         ssum = tk;
+    };
+    float P[NS];  // bilinear decay: product of A_bar per state
+#pragma unroll
+    for (int n = 0; n < NS; ++n) P[n] = 1.f;
+    const int64_t base_f = (int64_t)b * km1 + s;      // forward slot
+    const int64_t base_b = (int64_t)b * km1 + s - 1;  // adjoint slot
+
+    // Steps are walked in a loop (not unrolled): the exponentials do not
+    // depend on the state, and unrolled the compiler would form all of them
+    // at once.
+    if (do_fwd) {  // a segment before the last is full
+        float h[NS];
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.f;
+#pragma unroll MSSCAN_SEGSUM_UNROLL
+        for (int j = 0; j < kSeg; ++j) {
+            const float dt = step_size(in(1, j), bias, f.softplus);
+            kahan(dt);
+            const float uv = in(0, j), bl = bc(0, j);
+            if constexpr (DISC == kEuler) {
+                const float xv = dt * uv;
+                static_for(
+                    [&](auto nc) {
+                        constexpr int n = decltype(nc)::value;
+                        h[n] = fmaf(hw_exp2(dt * A2[n]), h[n], row_bcast<n>(bl) * xv);
+                    },
+                    std::make_integer_sequence<int, NS>{});
+            } else {
+                static_for(
+                    [&](auto nc) {
+                        constexpr int n = decltype(nc)::value;
+                        const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
+                        h[n] = fmaf(q.abar, h[n], q.f * row_bcast<n>(bl) * uv);
+                        if constexpr (BIL) P[n] *= q.abar;
+                    },
+                    std::make_integer_sequence<int, NS>{});
+            }
+        }
+        if (dvalid) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n)
+                if (n < N) f.agg[(base_f * N + n) * f.Dn + d] = h[n];
+            if constexpr (BIL) {
+#pragma unroll
+                for (int n = 0; n < NS; ++n)
+                    if (n < N) f.prod[(base_f * N + n) * f.Dn + d] = P[n];
+            } else {
+                f.sdt[base_f * f.Dn + d] = ssum;
+            }
+        }
     }
-    if (!dvalid) return;
-    const int km1 = f.chunks - 1;
-    const int64_t base = (int64_t)b * km1 + (s - 1);
+    if (do_bwd) {
+        float mu[NS];
 #pragma unroll
-    for (int n = 0; n < NS; ++n)
-        if (n < N) a.mu[(base * N + n) * f.Dn + d] = mu[n];
-    if constexpr (DISC == kBilinear) {
+        for (int n = 0; n < NS; ++n) mu[n] = 0.f;
+        const bool first = !do_fwd;  // the last segment: decay not formed yet
+#pragma unroll MSSCAN_SEGSUM_UNROLL
+        for (int j = (int)(t1 - t0) - 1; j >= 0; --j) {
+            const float dt = step_size(in(1, j), bias, f.softplus);
+            if (first) kahan(dt);
+            float g = in(3, j);
+            if (f.z) g *= silu_f(in(2, j));
+            const float cl = bc(1, j);
+            static_for(
+                [&](auto nc) {
+                    constexpr int n = decltype(nc)::value;
+                    const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                    const float t2 = dt * A2[n];
+                    float abar;
+                    if constexpr (BIL)
+                        abar = fmaf(2.f, bilinear_r(t2), -1.f);
+                    else
+                        abar = hw_exp2(t2);
+                    mu[n] = abar * l;
+                    if constexpr (BIL) {
+                        if (first) P[n] *= abar;
+                    }
+                },
+                std::make_integer_sequence<int, NS>{});
+        }
+        if (dvalid) {
 #pragma unroll
-        for (int n = 0; n < NS; ++n)
-            if (n < N) a.prod_b[(base * N + n) * f.Dn + d] = P[n];
-    } else {
-        a.sdt_b[base * f.Dn + d] = ssum;
+            for (int n = 0; n < NS; ++n)
+                if (n < N) a.mu[(base_b * N + n) * f.Dn + d] = mu[n];
+            if constexpr (BIL) {
+#pragma unroll
+                for (int n = 0; n < NS; ++n)
+                    if (n < N) a.prod_b[(base_b * N + n) * f.Dn + d] = P[n];
+            } else {
+                a.sdt_b[base_b * f.Dn + d] = ssum;
+            }
+        }
     }
 }
 
@@ -288,51 +423,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     constexpr bool STAGE = BF16;
     __shared__ uint16_t s_io[STAGE ? 4 * kSeg * 64 : 1];  // [u|delta|z|dy][step][lane]
     __shared__ uint16_t s_bc[STAGE ? 2 * kSeg * 16 : 1];  // [B|C][step][state]
-    if constexpr (STAGE) {
-        using R = Io<true>;
-        const uint32_t rowb = (uint32_t)f.Dn * 2u;
-        const uint32_t nrows = (uint32_t)(t1 - t0);
-        auto seg = [&](const void* p, uint32_t rb) {
-            return make_rsrc(static_cast<const char*>(p) + (row0 + t0) * (int64_t)rb, nrows * rb);
-        };
-        const auto rU = seg(f.u, rowb), rD = seg(f.delta, rowb), rY = seg(a.dy, rowb);
-        const auto rZ = f.z ? seg(f.z, rowb) : make_rsrc(f.u, 0u);
-        const uint32_t off = (uint32_t)dd * 2u;
-        uint16_t vu[kSeg], vd[kSeg], vz[kSeg], vy[kSeg];
-#pragma unroll
-        for (int j = 0; j < kSeg; ++j) {  // rows past the segment read 0 (never used)
-            const uint32_t o = off + (uint32_t)j * rowb;
-            vu[j] = R::load(rU, o);
-            vd[j] = R::load(rD, o);
-            vz[j] = R::load(rZ, o);
-            vy[j] = R::load(rY, o);
-        }
-        // B and C: lane l takes state l & 15 of step 4k + (l >> 4); states
-        // past N are zero.
-        const uint32_t bcrow = (uint32_t)N * 2u;
-        const auto rB = seg(f.B, bcrow), rC = seg(f.C, bcrow);
-        const int st = lane & 15, sr = lane >> 4;
-        uint16_t vb[kSeg / 4], vc[kSeg / 4];
-#pragma unroll
-        for (int k = 0; k < kSeg / 4; ++k) {
-            const uint32_t o = st < N ? (uint32_t)(4 * k + sr) * bcrow + (uint32_t)st * 2u : kOutOfRange;
-            vb[k] = R::load(rB, o);
-            vc[k] = R::load(rC, o);
-        }
-#pragma unroll
-        for (int j = 0; j < kSeg; ++j) {
-            s_io[(0 * kSeg + j) * 64 + lane] = vu[j];
-            s_io[(1 * kSeg + j) * 64 + lane] = vd[j];
-            s_io[(2 * kSeg + j) * 64 + lane] = vz[j];
-            s_io[(3 * kSeg + j) * 64 + lane] = vy[j];
-        }
-#pragma unroll
-        for (int k = 0; k < kSeg / 4; ++k) {
-            s_bc[(0 * kSeg + 4 * k + sr) * 16 + st] = vb[k];
-            s_bc[(1 * kSeg + 4 * k + sr) * 16 + st] = vc[k];
-        }
-        __syncthreads();
-    }
+    if constexpr (STAGE) stage_segment(a, row0, t0, t1, dd, lane, s_io, s_bc);
     auto wid = [](uint16_t v) { return __uint_as_float((uint32_t)v << 16); };
 
     // Inputs of the 4 steps from tb (indices clamped into the segment).
@@ -560,28 +651,36 @@ __global__ void __launch_bounds__(256) reduce_bc(BwdArgs a, float* dB, float* dC
         dC[row * f.N + k - f.N] = acc;
 }
 
-__global__ void __launch_bounds__(256) reduce_params(BwdArgs a, float* dA, float* dD,
-                                                     float* dbias) {
+// Parameter sums over the batch x K rows of pparam, in two fixed-order
+// levels: group g (blockIdx.y) adds the rows r with r mod kParamGroups == g
+// in increasing order, then reduce_param_groups adds the groups in order.
+__global__ void __launch_bounds__(256) reduce_params(BwdArgs a) {
     const ScanArgs& f = a.f;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (d, k), k < N+2
     const int64_t per = (int64_t)f.Dn * (f.N + 2);
     if (idx >= per) return;
-    // Eight independent partial sums keep eight loads in flight; they are
-    // combined in a fixed order, so the result does not depend on timing.
-    constexpr int P = 8;
-    float acc8[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) acc8[i] = 0.f;
+    const int g = blockIdx.y;
     const int64_t rows = (int64_t)f.batch * f.chunks;
-    int64_t r = 0;
-    for (; r + P <= rows; r += P) {
+    // Four partial sums keep four loads in flight, combined in a fixed order.
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+    int64_t r = g;
+    for (; r + 3 * kParamGroups < rows; r += 4 * kParamGroups) {
 #pragma unroll
-        for (int i = 0; i < P; ++i) acc8[i] += a.pparam[(r + i) * per + idx];
+        for (int i = 0; i < 4; ++i) acc4[i] += a.pparam[(r + i * kParamGroups) * per + idx];
     }
-    for (; r < rows; ++r) acc8[0] += a.pparam[r * per + idx];
+    for (; r < rows; r += kParamGroups) acc4[0] += a.pparam[r * per + idx];
+    a.pgroup[(int64_t)g * per + idx] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+}
+
+__global__ void __launch_bounds__(256) reduce_param_groups(BwdArgs a, float* dA, float* dD,
+                                                           float* dbias) {
+    const ScanArgs& f = a.f;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per = (int64_t)f.Dn * (f.N + 2);
+    if (idx >= per) return;
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < P; ++i) acc += acc8[i];
+    for (int g = 0; g < kParamGroups; ++g) acc += a.pgroup[(int64_t)g * per + idx];
     const int k = (int)(idx % (f.N + 2));
     const int64_t d = idx / (f.N + 2);
     if (k < f.N)
@@ -603,10 +702,11 @@ hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* 
     if (K > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((bwd_summary<NS, BF16, DISC>), dim3(tiles, K - 1, f.batch),
+            hipLaunchKernelGGL((seg_summaries<NS, BF16, DISC>), dim3(tiles, K, f.batch),
                                dim3(64), 0, s, a);
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_carry(f, s)) != hipSuccess) return e;  // forward segment starts
         const int64_t total = (int64_t)f.batch * f.N * f.Dn;
         {
             ProfScope ps(s, kPhaseCarry);
@@ -625,8 +725,10 @@ hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* 
                        tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t npar = (int64_t)f.Dn * (f.N + 2);
-    hipLaunchKernelGGL(reduce_params, dim3((unsigned)((npar + 255) / 256)), dim3(256), 0, s, a,
-                       dA, dD, dbias);
+    const unsigned pblocks = (unsigned)((npar + 255) / 256);
+    hipLaunchKernelGGL(reduce_params, dim3(pblocks, kParamGroups), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_param_groups, dim3(pblocks), dim3(256), 0, s, a, dA, dD, dbias);
     return hipGetLastError();
 }
 
@@ -658,6 +760,7 @@ hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s) {
     a.prod_b = L.prod_b;
     a.pbc = L.pbc;
     a.pparam = L.pparam;
+    a.pgroup = L.pgroup;
     switch (L.disc) {
 #define MS_BWD_(DI)                                                                     \
     case DI:                                                                            \

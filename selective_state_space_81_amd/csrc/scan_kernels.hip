@@ -365,43 +365,7 @@ hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, int disc, hi
 }
 
 namespace {
-template <int NS, bool BF16, int DISC>
-hipError_t summary_carry_ns(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    if (p.chunks < 2) return hipSuccess;
-    {
-        ProfScope ps(s, kPhaseSummary);
-        hipLaunchKernelGGL((scan_summary<NS, BF16, DISC>), dim3(p.chunks - 1, p.tiles, a.batch),
-                           dim3(64 * p.waves), 0, s, a);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_carry(a, s);
-}
-
-template <bool BF16, int DISC>
-hipError_t summary_carry_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    switch (p.ns) {
-        case 4: return summary_carry_ns<4, BF16, DISC>(p, a, s);
-        case 8: return summary_carry_ns<8, BF16, DISC>(p, a, s);
-        case 16: return summary_carry_ns<16, BF16, DISC>(p, a, s);
-        case 32: return summary_carry_ns<32, BF16, DISC>(p, a, s);
-        default: return hipErrorInvalidValue;
-    }
-}
 }  // namespace
-
-hipError_t launch_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
-                                hipStream_t s) {
-    switch (disc) {
-        case kEuler: return bf16 ? summary_carry_io<true, kEuler>(p, a, s)
-                                 : summary_carry_io<false, kEuler>(p, a, s);
-        case kZoh: return bf16 ? summary_carry_io<true, kZoh>(p, a, s)
-                               : summary_carry_io<false, kZoh>(p, a, s);
-        case kBilinear: return bf16 ? summary_carry_io<true, kBilinear>(p, a, s)
-                                    : summary_carry_io<false, kBilinear>(p, a, s);
-        default: return hipErrorInvalidValue;
-    }
-}
 
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
     const int64_t total = (int64_t)a.batch * a.N * a.Dn;

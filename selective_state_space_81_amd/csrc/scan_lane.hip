@@ -473,47 +473,7 @@ hipError_t dispatch_disc(const Plan& p, const ScanArgs& a, int disc, hipStream_t
     }
 }
 
-template <int N, bool BF16, int DISC, bool SP>
-hipError_t summary_carry_n(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    constexpr bool kBig = N >= 64 || (N >= 32 && DISC != kEuler);
-    constexpr int TB = kBig ? MSSCAN_LANE_TB64 : MSSCAN_LANE_TB;
-    constexpr bool DB = kBig ? MSSCAN_LANE_DB64 != 0 : MSSCAN_LANE_DB != 0;
-    if (p.chunks < 2) return hipSuccess;
-    {
-        ProfScope ps(s, kPhaseSummary);
-        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, true>),
-                           dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_carry(a, s);
-}
-
-template <bool BF16, int DISC>
-hipError_t summary_carry_sp(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    switch (p.ns) {
-        case 8: return a.softplus ? summary_carry_n<8, BF16, DISC, true>(p, a, s)
-                                  : summary_carry_n<8, BF16, DISC, false>(p, a, s);
-        case 16: return a.softplus ? summary_carry_n<16, BF16, DISC, true>(p, a, s)
-                                   : summary_carry_n<16, BF16, DISC, false>(p, a, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
 }  // namespace
-
-hipError_t launch_lane_summary_carry(const Plan& p, const ScanArgs& a, bool bf16, int disc,
-                                     hipStream_t s) {
-    switch (disc) {
-        case kEuler: return bf16 ? summary_carry_sp<true, kEuler>(p, a, s)
-                                 : summary_carry_sp<false, kEuler>(p, a, s);
-        case kZoh: return bf16 ? summary_carry_sp<true, kZoh>(p, a, s)
-                               : summary_carry_sp<false, kZoh>(p, a, s);
-        case kBilinear: return bf16 ? summary_carry_sp<true, kBilinear>(p, a, s)
-                                    : summary_carry_sp<false, kBilinear>(p, a, s);
-        default: return hipErrorInvalidValue;
-    }
-}
 
 hipError_t launch_scan_lanes_dtproj(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                                     hipStream_t s) {
