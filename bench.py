@@ -107,6 +107,16 @@ def valu_ops_per_element(n_state: int, disc: str, softplus: bool = True) -> int:
     return per_state * n_state + per_elem
 
 
+def bwd_ops_per_element(n_state: int) -> int:
+    """Minimum fp32 VALU operations of the backward's per-segment pass (Euler,
+    softplus, gate, D), counted as in valu_ops_per_element: one forward
+    recompute (5 per state), the adjoint (l, dB and dC terms, du, the A_bar
+    and dt terms of d(dt) and dA, mu: 14 per state), the sums over channels of
+    dB and dC (2 per state), and ~30 per element (softplus and its
+    derivative, the gate and its derivative, D, the stores' conversions)."""
+    return 21 * n_state + 30
+
+
 # ----------------------------------------------------------------- timing --
 def make_sets(w, n_sets):
     import torch
@@ -298,9 +308,13 @@ def measure_bwd(ms, reps=5):
     torch.cuda.synchronize()
     ph = ms.profile_end()
     elems = w.batch * w.L * w.Dn
+    main_ms = ph["main"]["mean_ms"]
     return {"workload": "gradients of the Mamba-130M-layer scan (ms_scan_bwd: du, ddelta, dz, "
                         "dA, dB, dC, dD, dbias, dh0), Euler, bf16",
             "ms_per_call": t_ms, "elem_per_s": elems / (t_ms * 1e-3),
+            "main_ops_per_element": bwd_ops_per_element(w.N),
+            "main_valu_frac": bwd_ops_per_element(w.N) * elems / (main_ms * 1e-3) / 1e12
+                              / VALU_PEAK_TOPS,
             "kernels_ms": {k: v["mean_ms"] for k, v in ph.items()
                            if k != "calls" and v["launches"]}}
 
