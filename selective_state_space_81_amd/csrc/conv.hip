@@ -55,6 +55,12 @@ __device__ __forceinline__ void load_ch(__amdgpu_buffer_rsrc_t r, uint32_t off, 
     }
 }
 
+// u is written once and not read back here: non-temporal stores (cache
+// policy bit nt) measured 27.5 -> 21.7 us on the 130M-layer shape.  The
+// loads stay cached: the W-1 halo rows of a chunk are read again by its
+// neighbour.
+constexpr int kStoreNt = 2;
+
 template <int CH, bool BF16>
 __device__ __forceinline__ void store_ch(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                          const float (&v)[CH]) {
@@ -64,12 +70,12 @@ __device__ __forceinline__ void store_ch(__amdgpu_buffer_rsrc_t r, uint32_t off,
         auto bits = [](float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); };
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
         const u2 w = {bits(v[0]) | (bits(v[1]) << 16), bits(v[2]) | (bits(v[3]) << 16)};
-        __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kStoreNt);
     } else {
         typedef uint32_t u4 __attribute__((ext_vector_type(4)));
         const u4 w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                       __float_as_uint(v[3])};
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, kStoreNt);
     }
 }
 
