@@ -105,9 +105,31 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
         hv[r] = load_state(a.h + e * N + n0);
         bv[r] = ld4<BF16>(a.B, (int64_t)b * N + n0);
         cv[r] = ld4<BF16>(a.C, (int64_t)b * N + n0);
-        xv[r] = ld<BF16>(a.x, e);
-        dr[r] = ld<BF16>(a.delta, e);
-        zv[r] = a.z ? ld<BF16>(a.z, e) : 0.f;
+        if constexpr (G >= 4) {
+            // x, delta and z of the channel: each lane of a quad (its j mod 4)
+            // loads one of them, and the quad shares them below -- one load
+            // instruction where there were three.
+            const int q = j & 3;
+            const void* src = q == 0 ? a.x : (q == 1 ? a.delta : (a.z ? a.z : a.x));
+            xv[r] = ld<BF16>(src, e);
+        } else {
+            xv[r] = ld<BF16>(a.x, e);
+            dr[r] = ld<BF16>(a.delta, e);
+            zv[r] = a.z ? ld<BF16>(a.z, e) : 0.f;
+        }
+    }
+    if constexpr (G >= 4) {
+        auto quad_bcast = [](float v, auto ctrl) {  // DPP quad_perm: lane k of each quad
+            return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v),
+                                                           decltype(ctrl)::value, 0xf, 0xf, true));
+        };
+#pragma unroll
+        for (int r = 0; r < BR; ++r) {
+            const float v = xv[r];
+            dr[r] = quad_bcast(v, std::integral_constant<int, 0x55>{});
+            zv[r] = a.z ? quad_bcast(v, std::integral_constant<int, 0xAA>{}) : 0.f;
+            xv[r] = quad_bcast(v, std::integral_constant<int, 0x00>{});
+        }
     }
     const float A2[4] = {av.x * kLog2e, av.y * kLog2e, av.z * kLog2e, av.w * kLog2e};
     const float an[4] = {av.x, av.y, av.z, av.w};
