@@ -74,7 +74,7 @@ typedef enum {
     MS_ERR_FLAGS = 4,       /* unknown flag bits, or MS_ZOH with MS_BILINEAR    */
     MS_ERR_ALIGN = 5,       /* a base pointer is not 16-byte aligned            */
     MS_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required       */
-    MS_ERR_UNSUPPORTED = 7, /* valid request this build cannot serve            */
+    MS_ERR_UNSUPPORTED = 7, /* valid request this library does not serve        */
     MS_ERR_HIP = 8          /* a HIP runtime call failed (text: ms_last_error)  */
 } ms_status;
 

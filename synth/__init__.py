@@ -10,7 +10,7 @@ tensor name), so adding or dropping a tensor never shifts another's stream.
 The same call on the same device and torch build gives the same bytes.
 
 Workloads (shapes from the pages' model configurations; value ranges from the
-pages' initialisation advice -- see the design notes for the full recipe):
+pages' initialisation advice; each recipe is listed in full below):
 
   tiny      batch 1, L 256, d_inner 64, d_state 16, all fp32.
             A[d,n] = -(n+1); u, B, C, z, D ~ N(0,1);
