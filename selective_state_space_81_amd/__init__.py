@@ -222,6 +222,52 @@ def state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None
     return y_t
 
 
+_scan_fn = None
+
+
+def _scan_function():
+    """torch.autograd.Function over ms_scan_fwd / ms_scan_bwd (built on first
+    use, so that importing this package does not import torch)."""
+    global _scan_fn
+    if _scan_fn is None:
+        import torch
+
+        class ScanFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, softplus, zoh, bilinear):
+                y = scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                             softplus=softplus, zoh=zoh, bilinear=bilinear, h0=h0)
+                ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0)
+                ctx.disc = (softplus, zoh, bilinear)
+                return y
+
+            @staticmethod
+            def backward(ctx, dy):
+                u, delta, A, B, C, D, z, delta_bias, h0 = ctx.saved_tensors
+                softplus, zoh, bilinear = ctx.disc
+                g = scan_bwd(u, delta, A, B, C, dy.contiguous(), D=D, z=z,
+                             delta_bias=delta_bias, softplus=softplus, zoh=zoh,
+                             bilinear=bilinear, h0=h0,
+                             want_dh0=h0 is not None and ctx.needs_input_grad[8])
+                return (g["du"], g["ddelta"], g["dA"], g["dB"].to(B.dtype),
+                        g["dC"].to(C.dtype), g["dD"], g["dz"],
+                        g["dbias"] if delta_bias is not None else None,
+                        g["dh0"] if h0 is not None else None, None, None, None)
+
+        _scan_fn = ScanFn
+    return _scan_fn
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
+                   softplus=True, zoh=False, bilinear=False):
+    """The scan as a differentiable torch operation: the forward is
+    ms_scan_fwd and the backward ms_scan_bwd (gradients of every tensor
+    argument; dB and dC are returned in B's and C's dtype).  Returns y.
+    The backward serves d_state <= 16."""
+    return _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, h0, softplus, zoh,
+                                  bilinear)
+
+
 def profile_begin(max_calls: int) -> None:
     """ms_profile_begin: time the kernels of the next max_calls calls."""
     rc = load().ms_profile_begin(max_calls)
