@@ -124,6 +124,47 @@ def _io(t) -> int:
     raise TypeError(f"io tensors must be float32 or bfloat16, got {t.dtype}")
 
 
+def _chk(t, name: str, dtype, shape) -> None:
+    """The layout include/msscan.h specifies for a tensor argument: a
+    contiguous device tensor of this dtype and shape (None passes: the
+    argument is optional).  Raises before anything reaches the library."""
+    if t is None:
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a device (GPU) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _chk_scan(u, delta, A, B, C, D, z, delta_bias, h0=None, h_last=None, y=None):
+    """Checks of the forward scan's arguments; returns (batch, L, Dn, N, io dtype)."""
+    import torch
+    if not getattr(u, "is_cuda", False) or u.dim() != 3:
+        raise ValueError("u must be a [batch, L, d_inner] device tensor")
+    _io(u)
+    batch, L, Dn = u.shape
+    if A is None or A.dim() != 2:
+        raise ValueError("A must be a [d_inner, d_state] tensor")
+    N = A.shape[1]
+    io, f32 = u.dtype, torch.float32
+    _chk(u, "u", io, (batch, L, Dn))
+    _chk(delta, "delta", io, (batch, L, Dn))
+    _chk(A, "A", f32, (Dn, N))
+    _chk(B, "B", io, (batch, L, N))
+    _chk(C, "C", io, (batch, L, N))
+    _chk(D, "D", f32, (Dn,))
+    _chk(z, "z", io, (batch, L, Dn))
+    _chk(delta_bias, "delta_bias", f32, (Dn,))
+    _chk(h0, "h0", f32, (batch, Dn, N))
+    _chk(h_last, "h_last", f32, (batch, Dn, N))
+    _chk(y, "y", io, (batch, L, Dn))
+    return batch, L, Dn, N, io
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -160,8 +201,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=Tru
     when not given -- that allocation is torch's, outside the library.
     Returns y."""
     import torch
-    batch, L, Dn = u.shape
-    N = A.shape[1]
+    batch, L, Dn, N, _ = _chk_scan(u, delta, A, B, C, D, z, delta_bias, h0, h_last, y)
     io = _io(u)
     fl = flags(softplus, zoh, bilinear)
     if y is None:
@@ -185,9 +225,12 @@ def scan_fwd_dtproj(u, dt_low, W_dt, A, B, C, D=None, z=None, delta_bias=None, *
     projected from dt_low [batch][L][rank] by W_dt [d_inner][rank] inside the
     kernel.  Allocates y (and the workspace) when not given.  Returns y."""
     import torch
-    batch, L, Dn = u.shape
-    N = A.shape[1]
+    batch, L, Dn, N, iod = _chk_scan(u, u, A, B, C, D, z, delta_bias, h0, h_last, y)
+    if W_dt is None or W_dt.dim() != 2:
+        raise ValueError("W_dt must be a [d_inner, rank] tensor")
     rank = int(W_dt.shape[1])
+    _chk(dt_low, "dt_low", iod, (batch, L, rank))
+    _chk(W_dt, "W_dt", iod, (Dn, rank))
     io = _io(u)
     fl = flags(softplus, zoh, bilinear)
     if y is None:
@@ -210,8 +253,23 @@ def state_update(h, x_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None
     """ms_state_update on torch device tensors; h is updated in place.
     Returns y_t."""
     import torch
+    if not getattr(x_t, "is_cuda", False) or x_t.dim() != 2:
+        raise ValueError("x_t must be a [batch, d_inner] device tensor")
+    _io(x_t)
     batch, Dn = x_t.shape
+    if A is None or A.dim() != 2:
+        raise ValueError("A must be a [d_inner, d_state] tensor")
     N = A.shape[1]
+    io, f32 = x_t.dtype, torch.float32
+    _chk(h, "h", f32, (batch, Dn, N))
+    _chk(delta_t, "delta_t", io, (batch, Dn))
+    _chk(A, "A", f32, (Dn, N))
+    _chk(B_t, "B_t", io, (batch, N))
+    _chk(C_t, "C_t", io, (batch, N))
+    _chk(D, "D", f32, (Dn,))
+    _chk(z_t, "z_t", io, (batch, Dn))
+    _chk(delta_bias, "delta_bias", f32, (Dn,))
+    _chk(y_t, "y_t", io, (batch, Dn))
     if y_t is None:
         y_t = torch.empty_like(x_t)
     rc = load().ms_state_update(_ptr(h), _ptr(x_t), _ptr(delta_t), _ptr(A), _ptr(B_t),
@@ -295,8 +353,18 @@ def conv1d_silu(x, weight, bias=None, x_prev=None, *, silu=True, u=None, stream=
     x_prev: [batch, width-1, d_inner] inputs before t = 0 (None = zeros).
     Returns u."""
     import torch
+    if not getattr(x, "is_cuda", False) or x.dim() != 3:
+        raise ValueError("x must be a [batch, L, d_inner] device tensor")
+    _io(x)
     batch, L, Dn = x.shape
+    if weight is None or weight.dim() != 2:
+        raise ValueError("weight must be a [d_inner, width] tensor")
     width = weight.shape[1]
+    _chk(weight, "weight", torch.float32, (Dn, width))
+    _chk(bias, "bias", torch.float32, (Dn,))
+    if width > 1:
+        _chk(x_prev, "x_prev", x.dtype, (batch, width - 1, Dn))
+    _chk(u, "u", x.dtype, (batch, L, Dn))
     if u is None:
         u = torch.empty_like(x)
     rc = load().ms_conv1d_silu(_ptr(x), _ptr(weight), _ptr(bias), _ptr(x_prev), width,
@@ -322,8 +390,9 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, *, softplus
     the workspace when not given).  Returns a dict: du, ddelta, dz (io dtype),
     dA, dB, dC, dD, dbias, dh0 (fp32); dz / dD are None when z / D are."""
     import torch
-    batch, L, Dn = u.shape
-    N = A.shape[1]
+    batch, L, Dn, N, iod = _chk_scan(u, delta, A, B, C, D, z, delta_bias, h0)
+    _chk(dy, "dy", iod, (batch, L, Dn))
+    _chk(dh_last, "dh_last", torch.float32, (batch, Dn, N))
     io = _io(u)
     fl = flags(softplus, zoh, bilinear)
     dev = u.device
