@@ -30,7 +30,7 @@ constexpr int kMaxState = 128;
 constexpr int64_t kMaxLen = 0x7fffffffLL;
 // Target number of waves for one call.  The chip has 256 CUs x 4 SIMDs; a
 // few waves per SIMD hide memory latency.  Below this the sequence is cut.
-constexpr int64_t kTargetWaves = 2048;
+constexpr int64_t kGenericTargetWaves = 2048;  // generic kernels (any d_state)
 constexpr int64_t kMinChunk = 64;  // never cut pieces shorter than this
 
 ms_status check_dims(const ms_dims* d) {
@@ -85,7 +85,7 @@ int disc_of(uint32_t flags) {
 #define MSSCAN_LANE_PATH 1
 #endif
 constexpr int kTileWaves = MSSCAN_TILE_WAVES;
-constexpr int64_t kTargetWaves2 = MSSCAN_TARGET_WAVES;
+constexpr int64_t kTargetWaves = MSSCAN_TARGET_WAVES;
 constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
 #ifndef MSSCAN_MIN_SEGMENT
 #define MSSCAN_MIN_SEGMENT 64  // 6144 waves (6 per SIMD) at the 130M layer
@@ -93,7 +93,7 @@ constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
 constexpr int64_t kMinSegment = MSSCAN_MIN_SEGMENT;
 
 void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) {
-    int64_t k = (kTargetWaves2 + waves_per_segment - 1) / waves_per_segment;
+    int64_t k = (kTargetWaves + waves_per_segment - 1) / waves_per_segment;
     const int64_t kmax = (d.seqlen + kMinSegment - 1) / kMinSegment;
     if (k > kmax) k = kmax;
     if (k < 1) k = 1;
@@ -155,7 +155,7 @@ msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
     p.waves = (N + p.ns - 1) / p.ns;
     p.tiles = (d.d_inner + 63) / 64;
     const int64_t per_chunk = (int64_t)d.batch * p.tiles * p.waves;
-    int64_t k = (kTargetWaves + per_chunk - 1) / per_chunk;
+    int64_t k = (kGenericTargetWaves + per_chunk - 1) / per_chunk;
     const int64_t kmax = (d.seqlen + kMinChunk - 1) / kMinChunk;
     if (k > kmax) k = kmax;
     if (k < 1) k = 1;

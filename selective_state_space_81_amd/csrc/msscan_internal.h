@@ -1,5 +1,6 @@
 // msscan_internal.h -- launch interface between the C ABI (api.cpp) and the
-// HIP kernels (scan_kernels.hip).  Not installed; not part of the public ABI.
+// HIP kernels (scan_lane, scan_tile, scan_kernels, decode, conv, scan_bwd).
+// Not installed; not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>

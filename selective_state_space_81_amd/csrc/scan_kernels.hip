@@ -1,4 +1,6 @@
-// scan_kernels.hip -- HIP kernels of the selective scan (S6) for gfx950.
+// scan_kernels.hip -- generic HIP kernels of the selective scan (S6) for
+// gfx950 (any d_state the fast paths do not take), the carry pass every path
+// shares, and the one-step decode fallback.
 //
 // Method (per batch b, channel d, state n; see include/msscan.h for the full
 // statement and the passages it follows):
@@ -17,7 +19,8 @@
 //     sums their partial readouts through LDS;
 //   * the sequence is cut into pieces ("chunks").  The scan is a composition
 //     of affine maps h -> a*h + b (jsqmd page section 3.4), so a chunk is
-//     summarised by (a, b) = (exp(A * sum dt), state reached from 0).  Pass 1
+//     summarised by (a, b) = (exp(A * sum dt), state reached from 0) -- for
+//     the bilinear form a is the product of the chunk's A_bar.  Pass 1
 //     (scan_summary) computes every chunk's b and sum dt, pass 2
 //     (carry_propagate) composes them in order to get each chunk's starting
 //     state, pass 3 (scan_chunks) rescans every chunk from its true starting
