@@ -50,7 +50,11 @@ using namespace dev;
 #define MSSCAN_SEGSUM_UNROLL 4  // steps per unrolled body of the summary walks
 #endif
 constexpr int kSeg = 16;  // timesteps per backward segment
-constexpr int kSub = 4;   // timesteps per recomputed sub-block
+// Timesteps per recomputed sub-block: 4 with the Euler form; 2 with ZOH and
+// bilinear, whose per-state factors need more registers (half the recomputed
+// states held, at the price of more recompute, instead of spilling).
+template <int DISC>
+constexpr int sub_len() { return DISC == kEuler ? 4 : 2; }
 
 // Per-state derivatives of the discretisation: A_bar, the B*u factor f, and
 // their partial derivatives w.r.t. dt and a (the continuous A), from
@@ -364,13 +368,15 @@ __global__ void __launch_bounds__(256) carry_reverse(BwdArgs a) {
 }
 
 // ---- 4. per-segment gradients ---------------------------------------------------
-// The segment's kSeg = 16 steps are walked back in sub-blocks of kSub = 4.
-// Forward states come from two kept states, the segment start and the state
-// after 8 steps (32 recomputed steps per segment), and each sub-block's
-// inputs are loaded in one batch before its arithmetic.
+// The segment's kSeg = 16 steps are walked back in sub-blocks of kSub steps
+// (sub_len: 4 Euler, 2 ZOH / bilinear).  Forward states come from two kept
+// states, the segment start and the state after 8 steps (32 recomputed steps
+// per segment with 4-step sub-blocks, 48 with 2-step ones), and each
+// sub-block's inputs are read in one batch before its arithmetic.
 template <int NS, bool BF16, int DISC>
 __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
-    static_assert(kSeg == 16 && kSub == 4, "the walk below is written for 4 x 4 steps");
+    constexpr int kSub = sub_len<DISC>();
+    static_assert(kSeg == 16 && (kSub == 4 || kSub == 2), "sub-blocks split the segment");
     const ScanArgs& f = a.f;
     // Per-step dB | dC contributions, [value][lane]; rows padded to 65 floats
     // so that the column sums below read distinct banks.
@@ -479,7 +485,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
         }
     };
     // Advance h over the 4 steps from tb.
-    auto advance4 = [&](float (&h)[NS], int64_t tb) {
+    auto advance_sub = [&](float (&h)[NS], int64_t tb) {
         Rows r;
         load_rows(r, tb, false);
 #pragma unroll
@@ -602,22 +608,25 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
         }
     };
 
-    float hm[NS];  // state after 8 steps (the start of sub-block 2)
+    float hm[NS];  // state after half the segment (8 steps)
 #pragma unroll
     for (int n = 0; n < NS; ++n) hm[n] = h0s[n];
-    advance4(hm, t0);
-    advance4(hm, t0 + 4);
-    // Sub-blocks 3, 2, 1, 0: start from the kept state below them (the
-    // half-way state for 3 and 2, the segment start for 1 and 0) and, for
-    // the odd ones, advance 4 steps.  One loop body keeps one sub-block's
-    // registers live at a time.
+#pragma unroll
+    for (int m = 0; m < kSeg / 2; m += kSub) advance_sub(hm, t0 + m);
+    // Sub-blocks from the last to the first: each starts from the kept state
+    // below it (the half-way state for the upper half, the segment start for
+    // the lower) advanced to its first step.  One loop body keeps one
+    // sub-block's registers live at a time.
+    constexpr int kBlocks = kSeg / kSub;
 #pragma unroll 1
-    for (int k = 3; k >= 0; --k) {
+    for (int k = kBlocks - 1; k >= 0; --k) {
+        const bool upper = k >= kBlocks / 2;
         float hb[NS];
 #pragma unroll
-        for (int n = 0; n < NS; ++n) hb[n] = k >= 2 ? hm[n] : h0s[n];
-        if (k & 1) advance4(hb, t0 + 4 * (k - 1));
-        sub_block(t0 + 4 * k, hb);
+        for (int n = 0; n < NS; ++n) hb[n] = upper ? hm[n] : h0s[n];
+#pragma unroll 1
+        for (int m = upper ? kBlocks / 2 : 0; m < k; ++m) advance_sub(hb, t0 + kSub * m);
+        sub_block(t0 + kSub * k, hb);
     }
 
     if (!dvalid) return;
