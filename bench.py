@@ -309,8 +309,31 @@ def measure_bwd(ms, reps=5):
     ph = ms.profile_end()
     elems = w.batch * w.L * w.Dn
     main_ms = ph["main"]["mean_ms"]
+
+    def other(zoh, bilinear):  # the same call with the other discretisations
+        ws2 = torch.empty(ms.scan_bwd_workspace_bytes(
+            w.batch, w.L, w.Dn, w.N, io, ms.flags(w.softplus, zoh, bilinear)),
+            dtype=torch.uint8, device="cuda")
+
+        def c():
+            ms.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                        delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh,
+                        bilinear=bilinear, workspace=ws2, stream=stream)
+
+        c()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(reps):
+            c()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / reps
+
+    t_zoh, t_bil = other(True, False), other(False, True)
     return {"workload": "gradients of the Mamba-130M-layer scan (ms_scan_bwd: du, ddelta, dz, "
                         "dA, dB, dC, dD, dbias, dh0), Euler, bf16",
+            "zoh_ms_per_call": t_zoh, "bilinear_ms_per_call": t_bil,
             "ms_per_call": t_ms, "elem_per_s": elems / (t_ms * 1e-3),
             "main_ops_per_element": bwd_ops_per_element(w.N),
             "main_valu_frac": bwd_ops_per_element(w.N) * elems / (main_ms * 1e-3) / 1e12
