@@ -223,7 +223,15 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         }
     };
 
-    float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (SUMMARY)
+    // SUMMARY: the sum of dt over the segment, compensated (Kahan) once per
+    // block of TB steps; a block's own steps are added plainly.
+    float s_sum = 0.f, s_comp = 0.f;
+    auto kahan = [&](float v) {
+        const float yk = v - s_comp;
+        const float tk = s_sum + yk;
+        s_comp = (tk - s_sum) - yk;
+        s_sum = tk;
+    };
 
     // One timestep: all N states of the lane's channel.
     auto step = [&](RT raw_u, float raw_d, RT raw_z, const RT (&raw_b)[KB], const RT (&raw_c)[KB],
@@ -266,10 +274,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             },
             std::make_integer_sequence<int, N>{});
         if constexpr (SUMMARY && !PROD) {
-            const float yk = dt - s_comp;
-            const float tk = s_sum + yk;
-            s_comp = (tk - s_sum) - yk;
-            s_sum = tk;
+            y_out = dt;  // summed by the caller
         } else if constexpr (!SUMMARY) {
             float y = DppReadout<RW>::run(R::widen(raw_c[0]), *reinterpret_cast<const float(*)[RW]>(h));
 #pragma unroll
@@ -342,12 +347,15 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             if (((tb - t0) & (kPT - 1)) == 0) project_tile(tb);
         }
         const auto rY = make_rsrc(block_base(a.y, tb), (uint32_t)TB * rowb);
+        float bsum = 0.f;
 #pragma unroll
         for (int tt = 0; tt < TB; ++tt) {
             float y = 0.f;
             step(ru[cur][tt], block_delta(cur, tb, tt), rz[cur][tt], vb[cur][tt], vc[cur][tt], y);
             if constexpr (!SUMMARY) R::store(rY, off0 + (uint32_t)tt * rowb, y);
+            else bsum += y;
         }
+        if constexpr (SUMMARY && !PROD) kahan(bsum);
     };
 
     const int nfull = (int)((t1 - t0) / TB);
@@ -386,6 +394,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         float y = 0.f;
         step(xu, xd, xz, xb, xc, y);
         if constexpr (!SUMMARY) R::store(make_rsrc(block_base(a.y, t), rowb), off0, y);
+        if constexpr (SUMMARY && !PROD) kahan(y);
     }
 
     if (!dvalid) return;
