@@ -24,7 +24,7 @@
  *   * Inference runs the same recurrence one token at a time with one kept
  *     state (lmnt page, sections 2.2 and 5.3): oracle_step.
  *
- * Readings where the pages are silent (each is listed in the design notes):
+ * Readings where the pages are silent:
  *   the state starts at zero unless h0 is given; "Euler" keeps A_bar=exp(dt*A)
  *   and only replaces B_bar by dt*B; the bias goes inside softplus; D*u is added
  *   before the gate; silu(z) = z/(1+exp(-z)); B_t and C_t are shared by all
