@@ -89,11 +89,10 @@ def test_dtproj_deterministic(gpu):
     assert torch.equal(y1, y2)
 
 
-def test_dtproj_130m_layer_sampled(gpu):
+def test_dtproj_130m_layer_full(gpu):
     """The 130M-layer workload (B8 L2048 D1536 N16, bf16) with a rank-16 step
-    projection, in the launch configuration the benchmark times; sampled
-    channels against the oracle over the whole sequence (channels are
-    independent, so the oracle on a channel subset is exact there)."""
+    projection, in the launch configuration the benchmark times; every output
+    against the oracle."""
     w = synth.workload("m130m")
     x = synth.scan_inputs(w, device=DEV, seed=0)
     x.update(synth.dtproj_inputs(w, 16, device=DEV, seed=0))
@@ -101,7 +100,7 @@ def test_dtproj_130m_layer_sampled(gpu):
                             z=x["z"], delta_bias=x.get("delta_bias"))
     torch.cuda.synchronize()
     assert torch.isfinite(y.float()).all()
-    idx = sample_channels(w.Dn, 24, seed=3)
+    idx = np.arange(w.Dn)  # every channel
     ii = torch.as_tensor(idx, device=DEV)
     b = x.get("delta_bias")
     ry, _ = oracle.scan_dtproj(x["u"].index_select(2, ii), x["dt_low"],
