@@ -219,7 +219,7 @@ def test_long_context_sampled(gpu):
     x = synth.scan_inputs(w, device=DEV, seed=0)
     hl = torch.empty(w.batch, w.Dn, w.N, device=DEV)
     y = _run(gpu, x, w.softplus, False, h_last=hl)
-    idx = sample_channels(w.Dn, 6, seed=2)
+    idx = sample_channels(w.Dn, 48, seed=2)
     yr, hr = oracle_on_channels(x, idx, w.softplus, False)
     ii = torch.as_tensor(idx, device=DEV)
     assert_within(y.index_select(2, ii), yr, w.io)
