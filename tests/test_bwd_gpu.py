@@ -128,3 +128,16 @@ def test_bwd_130m_layer(gpu):
     g.manual_seed(77)
     x["dy"] = torch.randn(w.batch, w.L, w.Dn, generator=g, device=DEV).to(x["u"].dtype)
     _compare(gpu, x, "bf16", "euler")
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_zero_A_entries(gpu, disc):
+    """Some A entries exactly 0 (and some tiny): the ZOH factor and its
+    derivative take their series branch there; every gradient must still
+    match the oracle (whose A = 0 case is pinned by finite differences)."""
+    x = _inputs(2, 90, 64, 16, "f32", seed=35)
+    A = x["A"].clone()
+    A[:, 0] = 0.0
+    A[::3, 5] = -1e-6
+    x["A"] = A
+    _compare(gpu, x, "f32", disc)
