@@ -536,7 +536,8 @@ def rocprof_summary(args):
         main = None
         for k in sorted(fetch):
             if k == "neg_kernel" or k not in write or not re.search(
-                    r"scan_|carry_|bc_prep|state_step|step_quads", k):
+                    r"scan_|carry_|bc_prep|state_step|step_quads|conv1d_kernel|bwd_main|"
+                    r"seg_summaries|reduce_", k):
                 continue
             mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
             print(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {mb:.2f} |")
