@@ -490,8 +490,8 @@ def _csv(dirname, suffix):
 
 def _short(name):
     m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|scan_chunks<[^>]*>|scan_summary<[^>]*>|"
-                  r"bc_prepare<[^>]*>|carry_propagate|state_step<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
-                  r"bwd_main<[^>]*>|seg_summaries<[^>]*>|carry_reverse|reduce_bc|"
+                  r"bc_prepare<[^>]*>|carry_chain<[^>]*>|state_step<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
+                  r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|"
                   r"reduce_param_groups|reduce_params|"
                   r"neg_kernel)", name)
     return m.group(1) if m else name[:60]

@@ -88,7 +88,24 @@ struct StepArgs {
 // disc: 0 Euler, 1 zero-order hold, 2 bilinear (kEuler / kZoh / kBilinear).
 hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
-hipError_t launch_carry(const ScanArgs& a, hipStream_t s);
+// Segment carries: val[b][i][n][d] holds segment i's summary (state reached
+// from zero); its decay is exp(A[d][n] * sdt[b][i][d]) or prod[b][i][n][d].
+// Replaced in place by the composed state after slot i, taking the slots in
+// order (reverse: last to first) from init[b][d][n] (null: zero).
+struct CarryArgs {
+    float* val;
+    const float* sdt;
+    const float* prod;
+    const float* A;
+    const float* init;
+    int batch;
+    int km1;
+    int N;
+    int Dn;
+};
+constexpr int kCarryGroup = 8;  // slots whose loads one carry thread issues together
+hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s);
+hipError_t launch_carry(const ScanArgs& a, hipStream_t s);  // the forward summaries of a
 bool tile_variant_exists(int ns, int waves);
 hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 bool lane_variant_exists(int n, int disc);

@@ -19,8 +19,8 @@
 //   1. seg_summaries: per segment, from a zero state its forward end state
 //      and, from mu = 0 at its end, the mu the adjoint passes left (beta),
 //      with the segment decay; bf16 inputs are staged in LDS first;
-//   2. carry_propagate composes the forward ones into every segment's
-//      starting state, carry_reverse the adjoint ones (last segment first)
+//   2. carry_chain<false> composes the forward ones into every segment's
+//      starting state, carry_chain<true> the adjoint ones (last segment first)
 //      into the mu entering each segment from the right;
 //   3. bwd_main: per segment, the forward states are recomputed from its
 //      starting state (the start and the state half way kept in registers,
@@ -115,6 +115,18 @@ __device__ __forceinline__ float ldio(const void* p, int64_t i) {
     return ld<BF16>(p, i);
 }
 
+// The softplus and z-gate options are wave-uniform flags.  Branching on them
+// per step split the step loops into many small blocks; instead both forms
+// are computed and one is kept by a mask (all ones: `on`, zero: `off`), so a
+// step stays one straight-line block.
+__device__ __forceinline__ float pick(uint32_t mask, float on, float off) {
+    return __uint_as_float((__float_as_uint(on) & mask) | (__float_as_uint(off) & ~mask));
+}
+__device__ __forceinline__ float step_pick(float draw, float bias, uint32_t spm) {
+    const float v = draw + bias;
+    return pick(spm, softplus_f(v), v);
+}
+
 // The raw bf16 inputs of steps [t0, t1) of one 64-channel tile, staged in
 // LDS by one batch of loads: s_io[k][j][lane] for k = u, delta, z, dy and
 // s_bc[k][j][state] for k = B, C (states past N zero; rows past t1 zero).
@@ -173,8 +185,8 @@ __device__ __forceinline__ void stage_segment(const BwdArgs& a, int64_t row0, in
 //             and its decay (sum of dt, or the product of A_bar per state);
 //   s >= 1  : from mu = 0 at its end, the adjoint run back over it gives the
 //             mu passed left (beta, a.mu slot s-1) and the same decay.
-// The carries then compose them (forward: carry_propagate; adjoint:
-// carry_reverse).
+// The carries then compose them (forward: carry_chain<false>; adjoint:
+// carry_chain<true>).
 template <int NS, bool BF16, int DISC>
 __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
     const ScanArgs& f = a.f;
@@ -189,6 +201,8 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
     const bool do_fwd = s < km1, do_bwd = s >= 1;
     const int jn = lane & (NS - 1);
     constexpr bool BIL = DISC == kBilinear;
+    const uint32_t spm = f.softplus ? ~0u : 0u;
+    const uint32_t zm = f.z ? ~0u : 0u;
     float A2[NS], invA[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
@@ -209,6 +223,7 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
         const int64_t t = min(t0 + j, t1 - 1);
         if constexpr (STAGE)
             return __uint_as_float((uint32_t)s_io[(k * kSeg + (int)(t - t0)) * 64 + lane] << 16);
+        if (k == 2 && !f.z) return 0.f;
         const void* p = k == 0 ? f.u : k == 1 ? f.delta : k == 2 ? f.z : a.dy;
         return ldio<BF16>(p, (row0 + t) * f.Dn + dd);
     };
@@ -243,7 +258,7 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
         for (int n = 0; n < NS; ++n) h[n] = 0.f;
 #pragma unroll MSSCAN_SEGSUM_UNROLL
         for (int j = 0; j < kSeg; ++j) {
-            const float dt = step_size(in(1, j), bias, f.softplus);
+            const float dt = step_pick(in(1, j), bias, spm);
             kahan(dt);
             const float uv = in(0, j), bl = bc(0, j);
             if constexpr (DISC == kEuler) {
@@ -285,10 +300,10 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
         const bool first = !do_fwd;  // the last segment: decay not formed yet
 #pragma unroll MSSCAN_SEGSUM_UNROLL
         for (int j = (int)(t1 - t0) - 1; j >= 0; --j) {
-            const float dt = step_size(in(1, j), bias, f.softplus);
+            const float dt = step_pick(in(1, j), bias, spm);
             if (first) kahan(dt);
-            float g = in(3, j);
-            if (f.z) g *= silu_f(in(2, j));
+            const float dyv = in(3, j);
+            const float g = pick(zm, dyv * silu_f(in(2, j)), dyv);
             const float cl = bc(1, j);
             static_for(
                 [&](auto nc) {
@@ -323,49 +338,9 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
 }
 
 // ---- 3. reverse carry ---------------------------------------------------------
-// One thread per (b, n, d).  Slot s-1 of mu holds beta_s (from segment s,
-// s = 1..K-1); it is replaced by the mu entering segment s-1 from the right:
+// Slot s-1 of mu holds beta_s (from segment s, s = 1..K-1); carry_chain<true>
+// replaces it by the mu entering segment s-1 from the right:
 //   mu_in(K-1) = dh_last (or 0),  mu_in(s-1) = decay_s mu_in(s) + beta_s.
-__global__ void __launch_bounds__(256) carry_reverse(BwdArgs a) {
-    const ScanArgs& f = a.f;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)f.batch * f.N * f.Dn;
-    if (idx >= total) return;
-    const int d = (int)(idx % f.Dn);
-    const int n = (int)((idx / f.Dn) % f.N);
-    const int b = (int)(idx / ((int64_t)f.Dn * f.N));
-    const float A2 = f.A[(int64_t)d * f.N + n] * kLog2e;
-    float m = a.dh_last ? a.dh_last[((int64_t)b * f.Dn + d) * f.N + n] : 0.f;
-    const int km1 = f.chunks - 1;
-    const bool prod = a.prod_b != nullptr;
-    // Loads of a group of slots are issued before its chain of updates, so
-    // the chain waits on memory once per group.
-    constexpr int G = 8;
-    for (int s1 = km1; s1 >= 1; s1 -= G) {  // slots s-1 for s = s1, s1-1, ...
-        float dv[G], bv[G];
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            dv[j] = 0.f;
-            bv[j] = 0.f;
-            const int s = s1 - j;
-            if (s >= 1) {
-                const int64_t base = (int64_t)b * km1 + (s - 1);
-                dv[j] = prod ? a.prod_b[(base * f.N + n) * f.Dn + d] : a.sdt_b[base * f.Dn + d];
-                bv[j] = a.mu[(base * f.N + n) * f.Dn + d];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int s = s1 - j;
-            if (s >= 1) {
-                const int64_t base = (int64_t)b * km1 + (s - 1);
-                const float decay = prod ? dv[j] : hw_exp2(A2 * dv[j]);
-                m = fmaf(decay, m, bv[j]);
-                a.mu[(base * f.N + n) * f.Dn + d] = m;
-            }
-        }
-    }
-}
 
 // ---- 4. per-segment gradients ---------------------------------------------------
 // The segment's kSeg = 16 steps are walked back in sub-blocks of kSub steps
@@ -392,6 +367,8 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     const int km1 = f.chunks - 1;
     const int jn = lane & (NS - 1);
     const float live = dvalid ? 1.f : 0.f;  // tail lanes repeat a channel: count it once
+    const uint32_t spm = f.softplus ? ~0u : 0u;
+    const uint32_t zm = f.z ? ~0u : 0u;
 
     float A2[NS], invA[NS], mu[NS], h0s[NS], dA[NS];
 #pragma unroll
@@ -465,7 +442,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     };
     // One forward step of all states (in place).
     auto fwd = [&](float (&h)[NS], float dl, float uv, float bl) {
-        const float dt = step_size(dl, bias, f.softplus);
+        const float dt = step_pick(dl, bias, spm);
         if constexpr (DISC == kEuler) {
             const float xv = dt * uv;  // B_bar u = B * (dt u)
             static_for(
@@ -514,7 +491,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             if (t >= t1) continue;
             const int64_t e = (row0 + t) * f.Dn + dd;
             const float v = r.dl[j] + bias;
-            const float dt = f.softplus ? softplus_f(v) : v;
+            const float dt = pick(spm, softplus_f(v), v);
             const float uv = r.u[j];
             const float bl = r.bl[j];
             const float cl = r.cl[j];
@@ -527,13 +504,10 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                     ypre = fmaf(row_bcast<n>(cl), hs[j][n], ypre);
                 },
                 std::make_integer_sequence<int, NS>{});
-            float g = dyv;
-            if (f.z) {
-                const float zv = r.z[j];
-                const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
-                g = dyv * zv * sg;
-                if (dvalid) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
-            }
+            const float zv = r.z[j];  // 0 when there is no gate
+            const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
+            const float g = pick(zm, dyv * zv * sg, dyv);
+            if (dvalid && f.z) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
             float du = g * Dd;
             dD = fmaf(g, uv, dD);
             float ddt = 0.f;
@@ -627,7 +601,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                     std::make_integer_sequence<int, NS>{});
                 du += sf;
             }
-            const float dv = f.softplus ? ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e)) : ddt;
+            const float dv = pick(spm, ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e)), ddt);
             dbias += dv;
             if (dvalid) {
                 st<BF16>(a.du, e, du);
@@ -697,8 +671,17 @@ __global__ void __launch_bounds__(256) reduce_bc(BwdArgs a, float* dB, float* dC
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, t, k), k < 2N
     const int64_t per = (int64_t)f.batch * f.L * 2 * f.N;
     if (idx >= per) return;
+    // Tiles are added in order; each group of 8 loads is issued before its adds.
     float acc = 0.f;
-    for (int tl = 0; tl < tiles; ++tl) acc += a.pbc[(int64_t)tl * per + idx];
+    int tl = 0;
+    for (; tl + 8 <= tiles; tl += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = a.pbc[(int64_t)(tl + i) * per + idx];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += v[i];
+    }
+    for (; tl < tiles; ++tl) acc += a.pbc[(int64_t)tl * per + idx];
     const int k = (int)(idx % (2 * f.N));
     const int64_t row = idx / (2 * f.N);
     if (k < f.N)
@@ -717,15 +700,19 @@ __global__ void __launch_bounds__(256) reduce_params(BwdArgs a) {
     if (idx >= per) return;
     const int g = blockIdx.y;
     const int64_t rows = (int64_t)f.batch * f.chunks;
-    // Four partial sums keep four loads in flight, combined in a fixed order.
-    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+    // The group's rows are added in increasing order; each batch of 8 loads is
+    // issued before its adds.
+    float acc = 0.f;
     int64_t r = g;
-    for (; r + 3 * kParamGroups < rows; r += 4 * kParamGroups) {
+    for (; r + 7 * kParamGroups < rows; r += 8 * kParamGroups) {
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc4[i] += a.pparam[(r + i * kParamGroups) * per + idx];
+        for (int i = 0; i < 8; ++i) v[i] = a.pparam[(r + i * kParamGroups) * per + idx];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += v[i];
     }
-    for (; r < rows; r += kParamGroups) acc4[0] += a.pparam[r * per + idx];
-    a.pgroup[(int64_t)g * per + idx] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+    for (; r < rows; r += kParamGroups) acc += a.pparam[r * per + idx];
+    a.pgroup[(int64_t)g * per + idx] = acc;
 }
 
 __global__ void __launch_bounds__(256) reduce_param_groups(BwdArgs a, float* dA, float* dD,
@@ -763,13 +750,17 @@ hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* 
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_carry(f, s)) != hipSuccess) return e;  // forward segment starts
-        const int64_t total = (int64_t)f.batch * f.N * f.Dn;
-        {
-            ProfScope ps(s, kPhaseCarry);
-            hipLaunchKernelGGL(carry_reverse, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                               s, a);
-        }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        CarryArgs c{};
+        c.val = a.mu;
+        c.sdt = a.sdt_b;
+        c.prod = a.prod_b;
+        c.A = f.A;
+        c.init = a.dh_last;
+        c.batch = f.batch;
+        c.km1 = K - 1;
+        c.N = f.N;
+        c.Dn = f.Dn;
+        if ((e = launch_carry(c, true, s)) != hipSuccess) return e;  // adjoint mu entering
     }
     {
         ProfScope ps(s, kPhaseMain);

@@ -22,7 +22,7 @@
 //     summarised by (a, b) = (exp(A * sum dt), state reached from 0) -- for
 //     the bilinear form a is the product of the chunk's A_bar.  Pass 1
 //     (scan_summary) computes every chunk's b and sum dt, pass 2
-//     (carry_propagate) composes them in order to get each chunk's starting
+//     (carry_chain) composes them in order to get each chunk's starting
 //     state, pass 3 (scan_chunks) rescans every chunk from its true starting
 //     state and writes y.  No pass waits on another workgroup, so there is no
 //     spin-wait and the association order -- hence every output bit -- is
@@ -33,6 +33,7 @@
 // instructions with log2(e) folded into A once per (d, n).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
 
 #include "device_common.h"
 #include "msscan_internal.h"
@@ -150,44 +151,52 @@ __global__ void __launch_bounds__(256) scan_summary(ScanArgs a) {
 }
 
 // ---- pass 2: compose chunk summaries in order --------------------------------
-// One thread per (b, n, d).  Replaces each summary slot c by the state at the
-// start of chunk c+1: h_{c+1} = a_c * h_c + b_c, h_0 = h0 or 0, where the
-// decay a_c is exp(A * sum dt_c) or, when the summaries hold products of
-// A_bar (bilinear), that product.
-__global__ void __launch_bounds__(256) carry_propagate(ScanArgs a) {
+// One thread per (b, n, d).  Slot i of the summaries holds chunk i's map
+// h -> a_i*h + b_i; it is replaced by the state at the start of chunk i+1:
+// h_{i+1} = a_i*h_i + b_i, h_0 = the initial state or 0.  The decay a_i is
+// exp(A * sum dt_i) or, when the summaries hold products of A_bar (bilinear),
+// that product.  REV takes the slots last to first, which is the adjoint's
+// carry in the backward.
+//
+// The kernel streams the summaries once in and once out (at the 130M layer's
+// backward about 200 MB per call) and is bound by HBM bandwidth.  Loads of a
+// group of slots are issued before its updates, so the chain waits on memory
+// once per group, not once per slot.  A two-level form (waves of one
+// workgroup folding runs of slots, then one barrier) and 16-byte accesses
+// over four channels per thread both measured slower.
+template <bool REV>
+__global__ void __launch_bounds__(256) carry_chain(CarryArgs c) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)a.batch * a.N * a.Dn;
+    const int64_t total = (int64_t)c.batch * c.N * c.Dn;
     if (idx >= total) return;
-    const int d = (int)(idx % a.Dn);
-    const int n = (int)((idx / a.Dn) % a.N);
-    const int b = (int)(idx / ((int64_t)a.Dn * a.N));
-    const float A2 = a.A[(int64_t)d * a.N + n] * kLog2e;
-    float h = a.h0 ? a.h0[((int64_t)b * a.Dn + d) * a.N + n] : 0.f;
-    const int km1 = a.chunks - 1;
-    // Loads of a group are issued before its stores so that the chain waits
-    // on memory once per group, not once per chunk.
-    // (Raw values are loaded; the decays are formed in the chain loop.)
-    const bool prod = a.prod != nullptr;
-    constexpr int G = 8;
-    for (int c0 = 0; c0 < km1; c0 += G) {
-        float s[G], g[G];
+    const int d = (int)(idx % c.Dn);
+    const int n = (int)((idx / c.Dn) % c.N);
+    const int b = (int)(idx / ((int64_t)c.Dn * c.N));
+    const bool prod = c.prod != nullptr;
+    const float A2 = c.A[(int64_t)d * c.N + n] * kLog2e;
+    float h = c.init ? c.init[((int64_t)b * c.Dn + d) * c.N + n] : 0.f;
+    const int km1 = c.km1;
+    for (int i0 = 0; i0 < km1; i0 += kCarryGroup) {
+        float dv[kCarryGroup], gv[kCarryGroup];
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            s[j] = 0.f;
-            g[j] = 0.f;
-            if (c0 + j < km1) {
-                const int64_t base = (int64_t)b * km1 + c0 + j;
-                s[j] = prod ? a.prod[(base * a.N + n) * a.Dn + d] : a.sdt[base * a.Dn + d];
-                g[j] = a.agg[(base * a.N + n) * a.Dn + d];
+        for (int j = 0; j < kCarryGroup; ++j) {
+            dv[j] = 0.f;
+            gv[j] = 0.f;
+            const int i = i0 + j;
+            if (i < km1) {
+                const int64_t base = (int64_t)b * km1 + (REV ? km1 - 1 - i : i);
+                dv[j] = prod ? c.prod[(base * c.N + n) * c.Dn + d] : c.sdt[base * c.Dn + d];
+                gv[j] = c.val[(base * c.N + n) * c.Dn + d];
             }
         }
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            if (c0 + j < km1) {
-                const int64_t base = (int64_t)b * km1 + c0 + j;
-                const float decay = prod ? s[j] : hw_exp2(A2 * s[j]);
-                h = fmaf(decay, h, g[j]);
-                a.agg[(base * a.N + n) * a.Dn + d] = h;
+        for (int j = 0; j < kCarryGroup; ++j) {
+            const int i = i0 + j;
+            if (i < km1) {
+                const int64_t base = (int64_t)b * km1 + (REV ? km1 - 1 - i : i);
+                const float decay = prod ? dv[j] : hw_exp2(A2 * dv[j]);
+                h = fmaf(decay, h, gv[j]);
+                c.val[(base * c.N + n) * c.Dn + d] = h;
             }
         }
     }
@@ -367,14 +376,30 @@ hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, int disc, hi
     return bf16 ? launch_disc<true>(p, a, disc, s) : launch_disc<false>(p, a, disc, s);
 }
 
-namespace {
-}  // namespace
+hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s) {
+    if (c.km1 <= 0) return hipSuccess;
+    const int64_t total = (int64_t)c.batch * c.N * c.Dn;
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    ProfScope ps(s, kPhaseCarry);
+    if (reverse)
+        hipLaunchKernelGGL(carry_chain<true>, grid, block, 0, s, c);
+    else
+        hipLaunchKernelGGL(carry_chain<false>, grid, block, 0, s, c);
+    return hipGetLastError();
+}
 
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
-    const int64_t total = (int64_t)a.batch * a.N * a.Dn;
-    ProfScope ps(s, kPhaseCarry);
-    hipLaunchKernelGGL(carry_propagate, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    CarryArgs c{};
+    c.val = a.agg;
+    c.sdt = a.sdt;
+    c.prod = a.prod;
+    c.A = a.A;
+    c.init = a.h0;
+    c.batch = a.batch;
+    c.km1 = a.chunks - 1;
+    c.N = a.N;
+    c.Dn = a.Dn;
+    return launch_carry(c, false, s);
 }
 
 hipError_t launch_step(const StepArgs& a, bool bf16, int disc, hipStream_t s) {
