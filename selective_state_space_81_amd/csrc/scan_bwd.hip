@@ -249,9 +249,9 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
     const int64_t base_f = (int64_t)b * km1 + s;      // forward slot
     const int64_t base_b = (int64_t)b * km1 + s - 1;  // adjoint slot
 
-    // Steps are walked in a loop (not unrolled): the exponentials do not
-    // depend on the state, and unrolled the compiler would form all of them
-    // at once.
+    // Steps are walked in a loop unrolled MSSCAN_SEGSUM_UNROLL ways, not
+    // fully: the exponentials do not depend on the state, and fully unrolled
+    // the compiler would form all of them at once and run out of registers.
     if (do_fwd) {  // a segment before the last is full
         float h[NS];
 #pragma unroll
@@ -297,11 +297,12 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
         float mu[NS];
 #pragma unroll
         for (int n = 0; n < NS; ++n) mu[n] = 0.f;
-        const bool first = !do_fwd;  // the last segment: decay not formed yet
-#pragma unroll MSSCAN_SEGSUM_UNROLL
-        for (int j = (int)(t1 - t0) - 1; j >= 0; --j) {
+        // One adjoint step; FIRST: this walk also forms the segment decay
+        // (the last segment, which has no forward walk and may be partial).
+        auto adj_step = [&](int j, auto first_c) {
+            constexpr bool FIRST = decltype(first_c)::value;
             const float dt = step_pick(in(1, j), bias, spm);
-            if (first) kahan(dt);
+            if constexpr (FIRST) kahan(dt);
             const float dyv = in(3, j);
             const float g = pick(zm, dyv * silu_f(in(2, j)), dyv);
             const float cl = bc(1, j);
@@ -316,11 +317,15 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
                     else
                         abar = hw_exp2(t2);
                     mu[n] = abar * l;
-                    if constexpr (BIL) {
-                        if (first) P[n] *= abar;
-                    }
+                    if constexpr (BIL && FIRST) P[n] *= abar;
                 },
                 std::make_integer_sequence<int, NS>{});
+        };
+        if (!do_fwd) {
+            for (int j = (int)(t1 - t0) - 1; j >= 0; --j) adj_step(j, std::true_type{});
+        } else {  // a segment before the last is full: a fixed trip count
+#pragma unroll MSSCAN_SEGSUM_UNROLL
+            for (int j = kSeg - 1; j >= 0; --j) adj_step(j, std::false_type{});
         }
         if (dvalid) {
 #pragma unroll
@@ -369,6 +374,14 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     const float live = dvalid ? 1.f : 0.f;  // tail lanes repeat a channel: count it once
     const uint32_t spm = f.softplus ? ~0u : 0u;
     const uint32_t zm = f.z ? ~0u : 0u;
+    // The mask form pays off with Euler.  ZOH and bilinear keep branches: their
+    // steps hold more values, and straight-line steps spilled registers there
+    // (measured 10% slower).
+    constexpr bool kMasks = DISC == kEuler;
+    auto dt_of = [&](float v) {
+        if constexpr (kMasks) return pick(spm, softplus_f(v), v);
+        return f.softplus ? softplus_f(v) : v;
+    };
 
     float A2[NS], invA[NS], mu[NS], h0s[NS], dA[NS];
 #pragma unroll
@@ -442,7 +455,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     };
     // One forward step of all states (in place).
     auto fwd = [&](float (&h)[NS], float dl, float uv, float bl) {
-        const float dt = step_pick(dl, bias, spm);
+        const float dt = dt_of(dl + bias);
         if constexpr (DISC == kEuler) {
             const float xv = dt * uv;  // B_bar u = B * (dt u)
             static_for(
@@ -491,7 +504,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             if (t >= t1) continue;
             const int64_t e = (row0 + t) * f.Dn + dd;
             const float v = r.dl[j] + bias;
-            const float dt = pick(spm, softplus_f(v), v);
+            const float dt = dt_of(v);
             const float uv = r.u[j];
             const float bl = r.bl[j];
             const float cl = r.cl[j];
@@ -504,10 +517,18 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                     ypre = fmaf(row_bcast<n>(cl), hs[j][n], ypre);
                 },
                 std::make_integer_sequence<int, NS>{});
-            const float zv = r.z[j];  // 0 when there is no gate
-            const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
-            const float g = pick(zm, dyv * zv * sg, dyv);
-            if (dvalid && f.z) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
+            float g = dyv;
+            if constexpr (kMasks) {
+                const float zv = r.z[j];  // 0 when there is no gate
+                const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
+                g = pick(zm, dyv * zv * sg, dyv);
+                if (dvalid && f.z) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
+            } else if (f.z) {
+                const float zv = r.z[j];
+                const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
+                g = dyv * zv * sg;
+                if (dvalid) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
+            }
             float du = g * Dd;
             dD = fmaf(g, uv, dD);
             float ddt = 0.f;
@@ -601,7 +622,11 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                     std::make_integer_sequence<int, NS>{});
                 du += sf;
             }
-            const float dv = pick(spm, ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e)), ddt);
+            float dv = ddt;
+            if constexpr (kMasks)
+                dv = pick(spm, ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e)), ddt);
+            else if (f.softplus)
+                dv = ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e));
             dbias += dv;
             if (dvalid) {
                 st<BF16>(a.du, e, du);
