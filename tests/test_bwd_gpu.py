@@ -108,6 +108,18 @@ def test_bwd_softplus_off(gpu):
     _compare(gpu, x, "f32", "euler", softplus=False)
 
 
+@pytest.mark.parametrize("softplus", [True, False], ids=["softplus", "raw_step"])
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_bf16_options_off(gpu, disc, softplus):
+    """bf16 io (inputs staged in LDS; no z reads a zero-size buffer) with no
+    gate, D or bias, softplus on and off; L = 70 leaves a partial last
+    segment, whose adjoint walk also forms its decay."""
+    x = _inputs(2, 70, 64, 16, "bf16", seed=35, optional=False)
+    if not softplus:
+        x["delta"] = (x["delta"].float().abs() * 0.05 + 0.01).to(x["delta"].dtype)
+    _compare(gpu, x, "bf16", disc, softplus=softplus)
+
+
 def test_bwd_deterministic(gpu):
     x = _inputs(2, 300, 192, 16, "bf16", seed=34)
     g1 = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
