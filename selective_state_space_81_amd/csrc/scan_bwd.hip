@@ -374,10 +374,10 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     const float live = dvalid ? 1.f : 0.f;  // tail lanes repeat a channel: count it once
     const uint32_t spm = f.softplus ? ~0u : 0u;
     const uint32_t zm = f.z ? ~0u : 0u;
-    // The mask form pays off with Euler.  ZOH and bilinear keep branches: their
-    // steps hold more values, and straight-line steps spilled registers there
-    // (measured 10% slower).
-    constexpr bool kMasks = DISC == kEuler;
+    // The mask form pays off with Euler and bf16 io.  ZOH and bilinear keep
+    // branches: their steps hold more values, and straight-line steps spilled
+    // registers there (measured 10% slower); so did the fp32-io Euler kernel.
+    constexpr bool kMasks = DISC == kEuler && BF16;
     auto dt_of = [&](float v) {
         if constexpr (kMasks) return pick(spm, softplus_f(v), v);
         return f.softplus ? softplus_f(v) : v;
