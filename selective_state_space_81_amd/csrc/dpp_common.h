@@ -148,6 +148,73 @@ struct DppReadoutAcc16 {
 };
 #undef MS_DPP_
 
+// The compiler folds a DPP move into v_mul but not into v_fma / v_fmac, so
+// fmaf(row_bcast<n>(v), x, acc) costs a separate v_mov_b32_dpp.  The two
+// helpers below issue v_fmac_f32_dpp with the broadcast operand directly (one
+// instruction per state; same single rounding as fmaf), for the first NS
+// states (NS = 4, 8 or 16, lane n of each row holding state n of v).
+//   dpp_axpy: acc[n] += v_n * x for every n (in place)
+//   dpp_dot:  y + sum_n v_n * h[n], accumulated in order n = 0, 1, ...
+#define MS_AX_(n) "v_fmac_f32_dpp %" #n ", %[v], %[x] row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
+#define MS_DT_(n, k) "v_fmac_f32_dpp %[y], %[v], %" #k " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n"
+template <int NS>
+__device__ __forceinline__ void dpp_axpy(float (&acc)[NS], float v, float x);
+template <>
+__device__ __forceinline__ void dpp_axpy<4>(float (&a)[4], float v, float x) {
+    asm("s_nop 1\n" MS_AX_(0) MS_AX_(1) MS_AX_(2) MS_AX_(3)
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+        : [v] "v"(v), [x] "v"(x));
+}
+template <>
+__device__ __forceinline__ void dpp_axpy<8>(float (&a)[8], float v, float x) {
+    asm("s_nop 1\n" MS_AX_(0) MS_AX_(1) MS_AX_(2) MS_AX_(3) MS_AX_(4) MS_AX_(5) MS_AX_(6)
+            MS_AX_(7)
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+          "+v"(a[7])
+        : [v] "v"(v), [x] "v"(x));
+}
+template <>
+__device__ __forceinline__ void dpp_axpy<16>(float (&a)[16], float v, float x) {
+    asm("s_nop 1\n" MS_AX_(0) MS_AX_(1) MS_AX_(2) MS_AX_(3) MS_AX_(4) MS_AX_(5) MS_AX_(6)
+            MS_AX_(7) MS_AX_(8) MS_AX_(9) MS_AX_(10) MS_AX_(11) MS_AX_(12) MS_AX_(13) MS_AX_(14)
+                MS_AX_(15)
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]),
+          "+v"(a[7]), "+v"(a[8]), "+v"(a[9]), "+v"(a[10]), "+v"(a[11]), "+v"(a[12]),
+          "+v"(a[13]), "+v"(a[14]), "+v"(a[15])
+        : [v] "v"(v), [x] "v"(x));
+}
+template <int NS>
+__device__ __forceinline__ float dpp_dot(float y, float v, const float (&h)[NS]);
+template <>
+__device__ __forceinline__ float dpp_dot<4>(float y, float v, const float (&h)[4]) {
+    asm("s_nop 1\n" MS_DT_(0, 2) MS_DT_(1, 3) MS_DT_(2, 4) MS_DT_(3, 5)
+        : [y] "+v"(y)
+        : [v] "v"(v), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]));
+    return y;
+}
+template <>
+__device__ __forceinline__ float dpp_dot<8>(float y, float v, const float (&h)[8]) {
+    asm("s_nop 1\n" MS_DT_(0, 2) MS_DT_(1, 3) MS_DT_(2, 4) MS_DT_(3, 5) MS_DT_(4, 6)
+            MS_DT_(5, 7) MS_DT_(6, 8) MS_DT_(7, 9)
+        : [y] "+v"(y)
+        : [v] "v"(v), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]),
+          "v"(h[6]), "v"(h[7]));
+    return y;
+}
+template <>
+__device__ __forceinline__ float dpp_dot<16>(float y, float v, const float (&h)[16]) {
+    asm("s_nop 1\n" MS_DT_(0, 2) MS_DT_(1, 3) MS_DT_(2, 4) MS_DT_(3, 5) MS_DT_(4, 6)
+            MS_DT_(5, 7) MS_DT_(6, 8) MS_DT_(7, 9) MS_DT_(8, 10) MS_DT_(9, 11) MS_DT_(10, 12)
+                MS_DT_(11, 13) MS_DT_(12, 14) MS_DT_(13, 15) MS_DT_(14, 16) MS_DT_(15, 17)
+        : [y] "+v"(y)
+        : [v] "v"(v), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]),
+          "v"(h[6]), "v"(h[7]), "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]),
+          "v"(h[13]), "v"(h[14]), "v"(h[15]));
+    return y;
+}
+#undef MS_AX_
+#undef MS_DT_
+
 template <typename F, int... Js>
 __device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, Js...>) {
     (f(std::integral_constant<int, Js>{}), ...);

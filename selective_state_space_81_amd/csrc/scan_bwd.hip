@@ -306,10 +306,11 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
             const float dyv = in(3, j);
             const float g = pick(zm, dyv * silu_f(in(2, j)), dyv);
             const float cl = bc(1, j);
+            dpp_axpy<NS>(mu, cl, g);  // mu[n] becomes l_n = C_n g + mu_n
             static_for(
                 [&](auto nc) {
                     constexpr int n = decltype(nc)::value;
-                    const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                    const float l = mu[n];
                     const float t2 = dt * A2[n];
                     float abar;
                     if constexpr (BIL)
@@ -510,13 +511,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             const float cl = r.cl[j];
             const float dyv = r.dy[j];
             // y_pre from the recomputed state, for the gate's derivative
-            float ypre = Dd * uv;
-            static_for(
-                [&](auto nc) {
-                    constexpr int n = decltype(nc)::value;
-                    ypre = fmaf(row_bcast<n>(cl), hs[j][n], ypre);
-                },
-                std::make_integer_sequence<int, NS>{});
+            const float ypre = dpp_dot<NS>(Dd * uv, cl, hs[j]);
             float g = dyv;
             if constexpr (kMasks) {
                 const float zv = r.z[j];  // 0 when there is no gate
@@ -532,22 +527,23 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             float du = g * Dd;
             dD = fmaf(g, uv, dD);
             float ddt = 0.f;
+            dpp_axpy<NS>(mu, cl, g);  // mu[n] becomes l_n = C_n g + mu_n
             if constexpr (DISC == kEuler) {
                 // f = dt for every state, so with s = sum_n l_n B_n:
                 //   du   = g D + dt s,   d(dt) = sum_n l_n h_{n,t-1} A_bar_n a_n + u s,
                 //   dA_n += l_n h_{n,t-1} A_bar_n dt,   dB_n = l_n dt u,  dC_n = g h_n.
                 const float lg = live * g;
                 const float fuv = live * dt * uv;
-                float sb = 0.f, dta = 0.f;  // dta: sum_n (l h A_bar) A2_n
+                const float sb = dpp_dot<NS>(0.f, bl, mu);
+                float dta = 0.f;  // dta: sum_n (l h A_bar) A2_n
                 static_for(
                     [&](auto nc) {
                         constexpr int n = decltype(nc)::value;
                         const float hp = j == 0 ? hb[n] : hs[j - 1][n];
                         const float abar = hw_exp2(dt * A2[n]);
-                        const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                        const float l = mu[n];
                         red[NS + n][lane] = lg * hs[j][n];  // dC contribution
                         red[n][lane] = l * fuv;             // dB contribution
-                        sb = fmaf(l, row_bcast<n>(bl), sb);
                         const float w = l * hp * abar;
                         dta = fmaf(w, A2[n], dta);
                         dA[n] = fmaf(w, dt, dA[n]);
@@ -575,7 +571,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                         const bool small = fabsf(t2) < kZohSwitch;
                         const float fz = small ? dt * fmaf(t2, fmaf(t2, kZohT2, kZohT1), 1.f)
                                                : fmaf(abar, invA[n], -invA[n]);
-                        const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                        const float l = mu[n];
                         red[NS + n][lane] = lg * hs[j][n];  // dC contribution
                         red[n][lane] = (l * fz) * luv;      // dB contribution
                         const float lb = l * row_bcast<n>(bl);
@@ -609,7 +605,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                         const float r2 = r * r;
                         const float abar = fmaf(2.f, r, -1.f);
                         const float fb = dt * r;
-                        const float l = fmaf(row_bcast<n>(cl), g, mu[n]);
+                        const float l = mu[n];
                         red[NS + n][lane] = lg * hs[j][n];  // dC contribution
                         red[n][lane] = (l * fb) * luv;      // dB contribution
                         const float lb = l * row_bcast<n>(bl);
