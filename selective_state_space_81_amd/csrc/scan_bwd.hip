@@ -544,10 +544,11 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                         const float l = mu[n];
                         red[NS + n][lane] = lg * hs[j][n];  // dC contribution
                         red[n][lane] = l * fuv;             // dB contribution
-                        const float w = l * hp * abar;
+                        const float q = abar * l;           // the mu passed to step t-1
+                        const float w = q * hp;
                         dta = fmaf(w, A2[n], dta);
                         dA[n] = fmaf(w, dt, dA[n]);
-                        mu[n] = abar * l;
+                        mu[n] = q;
                     },
                     std::make_integer_sequence<int, NS>{});
                 du = fmaf(dt, sb, du);
@@ -576,13 +577,14 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                         red[n][lane] = (l * fz) * luv;      // dB contribution
                         const float lb = l * row_bcast<n>(bl);
                         sf = fmaf(fz, lb, sf);
-                        const float w = (l * hp) * abar;
+                        const float q = abar * l;  // the mu passed to step t-1
+                        const float w = q * hp;
                         dta = fmaf(w, A2[n], dta);
                         dtb = fmaf(abar, lb, dtb);
                         const float dfda = small ? fmaf(t2, fmaf(t2, c2, c1), c0)
                                                  : fmaf(dt, abar, -fz) * invA[n];
                         dA[n] = fmaf(lb * uv, dfda, fmaf(w, dt, dA[n]));
-                        mu[n] = abar * l;
+                        mu[n] = q;
                     },
                     std::make_integer_sequence<int, NS>{});
                 du += sf;
