@@ -17,11 +17,10 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 __device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---- io -------------------------------------------------------------------
+// fp32 -> bf16 rounded to nearest even: the hardware conversion
+// (v_cvt_pk_bf16_f32 on gfx950; NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <bool BF16>
