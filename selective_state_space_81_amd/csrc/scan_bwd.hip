@@ -421,6 +421,16 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     __shared__ uint16_t s_io[STAGE ? 4 * kSeg * 64 : 1];  // [u|delta|z|dy][step][lane]
     __shared__ uint16_t s_bc[STAGE ? 2 * kSeg * 16 : 1];  // [B|C][step][state]
     if constexpr (STAGE) stage_segment(a, row0, t0, t1, dd, lane, s_io, s_bc);
+    // bf16 io: du, ddelta and dz go out through buffer resources over the
+    // segment's rows, so rows past t1 and tail lanes (offset out of range)
+    // are dropped by the hardware, with no branch and 32-bit offsets.
+    const uint32_t orowb = (uint32_t)f.Dn * 2u;
+    auto out_rows = [&](void* p) {
+        return make_rsrc(static_cast<char*>(p) + (row0 + t0) * (int64_t)orowb,
+                         p ? (uint32_t)(t1 - t0) * orowb : 0u);
+    };
+    const auto rDu = out_rows(a.du), rDdl = out_rows(a.ddelta), rDz = out_rows(a.dz);
+    const uint32_t ooff = dvalid ? (uint32_t)dd * 2u : kOutOfRange;
     auto wid = [](uint16_t v) { return __uint_as_float((uint32_t)v << 16); };
 
     // Inputs of the 4 steps from tb (indices clamped into the segment).
@@ -517,12 +527,17 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                 const float zv = r.z[j];  // 0 when there is no gate
                 const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
                 g = pick(zm, dyv * zv * sg, dyv);
-                if (dvalid && f.z) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
+                const float dzv = dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f);
+                Io<true>::store(rDz, ooff + (uint32_t)(t - t0) * orowb, dzv);  // no z: size 0
             } else if (f.z) {
                 const float zv = r.z[j];
                 const float sg = hw_rcp(1.f + hw_exp2(-zv * kLog2e));
                 g = dyv * zv * sg;
-                if (dvalid) st<BF16>(a.dz, e, dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
+                const float dzv = dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f);
+                if constexpr (BF16)
+                    Io<true>::store(rDz, ooff + (uint32_t)(t - t0) * orowb, dzv);
+                else if (dvalid)
+                    st<BF16>(a.dz, e, dzv);
             }
             float du = g * Dd;
             dD = fmaf(g, uv, dD);
@@ -626,7 +641,10 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             else if (f.softplus)
                 dv = ddt * hw_rcp(1.f + hw_exp2(-v * kLog2e));
             dbias += dv;
-            if (dvalid) {
+            if constexpr (BF16) {
+                Io<true>::store(rDu, ooff + (uint32_t)(t - t0) * orowb, du);
+                Io<true>::store(rDdl, ooff + (uint32_t)(t - t0) * orowb, dv);
+            } else if (dvalid) {
                 st<BF16>(a.du, e, du);
                 st<BF16>(a.ddelta, e, dv);
             }
