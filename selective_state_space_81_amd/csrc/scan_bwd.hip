@@ -495,7 +495,10 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     };
 
     float dbias = 0.f, dD = 0.f;
-    float* pbc_row = a.pbc + ((int64_t)tile * f.batch + b) * f.L * (2 * N);
+    // The tile's dB | dC partials of this segment's steps, [t - t0][2N] fp32,
+    // through a buffer resource (rows past t1 dropped).
+    const auto rPbc = make_rsrc(a.pbc + (((int64_t)tile * f.batch + b) * f.L + t0) * (2 * N),
+                                (uint32_t)(t1 - t0) * (uint32_t)(2 * N) * 4u);
 
     // Gradients of the sub-block of 4 steps from tb, whose starting state is hb.
     auto sub_block = [&](int64_t tb, const float (&hb)[NS]) {
@@ -663,8 +666,10 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                 acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf,
                                                                0xf, true));  // quad_perm 1,0,3,2
                 const int n = row < NS ? row : row - NS;
-                if (half == 0 && row < 2 * NS && n < N)
-                    pbc_row[t * (2 * N) + (row < NS ? 0 : N) + n] = acc;
+                const bool keep = half == 0 && row < 2 * NS && n < N;
+                const uint32_t po = (uint32_t)(t - t0) * (uint32_t)(2 * N) + (row < NS ? 0 : N) + n;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rPbc,
+                                                      keep ? po * 4u : kOutOfRange, 0, 0);
             }
             __syncthreads();
         }
