@@ -658,10 +658,13 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             {
                 const int row = lane >> 1;
                 const int half = lane & 1;
+                // four partial sums (i mod 4) keep the add chain short
                 float acc = 0.f;
                 if (row < 2 * NS) {
-#pragma unroll 8
-                    for (int i = 0; i < 32; ++i) acc += red[row][32 * half + i];
+                    float p4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) p4[i & 3] += red[row][32 * half + i];
+                    acc = (p4[0] + p4[1]) + (p4[2] + p4[3]);
                 }
                 acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf,
                                                                0xf, true));  // quad_perm 1,0,3,2
