@@ -185,10 +185,11 @@ __device__ __forceinline__ void stage_segment(const BwdArgs& a, int64_t row0, in
 //             and its decay (sum of dt, or the product of A_bar per state);
 //   s >= 1  : from mu = 0 at its end, the adjoint run back over it gives the
 //             mu passed left (beta, a.mu slot s-1) and the same decay.
+// Both come from one walk of the segment in time order.
 // The carries then compose them (forward: carry_chain<false>; adjoint:
 // carry_chain<true>).
 template <int NS, bool BF16, int DISC>
-__global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
+__global__ void __launch_bounds__(64, (BF16 && DISC != kZoh) ? 4 : 3) seg_summaries(BwdArgs a) {
     const ScanArgs& f = a.f;
     const int lane = threadIdx.x;
     const int b = blockIdx.z;
@@ -235,7 +236,7 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
     };
 
     // The compensated sum of dt over the segment (its decay for the
-    // exp-based forms), accumulated in whichever walk runs first.
+    // exp-based forms).
     float ssum = 0.f, scomp = 0.f;
     auto kahan = [&](float v) {
         const float yk = v - scomp;
@@ -243,44 +244,73 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
         scomp = (tk - ssum) - yk;
         ssum = tk;
     };
-    float P[NS];  // bilinear decay: product of A_bar per state
+    float P[NS];  // running product of A_bar per state (the bilinear decay)
 #pragma unroll
     for (int n = 0; n < NS; ++n) P[n] = 1.f;
     const int64_t base_f = (int64_t)b * km1 + s;      // forward slot
     const int64_t base_b = (int64_t)b * km1 + s - 1;  // adjoint slot
 
-    // Steps are walked in a loop unrolled MSSCAN_SEGSUM_UNROLL ways, not
-    // fully: the exponentials do not depend on the state, and fully unrolled
-    // the compiler would form all of them at once and run out of registers.
-    if (do_fwd) {  // a segment before the last is full
-        float h[NS];
+    // One walk in time order serves both summaries.  The forward one is the
+    // recurrence from a zero state.  The adjoint one, run back from mu = 0 at
+    // the segment end, equals sum_j (A_bar_0 ... A_bar_j) C_j g_j, so in time
+    // order it needs the running product of A_bar (P, also the bilinear
+    // decay) and one fma per state, sharing dt and A_bar with the forward
+    // walk.  The walk is unrolled MSSCAN_SEGSUM_UNROLL ways, not fully: the
+    // exponentials do not depend on the state, and fully unrolled the
+    // compiler would form all of them at once and run out of registers.
+    float h[NS], mu[NS];
 #pragma unroll
-        for (int n = 0; n < NS; ++n) h[n] = 0.f;
-#pragma unroll MSSCAN_SEGSUM_UNROLL
-        for (int j = 0; j < kSeg; ++j) {
-            const float dt = step_pick(in(1, j), bias, spm);
-            kahan(dt);
-            const float uv = in(0, j), bl = bc(0, j);
-            if constexpr (DISC == kEuler) {
-                const float xv = dt * uv;
-                static_for(
-                    [&](auto nc) {
-                        constexpr int n = decltype(nc)::value;
-                        h[n] = fmaf(hw_exp2(dt * A2[n]), h[n], row_bcast<n>(bl) * xv);
-                    },
-                    std::make_integer_sequence<int, NS>{});
-            } else {
-                static_for(
-                    [&](auto nc) {
-                        constexpr int n = decltype(nc)::value;
-                        const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
-                        h[n] = fmaf(q.abar, h[n], q.f * row_bcast<n>(bl) * uv);
-                        if constexpr (BIL) P[n] *= q.abar;
-                    },
-                    std::make_integer_sequence<int, NS>{});
-            }
+    for (int n = 0; n < NS; ++n) {
+        h[n] = 0.f;
+        mu[n] = 0.f;
+    }
+    auto walk_step = [&](int j, auto fwd_c, auto bwd_c) {
+        constexpr bool FWD = decltype(fwd_c)::value, BWD = decltype(bwd_c)::value;
+        const float dt = step_pick(in(1, j), bias, spm);
+        kahan(dt);
+        float uv = 0.f, bl = 0.f, g = 0.f, cl = 0.f;
+        if constexpr (FWD) {
+            uv = in(0, j);
+            bl = bc(0, j);
         }
-        if (dvalid) {
+        if constexpr (BWD) {
+            const float dyv = in(3, j);
+            g = pick(zm, dyv * silu_f(in(2, j)), dyv);
+            cl = bc(1, j);
+        }
+        const float xv = dt * uv;
+        static_for(
+            [&](auto nc) {
+                constexpr int n = decltype(nc)::value;
+                float abar;
+                if constexpr (DISC == kEuler) {
+                    abar = hw_exp2(dt * A2[n]);
+                    if constexpr (FWD) h[n] = fmaf(abar, h[n], row_bcast<n>(bl) * xv);
+                } else {
+                    const Disc<DISC> q(dt, dt * A2[n], A2[n], invA[n]);
+                    abar = q.abar;
+                    if constexpr (FWD) h[n] = fmaf(q.abar, h[n], q.f * row_bcast<n>(bl) * uv);
+                }
+                if constexpr (BWD || BIL) P[n] *= abar;
+                if constexpr (BWD) mu[n] = fmaf(row_bcast<n>(cl) * P[n], g, mu[n]);
+            },
+            std::make_integer_sequence<int, NS>{});
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    // fp32 io reads each step from memory: unrolled, its loads spill registers
+    constexpr int kUnroll = BF16 ? MSSCAN_SEGSUM_UNROLL : 1;
+    if (do_fwd && do_bwd) {  // a middle segment (full)
+#pragma unroll kUnroll
+        for (int j = 0; j < kSeg; ++j) walk_step(j, T_{}, T_{});
+    } else if (do_fwd) {  // the first segment (full)
+#pragma unroll kUnroll
+        for (int j = 0; j < kSeg; ++j) walk_step(j, T_{}, F_{});
+    } else {  // the last segment, possibly partial
+        for (int j = 0; j < (int)(t1 - t0); ++j) walk_step(j, F_{}, T_{});
+    }
+    if (dvalid) {
+        if (do_fwd) {
 #pragma unroll
             for (int n = 0; n < NS; ++n)
                 if (n < N) f.agg[(base_f * N + n) * f.Dn + d] = h[n];
@@ -292,43 +322,7 @@ __global__ void __launch_bounds__(64, 4) seg_summaries(BwdArgs a) {
                 f.sdt[base_f * f.Dn + d] = ssum;
             }
         }
-    }
-    if (do_bwd) {
-        float mu[NS];
-#pragma unroll
-        for (int n = 0; n < NS; ++n) mu[n] = 0.f;
-        // One adjoint step; FIRST: this walk also forms the segment decay
-        // (the last segment, which has no forward walk and may be partial).
-        auto adj_step = [&](int j, auto first_c) {
-            constexpr bool FIRST = decltype(first_c)::value;
-            const float dt = step_pick(in(1, j), bias, spm);
-            if constexpr (FIRST) kahan(dt);
-            const float dyv = in(3, j);
-            const float g = pick(zm, dyv * silu_f(in(2, j)), dyv);
-            const float cl = bc(1, j);
-            dpp_axpy<NS>(mu, cl, g);  // mu[n] becomes l_n = C_n g + mu_n
-            static_for(
-                [&](auto nc) {
-                    constexpr int n = decltype(nc)::value;
-                    const float l = mu[n];
-                    const float t2 = dt * A2[n];
-                    float abar;
-                    if constexpr (BIL)
-                        abar = fmaf(2.f, bilinear_r(t2), -1.f);
-                    else
-                        abar = hw_exp2(t2);
-                    mu[n] = abar * l;
-                    if constexpr (BIL && FIRST) P[n] *= abar;
-                },
-                std::make_integer_sequence<int, NS>{});
-        };
-        if (!do_fwd) {
-            for (int j = (int)(t1 - t0) - 1; j >= 0; --j) adj_step(j, std::true_type{});
-        } else {  // a segment before the last is full: a fixed trip count
-#pragma unroll MSSCAN_SEGSUM_UNROLL
-            for (int j = kSeg - 1; j >= 0; --j) adj_step(j, std::false_type{});
-        }
-        if (dvalid) {
+        if (do_bwd) {
 #pragma unroll
             for (int n = 0; n < NS; ++n)
                 if (n < N) a.mu[(base_b * N + n) * f.Dn + d] = mu[n];
