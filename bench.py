@@ -271,7 +271,7 @@ def measure_conv(ms, reps=20, width=4):
             "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9}
 
 
-def measure_bwd(ms, reps=5):
+def measure_bwd(ms, reps=20, warm=3):
     """ms_scan_bwd (gradients of every input) on the 130M-layer workload:
     ms per call (forward recompute included) and the main backward kernel's
     HIP-event time."""
@@ -293,7 +293,8 @@ def measure_bwd(ms, reps=5):
                     delta_bias=x.get("delta_bias"), softplus=w.softplus, workspace=ws,
                     stream=stream)
 
-    call()
+    for _ in range(warm):
+        call()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -320,7 +321,8 @@ def measure_bwd(ms, reps=5):
                         delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh,
                         bilinear=bilinear, workspace=ws2, stream=stream)
 
-        c()
+        for _ in range(warm):
+            c()
         torch.cuda.synchronize()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record(stream)
