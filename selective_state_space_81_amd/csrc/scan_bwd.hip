@@ -50,11 +50,12 @@ using namespace dev;
 #define MSSCAN_SEGSUM_UNROLL 4  // steps per unrolled body of the summary walks
 #endif
 constexpr int kSeg = 16;  // timesteps per backward segment
-// Timesteps per recomputed sub-block: 4 with the Euler form; 2 with ZOH and
-// bilinear, whose per-state factors need more registers (half the recomputed
-// states held, at the price of more recompute, instead of spilling).
-template <int DISC>
-constexpr int sub_len() { return DISC == kEuler ? 4 : 2; }
+// Timesteps per recomputed sub-block: 4, except 2 for ZOH and bilinear with
+// fp32 io, whose per-state factors and unstaged inputs need more registers
+// (half the recomputed states held, at the price of more recompute, instead
+// of spilling).
+template <int DISC, bool BF16>
+constexpr int sub_len() { return (DISC == kEuler || BF16) ? 4 : 2; }
 
 // Per-state derivatives of the discretisation: A_bar, the B*u factor f, and
 // their partial derivatives w.r.t. dt and a (the continuous A), from
@@ -344,13 +345,13 @@ __global__ void __launch_bounds__(64, (BF16 && DISC != kZoh) ? 4 : 3) seg_summar
 
 // ---- 4. per-segment gradients ---------------------------------------------------
 // The segment's kSeg = 16 steps are walked back in sub-blocks of kSub steps
-// (sub_len: 4 Euler, 2 ZOH / bilinear).  Forward states come from two kept
+// (sub_len: 4, or 2 for fp32-io ZOH / bilinear).  Forward states come from two kept
 // states, the segment start and the state after 8 steps (32 recomputed steps
 // per segment with 4-step sub-blocks, 48 with 2-step ones), and each
 // sub-block's inputs are read in one batch before its arithmetic.
 template <int NS, bool BF16, int DISC>
 __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
-    constexpr int kSub = sub_len<DISC>();
+    constexpr int kSub = sub_len<DISC, BF16>();
     static_assert(kSeg == 16 && (kSub == 4 || kSub == 2), "sub-blocks split the segment");
     const ScanArgs& f = a.f;
     // Per-step dB | dC contributions, [value][lane]; rows padded to 65 floats
