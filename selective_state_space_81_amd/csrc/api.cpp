@@ -367,7 +367,7 @@ BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
     q.mu = q.agg;
     q.bdecay = q.fdecay;
     q.pbc = (size_t)q.tiles * B * (size_t)d.seqlen * 2 * N;
-    q.pparam = B * (size_t)q.K * D * (N + 2);
+    q.pparam = B * (size_t)((q.K + msscan::kBwdWaves - 1) / msscan::kBwdWaves) * D * (N + 2);
     q.pgroup = (size_t)msscan::kParamGroups * D * (N + 2);
     msscan::Plan& p = q.fwd;
     p.tile_path = 0;

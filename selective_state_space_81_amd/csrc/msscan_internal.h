@@ -148,6 +148,7 @@ struct BwdLaunch {
 };
 int bwd_segment_len();
 constexpr int kParamGroups = 16;  // first-level groups of the parameter sums
+constexpr int kBwdWaves = 4;  // backward segments per workgroup (one wave each)
 hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s);
 
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;

@@ -107,7 +107,7 @@ struct BwdArgs {
     float* sdt_b;        // [batch][K-1][Dn] decay sums of segments 1..K-1 (exp-based)
     float* prod_b;       // [batch][K-1][N][Dn] decay products (bilinear)
     float* pbc;          // [tiles][batch][L][2N]: per-tile partial dB | dC
-    float* pparam;       // [batch][K][Dn][N+2]: per-segment partial dA | dD | dbias
+    float* pparam;       // [batch][ceil(K/kBwdWaves)][Dn][N+2]: partial dA | dD | dbias per group
     float* pgroup;       // [kParamGroups][Dn][N+2]: first-level sums of pparam
 };
 
@@ -126,6 +126,17 @@ __device__ __forceinline__ float pick(uint32_t mask, float on, float off) {
 __device__ __forceinline__ float step_pick(float draw, float bias, uint32_t spm) {
     const float v = draw + bias;
     return pick(spm, softplus_f(v), v);
+}
+
+// Orders one wave's LDS accesses across its lanes.  Each wave of a workgroup
+// works in LDS rows of its own, so no workgroup barrier is needed: the
+// fences keep the compiler from moving LDS accesses across this point, and
+// lgkmcnt(0) waits until the wave's LDS writes are done.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // The raw bf16 inputs of steps [t0, t1) of one 64-channel tile, staged in
@@ -177,7 +188,7 @@ __device__ __forceinline__ void stage_segment(const BwdArgs& a, int64_t row0, in
         s_bc[(0 * kSeg + 4 * k + sr) * 16 + st] = vb[k];
         s_bc[(1 * kSeg + 4 * k + sr) * 16 + st] = vc[k];
     }
-    __syncthreads();
+    wave_sync();
 }
 
 // ---- 1+2. segment summaries, forward and adjoint, in one pass -----------------
@@ -350,19 +361,28 @@ __global__ void __launch_bounds__(64, (BF16 && DISC != kZoh) ? 4 : 3) seg_summar
 // per segment with 4-step sub-blocks, 48 with 2-step ones), and each
 // sub-block's inputs are read in one batch before its arithmetic.
 template <int NS, bool BF16, int DISC>
-__global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kBwdWaves, 2) bwd_main(BwdArgs a) {
     constexpr int kSub = sub_len<DISC, BF16>();
     static_assert(kSeg == 16 && (kSub == 4 || kSub == 2), "sub-blocks split the segment");
     const ScanArgs& f = a.f;
     // Per-step dB | dC contributions, [value][lane]; rows padded to 65 floats
     // so that the column sums below read distinct banks.
-    __shared__ float red[2 * NS][65];
-    const int lane = threadIdx.x;
+    __shared__ float red_w[kBwdWaves][2 * NS][65];
+    // Wave w of the workgroup takes segment kBwdWaves * blockIdx.y + w of one
+    // tile; a spare wave of the last group repeats the last segment and
+    // stores nothing (so every wave runs the same code up to the final
+    // workgroup barrier).
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // uniform
+    float(*red)[65] = red_w[wave];
+    const int lane = (int)(threadIdx.x & 63);
     const int b = blockIdx.z;
-    const int s = blockIdx.y;
+    const int s_raw = blockIdx.y * kBwdWaves + wave;
+    const bool seg_ok = s_raw < f.chunks;
+    const int s = seg_ok ? s_raw : f.chunks - 1;
     const int tile = blockIdx.x;
     const int d = tile * 64 + lane;
     const bool dvalid = d < f.Dn;
+    const bool wvalid = dvalid && seg_ok;  // this lane stores results
     const int dd = dvalid ? d : f.Dn - 1;
     const int N = f.N;
     const int km1 = f.chunks - 1;
@@ -413,8 +433,10 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
     // state), so the walk below never waits on HBM.  fp32 io reads them
     // from memory per sub-block.
     constexpr bool STAGE = BF16;
-    __shared__ uint16_t s_io[STAGE ? 4 * kSeg * 64 : 1];  // [u|delta|z|dy][step][lane]
-    __shared__ uint16_t s_bc[STAGE ? 2 * kSeg * 16 : 1];  // [B|C][step][state]
+    __shared__ uint16_t s_io_w[kBwdWaves][STAGE ? 4 * kSeg * 64 : 1];  // [u|delta|z|dy][step][lane]
+    __shared__ uint16_t s_bc_w[kBwdWaves][STAGE ? 2 * kSeg * 16 : 1];  // [B|C][step][state]
+    uint16_t* s_io = s_io_w[wave];
+    uint16_t* s_bc = s_bc_w[wave];
     if constexpr (STAGE) stage_segment(a, row0, t0, t1, dd, lane, s_io, s_bc);
     // bf16 io: du, ddelta and dz go out through buffer resources over the
     // segment's rows, so rows past t1 and tail lanes (offset out of range)
@@ -425,7 +447,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                          p ? (uint32_t)(t1 - t0) * orowb : 0u);
     };
     const auto rDu = out_rows(a.du), rDdl = out_rows(a.ddelta), rDz = out_rows(a.dz);
-    const uint32_t ooff = dvalid ? (uint32_t)dd * 2u : kOutOfRange;
+    const uint32_t ooff = wvalid ? (uint32_t)dd * 2u : kOutOfRange;
     auto wid = [](uint16_t v) { return __uint_as_float((uint32_t)v << 16); };
 
     // Inputs of the 4 steps from tb (indices clamped into the segment).
@@ -534,7 +556,7 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                 const float dzv = dyv * ypre * sg * fmaf(zv, 1.f - sg, 1.f);
                 if constexpr (BF16)
                     Io<true>::store(rDz, ooff + (uint32_t)(t - t0) * orowb, dzv);
-                else if (dvalid)
+                else if (wvalid)
                     st<BF16>(a.dz, e, dzv);
             }
             float du = g * Dd;
@@ -642,14 +664,14 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
             if constexpr (BF16) {
                 Io<true>::store(rDu, ooff + (uint32_t)(t - t0) * orowb, du);
                 Io<true>::store(rDdl, ooff + (uint32_t)(t - t0) * orowb, dv);
-            } else if (dvalid) {
+            } else if (wvalid) {
                 st<BF16>(a.du, e, du);
                 st<BF16>(a.ddelta, e, dv);
             }
             // Sum the 2N contributions of this step over the wave's channels:
             // lane l adds half (l & 1) of row l >> 1, the pair is combined
             // with a DPP add, and the even lane stores the tile's partial.
-            __syncthreads();
+            wave_sync();
             {
                 const int row = lane >> 1;
                 const int half = lane & 1;
@@ -664,12 +686,12 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
                 acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf,
                                                                0xf, true));  // quad_perm 1,0,3,2
                 const int n = row < NS ? row : row - NS;
-                const bool keep = half == 0 && row < 2 * NS && n < N;
+                const bool keep = seg_ok && half == 0 && row < 2 * NS && n < N;
                 const uint32_t po = (uint32_t)(t - t0) * (uint32_t)(2 * N) + (row < NS ? 0 : N) + n;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rPbc,
                                                       keep ? po * 4u : kOutOfRange, 0, 0);
             }
-            __syncthreads();
+            wave_sync();
         }
     };
 
@@ -694,18 +716,35 @@ __global__ void __launch_bounds__(64, 2) bwd_main(BwdArgs a) {
         sub_block(t0 + kSub * k, hb);
     }
 
-    if (!dvalid) return;
-    // per-segment partials of dA, dD, dbias
-    float* pp = a.pparam + (((int64_t)b * f.chunks + s) * f.Dn + d) * (N + 2);
-#pragma unroll
-    for (int n = 0; n < NS; ++n)
-        if (n < N) pp[n] = dA[n];
-    pp[N] = dD;
-    pp[N + 1] = dbias;
-    if (s == 0 && a.dh0) {
+    if (s == 0 && a.dh0 && wvalid) {
 #pragma unroll
         for (int n = 0; n < NS; ++n)
             if (n < N) a.dh0[((int64_t)b * f.Dn + d) * N + n] = mu[n];
+    }
+
+    // The waves' partials of dA, dD and dbias are added in wave order through
+    // LDS (each wave's own rows are free now), and wave 0 stores the group's.
+    static_assert(NS >= 2, "N + 2 partial rows fit the 2 * NS rows of a wave");
+    wave_sync();
+#pragma unroll
+    for (int n = 0; n < NS; ++n) red[n][lane] = seg_ok ? dA[n] : 0.f;
+    red[NS][lane] = seg_ok ? dD : 0.f;
+    red[NS + 1][lane] = seg_ok ? dbias : 0.f;
+    __syncthreads();
+    if (wave == 0 && dvalid) {
+        const int groups = (f.chunks + kBwdWaves - 1) / kBwdWaves;
+        float* pp = a.pparam + (((int64_t)b * groups + blockIdx.y) * f.Dn + d) * (N + 2);
+        auto sum_w = [&](int row) {
+            float acc = red_w[0][row][lane];
+#pragma unroll
+            for (int w = 1; w < kBwdWaves; ++w) acc += red_w[w][row][lane];
+            return acc;
+        };
+#pragma unroll
+        for (int n = 0; n < NS; ++n)
+            if (n < N) pp[n] = sum_w(n);
+        pp[N] = sum_w(NS);
+        pp[N + 1] = sum_w(NS + 1);
     }
 }
 
@@ -734,7 +773,7 @@ __global__ void __launch_bounds__(256) reduce_bc(BwdArgs a, float* dB, float* dC
         dC[row * f.N + k - f.N] = acc;
 }
 
-// Parameter sums over the batch x K rows of pparam, in two fixed-order
+// Parameter sums over the batch x ceil(K/kBwdWaves) rows of pparam, in two fixed-order
 // levels: group g (blockIdx.y) adds the rows r with r mod kParamGroups == g
 // in increasing order, then reduce_param_groups adds the groups in order.
 __global__ void __launch_bounds__(256) reduce_params(BwdArgs a) {
@@ -743,7 +782,7 @@ __global__ void __launch_bounds__(256) reduce_params(BwdArgs a) {
     const int64_t per = (int64_t)f.Dn * (f.N + 2);
     if (idx >= per) return;
     const int g = blockIdx.y;
-    const int64_t rows = (int64_t)f.batch * f.chunks;
+    const int64_t rows = (int64_t)f.batch * ((f.chunks + kBwdWaves - 1) / kBwdWaves);
     // The group's rows are added in increasing order; each batch of 8 loads is
     // issued before its adds.
     float acc = 0.f;
@@ -808,7 +847,9 @@ hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* 
     }
     {
         ProfScope ps(s, kPhaseMain);
-        hipLaunchKernelGGL((bwd_main<NS, BF16, DISC>), dim3(tiles, K, f.batch), dim3(64), 0, s, a);
+        hipLaunchKernelGGL((bwd_main<NS, BF16, DISC>),
+                           dim3(tiles, (K + kBwdWaves - 1) / kBwdWaves, f.batch), dim3(64 * kBwdWaves),
+                           0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nbc = (int64_t)f.batch * f.L * 2 * f.N;
