@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     // Register double buffer of the raw inputs of one block.
     RT ru[2][J], rd[2][J], rz[2][J];
     float vb[2][TB], vc[2][TB];
-    auto load_block = [&](int buf, int64_t tb) {
+    auto load_block = [&](int buf, int64_t tb) __attribute__((always_inline)) {
         const uint32_t nr = block_rows(tb);
         const auto rU = make_rsrc(block_base(a.u, tb), nr * rowb);
         const auto rD = make_rsrc(block_base(a.delta, tb), nr * rowb);
@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     float s_sum = 0.f, s_comp = 0.f;  // Kahan sum of dt (wave 0, SUMMARY)
 
     // One timestep of this wave's NS states.
-    auto step = [&](int cur, int tt, float2 dx, float vbt, float vct) {
+    auto step = [&](int cur, int tt, float2 dx, float vbt, float vct) __attribute__((always_inline)) {
         static_for(
             [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
@@ -170,6 +170,9 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
                 }
                 h[j] = fmaf(abar, h[j], bx);
                 if constexpr (PROD) P[j] *= abar;
+                // With a block's steps unrolled, the scheduler would start the
+                // exponentials of many steps ahead of their updates and spill.
+                if constexpr (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
             },
             std::make_integer_sequence<int, NS>{});
         if constexpr (!SUMMARY) {
@@ -186,7 +189,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
 
     // One block of TB timesteps; CUR (the buffer parity) is a compile-time
     // constant so the register double buffer is indexed statically.
-    auto do_block = [&](auto cur_c, int blk) {
+    auto do_block = [&](auto cur_c, int blk) __attribute__((always_inline)) {
         constexpr int cur = decltype(cur_c)::value;
         const int64_t tb = t0 + (int64_t)blk * TB;
         const int cnt = (int)min((int64_t)TB, t1 - tb);
