@@ -129,7 +129,8 @@ struct Frag8<false> {
     }
 };
 
-template <int N, int TB, bool DB, bool BF16, int DISC, bool SP, bool SUMMARY, bool DTP = false>
+template <int N, int TB, bool DB, bool BF16, int DISC, bool SP, bool SUMMARY, bool DTP = false,
+          bool PAD = false>
 __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(ScanArgs a) {
     static_assert(N == 8 || N == 16 || N == 32 || N == 64, "states per lane");
     constexpr bool ZOH = DISC == kZoh;
@@ -151,10 +152,14 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     const bool dvalid = d < a.Dn;
     const int dd = dvalid ? d : a.Dn - 1;
 
+    // PAD: the true d_state Nr = a.N is below N.  States Nr..N-1 get A = 0
+    // and B = C = 0, so they stay zero and add nothing; they are never
+    // stored, and every stride uses Nr.
+    const int Nr = PAD ? a.N : N;
     float A2[N], invA[N], A2sq[N], h[N], P[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        const float av = a.A[(int64_t)dd * N + n];
+        const float av = (!PAD || n < Nr) ? a.A[(int64_t)dd * Nr + n] : 0.f;
         A2[n] = av * kLog2e;
         if constexpr (ZOH) {
             invA[n] = (av != 0.f) ? 1.f / av : 0.f;
@@ -166,10 +171,12 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     for (int n = 0; n < N; ++n) {
         float v = 0.f;
         if constexpr (!SUMMARY) {
-            if (seg == 0) {
-                if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * N + n];
-            } else {
-                v = a.agg[(((int64_t)b * km1 + (seg - 1)) * N + n) * a.Dn + dd];
+            if (!PAD || n < Nr) {
+                if (seg == 0) {
+                    if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * Nr + n];
+                } else {
+                    v = a.agg[(((int64_t)b * km1 + (seg - 1)) * Nr + n) * a.Dn + dd];
+                }
             }
         }
         h[n] = v;
@@ -191,8 +198,15 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     auto block_base = [&](const void* p, int64_t tb) -> const void* {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)rowb;
     };
-    constexpr uint32_t kBRow = (uint32_t)N * R::kSize;  // one timestep of B or C
-    const uint32_t bcoff = (uint32_t)(lane & (RW - 1)) * R::kSize;
+    const uint32_t kBRow = (uint32_t)Nr * R::kSize;  // one timestep of B or C
+    // Byte offset in a B/C row of the state lane `lane` holds in group k
+    // (padded states read past the row: 0).
+    uint32_t boff[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const int st = 16 * k + (lane & (RW - 1));
+        boff[k] = (!PAD || st < Nr) ? (uint32_t)st * R::kSize : kOutOfRange;
+    }
     auto bc_base = [&](const void* p, int64_t tb) -> const void* {
         return static_cast<const char*>(p) + (row0 + tb) * (int64_t)kBRow;
     };
@@ -216,7 +230,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             if constexpr (!SUMMARY) rz[buf][tt] = R::load(rZ, off);
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
-                const uint32_t o = (uint32_t)tt * kBRow + (uint32_t)(16 * k) * R::kSize + bcoff;
+                const uint32_t o = (uint32_t)tt * kBRow + boff[k];
                 vb[buf][tt][k] = R::load(rB, o);
                 if constexpr (!SUMMARY) vc[buf][tt][k] = R::load(rC, o);
             }
@@ -387,7 +401,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
         RT xb[KB], xc[KB];
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
-            const uint32_t o = (uint32_t)(16 * k) * R::kSize + bcoff;
+            const uint32_t o = boff[k];
             xb[k] = R::load(make_rsrc(bc_base(a.B, t), kBRow), o);
             xc[k] = SUMMARY ? RT{} : R::load(make_rsrc(bc_base(a.C, t), kBRow), o);
         }
@@ -401,22 +415,25 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
     if constexpr (SUMMARY) {
         const int64_t base = (int64_t)b * km1 + seg;
 #pragma unroll
-        for (int n = 0; n < N; ++n) a.agg[(base * N + n) * a.Dn + d] = h[n];
+        for (int n = 0; n < N; ++n)
+            if (!PAD || n < Nr) a.agg[(base * Nr + n) * a.Dn + d] = h[n];
         if constexpr (PROD) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) a.prod[(base * N + n) * a.Dn + d] = P[n];
+            for (int n = 0; n < N; ++n)
+                if (!PAD || n < Nr) a.prod[(base * Nr + n) * a.Dn + d] = P[n];
         } else {
             a.sdt[base * a.Dn + d] = s_sum;
         }
     } else {
         if (seg == a.chunks - 1 && a.h_last) {
 #pragma unroll
-            for (int n = 0; n < N; ++n) a.h_last[((int64_t)b * a.Dn + d) * N + n] = h[n];
+            for (int n = 0; n < N; ++n)
+                if (!PAD || n < Nr) a.h_last[((int64_t)b * a.Dn + d) * Nr + n] = h[n];
         }
     }
 }
 
-template <int N, bool BF16, int DISC, bool SP, bool DTP = false>
+template <int N, bool BF16, int DISC, bool SP, bool DTP = false, bool PAD = false>
 hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     // 64 states (32 with the extra per-state values of ZOH or the bilinear
     // summary) leave room for one register block only: no prefetch.
@@ -427,7 +444,7 @@ hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, true, DTP>),
+            hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, true, DTP, PAD>),
                                dim3(p.tiles, p.chunks - 1, a.batch), dim3(64), 0, s, a);
         }
         e = hipGetLastError();
@@ -437,7 +454,7 @@ hipError_t launch_lanes(const Plan& p, const ScanArgs& a, hipStream_t s) {
     }
     {
         ProfScope ps(s, kPhaseMain);
-        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, false, DTP>),
+        hipLaunchKernelGGL((scan_lane<N, TB, DB, BF16, DISC, SP, false, DTP, PAD>),
                            dim3(p.tiles, p.chunks, a.batch), dim3(64), 0, s, a);
     }
     return hipGetLastError();
@@ -454,14 +471,14 @@ hipError_t dispatch_dtp(const Plan& p, const ScanArgs& a, hipStream_t s) {
     }
 }
 
-template <bool BF16, int DISC, bool SP>
+template <bool BF16, int DISC, bool SP, bool PAD>
 hipError_t dispatch_n(const Plan& p, const ScanArgs& a, hipStream_t s) {
     switch (p.ns) {
-        case 8: return launch_lanes<8, BF16, DISC, SP>(p, a, s);
-        case 16: return launch_lanes<16, BF16, DISC, SP>(p, a, s);
-        case 32: return launch_lanes<32, BF16, DISC, SP>(p, a, s);
+        case 8: return launch_lanes<8, BF16, DISC, SP, false, PAD>(p, a, s);
+        case 16: return launch_lanes<16, BF16, DISC, SP, false, PAD>(p, a, s);
+        case 32: return launch_lanes<32, BF16, DISC, SP, false, PAD>(p, a, s);
         case 64:
-            if constexpr (DISC == kEuler) return launch_lanes<64, BF16, DISC, SP>(p, a, s);
+            if constexpr (DISC == kEuler) return launch_lanes<64, BF16, DISC, SP, false, PAD>(p, a, s);
             return hipErrorInvalidValue;  // 64 ZOH/bilinear states do not fit a lane
         default: return hipErrorInvalidValue;
     }
@@ -469,7 +486,11 @@ hipError_t dispatch_n(const Plan& p, const ScanArgs& a, hipStream_t s) {
 
 template <bool BF16, int DISC>
 hipError_t dispatch(const Plan& p, const ScanArgs& a, hipStream_t s) {
-    return a.softplus ? dispatch_n<BF16, DISC, true>(p, a, s) : dispatch_n<BF16, DISC, false>(p, a, s);
+    if (a.N != p.ns)  // d_state padded up to the variant's states
+        return a.softplus ? dispatch_n<BF16, DISC, true, true>(p, a, s)
+                          : dispatch_n<BF16, DISC, false, true>(p, a, s);
+    return a.softplus ? dispatch_n<BF16, DISC, true, false>(p, a, s)
+                      : dispatch_n<BF16, DISC, false, false>(p, a, s);
 }
 
 template <bool BF16>
