@@ -73,8 +73,12 @@ def test_validation_statuses_host_only():
 
 def test_workspace_size_function():
     lib = ms.load()
-    # Generic kernels (odd d_state) over one piece need no workspace.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(64, 256, 4096, 17, 1)), 1) == 0
+    # Generic kernels (d_state 65-127) over one piece need no workspace.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(64, 256, 4096, 100, 1)), 1) == 0
+    # A d_state without a lane kernel of its own (17) runs padded on one: its
+    # segment summaries keep the true d_state, N + 1 floats per boundary.
+    n17 = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 17, 1)), 1)
+    assert n17 > 0 and n17 % (8 * 1536 * 18 * 4) < 1024
     # Invalid dims -> (size_t)-1.
     bad = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 0, 64, 16, 1)), 1)
     assert bad == ctypes.c_size_t(-1).value
