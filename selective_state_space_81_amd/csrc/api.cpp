@@ -125,7 +125,10 @@ bool lane_plan(const ms_dims& d, int disc, msscan::Plan& p) {
 }
 
 bool tile_plan(const ms_dims& d, msscan::Plan& p) {
-    const int N = d.d_state;
+    // d_state 33-64 (the lane kernels take ZOH and bilinear up to 32) and
+    // 65-128 run on the 64- and 128-state tile kernels, the extra states
+    // padded out (zero A, B and C; never stored).
+    const int N = d.d_state <= 64 ? (d.d_state > 32 ? 64 : d.d_state) : 128;
     int waves = kTileWaves;
     if (N % waves) return false;
     int ns = N / waves;
@@ -155,7 +158,8 @@ msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
         }
         // tile path: fp32 copy of B and C, rows [b][t][B_t | C_t], read as DPP
         // operands (the lane path reads B and C in place).
-        if (p.tile_path == 1) p.bc_floats = (size_t)d.batch * (size_t)d.seqlen * 2 * (size_t)N;
+        if (p.tile_path == 1)  // B/C rows as wide as the tile kernels' states
+            p.bc_floats = (size_t)d.batch * (size_t)d.seqlen * 2 * (size_t)(p.ns * p.waves);
         return p;
     }
     p.tile_path = 0;

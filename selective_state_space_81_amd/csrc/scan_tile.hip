@@ -72,11 +72,15 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     const int dd = dvalid ? d : a.Dn - 1;
     const int n0 = w * NS;
 
+    // The true d_state Nr may be below N: states Nr..N-1 get A = 0 and, in
+    // the prepared B/C rows, B = C = 0, so they stay zero; they are never
+    // stored, and every stride outside the prepared rows uses Nr.
+    const int Nr = a.N;
     float A2[NS], invA[NS], h[NS], P[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         P[j] = 1.f;
-        const float av = a.A[(int64_t)dd * N + n0 + j];
+        const float av = n0 + j < Nr ? a.A[(int64_t)dd * Nr + n0 + j] : 0.f;
         A2[j] = av * kLog2e;
         if constexpr (ZOH) invA[j] = (av != 0.f) ? 1.f / av : 0.f;
     }
@@ -85,10 +89,12 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     for (int j = 0; j < NS; ++j) {
         float v = 0.f;
         if constexpr (!SUMMARY) {
-            if (seg == 0) {
-                if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * N + n0 + j];
-            } else {
-                v = a.agg[(((int64_t)b * km1 + (seg - 1)) * N + n0 + j) * a.Dn + dd];
+            if (n0 + j < Nr) {
+                if (seg == 0) {
+                    if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * Nr + n0 + j];
+                } else {
+                    v = a.agg[(((int64_t)b * km1 + (seg - 1)) * Nr + n0 + j) * a.Dn + dd];
+                }
             }
         }
         h[j] = v;
@@ -255,36 +261,41 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
     if constexpr (SUMMARY) {
         const int64_t base = (int64_t)b * km1 + seg;
 #pragma unroll
-        for (int j = 0; j < NS; ++j) a.agg[(base * N + n0 + j) * a.Dn + d] = h[j];
+        for (int j = 0; j < NS; ++j)
+            if (n0 + j < Nr) a.agg[(base * Nr + n0 + j) * a.Dn + d] = h[j];
         if constexpr (PROD) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) a.prod[(base * N + n0 + j) * a.Dn + d] = P[j];
+            for (int j = 0; j < NS; ++j)
+                if (n0 + j < Nr) a.prod[(base * Nr + n0 + j) * a.Dn + d] = P[j];
         } else {
             if (w == 0) a.sdt[base * a.Dn + d] = s_sum;
         }
     } else {
         if (seg == a.chunks - 1 && a.h_last) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) a.h_last[((int64_t)b * a.Dn + d) * N + n0 + j] = h[j];
+            for (int j = 0; j < NS; ++j)
+                if (n0 + j < Nr) a.h_last[((int64_t)b * a.Dn + d) * Nr + n0 + j] = h[j];
         }
     }
 }
 
-// Widen B and C to fp32 rows [b][t][B_t row | C_t row] for the DPP delivery.
+// Widen B and C to fp32 rows [b][t][B_t row | C_t row] for the DPP delivery,
+// each row np wide (np = the kernel's states; entries past d_state are 0).
 // One thread per output float: reads and writes are both contiguous.
 template <bool BF16>
-__global__ void __launch_bounds__(256) bc_prepare(ScanArgs a) {
+__global__ void __launch_bounds__(256) bc_prepare(ScanArgs a, int np) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t row = i / (2 * a.N);
+    const int64_t row = i / (2 * np);
     if (row >= (int64_t)a.batch * a.L) return;
-    const int k = (int)(i - row * 2 * a.N);
-    a.bcw[i] = k < a.N ? ld<BF16>(a.B, row * a.N + k) : ld<BF16>(a.C, row * a.N + k - a.N);
+    const int k = (int)(i - row * 2 * np);
+    const int n = k < np ? k : k - np;
+    a.bcw[i] = n >= a.N ? 0.f : k < np ? ld<BF16>(a.B, row * a.N + n) : ld<BF16>(a.C, row * a.N + n);
 }
 
 template <int NS, int S, int TB, bool BF16, int DISC>
 hipError_t launch_tiles(const Plan& p, const ScanArgs& a, hipStream_t s) {
     const dim3 block(64 * S);
-    hipError_t e = launch_bc_prepare(a, BF16, s);
+    hipError_t e = launch_bc_prepare(a, NS * S, BF16, s);
     if (e != hipSuccess) return e;
     if (p.chunks > 1) {
         {
@@ -329,14 +340,14 @@ hipError_t dispatch_io(const Plan& p, const ScanArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bc_prepare(const ScanArgs& a, bool bf16, hipStream_t s) {
-    const int64_t total = (int64_t)a.batch * a.L * 2 * a.N;
+hipError_t launch_bc_prepare(const ScanArgs& a, int np, bool bf16, hipStream_t s) {
+    const int64_t total = (int64_t)a.batch * a.L * 2 * np;
     const dim3 grid((unsigned)((total + 255) / 256));
     ProfScope ps(s, kPhasePrep);
     if (bf16)
-        hipLaunchKernelGGL((bc_prepare<true>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bc_prepare<true>), grid, dim3(256), 0, s, a, np);
     else
-        hipLaunchKernelGGL((bc_prepare<false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bc_prepare<false>), grid, dim3(256), 0, s, a, np);
     return hipGetLastError();
 }
 

@@ -73,8 +73,10 @@ def test_validation_statuses_host_only():
 
 def test_workspace_size_function():
     lib = ms.load()
-    # Generic kernels (d_state 65-127) over one piece need no workspace.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(64, 256, 4096, 100, 1)), 1) == 0
+    # d_state 100 runs padded on the 128-state tile kernels; over one piece its
+    # workspace is just their staged fp32 B/C rows, 128 states wide.
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(64, 256, 4096, 100, 1)), 1) == \
+        64 * 256 * 2 * 128 * 4
     # A d_state without a lane kernel of its own (17) runs padded on one: its
     # segment summaries keep the true d_state, N + 1 floats per boundary.
     n17 = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 17, 1)), 1)
