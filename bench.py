@@ -44,8 +44,8 @@ HBM_PEAK_GBPS = 8000.0
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 COPY_MIB = 256  # size of the calibration copy (read and written)
 # the pass that writes y: scan_lane with SUMMARY (its 7th argument) false,
-# scan_tile with SUMMARY (its last) false, or the generic scan_chunks
-MAIN_KERNEL_RE = r"scan_lane<(?:[^,>]*, ){6}false[,>]|scan_tile<[^>]*false>|scan_chunks<"
+# or scan_tile with SUMMARY (its last) false
+MAIN_KERNEL_RE = r"scan_lane<(?:[^,>]*, ){6}false[,>]|scan_tile<[^>]*false>"
 WORKLOAD_TITLE = {"m130m": "Mamba-130M-layer selective scan (S6) forward",
                   "m3b": "Mamba-3B-layer selective scan (S6) forward",
                   "long": "long-context selective scan (S6) forward, d_state 64"}
@@ -491,7 +491,7 @@ def _csv(dirname, suffix):
 
 
 def _short(name):
-    m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|scan_chunks<[^>]*>|scan_summary<[^>]*>|"
+    m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|"
                   r"bc_prepare<[^>]*>|carry_chain<[^>]*>|state_step<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
                   r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|"
                   r"reduce_param_groups|reduce_params|"

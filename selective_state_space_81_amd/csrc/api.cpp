@@ -28,10 +28,6 @@ bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 1
 
 constexpr int kMaxState = 128;
 constexpr int64_t kMaxLen = 0x7fffffffLL;
-// Target number of waves for one call.  The chip has 256 CUs x 4 SIMDs; a
-// few waves per SIMD hide memory latency.  Below this the sequence is cut.
-constexpr int64_t kGenericTargetWaves = 2048;  // generic kernels (any d_state)
-constexpr int64_t kMinChunk = 64;  // never cut pieces shorter than this
 
 ms_status check_dims(const ms_dims* d) {
     if (!d) return fail(MS_ERR_NULL, "dims is NULL");
@@ -81,9 +77,6 @@ int disc_of(uint32_t flags) {
 #ifndef MSSCAN_TARGET_WAVES
 #define MSSCAN_TARGET_WAVES 16384
 #endif
-#ifndef MSSCAN_LANE_PATH
-#define MSSCAN_LANE_PATH 1
-#endif
 constexpr int kTileWaves = MSSCAN_TILE_WAVES;
 constexpr int64_t kTargetWaves = MSSCAN_TARGET_WAVES;
 constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
@@ -104,11 +97,10 @@ void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) 
 }
 
 bool lane_plan(const ms_dims& d, int disc, msscan::Plan& p) {
-    if (!MSSCAN_LANE_PATH) return false;
     // The smallest lane variant that holds d_state.  Other sizes run on it
     // with the extra states padded out (zero A, B and C; never stored): at up
-    // to 8x the state work (d_state 1) it still beat the generic kernels by
-    // 2.5-6x at every size measured (1 to 48).
+    // to 8x the state work (d_state 1) it beat the generic kernels it replaced
+    // by 2.5-6x at every size measured (1 to 48).
     int ns = 0;
     for (const int c : {8, 16, 32, 64})
         if (c >= d.d_state && msscan::lane_variant_exists(c, disc)) {
@@ -162,29 +154,7 @@ msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
             p.bc_floats = (size_t)d.batch * (size_t)d.seqlen * 2 * (size_t)(p.ns * p.waves);
         return p;
     }
-    p.tile_path = 0;
-    if (N <= 4) p.ns = 4;
-    else if (N <= 8) p.ns = 8;
-    else if (N <= 16) p.ns = 16;
-    else p.ns = 32;
-    p.waves = (N + p.ns - 1) / p.ns;
-    p.tiles = (d.d_inner + 63) / 64;
-    const int64_t per_chunk = (int64_t)d.batch * p.tiles * p.waves;
-    int64_t k = (kGenericTargetWaves + per_chunk - 1) / per_chunk;
-    const int64_t kmax = (d.seqlen + kMinChunk - 1) / kMinChunk;
-    if (k > kmax) k = kmax;
-    if (k < 1) k = 1;
-    int64_t len = (d.seqlen + k - 1) / k;
-    len = (len + 15) / 16 * 16;  // whole LDS exchange blocks
-    if (len > d.seqlen) len = d.seqlen;
-    p.chunk_len = len;
-    p.chunks = (int)((d.seqlen + len - 1) / len);
-    if (p.chunks > 1) {
-        const size_t km1 = (size_t)(p.chunks - 1);
-        p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * per_channel;
-    } else {
-        p.ws_floats = 0;
-    }
+    p.tile_path = -1;  // no kernel takes it (not reached for d_state 1..128)
     return p;
 }
 
@@ -240,6 +210,7 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
     for (const void* p : ptrs)
         if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
     const msscan::Plan p = make_plan(*dims, flags);
+    if (p.tile_path < 0) return fail(MS_ERR_UNSUPPORTED, "no scan kernel for d_state %d", dims->d_state);
     const size_t need = ws_bytes(p);
     if (need && (!workspace || workspace_bytes < need))
         return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -270,9 +241,8 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
     const int disc = disc_of(flags);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     msscan::prof_call();
-    hipError_t e = p.tile_path == 2   ? msscan::launch_scan_lanes(p, a, bf16, disc, hs)
-                   : p.tile_path == 1 ? msscan::launch_scan_tiles(p, a, bf16, disc, hs)
-                                      : msscan::launch_scan(p, a, bf16, disc, hs);
+    hipError_t e = p.tile_path == 2 ? msscan::launch_scan_lanes(p, a, bf16, disc, hs)
+                                    : msscan::launch_scan_tiles(p, a, bf16, disc, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }
@@ -385,7 +355,7 @@ BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
     q.pparam = B * (size_t)((q.K + msscan::kBwdWaves - 1) / msscan::kBwdWaves) * D * (N + 2);
     q.pgroup = (size_t)msscan::kParamGroups * D * (N + 2);
     msscan::Plan& p = q.fwd;
-    p.tile_path = 0;
+    p.tile_path = 2;  // the backward's own segment plan (its kernels read ns)
     p.ns = d.d_state <= 4 ? 4 : (d.d_state <= 8 ? 8 : 16);
     p.waves = 1;
     p.tiles = (int)q.tiles;

@@ -16,7 +16,7 @@ namespace msscan {
 // computed by a separate pass (chunk summaries + carry propagation).
 struct Plan {
     int tile_path;      // 2: scan_lane kernels (all states in a lane);
-                        // 1: scan_tile kernels (waves split d_state); 0: generic
+                        // 1: scan_tile kernels (waves split d_state); -1: none
     int ns;             // states per lane (compile-time variant)
     int waves;          // waves per workgroup = ceil(d_state / ns)
     int chunks;         // pieces along L
@@ -86,7 +86,6 @@ struct StepArgs {
 
 // Each returns hipSuccess or the first launch error.
 // disc: 0 Euler, 1 zero-order hold, 2 bilinear (kEuler / kZoh / kBilinear).
-hipError_t launch_scan(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 hipError_t launch_scan_tiles(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 // Segment carries: val[b][i][n][d] holds segment i's summary (state reached
 // from zero); its decay is exp(A[d][n] * sdt[b][i][d]) or prod[b][i][n][d].

@@ -29,7 +29,7 @@
 //
 // With several segments, a summary variant of the same kernel (no readout,
 // SUMMARY = true) computes each segment's end state from zero and its
-// compensated sum of dt; the generic carry pass composes them in order (the
+// compensated sum of dt; the shared carry pass composes them in order (the
 // scan is a composition of affine maps, jsqmd page section 3.4) and the main
 // variant starts every segment from its true state.
 #include <hip/hip_runtime.h>

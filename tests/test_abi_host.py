@@ -109,7 +109,8 @@ def test_workspace_size_function():
     assert lib.ms_scan_workspace_bytes(ctypes.byref(d16), 1 | 4) > \
         lib.ms_scan_workspace_bytes(ctypes.byref(d16), 1)
     assert lib.ms_scan_workspace_bytes(ctypes.byref(d16), 2 | 4) == ctypes.c_size_t(-1).value
-    # Odd d_state takes the generic kernels, which also size their workspace.
+    # A long sequence at an odd d_state (padded onto a lane kernel) is cut
+    # into segments and needs their summaries.
     assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 65536, 256, 17, 1)), 1) > 0
 
 
