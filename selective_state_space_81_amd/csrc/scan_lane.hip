@@ -1,5 +1,7 @@
 // scan_lane.hip -- selective scan (S6) kernel with every state of a channel
-// in one lane, for d_state 8, 16 and 32 (64 with the Euler form) on gfx950.
+// in one lane, for d_state 8, 16 and 32 (64 with the Euler form) on gfx950;
+// with PAD, any smaller d_state on the next of these sizes (the extra states
+// get A = B = C = 0, stay zero and are never stored).
 //
 // A workgroup is a single wave: lane = one channel of a 64-channel tile, and
 // the lane keeps all N states of its channel in VGPRs.  The wave walks one
