@@ -321,9 +321,9 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
     const bool bf16 = io == MS_BF16;
     const int disc = disc_of(flags);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    hipError_t e = msscan::step_quads_supported(batch, d_inner, d_state)
-                       ? msscan::launch_step_quads(a, bf16, disc, hs)
-                       : msscan::launch_step(a, bf16, disc, hs);
+    if (!msscan::step_quads_supported(batch, d_inner, d_state))
+        return fail(MS_ERR_UNSUPPORTED, "d_inner %d too large for the decode step", d_inner);
+    hipError_t e = msscan::launch_step_quads(a, bf16, disc, hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

@@ -77,9 +77,15 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-template <int G, int BR, bool BF16, int DISC>
+// PAD: the true d_state Nr = a.N is below 4 G (G the next power of two of
+// its quads).  States past Nr load as 0 (A, B, C and h), so they stay 0 and
+// add nothing to the readout; they are never stored.  When Nr is a multiple
+// of 4, rows stay 16-byte aligned and a quad is wholly in or out, so quads
+// move as vectors; otherwise states move one float at a time.
+template <int G, int BR, bool BF16, int DISC, bool PAD = false>
 __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
-    constexpr int N = 4 * G;
+    constexpr int NG = 4 * G;
+    const int N = PAD ? a.N : NG;
     const int quads = a.Dn * G;
     const int qi = blockIdx.x * blockDim.x + threadIdx.x;
     // Quads past the row's end are clamped to its last quad (so every
@@ -93,7 +99,18 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
 
     // Every load is issued here, before any arithmetic, so that a wave waits
     // on memory once.
-    const float4 av = *reinterpret_cast<const float4*>(a.A + (int64_t)d * N + n0);
+    auto ld4s = [&](auto ld1) __attribute__((always_inline)) {  // the quad's 4 states, past N read as 0
+        return make_float4(n0 < N ? ld1(n0) : 0.f, n0 + 1 < N ? ld1(n0 + 1) : 0.f,
+                           n0 + 2 < N ? ld1(n0 + 2) : 0.f, n0 + 3 < N ? ld1(n0 + 3) : 0.f);
+    };
+    const bool vec = !PAD || (N & 3) == 0;  // whole quads, 16-byte aligned rows
+    const bool qin = n0 < N;                // (for vec) this quad holds states
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 av = zero4;
+    if (!vec)
+        av = ld4s([&](int n) __attribute__((always_inline)) { return a.A[(int64_t)d * N + n]; });
+    else if (qin)
+        av = *reinterpret_cast<const float4*>(a.A + (int64_t)d * N + n0);
     const float bias = a.bias ? a.bias[d] : 0.f;
     const float Dd = a.D ? a.D[d] : 0.f;
     float4 hv[BR], bv[BR], cv[BR];
@@ -102,9 +119,18 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
     for (int r = 0; r < BR; ++r) {
         const int b = min(b0 + r, a.batch - 1);
         const int64_t e = (int64_t)b * a.Dn + d;
-        hv[r] = load_state(a.h + e * N + n0);
-        bv[r] = ld4<BF16>(a.B, (int64_t)b * N + n0);
-        cv[r] = ld4<BF16>(a.C, (int64_t)b * N + n0);
+        hv[r] = bv[r] = cv[r] = zero4;
+        if (vec) {
+            if (qin) {
+                hv[r] = load_state(a.h + e * N + n0);
+                bv[r] = ld4<BF16>(a.B, (int64_t)b * N + n0);
+                cv[r] = ld4<BF16>(a.C, (int64_t)b * N + n0);
+            }
+        } else {
+            hv[r] = ld4s([&](int n) __attribute__((always_inline)) { return a.h[e * N + n]; });
+            bv[r] = ld4s([&](int n) __attribute__((always_inline)) { return ld<BF16>(a.B, (int64_t)b * N + n); });
+            cv[r] = ld4s([&](int n) __attribute__((always_inline)) { return ld<BF16>(a.C, (int64_t)b * N + n); });
+        }
         if constexpr (G >= 4) {
             // x, delta and z of the channel: each lane of a quad (its j mod 4)
             // loads one of them, and the quad shares them below -- one load
@@ -165,7 +191,13 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
         const int b = b0 + r;
         if (!qvalid || b >= a.batch) continue;
         const int64_t e = (int64_t)b * a.Dn + d;
-        store_state(a.h + e * N + n0, hs);
+        if (vec) {
+            if (qin) store_state(a.h + e * N + n0, hs);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (n0 + k < N) a.h[e * N + n0 + k] = hs[k];
+        }
         if (j == 0) {
             y = fmaf(Dd, xv[r], y);
             if (a.z) y *= silu_f(zv[r]);
@@ -174,30 +206,37 @@ __global__ void __launch_bounds__(256) step_quads(StepArgs a) {
     }
 }
 
-template <int BR, bool BF16, int DISC>
+// G: the next power of two of the d_state's quads; PAD when it holds more.
+inline int quad_groups(int n) {
+    int g = 1;
+    while (4 * g < n) g *= 2;
+    return g;
+}
+
+template <int BR, bool BF16, int DISC, bool PAD>
 hipError_t launch_g(const StepArgs& a, hipStream_t s) {
-    const int G = a.N / 4;
+    const int G = quad_groups(a.N);
     const int64_t quads = (int64_t)a.Dn * G;
     const dim3 grid((unsigned)((quads + 255) / 256), (unsigned)((a.batch + BR - 1) / BR)),
         block(256);
     switch (G) {
-        case 1: hipLaunchKernelGGL((step_quads<1, BR, BF16, DISC>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((step_quads<2, BR, BF16, DISC>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((step_quads<4, BR, BF16, DISC>), grid, block, 0, s, a); break;
-        case 8: hipLaunchKernelGGL((step_quads<8, BR, BF16, DISC>), grid, block, 0, s, a); break;
-        case 16: hipLaunchKernelGGL((step_quads<16, BR, BF16, DISC>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((step_quads<32, BR, BF16, DISC>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((step_quads<1, BR, BF16, DISC, PAD>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((step_quads<2, BR, BF16, DISC, PAD>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((step_quads<4, BR, BF16, DISC, PAD>), grid, block, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((step_quads<8, BR, BF16, DISC, PAD>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((step_quads<16, BR, BF16, DISC, PAD>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((step_quads<32, BR, BF16, DISC, PAD>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, bool PAD>
 hipError_t launch_p(const StepArgs& a, int disc, hipStream_t s) {
     switch (disc) {
-        case kEuler: return launch_g<MSSCAN_STEP_ROWS, BF16, kEuler>(a, s);
-        case kZoh: return launch_g<MSSCAN_STEP_ROWS, BF16, kZoh>(a, s);
-        case kBilinear: return launch_g<MSSCAN_STEP_ROWS, BF16, kBilinear>(a, s);
+        case kEuler: return launch_g<MSSCAN_STEP_ROWS, BF16, kEuler, PAD>(a, s);
+        case kZoh: return launch_g<MSSCAN_STEP_ROWS, BF16, kZoh, PAD>(a, s);
+        case kBilinear: return launch_g<MSSCAN_STEP_ROWS, BF16, kBilinear, PAD>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -206,14 +245,16 @@ hipError_t launch_p(const StepArgs& a, int disc, hipStream_t s) {
 
 bool step_quads_supported(int batch, int d_inner, int n) {
     (void)batch;  // batch rows go to grid.y (<= 65535, checked by the caller)
-    if (n % 4 != 0 || n < 4 || n > 128 || ((n / 4) & (n / 4 - 1)) != 0) return false;
-    return (int64_t)d_inner * (n / 4) < (1LL << 30);  // quad index of a row fits int
+    if (n < 1 || n > 128) return false;
+    return (int64_t)d_inner * quad_groups(n) < (1LL << 30);  // quad index of a row fits int
 }
 
 hipError_t launch_step_quads(const StepArgs& a, bool bf16, int disc, hipStream_t s) {
     if (!step_quads_supported(a.batch, a.Dn, a.N)) return hipErrorInvalidValue;
     ProfScope ps(s, kPhaseStep);
-    return bf16 ? launch_p<true>(a, disc, s) : launch_p<false>(a, disc, s);
+    const bool pad = 4 * quad_groups(a.N) != a.N;
+    if (pad) return bf16 ? launch_p<true, true>(a, disc, s) : launch_p<false, true>(a, disc, s);
+    return bf16 ? launch_p<true, false>(a, disc, s) : launch_p<false, false>(a, disc, s);
 }
 
 }  // namespace msscan

@@ -113,7 +113,6 @@ hipError_t launch_scan_lanes_dtproj(const Plan& p, const ScanArgs& a, bool bf16,
                                     hipStream_t s);
 bool dtproj_variant_exists(int n);
 hipError_t launch_bc_prepare(const ScanArgs& a, int np, bool bf16, hipStream_t s);  // rows np wide
-hipError_t launch_step(const StepArgs& a, bool bf16, int disc, hipStream_t s);
 // Causal depthwise conv1d (+ silu), width 1..8.
 hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s);
 // Decode step with 4 states per lane (d_state in {4, 8, ..., 128}).

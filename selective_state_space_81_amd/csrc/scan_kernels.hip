@@ -1,6 +1,5 @@
-// scan_kernels.hip -- the pieces every scan path shares, for gfx950: the
-// carry pass that composes segment summaries, and the one-step decode
-// fallback for d_state without a quad kernel.
+// scan_kernels.hip -- the carry pass every scan path shares, for gfx950: it
+// composes the segment summaries in order.
 //
 // The scan is a composition of affine maps h -> a*h + b (jsqmd page section
 // 3.4), so a segment of the sequence is summarised by (a, b) = (exp(A * sum
@@ -73,48 +72,6 @@ __global__ void __launch_bounds__(256) carry_chain(CarryArgs c) {
     }
 }
 
-// ---- decode step ---------------------------------------------------------------
-// One thread per (b, d): the channel's N-state row (contiguous in h) is read,
-// advanced one step and written back; B_t, C_t are uniform over the block's
-// channels (one batch row per block).
-template <bool BF16, int DISC>
-__global__ void __launch_bounds__(256) state_step(StepArgs a) {
-    const int d = blockIdx.x * blockDim.x + threadIdx.x;
-    const int b = blockIdx.y;
-    if (d >= a.Dn) return;
-    const int64_t e = (int64_t)b * a.Dn + d;
-    const float xv = ld<BF16>(a.x, e);
-    const float dt = step_size(ld<BF16>(a.delta, e), a.bias ? a.bias[d] : 0.f, a.softplus);
-    const float dx = dt * xv;
-    float* hrow = a.h + e * a.N;
-    const float* arow = a.A + (int64_t)d * a.N;
-    const int64_t brow = (int64_t)b * a.N;
-    float y = 0.f;
-    for (int n = 0; n < a.N; ++n) {
-        const float an = arow[n];
-        const float arg = dt * (an * kLog2e);
-        const float bn = ld<BF16>(a.B, brow + n);
-        float abar, bx;
-        if constexpr (DISC == kBilinear) {
-            const float r = bilinear_r(arg);
-            abar = fmaf(2.f, r, -1.f);
-            bx = (dx * r) * bn;
-        } else {
-            abar = hw_exp2(arg);
-            if constexpr (DISC == kZoh)
-                bx = zoh_factor(dt, arg, abar, an != 0.f ? 1.f / an : 0.f) * (bn * xv);
-            else
-                bx = dx * bn;
-        }
-        const float hn = fmaf(abar, hrow[n], bx);
-        hrow[n] = hn;
-        y = fmaf(ld<BF16>(a.C, brow + n), hn, y);
-    }
-    y = fmaf(a.D ? a.D[d] : 0.f, xv, y);
-    if (a.z) y *= silu_f(ld<BF16>(a.z, e));
-    st<BF16>(a.y, e, y);
-}
-
 }  // namespace
 
 hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s) {
@@ -141,24 +98,6 @@ hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
     c.N = a.N;
     c.Dn = a.Dn;
     return launch_carry(c, false, s);
-}
-
-hipError_t launch_step(const StepArgs& a, bool bf16, int disc, hipStream_t s) {
-    const dim3 grid((a.Dn + 255) / 256, a.batch), block(256);
-    ProfScope ps(s, kPhaseStep);
-#define MS_STEP_(DI)                                                           \
-    if (bf16)                                                                  \
-        hipLaunchKernelGGL((state_step<true, DI>), grid, block, 0, s, a);      \
-    else                                                                       \
-        hipLaunchKernelGGL((state_step<false, DI>), grid, block, 0, s, a);
-    switch (disc) {
-        case kEuler: MS_STEP_(kEuler) break;
-        case kZoh: MS_STEP_(kZoh) break;
-        case kBilinear: MS_STEP_(kBilinear) break;
-        default: return hipErrorInvalidValue;
-    }
-#undef MS_STEP_
-    return hipGetLastError();
 }
 
 }  // namespace msscan

@@ -42,7 +42,8 @@ def test_decode_workload_every_step(gpu, disc):
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (3, 70, 7), (2, 64, 16), (5, 300, 64),
                                    (2, 33, 128), (1, 5, 4), (3, 37, 8), (2, 19, 32),
-                                   (1, 3, 12)], ids=lambda s: "B{}D{}N{}".format(*s))
+                                   (1, 3, 12), (2, 70, 100), (1, 40, 17), (2, 65, 24)],
+                         ids=lambda s: "B{}D{}N{}".format(*s))
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_decode_edge_shapes(gpu, shape, io):
     batch, Dn, N = shape
