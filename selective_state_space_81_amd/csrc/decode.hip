@@ -1,5 +1,5 @@
-// decode.hip -- one recurrent decode step (ms_state_update) for d_state a
-// multiple of 4, up to 128.
+// decode.hip -- one recurrent decode step (ms_state_update), any d_state up
+// to 128 (4 * 2^k exactly, other sizes padded up to the next such).
 //
 // The step is one timestep of the scan with the state kept in HBM between
 // calls (lmnt.cn page, section 5.3; the state cache of the jsqmd page,
