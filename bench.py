@@ -492,7 +492,7 @@ def _csv(dirname, suffix):
 
 def _short(name):
     m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|"
-                  r"bc_prepare<[^>]*>|carry_chain<[^>]*>|state_step<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
+                  r"bc_prepare<[^>]*>|carry_chain<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
                   r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|"
                   r"reduce_param_groups|reduce_params|"
                   r"neg_kernel)", name)
@@ -538,7 +538,7 @@ def rocprof_summary(args):
         main = None
         for k in sorted(fetch):
             if k == "neg_kernel" or k not in write or not re.search(
-                    r"scan_|carry_|bc_prep|state_step|step_quads|conv1d_kernel|bwd_main|"
+                    r"scan_|carry_|bc_prep|step_quads|conv1d_kernel|bwd_main|"
                     r"seg_summaries|reduce_", k):
                 continue
             mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
@@ -552,7 +552,7 @@ def rocprof_summary(args):
         acc = {}
         for r in _csv(dirname, "counter_collection.csv"):
             k = _short(r["Kernel_Name"])
-            if not re.search(r"scan_|carry_|bc_prep|state_step|step_quads", k):
+            if not re.search(r"scan_|carry_|bc_prep|step_quads", k):
                 continue
             acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
