@@ -22,13 +22,15 @@
 //   2. carry_chain<false> composes the forward ones into every segment's
 //      starting state, carry_chain<true> the adjoint ones (last segment first)
 //      into the mu entering each segment from the right;
-//   3. bwd_main: per segment, the forward states are recomputed from its
+//   3. bwd_main (one wave per segment, kBwdWaves consecutive segments of
+//      one 64-channel tile per workgroup): the forward states are recomputed from its
 //      starting state (the start and the state half way kept in registers,
 //      each sub-block's states recomputed from them), and the adjoint runs
 //      back over the segment producing every gradient.  The
 //      per-step sums over channels of dB and dC are reduced across the wave
-//      through LDS and stored per 64-channel tile; the sums over time and batch
-//      of dA, dD and dbias are stored per segment;
+//      through LDS and stored per 64-channel tile; the sums over time of dA,
+//      dD and dbias are added over the workgroup's segments in LDS and
+//      stored per workgroup;
 //   4. small passes add those partials in a fixed order.
 // No pass waits on another workgroup: the results are deterministic.
 #include <hip/hip_runtime.h>
