@@ -60,6 +60,8 @@ EDGE = [
     (1, 333, 64, 33, "f32"),
     (2, 2500, 64, 64, "bf16"),
     (1, 260, 40, 100, "f32"),
+    (2, 300, 70, 80, "bf16"),   # bf16 rows padded to the 128-state tile
+    (1, 350, 64, 40, "bf16"),   # bf16, padded to 64 states (lane or tile)
     (1, 1100, 128, 128, "bf16"),
 ]
 
