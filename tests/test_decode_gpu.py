@@ -61,10 +61,12 @@ def test_decode_edge_shapes(gpu, shape, io):
             assert_within(h, href, "f32", f"h step {t}")
 
 
+@pytest.mark.parametrize("N", [16, 40, 100])
 @pytest.mark.parametrize("disc", DISCS)
-def test_steps_equal_scan(gpu, disc):
-    """L decode steps from h0 reproduce one scan over the same L tokens."""
-    batch, L, Dn, N = 2, 40, 96, 16
+def test_steps_equal_scan(gpu, disc, N):
+    """L decode steps from h0 reproduce one scan over the same L tokens (at
+    d_state 40 and 100 both paths run padded, each in its own way)."""
+    batch, L, Dn = 2, 40, 96
     w = synth.workload("tiny", batch=batch, L=L, Dn=Dn, N=N)
     x = synth.scan_inputs(w, device=DEV, seed=9)
     h0 = torch.randn(batch, Dn, N, device=DEV)
