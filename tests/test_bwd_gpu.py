@@ -83,6 +83,7 @@ SHAPES = [
     (1, 100, 64, 8, "bf16"),
     (2, 257, 130, 16, "bf16"),
     (1, 48, 33, 5, "f32"),     # d_state 5: masked states
+    (2, 90, 70, 12, "bf16"),   # d_state 12 with bf16 io: staged B/C rows padded to 16
     (3, 16, 64, 1, "f32"),
 ]
 
