@@ -360,7 +360,7 @@ def measure_dtproj(ms, rank=16, reps=20):
         x.update(synth.dtproj_inputs(w, rank, device="cuda", seed=i))
         sets.append((x, torch.empty_like(base["u"])))
     io = ms.MS_BF16 if w.io == "bf16" else ms.MS_F32
-    ws = torch.empty(max(1, ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, io,
+    ws = torch.empty(max(1, ms.dtproj_workspace_bytes(w.batch, w.L, w.Dn, w.N, io,
                                                ms.flags(w.softplus))),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()

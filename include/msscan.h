@@ -109,7 +109,10 @@ size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags);
  *                                identical to a zero bias).
  *   h0                         : optional initial state (NULL = zeros).
  *   h_last                     : optional; receives the state after step L-1.
- *                                h_last may equal h0 (h0 is read first).
+ *                                h_last may equal h0: when the sequence is cut
+ *                                into segments, the carry pass copies h0 into the
+ *                                workspace before the pass that writes h_last,
+ *                                and the first segment starts from that copy.
  *   workspace, workspace_bytes : device scratch of at least
  *                                ms_scan_workspace_bytes(dims, flags) bytes,
  *                                16-byte aligned; may be NULL when that is 0.
@@ -143,12 +146,14 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
  *   W_dt   : [d_inner][dt_rank] io dtype          (required; the layout of a
  *            linear layer's weight, out x in)
  *   dt_rank: 1 .. 64
- *   all other arguments as for ms_scan_fwd (the workspace is
- *   ms_scan_workspace_bytes(dims, flags) bytes).
+ *   all other arguments as for ms_scan_fwd, except the workspace: at least
+ *   ms_scan_dtproj_workspace_bytes(dims, flags) bytes (this call runs on
+ *   kernels of its own, whose plan may need more than ms_scan_fwd's).
  *
  * Statuses as for ms_scan_fwd; MS_ERR_SHAPE for dt_rank outside 1..64;
  * MS_ERR_UNSUPPORTED for d_state other than 8 or 16.  Deterministic.
  */
+size_t ms_scan_dtproj_workspace_bytes(const ms_dims* dims, uint32_t flags);
 ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt,
                              int32_t dt_rank, const float* A, const void* B, const void* C,
                              const float* D, const void* z, const float* delta_bias,

@@ -29,7 +29,7 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
            "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end",
            "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd",
-           "ms_scan_fwd_dtproj")
+           "ms_scan_fwd_dtproj", "ms_scan_dtproj_workspace_bytes")
 
 PHASES = ("prep", "summary", "carry", "main", "step", "conv")  # ms_phase order
 
@@ -78,6 +78,8 @@ def load(path: Optional[str] = None):
     lib.ms_scan_fwd.restype = ctypes.c_int
     lib.ms_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
                                 ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
+    lib.ms_scan_dtproj_workspace_bytes.restype = ctypes.c_size_t
+    lib.ms_scan_dtproj_workspace_bytes.argtypes = [ctypes.POINTER(MsDims), u32]
     lib.ms_scan_fwd_dtproj.restype = ctypes.c_int
     lib.ms_scan_fwd_dtproj.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
                                        ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
@@ -195,6 +197,16 @@ def workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int, io: int
     return int(n)
 
 
+def dtproj_workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int, io: int,
+                           flag_bits: int = MS_SOFTPLUS) -> int:
+    """ms_scan_dtproj_workspace_bytes: workspace of ms_scan_fwd_dtproj."""
+    d = dims(batch, seqlen, d_inner, d_state, io)
+    n = load().ms_scan_dtproj_workspace_bytes(ctypes.byref(d), flag_bits)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsError(2, "invalid dims")
+    return int(n)
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=True, zoh=False,
              y=None, h0=None, h_last=None, workspace=None, stream=None, bilinear=False):
     """ms_scan_fwd on torch device tensors.  Allocates y (and the workspace)
@@ -235,7 +247,7 @@ def scan_fwd_dtproj(u, dt_low, W_dt, A, B, C, D=None, z=None, delta_bias=None, *
     fl = flags(softplus, zoh, bilinear)
     if y is None:
         y = torch.empty_like(u)
-    ws_n = workspace_bytes(batch, L, Dn, N, io, fl)
+    ws_n = dtproj_workspace_bytes(batch, L, Dn, N, io, fl)
     if workspace is None and ws_n:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=u.device)
     ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -85,15 +85,38 @@ constexpr int64_t kSegmentQuantum = 16;  // whole register blocks of timesteps
 #endif
 constexpr int64_t kMinSegment = MSSCAN_MIN_SEGMENT;
 
-void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p) {
-    int64_t k = (kTargetWaves + waves_per_segment - 1) / waves_per_segment;
-    const int64_t kmax = (d.seqlen + kMinSegment - 1) / kMinSegment;
+void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p,
+                  int64_t target_waves = kTargetWaves, int64_t min_segment = kMinSegment) {
+    int64_t k = (target_waves + waves_per_segment - 1) / waves_per_segment;
+    const int64_t kmax = (d.seqlen + min_segment - 1) / min_segment;
     if (k > kmax) k = kmax;
     if (k < 1) k = 1;
     int64_t len = (d.seqlen + k - 1) / k;
     len = (len + kSegmentQuantum - 1) / kSegmentQuantum * kSegmentQuantum;
     p.chunk_len = len;
     p.chunks = (int)((d.seqlen + len - 1) / len);
+}
+
+// Row path (d_state 9..16): a channel's states spread over one 16-lane DPP
+// row, so there are 16x more waves than on the lane path and the sequence
+// needs cutting only when batch x d_inner is small.  A segment after the
+// first costs a summary walk over it (about as much as the scan itself), so
+// the row path cuts only to about two waves per SIMD.
+#ifndef MSSCAN_ROW_TARGET_WAVES
+#define MSSCAN_ROW_TARGET_WAVES 2048
+#endif
+#ifndef MSSCAN_ROW_MIN_SEGMENT
+#define MSSCAN_ROW_MIN_SEGMENT 256
+#endif
+bool row_plan(const ms_dims& d, msscan::Plan& p) {
+    if (d.d_state <= 8 || d.d_state > 16) return false;
+    p.tile_path = 3;
+    p.ns = 16;
+    p.waves = msscan::kRowWaves;
+    p.tiles = (d.d_inner + msscan::kRowCh - 1) / msscan::kRowCh;
+    cut_sequence(d, (int64_t)d.batch * p.tiles * msscan::kRowWaves, p, MSSCAN_ROW_TARGET_WAVES,
+                 MSSCAN_ROW_MIN_SEGMENT);
+    return true;
 }
 
 bool lane_plan(const ms_dims& d, int disc, msscan::Plan& p) {
@@ -137,13 +160,15 @@ bool tile_plan(const ms_dims& d, msscan::Plan& p) {
     return true;
 }
 
-msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
+// rows: whether the row path may be chosen (the fused step projection runs on
+// the lane kernels only).
+msscan::Plan make_plan(const ms_dims& d, uint32_t flags, bool rows = true) {
     msscan::Plan p{};
     const int N = d.d_state;
     // Per segment boundary and channel: N summary states, plus the segment
     // decay -- one sum of dt, or N products of A_bar for the bilinear form.
     const size_t per_channel = (size_t)N + ((flags & MS_BILINEAR) ? (size_t)N : 1);
-    if (lane_plan(d, disc_of(flags), p) || tile_plan(d, p)) {
+    if ((rows && row_plan(d, p)) || lane_plan(d, disc_of(flags), p) || tile_plan(d, p)) {
         if (p.chunks > 1) {
             const size_t km1 = (size_t)(p.chunks - 1);
             p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * per_channel;
@@ -160,14 +185,112 @@ msscan::Plan make_plan(const ms_dims& d, uint32_t flags) {
 
 size_t round256(size_t bytes) { return (bytes + 255) / 256 * 256; }
 
-// Workspace layout: [fp32 B/C slices][chunk summaries + carries][sum of dt].
-size_t ws_bytes(const msscan::Plan& p) {
-    size_t n = round256(p.bc_floats * sizeof(float));
-    if (p.ws_floats) n += round256(p.ws_floats * sizeof(float)) + 256;
-    return n;
+// Workspace layout: [fp32 B/C rows][segment summaries + carries][sum of dt or
+// product of A_bar][copy of h0 for the first segment], each region 256-byte
+// aligned; the last three only when the sequence is cut into segments.
+struct WsLayout {
+    size_t bc, agg, decay, start0, total;  // byte offsets (total = size)
+};
+
+WsLayout ws_layout(const msscan::Plan& p, const ms_dims& d, uint32_t flags) {
+    WsLayout w{};
+    size_t off = round256(p.bc_floats * sizeof(float));
+    w.bc = 0;
+    if (p.chunks > 1) {
+        const size_t km1 = (size_t)(p.chunks - 1);
+        const size_t bdn = (size_t)d.batch * (size_t)d.d_inner * (size_t)d.d_state;
+        w.agg = off;
+        off += round256(km1 * bdn * sizeof(float));
+        w.decay = off;
+        off += round256(km1 * (size_t)d.batch * (size_t)d.d_inner *
+                        ((flags & MS_BILINEAR) ? (size_t)d.d_state : 1) * sizeof(float));
+        w.start0 = off;
+        off += round256(bdn * sizeof(float));
+    }
+    w.total = off;
+    return w;
+}
+
+size_t ws_bytes(const msscan::Plan& p, const ms_dims& d, uint32_t flags) {
+    return ws_layout(p, d, flags).total;
+}
+
+// Points the workspace regions of a at `workspace` (laid out by ws_layout).
+void bind_workspace(msscan::ScanArgs& a, const msscan::Plan& p, const ms_dims& d, uint32_t flags,
+                    void* workspace) {
+    const WsLayout w = ws_layout(p, d, flags);
+    char* ws = static_cast<char*>(workspace);
+    if (p.bc_floats) a.bcw = reinterpret_cast<float*>(ws + w.bc);
+    if (p.chunks > 1) {
+        a.agg = reinterpret_cast<float*>(ws + w.agg);
+        float* decay = reinterpret_cast<float*>(ws + w.decay);
+        if (flags & MS_BILINEAR)
+            a.prod = decay;  // [batch][chunks-1][N][Dn], like the summaries
+        else
+            a.sdt = decay;  // [batch][chunks-1][Dn]
+        if (a.h0) a.start0 = reinterpret_cast<float*>(ws + w.start0);
+    }
+}
+
+// One forward scan: validation, plan, workspace binding and launch (the body
+// of ms_scan_fwd and ms_scan_fwd_noalloc).
+ms_status scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* delta_bias,
+                        uint32_t flags, void* y, const float* h0, float* h_last,
+                        const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    ms_status st = check_dims(dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (!u || !delta || !A || !B || !C || !y)
+        return fail(MS_ERR_NULL, "u, delta, A, B, C and y are required");
+    const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    const msscan::Plan p = make_plan(*dims, flags);
+    if (p.tile_path < 0) return fail(MS_ERR_UNSUPPORTED, "no scan kernel for d_state %d", dims->d_state);
+    const size_t need = ws_bytes(p, *dims, flags);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    msscan::ScanArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+    a.h0 = h0; a.h_last = h_last; a.y = y;
+    a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
+    a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    a.waves = p.waves;
+    a.tiles = p.tiles;
+    bind_workspace(a, p, *dims, flags, workspace);
+    const bool bf16 = dims->io == MS_BF16;
+    const int disc = disc_of(flags);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    msscan::prof_call();
+    hipError_t e;
+    if (p.tile_path == 3)
+        e = msscan::launch_scan_rows(p, a, bf16, disc, hs);
+    else if (p.tile_path == 2)
+        e = msscan::launch_scan_lanes(p, a, bf16, disc, hs);
+    else
+        e = msscan::launch_scan_tiles(p, a, bf16, disc, hs);
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
 }
 
 }  // namespace
+
+namespace msscan {
+void clear_error() { g_err[0] = '\0'; }
+ms_status report(ms_status s, const char* text) { return fail(s, "%s", text); }
+ms_status scan_fwd_checked(const void* u, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* delta_bias,
+                           uint32_t flags, void* y, const float* h0, float* h_last,
+                           const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, y, h0, h_last, dims,
+                         workspace, workspace_bytes, stream);
+}
+}  // namespace msscan
 
 extern "C" {
 
@@ -192,7 +315,12 @@ const char* ms_status_string(ms_status s) {
 
 size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags) {
     if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
-    return ws_bytes(make_plan(*dims, flags));
+    return ws_bytes(make_plan(*dims, flags), *dims, flags);
+}
+
+size_t ms_scan_dtproj_workspace_bytes(const ms_dims* dims, uint32_t flags) {
+    if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
+    return ws_bytes(make_plan(*dims, flags, false), *dims, flags);
 }
 
 ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
@@ -201,50 +329,8 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
                       const ms_dims* dims, void* workspace, size_t workspace_bytes,
                       void* stream) {
     g_err[0] = '\0';
-    ms_status st = check_dims(dims);
-    if (st != MS_OK) return st;
-    if ((st = check_flags(flags)) != MS_OK) return st;
-    if (!u || !delta || !A || !B || !C || !y)
-        return fail(MS_ERR_NULL, "u, delta, A, B, C and y are required");
-    const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
-    for (const void* p : ptrs)
-        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
-    const msscan::Plan p = make_plan(*dims, flags);
-    if (p.tile_path < 0) return fail(MS_ERR_UNSUPPORTED, "no scan kernel for d_state %d", dims->d_state);
-    const size_t need = ws_bytes(p);
-    if (need && (!workspace || workspace_bytes < need))
-        return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                    workspace ? workspace_bytes : (size_t)0);
-
-    msscan::ScanArgs a{};
-    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-    a.h0 = h0; a.h_last = h_last; a.y = y;
-    a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
-    a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
-    a.waves = p.waves;
-    float* ws = static_cast<float*>(workspace);
-    if (p.bc_floats) {
-        a.bcw = ws;
-        ws += round256(p.bc_floats * sizeof(float)) / sizeof(float);
-    }
-    if (p.chunks > 1) {
-        const size_t km1 = (size_t)(p.chunks - 1);
-        a.agg = ws;
-        const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
-        float* after = ws + ((agg_n + 63) / 64) * 64;
-        if (flags & MS_BILINEAR)
-            a.prod = after;  // [batch][chunks-1][N][Dn], like the summaries
-        else
-            a.sdt = after;
-    }
-    const bool bf16 = dims->io == MS_BF16;
-    const int disc = disc_of(flags);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    msscan::prof_call();
-    hipError_t e = p.tile_path == 2 ? msscan::launch_scan_lanes(p, a, bf16, disc, hs)
-                                    : msscan::launch_scan_tiles(p, a, bf16, disc, hs);
-    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-    return MS_OK;
+    return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, flags, y, h0, h_last, dims,
+                         workspace, workspace_bytes, stream);
 }
 
 ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt,
@@ -264,11 +350,11 @@ ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt
     const void* ptrs[] = {u, dt_low, W_dt, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
     for (const void* p : ptrs)
         if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
-    const msscan::Plan p = make_plan(*dims, flags);
+    const msscan::Plan p = make_plan(*dims, flags, false);
     if (p.tile_path != 2 || p.ns != dims->d_state || !msscan::dtproj_variant_exists(dims->d_state))
         return fail(MS_ERR_UNSUPPORTED, "the fused dt projection needs d_state 8 or 16 (got %d)",
                     dims->d_state);
-    const size_t need = ws_bytes(p);
+    const size_t need = ws_bytes(p, *dims, flags);
     if (need && (!workspace || workspace_bytes < need))
         return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -280,17 +366,8 @@ ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt
     a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
     a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
     a.waves = p.waves;
-    if (p.chunks > 1) {
-        const size_t km1 = (size_t)(p.chunks - 1);
-        float* ws = static_cast<float*>(workspace);
-        a.agg = ws;
-        const size_t agg_n = km1 * (size_t)dims->batch * (size_t)dims->d_state * (size_t)dims->d_inner;
-        float* after = ws + ((agg_n + 63) / 64) * 64;
-        if (flags & MS_BILINEAR)
-            a.prod = after;
-        else
-            a.sdt = after;
-    }
+    a.tiles = p.tiles;
+    bind_workspace(a, p, *dims, flags, workspace);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     msscan::prof_call();
     const hipError_t e =

@@ -7,7 +7,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/msscan.h"
+
 namespace msscan {
+
+// The C ABI's shared pieces (api.cpp), for entry points in other files:
+// the thread-local error text, and ms_scan_fwd's validation + launch.
+void clear_error();
+ms_status report(ms_status s, const char* text);  // sets the error text, returns s
+ms_status scan_fwd_checked(const void* u, const void* delta, const float* A, const void* B,
+                           const void* C, const float* D, const void* z, const float* delta_bias,
+                           uint32_t flags, void* y, const float* h0, float* h_last,
+                           const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 // How one ms_scan_fwd call is cut into work.  Lanes of a wave own 64
 // consecutive channels; a workgroup holds `waves` waves that split the
@@ -15,13 +27,14 @@ namespace msscan {
 // `chunk_len` steps each.  Pieces after the first start from a carried state
 // computed by a separate pass (chunk summaries + carry propagation).
 struct Plan {
-    int tile_path;      // 2: scan_lane kernels (all states in a lane);
+    int tile_path;      // 3: scan_row kernels (a 16-lane row per channel, a state per lane);
+                        // 2: scan_lane kernels (all states in a lane);
                         // 1: scan_tile kernels (waves split d_state); -1: none
     int ns;             // states per lane (compile-time variant)
     int waves;          // waves per workgroup = ceil(d_state / ns)
     int chunks;         // pieces along L
     int64_t chunk_len;  // steps per piece (last piece may be shorter)
-    int tiles;          // ceil(d_inner / 64)
+    int tiles;          // channel tiles per batch row: ceil(d_inner / 64), or / kRowCh (rows)
     size_t ws_floats;   // workspace floats (0 when chunks == 1)
     size_t bc_floats;   // tile path: fp32 B/C copy laid out per wave (0 if unused)
 };
@@ -42,6 +55,9 @@ struct ScanArgs {
     float* sdt;   // [batch][chunks-1][Dn]: sum of dt over each chunk (exp-based A_bar)
     float* prod;  // [batch][chunks-1][N][Dn]: product of A_bar over each chunk (bilinear)
     float* bcw;   // tile path: [batch][waves][L][2*ns] fp32 B_t then C_t slices
+    float* start0;  // several segments and h0 given: [batch][Dn][N] copy of h0 written by
+                    // the carry pass; the first segment reads it instead of h0, so that
+                    // h_last (written by the last segment in the same launch) may alias h0
     const void* dtx;  // fused dt projection: [batch][L][rank] low-rank input, io dtype
     const void* wdt;  // fused dt projection: [Dn][rank] weight, io dtype
     int rank;         // fused dt projection: columns of dtx and wdt (0: delta is given)
@@ -53,6 +69,7 @@ struct ScanArgs {
     int chunks;
     int softplus;
     int waves;    // tile path: waves per workgroup
+    int tiles;    // row path: channel tiles (kRowCh channels each) per batch row
 };
 
 struct ConvArgs {
@@ -97,6 +114,7 @@ struct CarryArgs {
     const float* prod;
     const float* A;
     const float* init;
+    float* start0;  // if set: receives init ([batch][Dn][N], zero when init is null)
     int batch;
     int km1;
     int N;
@@ -106,6 +124,10 @@ constexpr int kCarryGroup = 8;  // slots whose loads one carry thread issues tog
 hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s);
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);  // the forward summaries of a
 bool tile_variant_exists(int ns, int waves);
+// Row path (scan_row.hip): d_state <= 16, one 16-lane DPP row per channel.
+constexpr int kRowWaves = 4;            // waves per workgroup
+constexpr int kRowCh = 4 * kRowWaves;   // channels per workgroup (4 rows per wave)
+hipError_t launch_scan_rows(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 bool lane_variant_exists(int n, int disc);
 // Lane path with the low-rank dt projection fused in (a.dtx, a.wdt, a.rank).

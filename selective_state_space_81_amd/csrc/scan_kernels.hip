@@ -45,6 +45,7 @@ __global__ void __launch_bounds__(256) carry_chain(CarryArgs c) {
     const bool prod = c.prod != nullptr;
     const float A2 = c.A[(int64_t)d * c.N + n] * kLog2e;
     float h = c.init ? c.init[((int64_t)b * c.Dn + d) * c.N + n] : 0.f;
+    if (c.start0) c.start0[((int64_t)b * c.Dn + d) * c.N + n] = h;
     const int km1 = c.km1;
     for (int i0 = 0; i0 < km1; i0 += kCarryGroup) {
         float dv[kCarryGroup], gv[kCarryGroup];
@@ -93,6 +94,7 @@ hipError_t launch_carry(const ScanArgs& a, hipStream_t s) {
     c.prod = a.prod;
     c.A = a.A;
     c.init = a.h0;
+    c.start0 = a.start0;
     c.batch = a.batch;
     c.km1 = a.chunks - 1;
     c.N = a.N;

@@ -91,7 +91,9 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
         if constexpr (!SUMMARY) {
             if (n0 + j < Nr) {
                 if (seg == 0) {
-                    if (a.h0) v = a.h0[((int64_t)b * a.Dn + dd) * Nr + n0 + j];
+                    // several segments: the carry pass's copy of h0 (h_last may alias h0)
+                    const float* h0 = a.chunks > 1 ? a.start0 : a.h0;
+                    if (h0) v = h0[((int64_t)b * a.Dn + dd) * Nr + n0 + j];
                 } else {
                     v = a.agg[(((int64_t)b * km1 + (seg - 1)) * Nr + n0 + j) * a.Dn + dd];
                 }

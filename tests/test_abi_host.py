@@ -71,47 +71,70 @@ def test_validation_statuses_host_only():
     assert r == 4  # ZOH with bilinear
 
 
+def _seg_ws(batch, Dn, N, km1, bilinear=False):
+    """Workspace of a plan cut into km1 + 1 segments (no staged B/C rows):
+    summaries [batch][km1][N][Dn], the decay (sum of dt, or N products of
+    A_bar), and the copy of h0 [batch][Dn][N], each region rounded up to 256 bytes."""
+    r = lambda n: (n * 4 + 255) // 256 * 256  # noqa: E731
+    return r(km1 * batch * Dn * N) + r(km1 * batch * Dn * (N if bilinear else 1)) + \
+        r(batch * Dn * N)
+
+
 def test_workspace_size_function():
     lib = ms.load()
+
+    def ws(b, L, D, N, flags=1):
+        return lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(b, L, D, N, 1)), flags)
+
     # d_state 100 runs padded on the 128-state tile kernels; over one piece its
     # workspace is just their staged fp32 B/C rows, 128 states wide.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(64, 256, 4096, 100, 1)), 1) == \
-        64 * 256 * 2 * 128 * 4
+    assert ws(64, 256, 4096, 100) == 64 * 256 * 2 * 128 * 4
+    # The row kernels (d_state 9..16) run the 130M and 3B layers whole: one
+    # pass, no segment summaries, no workspace.
+    assert ws(8, 2048, 1536, 16) == 0
+    assert ws(4, 8192, 5120, 16, 1 | 2) == 0 and ws(4, 8192, 5120, 16, 1 | 4) == 0
+    assert ws(8, 2048, 1536, 12) == 0
+    # Few channels: the row plan cuts the sequence (segments of at least 256
+    # steps, quantum 16) and needs the summaries and the h0 copy.
+    n = ws(1, 65536, 256, 16)
+    km1 = 32 - 1  # 64 waves per segment -> 2048 / 64 = 32 segments
+    assert n == _seg_ws(1, 256, 16, km1)
+    assert ws(1, 65536, 256, 16, 1 | 4) == _seg_ws(1, 256, 16, km1, bilinear=True)
     # A d_state without a lane kernel of its own (17) runs padded on one: its
-    # segment summaries keep the true d_state, N + 1 floats per boundary.
-    n17 = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 17, 1)), 1)
-    assert n17 > 0 and n17 % (8 * 1536 * 18 * 4) < 1024
+    # segment summaries keep the true d_state.
+    n17 = ws(8, 2048, 1536, 17)
+    k17 = 2048 // 64 - 1  # lane plan: 16384 / 192 waves -> capped at 64-step segments
+    assert n17 == _seg_ws(8, 1536, 17, k17)
     # Invalid dims -> (size_t)-1.
-    bad = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 0, 64, 16, 1)), 1)
-    assert bad == ctypes.c_size_t(-1).value
+    assert ws(1, 0, 64, 16) == ctypes.c_size_t(-1).value
     # The tile kernels (d_state 128, or 64 with ZOH) stage fp32 B/C rows: at
     # least batch*L*2*N floats.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 128, 1)), 1) >= \
-        2 * 2048 * 2 * 128 * 4
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 3) >= \
-        2 * 2048 * 2 * 64 * 4
+    assert ws(2, 2048, 1536, 128) >= 2 * 2048 * 2 * 128 * 4
+    assert ws(2, 2048, 1536, 64, 3) >= 2 * 2048 * 2 * 64 * 4
     # d_state 64 with Euler takes the lane kernels (summaries only, no staged
     # B/C rows), so it needs less than the same shape with ZOH.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 1) < \
-        lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 2048, 1536, 64, 1)), 3)
-    # The lane kernels (d_state 16) keep only segment summaries: N + 1 floats
-    # per (segment boundary, batch, channel).
-    n16 = lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 16, 1)), 1)
-    assert n16 > 0 and n16 % (8 * 1536 * 17 * 4) < 1024
+    assert ws(2, 2048, 1536, 64) < ws(2, 2048, 1536, 64, 3)
     # Deterministic and independent of flags that do not change the plan.
-    d = ms.dims(1, 65536, 256, 16, 1)
-    a = lib.ms_scan_workspace_bytes(ctypes.byref(d), 1)
-    assert a == lib.ms_scan_workspace_bytes(ctypes.byref(d), 3)
+    a = ws(1, 65536, 256, 16)
+    assert a == ws(1, 65536, 256, 16, 3)
     assert a % 256 == 0 and a > 0
-    # The bilinear form keeps N products of A_bar per segment boundary instead
-    # of one sum of dt, so its summaries take more room.
-    d16 = ms.dims(8, 2048, 1536, 16, 1)
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(d16), 1 | 4) > \
-        lib.ms_scan_workspace_bytes(ctypes.byref(d16), 1)
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(d16), 2 | 4) == ctypes.c_size_t(-1).value
+    assert ws(8, 2048, 1536, 16, 2 | 4) == ctypes.c_size_t(-1).value
     # A long sequence at an odd d_state (padded onto a lane kernel) is cut
     # into segments and needs their summaries.
-    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(1, 65536, 256, 17, 1)), 1) > 0
+    assert ws(1, 65536, 256, 17) > 0
+
+
+def test_dtproj_workspace_size_function():
+    lib = ms.load()
+
+    def ws(b, L, D, N, flags=1):
+        return lib.ms_scan_dtproj_workspace_bytes(ctypes.byref(ms.dims(b, L, D, N, 1)), flags)
+
+    # The fused projection runs on the lane kernels (one lane per channel),
+    # which cut the 130M layer into 64-step segments.
+    assert ws(8, 2048, 1536, 16) == _seg_ws(8, 1536, 16, 2048 // 64 - 1)
+    assert ws(8, 2048, 1536, 8) == _seg_ws(8, 1536, 8, 2048 // 64 - 1)
+    assert ws(1, 0, 64, 16) == ctypes.c_size_t(-1).value
 
 
 def test_profile_errors_without_gpu_work():

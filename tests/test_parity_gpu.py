@@ -63,6 +63,14 @@ EDGE = [
     (2, 300, 70, 80, "bf16"),   # bf16 rows padded to the 128-state tile
     (1, 350, 64, 40, "bf16"),   # bf16, padded to 64 states (lane or tile)
     (1, 1100, 128, 128, "bf16"),
+    # row kernels (d_state 9..16): padded states, channel tails inside a
+    # 16-channel workgroup, and sequences cut into several segments
+    (1, 2000, 48, 12, "bf16"),
+    (2, 777, 20, 9, "f32"),
+    (1, 300, 17, 15, "f32"),
+    (3, 5000, 33, 16, "bf16"),
+    (1, 16, 16, 16, "f32"),
+    (1, 17, 5, 13, "bf16"),
 ]
 
 
@@ -156,6 +164,41 @@ def test_split_resume_matches_single_scan(gpu):
     y3 = _run(gpu, x, True, False, h0=hh, h_last=hh)
     assert torch.equal(y3, y)
     assert torch.equal(hh, hl)
+
+
+# h_last may alias h0 (include/msscan.h).  With one segment each channel's
+# lanes read h0 before they write h_last; with several, the first segment
+# starts from the carry pass's copy of h0.  Cases: the full 3B layer (row
+# kernels, one segment), and segmented plans of the row, lane and tile kernels.
+ALIAS = [("m3b", None, "euler"), ("tiny", (1, 6000, 40, 16), "zoh"),
+         ("tiny", (2, 3000, 64, 32), "euler"), ("tiny", (1, 3000, 64, 64), "zoh"),
+         ("tiny", (1, 4000, 64, 8), "bilinear")]
+
+
+@pytest.mark.parametrize("name,shape,disc", ALIAS,
+                         ids=["m3b", "rows-seg", "lane32-seg", "tile64-seg", "lane8-seg"])
+def test_h0_aliases_h_last(gpu, name, shape, disc):
+    if shape is None:
+        w = synth.workload(name)
+    else:
+        b, L, Dn, N = shape
+        w = synth.workload(name, batch=b, L=L, Dn=Dn, N=N, io="bf16")
+    x = synth.scan_inputs(w, device=DEV, seed=12)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    h0 = torch.randn(w.batch, w.Dn, w.N, generator=g, device=DEV) * 0.5
+    hl = torch.empty_like(h0)
+    y = _run(gpu, x, w.softplus, disc, h0=h0, h_last=hl).clone()
+    hh = h0.clone()
+    y2 = _run(gpu, x, w.softplus, disc, h0=hh, h_last=hh)
+    assert torch.equal(y2, y)
+    assert torch.equal(hh, hl)
+    if shape is not None:
+        yr, hr = _oracle_full(x, w.softplus, disc, h0=h0)
+        assert_within(y, yr, "bf16")
+        assert_within(hl, hr, "f32", "h_last")
+    del x, y, y2
+    torch.cuda.empty_cache()
 
 
 def test_deterministic_and_workspace_reuse(gpu):
