@@ -130,6 +130,35 @@ ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const vo
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ms_scan_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * arguments and results are ms_scan_fwd's without the workspace: the scratch
+ * that call takes as a workspace (ms_scan_workspace_bytes(dims, flags) bytes)
+ * comes from a device array inside the library, MS_NOALLOC_MAX_BYTES per GPU,
+ * held from the first call on that GPU until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).
+ *
+ *   - MS_ERR_UNSUPPORTED (nothing launched) when ms_scan_workspace_bytes
+ *     exceeds MS_NOALLOC_MAX_BYTES; use ms_scan_fwd with a workspace then.
+ *     Shapes that the library runs in one pass (e.g. d_state 9..16 with
+ *     batch x d_inner >= 8192) need no scratch at all.
+ *   - The scratch used is that of the calling thread's current device; the
+ *     stream must belong to that device.
+ *   - Every call on one GPU shares that GPU's array (its contents need no
+ *     initialisation and are undefined afterwards): two calls that overlap in
+ *     time on one GPU (different streams, or different host threads) race.
+ *     Calls on one stream are ordered and do not.
+ * Other statuses as for ms_scan_fwd; deterministic, with outputs bit-identical
+ * to ms_scan_fwd's for the same inputs.
+ */
+#define MS_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+ms_status ms_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                              const void* C, const float* D, const void* z,
+                              const float* delta_bias, uint32_t flags, void* y,
+                              const float* h0, float* h_last, const ms_dims* dims,
+                              void* stream);
+
+/*
  * ms_scan_fwd with the step size's low-rank projection fused into the scan.
  * The step size is softplus of a linear map of the input plus a bias (jsqmd
  * page, section 2.2); in the block that map is low-rank: x_proj yields a

@@ -29,7 +29,7 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
            "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end",
            "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd",
-           "ms_scan_fwd_dtproj", "ms_scan_dtproj_workspace_bytes")
+           "ms_scan_fwd_dtproj", "ms_scan_dtproj_workspace_bytes", "ms_scan_fwd_noalloc")
 
 PHASES = ("prep", "summary", "carry", "main", "step", "conv")  # ms_phase order
 
@@ -78,6 +78,9 @@ def load(path: Optional[str] = None):
     lib.ms_scan_fwd.restype = ctypes.c_int
     lib.ms_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
                                 ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
+    lib.ms_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ms_scan_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, u32, vp, vp, vp,
+                                        ctypes.POINTER(MsDims), vp]
     lib.ms_scan_dtproj_workspace_bytes.restype = ctypes.c_size_t
     lib.ms_scan_dtproj_workspace_bytes.argtypes = [ctypes.POINTER(MsDims), u32]
     lib.ms_scan_fwd_dtproj.restype = ctypes.c_int
@@ -226,6 +229,26 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=Tru
     rc = load().ms_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                             _ptr(delta_bias), fl, _ptr(y), _ptr(h0), _ptr(h_last),
                             ctypes.byref(d), _ptr(workspace), ws_size, _stream(stream))
+    _check(rc)
+    return y
+
+
+NOALLOC_MAX_BYTES = 64 << 20  # MS_NOALLOC_MAX_BYTES
+
+
+def scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=True,
+                     zoh=False, bilinear=False, y, h0=None, h_last=None, stream=None):
+    """ms_scan_fwd_noalloc on torch device tensors: the forward scan with the
+    library's own device scratch (no workspace argument).  y must be given
+    (nothing is allocated here either).  Returns y."""
+    batch, L, Dn, N, _ = _chk_scan(u, delta, A, B, C, D, z, delta_bias, h0, h_last, y)
+    if y is None:
+        raise ValueError("y is required (scan_fwd_noalloc allocates nothing)")
+    d = dims(batch, L, Dn, N, _io(u))
+    rc = load().ms_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(delta_bias), flags(softplus, zoh, bilinear),
+                                    _ptr(y), _ptr(h0), _ptr(h_last), ctypes.byref(d),
+                                    _stream(stream))
     _check(rc)
     return y
 
