@@ -67,6 +67,12 @@ using namespace dev;
 
 constexpr int kRT = 16;        // timesteps per block = lanes of a DPP row
 constexpr int kBcS = 20;       // LDS stride (floats) of one state's 16 timesteps
+#ifndef MSSCAN_ROW_PF
+#define MSSCAN_ROW_PF 4
+#endif
+constexpr int kRowPf = MSSCAN_ROW_PF;  // blocks between a block's loads and its staging
+constexpr int kNb = 4;                 // LDS buffers of staged blocks (>= 3)
+static_assert(kRowPf % kNb == 0, "block j uses load set j mod kRowPf and buffer j mod kNb");
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -161,16 +167,26 @@ __device__ __forceinline__ float widen_bits(uint32_t bits) {
     return __uint_as_float(BF16 ? bits << 16 : bits);
 }
 
-template <bool BF16, int DISC, bool SP, bool SUMMARY>
+template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP>
 __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     constexpr bool ZOH = DISC == kZoh;
     constexpr bool BIL = DISC == kBilinear;
     constexpr bool PROD = SUMMARY && BIL;  // bilinear summary: product of A_bar
     using R = Io<BF16>;
     using RT = typename R::T;
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-    // B (and C) tiles of a block, [buffer][tensor][state][timestep].
-    __shared__ __attribute__((aligned(16))) float s_bc[2][SUMMARY ? 1 : 2][kRT][kBcS];
+    constexpr int kCw = BF16 ? 8 : 4;     // channels per 16-byte chunk
+    constexpr int kCpr = kRowCh / kCw;    // chunks per tile row
+    constexpr int kIoS = BF16 ? 24 : 20;  // LDS row stride (elements) of an io tile: 16-byte rows
+    constexpr int kIoT = SUMMARY ? 2 : 3; // io tiles staged: u, delta (, z)
+    // LDS.  Block j is staged in buffer j mod kNb: its B (and C) tile, widened,
+    // [tensor][state][timestep]; with COOP also its u, delta (, z) tiles
+    // [tensor][timestep][channel].  y tiles [timestep][channel] alternate
+    // between two buffers (COOP).
+    __shared__ __attribute__((aligned(16))) float s_bc[kNb][SUMMARY ? 1 : 2][kRT][kBcS];
+    __shared__ __attribute__((aligned(16))) RT s_io[COOP ? kNb : 1][COOP ? kIoT : 1][kRT][kIoS];
+    __shared__ __attribute__((aligned(16))) RT s_y[(COOP && !SUMMARY) ? 2 : 1][kRT][kIoS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -183,12 +199,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     const int b = (int)(l / ((uint32_t)tiles * (uint32_t)segs));
 
     const int c = tile * kRowCh + (tid >> 4);  // 4 rows per wave, 16 per workgroup
-    // Memory order of the per-element io: lane i of the wave holds channel
-    // (i & 3) of the wave's 4 at timestep i >> 2.
-    const int cm = tile * kRowCh + (tid >> 6) * 4 + (lane & 3);
-    const int tm = lane >> 2;
-    const int to_row = 4 * (((n << 2) | (lane >> 4)));         // bpermute: memory -> row order
-    const int to_mem = 4 * ((((lane & 3) << 4) | (lane >> 2)));  // bpermute: row -> memory order
+    const int cl = (tid >> 4) & (kRowCh - 1);  // the row's channel within the tile
     const bool cvalid = c < a.Dn;
     const int cc = cvalid ? c : a.Dn - 1;
     const int Nr = a.N;
@@ -221,62 +232,126 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     const int64_t t1 = min(a.L, t0 + a.chunk_len);
     const int64_t row0 = (int64_t)b * a.L;
     const uint32_t rowb = (uint32_t)a.Dn * R::kSize;
-    // this lane's element of a block in memory order: timestep slot tm, channel cm
-    const uint32_t eoff = cm < a.Dn ? (uint32_t)tm * rowb + (uint32_t)cm * R::kSize : kOutOfRange;
-    // this thread's element of the block's B/C tile: timestep bt, state bs
+    // Element io without COOP, in memory order: lane i of the wave holds the
+    // wave's channel (i & 3) at timestep i >> 2 (one cache line per quad);
+    // ds_bpermute moves values between that order and the row order.
+    const int cm = tile * kRowCh + (tid >> 6) * 4 + (lane & 3);
+    const uint32_t eoff =
+        cm < a.Dn ? (uint32_t)(lane >> 2) * rowb + (uint32_t)cm * R::kSize : kOutOfRange;
+    const int to_row = 4 * ((n << 2) | (lane >> 4));
+    const int to_mem = 4 * (((lane & 3) << 4) | (lane >> 2));
+    // COOP: wave w < kIoT moves io tile w (u, delta, z) with one 16-byte access
+    // per lane (chunk cch of row crow); wave 3 stores the y tiles.  d_inner is
+    // a multiple of kCw, so every chunk lies wholly inside or outside a row.
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int crow = lane / kCpr, cch = lane % kCpr;
+    const int cchan = tile * kRowCh + cch * kCw;
+    const uint32_t coff = (lane < kRT * kCpr && cchan < a.Dn)
+                              ? (uint32_t)crow * rowb + (uint32_t)cchan * R::kSize
+                              : kOutOfRange;
+    const int ntiles_io = SUMMARY ? 2 : (has_z ? 3 : 2);
+    // this thread's element of a block's B/C tile: timestep bt, state bs
     const int bt = tid >> 4, bs = tid & 15;
     const uint32_t kBRow = (uint32_t)Nr * R::kSize;
     const uint32_t boff = bs < Nr ? (uint32_t)bt * kBRow + (uint32_t)bs * R::kSize : kOutOfRange;
 
     // Block starts are kept relative to t0 in 32 bits (a segment is < 2^31 steps).
     const int len = (int)(t1 - t0);
-    // Rows of the block at rel inside the segment (0 past its end: a prefetch
-    // there reads zeros).  Wave-uniform; readfirstlane keeps it in an SGPR, so
-    // the buffer descriptors built from it stay scalar.
+    // Rows of the block at rel inside the segment (0 past its end: loads there
+    // read zeros and stores are dropped).  Wave-uniform; readfirstlane keeps
+    // it in an SGPR, so the buffer descriptors built from it stay scalar.
     auto rows_of = [&](int rel) -> uint32_t {
         return (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kRT, len - rel)));
     };
     auto base = [&](const void* p, int rel, uint32_t rb) -> const void* {
         return static_cast<const char*>(p) + (row0 + t0 + rel) * (int64_t)rb;
     };
+
+    // Raw global data of one block, loaded kRowPf blocks before it is staged.
     struct Raw {
-        RT u, d, z, bb, cb;
+        RT u, d, z, bb, cb;  // u, d, z: without COOP
+        u4 t;                // COOP: this lane's chunk of io tile wv
     };
     auto load = [&](Raw& r, int rel) {
         const uint32_t nr = rows_of(rel);
-        r.u = R::load(make_rsrc(base(a.u, rel, rowb), nr * rowb), eoff);
-        r.d = R::load(make_rsrc(base(a.delta, rel, rowb), nr * rowb), eoff);
+        if constexpr (COOP) {
+            if (wv < ntiles_io) {
+                const void* src = wv == 0 ? a.u : (wv == 1 ? a.delta : a.z);
+                r.t = __builtin_amdgcn_raw_buffer_load_b128(
+                    make_rsrc(base(src, rel, rowb), nr * rowb), coff, 0, 0);
+            }
+        } else {
+            r.u = R::load(make_rsrc(base(a.u, rel, rowb), nr * rowb), eoff);
+            r.d = R::load(make_rsrc(base(a.delta, rel, rowb), nr * rowb), eoff);
+            if constexpr (!SUMMARY)
+                r.z = has_z ? R::load(make_rsrc(base(a.z, rel, rowb), nr * rowb), eoff) : RT{};
+        }
         r.bb = R::load(make_rsrc(base(a.B, rel, kBRow), nr * kBRow), boff);
-        if constexpr (!SUMMARY) {
-            r.z = has_z ? R::load(make_rsrc(base(a.z, rel, rowb), nr * rowb), eoff) : RT{};
-            r.cb = R::load(make_rsrc(base(a.C, rel, kBRow), nr * kBRow), boff);
+        if constexpr (!SUMMARY) r.cb = R::load(make_rsrc(base(a.C, rel, kBRow), nr * kBRow), boff);
+    };
+    // Without COOP the io values of a staged block wait in registers, in row order.
+    struct Staged {
+        uint32_t u = 0, d = 0, z = 0;
+    };
+    // Stage the block at rel (raw set r) into LDS buffer buf, then refill r
+    // with the block kRowPf ahead.
+    auto stage = [&](Raw& r, int rel, int buf, Staged& sg) {
+        s_bc[buf][0][bs][bt] = R::widen(r.bb);
+        if constexpr (!SUMMARY) s_bc[buf][1][bs][bt] = R::widen(r.cb);
+        if constexpr (COOP) {
+            if (wv < ntiles_io && lane < kRT * kCpr)
+                *reinterpret_cast<u4*>(&s_io[buf][wv][crow][cch * kCw]) = r.t;
+        } else {
+            sg.u = permute_bits(r.u, to_row);
+            sg.d = permute_bits(r.d, to_row);
+            if constexpr (!SUMMARY) {
+                if (has_z) sg.z = permute_bits(r.z, to_row);
+            }
+        }
+        load(r, rel + kRowPf * kRT);
+    };
+    // Per-element values of a staged block, in row order: lane k holds
+    // timestep k of its row's channel.
+    struct Elem {
+        float dt, xv, u, z;
+    };
+    auto prologue = [&](int rel, int buf, const Staged& sg) -> Elem {
+        Elem e{};
+        float draw;
+        if constexpr (COOP) {
+            e.u = R::widen(s_io[buf][0][n][cl]);
+            draw = R::widen(s_io[buf][1][n][cl]);
+            if constexpr (!SUMMARY) {
+                if (has_z) e.z = R::widen(s_io[buf][2][n][cl]);
+            }
+        } else {
+            e.u = widen_bits<BF16>(sg.u);
+            draw = widen_bits<BF16>(sg.d);
+            if constexpr (!SUMMARY) e.z = widen_bits<BF16>(sg.z);
+        }
+        float dt = draw + bias;
+        if constexpr (SP) dt = softplus_f(dt);
+        e.dt = n < (int)rows_of(rel) ? dt : 0.f;  // steps past the end change nothing
+        e.xv = ZOH ? e.u : e.dt * e.u;            // B is scaled by u (ZOH) or dt*u
+        return e;
+    };
+    // COOP: wave 3 stores the y tile of the block at rel from buffer buf.
+    auto store_y_tile = [&](int rel, int buf) {
+        if constexpr (COOP && !SUMMARY) {
+            if (wv == kRowWaves - 1 && lane < kRT * kCpr) {
+                const u4 v = *reinterpret_cast<const u4*>(&s_y[buf][crow][cch * kCw]);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, make_rsrc(base(a.y, rel, rowb), rows_of(rel) * rowb), coff, 0, 0);
+            }
         }
     };
 
     float s_sum = 0.f, s_comp = 0.f;  // SUMMARY: Kahan sum of this lane's dt values
     float P = 1.f;                    // PROD: product of A_bar
 
-    // One block from the register set r (loaded two blocks earlier), which is
-    // then refilled with the block two ahead: the loads have two blocks of
-    // work to arrive.  Even blocks use set 0 and LDS buffer 0, odd blocks set
-    // 1 and buffer 1; one barrier per block.
-    auto do_block = [&](Raw& r, int rel, int buf) __attribute__((always_inline)) {
-        s_bc[buf][0][bs][bt] = R::widen(r.bb);
-        if constexpr (!SUMMARY) s_bc[buf][1][bs][bt] = R::widen(r.cb);
-        const float uv = widen_bits<BF16>(permute_bits(r.u, to_row));
-        const float draw = widen_bits<BF16>(permute_bits(r.d, to_row));
-        float zv = 0.f;
-        if constexpr (!SUMMARY) {
-            if (has_z) zv = widen_bits<BF16>(permute_bits(r.z, to_row));
-        }
-        load(r, rel + 2 * kRT);
-        __syncthreads();
-
-        const int nvalid = (int)rows_of(rel);
-        float dt = draw + bias;
-        if constexpr (SP) dt = softplus_f(dt);
-        dt = n < nvalid ? dt : 0.f;  // steps past the end change nothing
-        const float xv = ZOH ? uv : dt * uv;  // B is scaled by u (ZOH) or dt*u
+    // The recurrence over the block at rel (staged in buffer buf) and, unless
+    // SUMMARY, its readout and output (y tile ybuf with COOP).
+    auto compute = [&](int rel, int buf, int ybuf, const Elem& e) __attribute__((always_inline)) {
         f4 Bq[4], Cq[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -288,17 +363,18 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
             [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const float bj = Bq[j / 4][j % 4];
-                const float arg = row_bcast<j>(dt) * A2;
+                const float arg = row_bcast<j>(e.dt) * A2;
                 float abar, bx;
                 if constexpr (BIL) {
                     const float r = bilinear_r(arg);
                     abar = fmaf(2.f, r, -1.f);
-                    bx = (row_bcast<j>(xv) * bj) * r;
+                    bx = (row_bcast<j>(e.xv) * bj) * r;
                 } else {
                     abar = hw_exp2(arg);
-                    const float ub = row_bcast<j>(xv) * bj;
+                    const float ub = row_bcast<j>(e.xv) * bj;
                     if constexpr (ZOH) {
-                        const float ser = row_bcast<j>(dt) * fmaf(arg, fmaf(arg, kZohT2, kZohT1), 1.f);
+                        const float ser =
+                            row_bcast<j>(e.dt) * fmaf(arg, fmaf(arg, kZohT2, kZohT1), 1.f);
                         const float big = fmaf(abar, invA, -invA);
                         bx = (fabsf(arg) < kZohSwitch ? ser : big) * ub;
                     } else {
@@ -312,30 +388,68 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
             std::make_integer_sequence<int, kRT>{});
         if constexpr (SUMMARY) {
             if constexpr (!PROD) {
-                const float yk = dt - s_comp;
+                const float yk = e.dt - s_comp;
                 const float tk = s_sum + yk;
                 s_comp = (tk - s_sum) - yk;
                 s_sum = tk;
             }
         } else {
             float y = row_reduce_scatter(p, bit1, bit0);
-            y = fmaf(Dd, uv, y);
-            if (has_z) y *= silu_f(zv);
-            y = __int_as_float(__builtin_amdgcn_ds_bpermute(to_mem, __float_as_int(y)));
-            R::store(make_rsrc(base(a.y, rel, rowb), (uint32_t)nvalid * rowb), eoff, y);
+            y = fmaf(Dd, e.u, y);
+            if (has_z) y *= silu_f(e.z);
+            if constexpr (COOP) {
+                if constexpr (BF16)
+                    s_y[ybuf][n][cl] = f32_to_bf16_rne(y);
+                else
+                    s_y[ybuf][n][cl] = y;
+            } else {
+                y = __int_as_float(__builtin_amdgcn_ds_bpermute(to_mem, __float_as_int(y)));
+                R::store(make_rsrc(base(a.y, rel, rowb), rows_of(rel) * rowb), eoff, y);
+            }
         }
     };
 
+    // Software pipeline, one barrier per block j: stage block j + 1 (its raw
+    // data loaded kRowPf blocks earlier), barrier, store the y tile of block
+    // j - 1, form the per-element values of block j + 1, and run block j's
+    // recurrence with the values formed one block earlier.  Block j + 1 is
+    // staged while slower waves may still read block j's buffer, and block
+    // j + 2 only after every wave has passed block j + 1's barrier, so
+    // kNb >= 3 buffers suffice.  Blocks past the end stage zeros, harmlessly.
     const int nblk = (len + kRT - 1) / kRT;
-    Raw r0, r1;
-    load(r0, 0);
-    load(r1, kRT);
-    int blk = 0;
-    for (; blk + 1 < nblk; blk += 2) {
-        do_block(r0, blk * kRT, 0);
-        do_block(r1, (blk + 1) * kRT, 1);
+    Raw r[kRowPf];
+    static_for([&](auto ic) { load(r[decltype(ic)::value], decltype(ic)::value * kRT); },
+               std::make_integer_sequence<int, kRowPf>{});
+    Elem e;
+    {
+        Staged sg;
+        stage(r[0], 0, 0, sg);
+        __syncthreads();
+        e = prologue(0, 0, sg);
     }
-    if (blk < nblk) do_block(r0, blk * kRT, 0);
+    auto do_block = [&](auto ic, int j) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;  // j mod kRowPf
+        Staged sg;
+        stage(r[(i + 1) % kRowPf], (j + 1) * kRT, (i + 1) % kNb, sg);
+        __syncthreads();
+        if (j > 0) store_y_tile((j - 1) * kRT, (i + 1) & 1);
+        const Elem en = prologue((j + 1) * kRT, (i + 1) % kNb, sg);
+        compute(j * kRT, i % kNb, i & 1, e);
+        e = en;
+    };
+    int blk = 0;
+    for (; blk + kRowPf - 1 < nblk; blk += kRowPf)
+        static_for([&](auto ic) { do_block(ic, blk + decltype(ic)::value); },
+                   std::make_integer_sequence<int, kRowPf>{});
+    static_for(
+        [&](auto ic) {
+            if (blk + decltype(ic)::value < nblk) do_block(ic, blk + decltype(ic)::value);
+        },
+        std::make_integer_sequence<int, kRowPf - 1>{});
+    if constexpr (COOP && !SUMMARY) {  // the last block's y tile
+        __syncthreads();
+        store_y_tile((nblk - 1) * kRT, (nblk - 1) & 1);
+    }
 
     if constexpr (SUMMARY) {
         const int64_t sb = (int64_t)b * km1 + seg;
@@ -354,14 +468,14 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     }
 }
 
-template <bool BF16, int DISC, bool SP>
-hipError_t launch_rows_t(const Plan& p, const ScanArgs& a, hipStream_t s) {
+template <bool BF16, int DISC, bool SP, bool COOP>
+hipError_t launch_rows_c(const Plan& p, const ScanArgs& a, hipStream_t s) {
     const unsigned per_seg = (unsigned)a.batch * (unsigned)p.tiles;
     if (p.chunks > 1) {
         {
             ProfScope ps(s, kPhaseSummary);
-            hipLaunchKernelGGL((scan_row<BF16, DISC, SP, true>), dim3(per_seg * (p.chunks - 1)),
-                               dim3(64 * kRowWaves), 0, s, a);
+            hipLaunchKernelGGL((scan_row<BF16, DISC, SP, true, COOP>),
+                               dim3(per_seg * (p.chunks - 1)), dim3(64 * kRowWaves), 0, s, a);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -370,10 +484,18 @@ hipError_t launch_rows_t(const Plan& p, const ScanArgs& a, hipStream_t s) {
     }
     {
         ProfScope ps(s, kPhaseMain);
-        hipLaunchKernelGGL((scan_row<BF16, DISC, SP, false>), dim3(per_seg * p.chunks),
+        hipLaunchKernelGGL((scan_row<BF16, DISC, SP, false, COOP>), dim3(per_seg * p.chunks),
                            dim3(64 * kRowWaves), 0, s, a);
     }
     return hipGetLastError();
+}
+
+// Tiles move through LDS with 16-byte accesses (COOP) when every 16-byte
+// chunk of a row is wholly inside or outside it; else one element per lane.
+template <bool BF16, int DISC, bool SP>
+hipError_t launch_rows_t(const Plan& p, const ScanArgs& a, hipStream_t s) {
+    if (a.Dn % (BF16 ? 8 : 4) == 0) return launch_rows_c<BF16, DISC, SP, true>(p, a, s);
+    return launch_rows_c<BF16, DISC, SP, false>(p, a, s);
 }
 
 template <bool BF16, int DISC>
