@@ -10,10 +10,18 @@ not find the previous step's data in the 256 MB Infinity Cache.
 Prints ONE JSON line: elements/s (B*L*d_inner per second); the dominant
 kernel's roofline position, from its HIP-event kernel times recorded on the
 launch stream over the timed region (ms_profile_*); the whole call's HBM
-rate against the 8 TB/s peak; a Mamba-3B-layer line item; and the fp64 CPU
+rate against the 8 TB/s peak and its VALU fraction; line items for the 3B
+layer (Euler, ZOH, bilinear), the long-context d_state 64 scan (with its
+exponential rate against the measured v_exp_f32 rate), decode, conv1d,
+backward and the fused step projection; the chip rates measured by
+libmsprobe (v_exp_f32, fp32 FMA, copy and read bandwidth); and the fp64 CPU
 oracle timed on this host's cores on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Warm-up: at least --warmup untimed calls and at least --warm-seconds of
+them, so the GPU clock has ramped before the timed calls (kernel times fall
+by ~10% over the first ~20 ms of load).
 
 Profile helpers (used to write the summaries kept under profiles/):
     python bench.py --steps 3 --warmup 1 --no-cpu --no-secondary --copy-calibration
@@ -38,14 +46,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scan elem/s (B·L·D_inner) + achieved HBM GB/s vs peak, 130M & 3B layer shapes"
 HBM_PEAK_GBPS = 8000.0
-# Peak VALU issue of the chip for plain (non-packed) fp32 instructions:
-# 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.32e12 lane-ops/s (the 157.3
-# TFLOP/s fp32 vector figure counts a packed FMA, 2 lanes x 2 flops, per slot).
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Peak VALU rate of the chip for fp32 lane-operations (an FMA counted as one
+# operation): the published 157.3 TFLOP/s fp32 vector figure is 2 flops x
+# 78.6e12 FMA/s = 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz.  Plain VOP2
+# instructions reach it without packed math: libmsprobe measures ~1.5 wave64
+# FMAs per SIMD per 4 cycles, i.e. two 16-lane passes overlap; DPP and
+# transcendental instructions do not (rates in the bench line's "rates").
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
 COPY_MIB = 256  # size of the calibration copy (read and written)
-# the pass that writes y: scan_lane with SUMMARY (its 7th argument) false,
-# or scan_tile with SUMMARY (its last) false
-MAIN_KERNEL_RE = r"scan_lane<(?:[^,>]*, ){6}false[,>]|scan_tile<[^>]*false>"
+# the pass that writes y: scan_row with SUMMARY (its 4th argument) false,
+# scan_lane with SUMMARY (its 7th) false, or scan_tile with SUMMARY (its last) false
+MAIN_KERNEL_RE = (r"scan_row<(?:[^,>]*, ){3}false[,>]|scan_lane<(?:[^,>]*, ){6}false[,>]|"
+                  r"scan_tile<[^>]*false>")
 WORKLOAD_TITLE = {"m130m": "Mamba-130M-layer selective scan (S6) forward",
                   "m3b": "Mamba-3B-layer selective scan (S6) forward",
                   "long": "long-context selective scan (S6) forward, d_state 64"}
@@ -56,6 +68,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=0.25,
+                    help="minimum wall time of the untimed warm-up calls")
     ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b", "long"])
     ap.add_argument("--zoh", action="store_true", help="zero-order hold instead of Euler")
     ap.add_argument("--bilinear", action="store_true", help="bilinear instead of Euler")
@@ -63,7 +77,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle sample")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the 3B-layer line item")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the line items")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"also run a {COPY_MIB} MiB device copy (HBM counter calibration)")
     ap.add_argument("--rocprof-summary", metavar="KTRACE_DIR",
@@ -129,7 +143,20 @@ def make_sets(w, n_sets):
     return sets
 
 
-def time_calls(ms, sets, w, steps, warmup, zoh=False, bilinear=False):
+def warm_up(call, n, seconds):
+    """At least n untimed calls, and at least `seconds` of them."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or time.perf_counter() - t0 < seconds:
+        call(i)
+        i += 1
+        if i % 16 == 0 or i >= n:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_calls(ms, sets, w, steps, warmup, zoh=False, bilinear=False, warm_seconds=0.25):
     """Two timed regions of `steps` ms_scan_fwd calls each, on the stream the
     calls are enqueued on (torch's current stream):
       1. plain calls, bracketed by torch events -> ms per call (the value);
@@ -149,9 +176,7 @@ def time_calls(ms, sets, w, steps, warmup, zoh=False, bilinear=False):
                     delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh,
                     bilinear=bilinear, y=y, workspace=ws if ws_n else None, stream=stream)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, warm_seconds)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
@@ -340,7 +365,7 @@ def measure_bwd(ms, reps=20, warm=3):
             "main_ops_per_element": bwd_ops_per_element(w.N),
             "main_valu_frac": bwd_ops_per_element(w.N) * elems / (main_ms * 1e-3) / 1e12
                               / VALU_PEAK_TOPS,
-            "kernels_ms": {k: v["mean_ms"] for k, v in ph.items()
+            "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
                            if k != "calls" and v["launches"]}}
 
 
@@ -409,7 +434,7 @@ def measure_dtproj(ms, rank=16, reps=20):
             "two_step": "torch.matmul (raw step written in bf16) + ms_scan_fwd",
             "main_valu_frac": ops / (main_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
             "projection_flops_per_call": 2 * rank * elems,
-            "kernels_ms": {k: v["mean_ms"] for k, v in ph.items()
+            "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
                            if k != "calls" and v["launches"]}}
 
 
@@ -491,7 +516,7 @@ def _csv(dirname, suffix):
 
 
 def _short(name):
-    m = re.search(r"(scan_lane<[^>]*>|scan_tile<[^>]*>|"
+    m = re.search(r"(scan_row<[^>]*>|scan_lane<[^>]*>|scan_tile<[^>]*>|"
                   r"bc_prepare<[^>]*>|carry_chain<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
                   r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|"
                   r"reduce_param_groups|reduce_params|"
@@ -539,7 +564,7 @@ def rocprof_summary(args):
         for k in sorted(fetch):
             if k == "neg_kernel" or k not in write or not re.search(
                     r"scan_|carry_|bc_prep|step_quads|conv1d_kernel|bwd_main|"
-                    r"seg_summaries|reduce_", k):
+                    r"seg_summaries|reduce_|copy16|read16", k):
                 continue
             mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
             print(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {mb:.2f} |")
@@ -552,7 +577,7 @@ def rocprof_summary(args):
         acc = {}
         for r in _csv(dirname, "counter_collection.csv"):
             k = _short(r["Kernel_Name"])
-            if not re.search(r"scan_|carry_|bc_prep|step_quads", k):
+            if not re.search(r"scan_|carry_|bc_prep|step_quads|bwd_main|seg_summ|conv1d", k):
                 continue
             acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
@@ -567,13 +592,91 @@ def rocprof_summary(args):
 
 
 # ------------------------------------------------------------------ main --
-def measure(ms, w_name, steps, warmup, n_sets, zoh=False, bilinear=False):
+def measure(ms, w_name, steps, warmup, n_sets, zoh=False, bilinear=False, warm_seconds=0.25):
     import synth
     w = synth.workload(w_name)
     sets = make_sets(w, n_sets)
-    t_ms, ph = time_calls(ms, sets, w, steps, warmup, zoh=zoh, bilinear=bilinear)
+    t_ms, ph = time_calls(ms, sets, w, steps, warmup, zoh=zoh, bilinear=bilinear,
+                          warm_seconds=warm_seconds)
     del sets
     return w, t_ms, ph
+
+
+def fwd_item(ms, w_name, disc, steps, warmup, n_sets, warm_seconds):
+    """One forward line item: call time, rates and kernel times."""
+    import synth
+    w, t_ms, ph = measure(ms, w_name, steps, warmup, n_sets, zoh=disc == "zoh",
+                          bilinear=disc == "bilinear", warm_seconds=warm_seconds)
+    e = w.batch * w.L * w.Dn
+    opsel = valu_ops_per_element(w.N, disc, softplus=w.softplus)
+    main_ms = ph["main"]["mean_ms"]
+    item = {"workload": f"{WORKLOAD_TITLE[w.name]} (B{w.batch} L{w.L} D{w.Dn} N{w.N} {w.io}, "
+                        f"{disc})",
+            "ms_per_call": t_ms, "elem_per_s": e / (t_ms * 1e-3),
+            "hbm_gbps": synth.algorithmic_bytes(w) / (t_ms * 1e-3) / 1e9,
+            "hbm_frac": synth.algorithmic_bytes(w) / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "ops_per_element": opsel,
+            "call_valu_frac": opsel * e / (t_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
+            "main_valu_frac": opsel * e / (main_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
+            "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
+                           if k != "calls" and v["launches"]}}
+    return w, t_ms, ph, item
+
+
+def measure_rates():
+    """Chip rates from libmsprobe: v_exp_f32 and fp32 FMA issue (lane
+    operations per second, 8 independent chains per lane, 2048 workgroups of
+    256 threads), and copy / read bandwidth over 2 GiB (bytes moved per
+    second).  Each is the best of 3 timed launches after one warm launch."""
+    import ctypes
+    import torch
+    from selective_state_space_81_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.msprobe_exp.argtypes = [vp, i32, i32, vp]
+    lib.msprobe_fma.argtypes = [vp, i32, i32, vp]
+    lib.msprobe_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.msprobe_read.argtypes = [vp, vp, i64, i32, vp]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            rc = fn()
+            s1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: {rc}")
+            ts.append(s0.elapsed_time(s1) * 1e-3)
+        return min(ts)
+
+    blocks, iters = 2048, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    lane_ops = blocks * 256 * 8 * iters
+    t_exp = best(lambda: lib.msprobe_exp(out.data_ptr(), iters, blocks, sp))
+    t_fma = best(lambda: lib.msprobe_fma(out.data_ptr(), iters, blocks, sp))
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    words = nbytes // 16
+    cblocks = 256 * 16
+    acc = torch.empty(cblocks * 256, dtype=torch.int32, device="cuda")
+    t_copy = best(lambda: lib.msprobe_copy(src.data_ptr(), dst.data_ptr(), words, cblocks, sp))
+    t_read = best(lambda: lib.msprobe_read(src.data_ptr(), acc.data_ptr(), words, cblocks, sp))
+    del src, dst, acc, out
+    torch.cuda.empty_cache()
+    return {"exp_lane_ops_per_s": lane_ops / t_exp, "fma_lane_ops_per_s": lane_ops / t_fma,
+            "exp_vs_fma": t_fma / t_exp,
+            "copy_gbps": 2 * nbytes / t_copy / 1e9, "read_gbps": nbytes / t_read / 1e9,
+            "valu_peak_lane_ops_per_s": VALU_PEAK_TOPS * 1e12,
+            "method": "libmsprobe: 8 independent v_exp_f32 / v_fma_f32 chains per lane, "
+                      "2048 x 256 threads x 4096 steps; copy and read of 2 GiB with 16-byte "
+                      "non-temporal accesses; best of 3"}
 
 
 def main():
@@ -599,13 +702,14 @@ def main():
         print("--zoh and --bilinear are exclusive", file=sys.stderr)
         sys.exit(2)
     w, t_ms, ph = measure(ms, args.workload, args.steps, args.warmup, n_sets, zoh=args.zoh,
-                          bilinear=args.bilinear)
+                          bilinear=args.bilinear, warm_seconds=args.warm_seconds)
     disc = "zoh" if args.zoh else ("bilinear" if args.bilinear else "euler")
     torch.cuda.empty_cache()
     elems = w.batch * w.L * w.Dn
     alg_bytes = synth.algorithmic_bytes(w)
     main_ms = ph["main"]["mean_ms"]
-    ops = valu_ops_per_element(w.N, disc, softplus=w.softplus) * elems
+    opsel = valu_ops_per_element(w.N, disc, softplus=w.softplus)
+    ops = opsel * elems
     achieved = ops / (main_ms * 1e-3) / 1e12
     src = source_hash()
     gbps = alg_bytes / (t_ms * 1e-3) / 1e9
@@ -620,7 +724,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": f"f32 compute, {w.io} io",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TITLE[w.name],
                    "batch": w.batch, "seq_len": w.L, "d_inner": w.Dn, "d_state": w.N,
@@ -633,30 +737,43 @@ def main():
                      "traffic": load_traffic(w.name, src),
                      "kernel": "scan main pass (writes y)",
                      "kernel_mean_ms": main_ms,
-                     "ops_per_element": valu_ops_per_element(w.N, disc,
-                                                             softplus=w.softplus),
+                     "ops_per_element": opsel,
                      "ops_per_launch": ops,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS, "scope": "whole ms_scan_fwd call",
                 "algorithmic_bytes_per_call": alg_bytes},
-        "kernels_ms": {k: v["mean_ms"] for k, v in ph.items() if k != "calls" and v["launches"]},
+        "call_valu_frac": ops / (t_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
+        "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items() if k != "calls" and v["launches"]},
         "source_hash": src,
     }
-    if not args.no_secondary and args.workload == "m130m" and disc == "euler":
-        w3, t3, ph3 = measure(ms, "m3b", max(3, args.steps // 4), 2, 2)
-        e3 = w3.batch * w3.L * w3.Dn
-        out["secondary"] = {"workload": WORKLOAD_TITLE["m3b"] + " (B4 L8192 D5120 N16 bf16, "
-                                                                 "Euler)",
-                            "ms_per_call": t3, "elem_per_s": e3 / (t3 * 1e-3),
-                            "hbm_gbps": synth.algorithmic_bytes(w3) / (t3 * 1e-3) / 1e9,
-                            "kernels_ms": {k: v["mean_ms"] for k, v in ph3.items()
-                                           if k != "calls" and v["launches"]}}
+    secondary = not args.no_secondary and args.workload == "m130m" and disc == "euler"
+    if secondary:
+        rates = measure_rates()
+        out["rates"] = rates
+        out["hbm"]["frac_of_measured_copy"] = gbps / rates["copy_gbps"]
+        items = []
+        for d in ("euler", "zoh", "bilinear"):
+            _, _, _, it = fwd_item(ms, "m3b", d, max(4, args.steps // 4), 3, 2,
+                                   args.warm_seconds)
+            items.append(it)
+            torch.cuda.empty_cache()
+        out["secondary"] = items[0]
+        out["m3b_zoh"] = items[1]
+        out["m3b_bilinear"] = items[2]
+        wl, _, phl, it = fwd_item(ms, "long", "euler", 3, 1, 1, 0.0)
+        exps = wl.batch * wl.L * wl.Dn * wl.N
+        it["exps_per_call"] = exps
+        it["main_exp_per_s"] = exps / (phl["main"]["mean_ms"] * 1e-3)
+        it["main_exp_frac_of_measured_rate"] = it["main_exp_per_s"] / rates["exp_lane_ops_per_s"]
+        it["call_exp_per_s"] = exps / (it["ms_per_call"] * 1e-3)
+        out["long"] = it
         torch.cuda.empty_cache()
-    if not args.no_secondary and args.workload == "m130m" and disc == "euler":
         out["decode"] = measure_decode(ms)
+        out["decode"]["frac_of_measured_copy"] = out["decode"]["hbm_gbps"] / rates["copy_gbps"]
         torch.cuda.empty_cache()
         out["conv1d"] = measure_conv(ms)
+        out["conv1d"]["frac_of_measured_copy"] = out["conv1d"]["hbm_gbps"] / rates["copy_gbps"]
         torch.cuda.empty_cache()
         out["backward"] = measure_bwd(ms)
         torch.cuda.empty_cache()

@@ -285,17 +285,20 @@ int ms_abi_version(void);
 /*
  * Kernel timing, for benchmarks and profiling (not an operation of the
  * method).  Between ms_profile_begin and ms_profile_end, each of the next
- * `max_calls` successful calls of ms_scan_fwd / ms_state_update /
- * ms_conv1d_silu records a
- * pair of HIP events on its own stream around every kernel it launches, and
- * ms_profile_end waits for those events and returns the summed kernel times
- * per phase:
+ * `max_calls` successful calls of the library's entry points records a pair
+ * of HIP events on its own stream around every kernel it launches (up to 16
+ * per call), and ms_profile_end waits for those events and returns, per
+ * phase, the number of timed launches and their summed kernel time (a call
+ * that launches two kernels of one phase, like the backward's two carries,
+ * counts two launches):
  *   MS_PHASE_PREP     B/C staging pass
  *   MS_PHASE_SUMMARY  per-segment end states (sequence cut into segments)
  *   MS_PHASE_CARRY    composition of segment summaries into start states
- *   MS_PHASE_MAIN     the scan that writes y (and h_last)
+ *   MS_PHASE_MAIN     the scan that writes y (and h_last); the backward's
+ *                     per-segment gradient pass
  *   MS_PHASE_STEP     ms_state_update's kernel
  *   MS_PHASE_CONV     ms_conv1d_silu's kernel
+ *   MS_PHASE_REDUCE   the backward's fixed-order sums of partial gradients
  * A phase a call does not need records nothing.  Calls after the first
  * max_calls are not timed (out->calls counts the timed ones).  The event
  * records add a few microseconds per kernel to a call's wall time.
@@ -316,7 +319,8 @@ typedef enum {
     MS_PHASE_MAIN = 3,
     MS_PHASE_STEP = 4,
     MS_PHASE_CONV = 5,
-    MS_PHASE_COUNT = 6
+    MS_PHASE_REDUCE = 6,
+    MS_PHASE_COUNT = 7
 } ms_phase;
 
 typedef struct {

@@ -31,7 +31,7 @@ EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_stat
            "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd",
            "ms_scan_fwd_dtproj", "ms_scan_dtproj_workspace_bytes", "ms_scan_fwd_noalloc")
 
-PHASES = ("prep", "summary", "carry", "main", "step", "conv")  # ms_phase order
+PHASES = ("prep", "summary", "carry", "main", "step", "conv", "reduce")  # ms_phase order
 
 
 class MsDims(ctypes.Structure):
@@ -370,7 +370,9 @@ def profile_begin(max_calls: int) -> None:
 
 def profile_end() -> dict:
     """ms_profile_end: wait for the recorded events and return, per phase,
-    the number of timed launches and their mean kernel time in ms."""
+    the number of timed launches, their mean kernel time (ms per launch) and
+    the phase's kernel time per timed call (ms; a call may launch a phase's
+    kernel more than once)."""
     out = MsProfile()
     rc = load().ms_profile_end(ctypes.byref(out))
     if rc != MS_OK:
@@ -378,7 +380,8 @@ def profile_end() -> dict:
     res = {"calls": out.calls}
     for i, name in enumerate(PHASES):
         n = out.launches[i]
-        res[name] = {"launches": n, "mean_ms": (out.total_ms[i] / n) if n else None}
+        res[name] = {"launches": n, "mean_ms": (out.total_ms[i] / n) if n else None,
+                     "per_call_ms": (out.total_ms[i] / out.calls) if n else None}
     return res
 
 

@@ -17,6 +17,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsscan.so")
+# hardware rate probes used by bench.py (not part of libmsscan's C ABI)
+PROBE_SRC = os.path.join(CSRC, "probe.hip")
+PROBE_LIB = os.path.join(HERE, "libmsprobe.so")
 SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "scan_tile.hip"),
            os.path.join(CSRC, "scan_lane.hip"), os.path.join(CSRC, "scan_row.hip"),
            os.path.join(CSRC, "decode.hip"),
@@ -76,7 +79,21 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile libmsprobe.so (the benchmark's rate probes) for gfx950."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc()] + flags() + ["-x", "hip", "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def asm(out_dir: str) -> None:

@@ -183,7 +183,8 @@ enum : int {
     kPhaseCarry = 2,
     kPhaseMain = 3,
     kPhaseStep = 4,
-    kPhaseConv = 5
+    kPhaseConv = 5,
+    kPhaseReduce = 6
 };
 struct ProfScope {
     hipStream_t s;

@@ -16,14 +16,21 @@ namespace msscan {
 namespace {
 
 constexpr int kMaxCalls = 4096;
+constexpr int kMaxLaunchesPerCall = 16;  // event pairs kept per timed call
 
+// One pair of events per kernel launch: a call may launch several kernels of
+// one phase (the backward's two carries), and each launch is timed on its own.
 struct Profile {
     std::atomic<bool> on{false};
     std::mutex mu;
     int max_calls = 0;
-    int call = -1;                 // index of the call being recorded
-    std::vector<hipEvent_t> ev;    // [call][phase][edge]
-    std::vector<unsigned char> used;  // [call][phase]
+    int call = -1;                  // index of the call being recorded
+    int launches_in_call = 0;       // pairs taken by the current call
+    int open = -1;                  // pair whose end event is pending
+    std::vector<hipEvent_t> ev;     // [pair][edge]
+    std::vector<int> phase_of;      // [pair]: phase, or -1 (unused)
+    std::vector<unsigned char> done;  // [pair]: end event recorded
+    size_t next = 0;                // next free pair
 };
 
 Profile& prof() {
@@ -35,9 +42,13 @@ void release(Profile& p) {
     for (hipEvent_t e : p.ev)
         if (e) (void)hipEventDestroy(e);
     p.ev.clear();
-    p.used.clear();
+    p.phase_of.clear();
+    p.done.clear();
+    p.next = 0;
     p.max_calls = 0;
     p.call = -1;
+    p.open = -1;
+    p.launches_in_call = 0;
 }
 
 }  // namespace
@@ -47,6 +58,8 @@ void prof_call() {
     if (!p.on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> g(p.mu);
     if (p.call < p.max_calls) ++p.call;
+    p.launches_in_call = 0;
+    p.open = -1;
 }
 
 void prof_mark(hipStream_t s, int phase, int edge) {
@@ -54,8 +67,19 @@ void prof_mark(hipStream_t s, int phase, int edge) {
     if (!p.on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> g(p.mu);
     if (p.call < 0 || p.call >= p.max_calls || phase < 0 || phase >= MS_PHASE_COUNT) return;
-    const size_t k = (size_t)p.call * MS_PHASE_COUNT + (size_t)phase;
-    if (hipEventRecord(p.ev[2 * k + (edge ? 1 : 0)], s) == hipSuccess && edge) p.used[k] = 1;
+    if (edge == 0) {
+        if (p.launches_in_call >= kMaxLaunchesPerCall || p.next >= p.phase_of.size()) return;
+        const size_t k = p.next++;
+        ++p.launches_in_call;
+        if (hipEventRecord(p.ev[2 * k], s) != hipSuccess) return;
+        p.phase_of[k] = phase;
+        p.open = (int)k;
+    } else if (p.open >= 0) {
+        const size_t k = (size_t)p.open;
+        p.open = -1;
+        if (p.phase_of[k] == phase && hipEventRecord(p.ev[2 * k + 1], s) == hipSuccess)
+            p.done[k] = 1;
+    }
 }
 
 }  // namespace msscan
@@ -68,9 +92,11 @@ ms_status ms_profile_begin(int32_t max_calls) {
     Profile& p = prof();
     std::lock_guard<std::mutex> g(p.mu);
     if (p.on.load()) return MS_ERR_UNSUPPORTED;
-    const size_t n = (size_t)max_calls * MS_PHASE_COUNT;
-    p.ev.assign(2 * n, nullptr);
-    p.used.assign(n, 0);
+    const size_t pairs = (size_t)max_calls * kMaxLaunchesPerCall;
+    p.ev.assign(2 * pairs, nullptr);
+    p.phase_of.assign(pairs, -1);
+    p.done.assign(pairs, 0);
+    p.next = 0;
     for (hipEvent_t& e : p.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
@@ -80,6 +106,7 @@ ms_status ms_profile_begin(int32_t max_calls) {
     }
     p.max_calls = max_calls;
     p.call = -1;
+    p.open = -1;
     p.on.store(true);
     return MS_OK;
 }
@@ -92,21 +119,17 @@ ms_status ms_profile_end(ms_profile* out) {
     p.on.store(false);
     ms_profile r{};
     ms_status st = MS_OK;
-    const int calls = p.call < 0 ? 0 : (p.call < p.max_calls ? p.call + 1 : p.max_calls);
-    r.calls = calls;
-    for (int c = 0; c < calls; ++c) {
-        for (int ph = 0; ph < MS_PHASE_COUNT; ++ph) {
-            const size_t k = (size_t)c * MS_PHASE_COUNT + (size_t)ph;
-            if (!p.used[k]) continue;
-            float ms = 0.f;
-            if (hipEventSynchronize(p.ev[2 * k + 1]) != hipSuccess ||
-                hipEventElapsedTime(&ms, p.ev[2 * k], p.ev[2 * k + 1]) != hipSuccess) {
-                st = MS_ERR_HIP;
-                continue;
-            }
-            r.launches[ph] += 1;
-            r.total_ms[ph] += ms;
+    r.calls = p.call < 0 ? 0 : (p.call < p.max_calls ? p.call + 1 : p.max_calls);
+    for (size_t k = 0; k < p.next; ++k) {
+        if (!p.done[k]) continue;
+        float ms = 0.f;
+        if (hipEventSynchronize(p.ev[2 * k + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, p.ev[2 * k], p.ev[2 * k + 1]) != hipSuccess) {
+            st = MS_ERR_HIP;
+            continue;
         }
+        r.launches[p.phase_of[k]] += 1;
+        r.total_ms[p.phase_of[k]] += ms;
     }
     release(p);
     if (out) *out = r;

@@ -855,14 +855,23 @@ hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* 
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t nbc = (int64_t)f.batch * f.L * 2 * f.N;
-    hipLaunchKernelGGL(reduce_bc, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a, dB, dC,
-                       tiles);
+    {
+        ProfScope ps(s, kPhaseReduce);
+        hipLaunchKernelGGL(reduce_bc, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a,
+                           dB, dC, tiles);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t npar = (int64_t)f.Dn * (f.N + 2);
     const unsigned pblocks = (unsigned)((npar + 255) / 256);
-    hipLaunchKernelGGL(reduce_params, dim3(pblocks, kParamGroups), dim3(256), 0, s, a);
+    {
+        ProfScope ps(s, kPhaseReduce);
+        hipLaunchKernelGGL(reduce_params, dim3(pblocks, kParamGroups), dim3(256), 0, s, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_param_groups, dim3(pblocks), dim3(256), 0, s, a, dA, dD, dbias);
+    {
+        ProfScope ps(s, kPhaseReduce);
+        hipLaunchKernelGGL(reduce_param_groups, dim3(pblocks), dim3(256), 0, s, a, dA, dD, dbias);
+    }
     return hipGetLastError();
 }
 

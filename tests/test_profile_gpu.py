@@ -46,3 +46,21 @@ def test_profile_times_decode_step(gpu):
     assert prof["main"]["launches"] == 0
     with pytest.raises(gpu.MsError):
         gpu.profile_end()  # already closed
+
+
+def test_profile_times_every_backward_launch(gpu):
+    """The backward launches two carries (forward starts, adjoint) and three
+    reduction kernels per call: each launch is timed on its own."""
+    w = synth.workload("m130m", batch=2, L=512, Dn=128)
+    x = synth.scan_inputs(w, device="cuda", seed=4)
+    dy = torch.randn(w.batch, w.L, w.Dn, device="cuda").to(x["u"].dtype)
+    gpu.profile_begin(3)
+    for _ in range(3):
+        gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                     delta_bias=x["delta_bias"])
+    prof = gpu.profile_end()
+    assert prof["calls"] == 3
+    assert prof["carry"]["launches"] == 6 and prof["reduce"]["launches"] == 9
+    assert prof["summary"]["launches"] == 3 and prof["main"]["launches"] == 3
+    for k in ("carry", "reduce", "summary", "main"):
+        assert prof[k]["mean_ms"] > 0
