@@ -208,7 +208,7 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
                           int32_t io, void* stream);
 
 /*
- * Gradients of ms_scan_fwd, for training (reverse mode; d_state <= 16).
+ * Gradients of ms_scan_fwd, for training (reverse mode; any d_state 1..128).
  * Given dy = dL/dy ([batch][L][d_inner], io dtype) and optionally dh_last =
  * dL/dh_last ([batch][d_inner][d_state] fp32), returns dL/d of the inputs:
  *   du, ddelta, dz : [batch][L][d_inner] io dtype (ddelta is w.r.t. the raw
@@ -230,8 +230,12 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
  *   h0, D, z, delta_bias optional (NULL).  Outputs must not overlap inputs.
  *   workspace: ms_scan_bwd_workspace_bytes(dims, flags) bytes (never 0),
  *   16-byte aligned, no initialisation needed.
- * Statuses as for ms_scan_fwd; MS_ERR_UNSUPPORTED for d_state > 16.
- * Deterministic: partial sums are added in a fixed order.
+ * Statuses as for ms_scan_fwd.  Deterministic: partial sums are added in a
+ * fixed order.  Above 16 states the state is differentiated in slices of 16
+ * (the recurrence is diagonal, so the per-element gradients are sums over
+ * slices), each an fp32 problem with the gate and D taken out, and the
+ * workspace holds fp32 intermediates of the whole problem (about 40 bytes
+ * per element).
  */
 size_t ms_scan_bwd_workspace_bytes(const ms_dims* dims, uint32_t flags);
 ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const void* B,

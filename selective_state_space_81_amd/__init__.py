@@ -355,8 +355,7 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, 
                    softplus=True, zoh=False, bilinear=False):
     """The scan as a differentiable torch operation: the forward is
     ms_scan_fwd and the backward ms_scan_bwd (gradients of every tensor
-    argument; dB and dC are returned in B's and C's dtype).  Returns y.
-    The backward serves d_state <= 16."""
+    argument; dB and dC are returned in B's and C's dtype).  Returns y."""
     return _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, h0, softplus, zoh,
                                   bilinear)
 

@@ -445,11 +445,105 @@ size_t bwd_ws_floats(const BwdPlan& q) {
     return pad64(q.agg) + pad64(q.fdecay) + pad64(q.mu) + pad64(q.bdecay) + pad64(q.pbc) +
            pad64(q.pparam) + pad64(q.pgroup);
 }
+
+// Launches the 16-states-or-fewer backward kernels on one problem (the
+// inputs in `f`, the workspace at ws laid out by bwd_plan).
+hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, float* ws,
+                          const void* dy, const float* dh_last, void* du, void* ddelta, void* dz,
+                          float* dA, float* dB, float* dC, float* dD, float* dbias, float* dh0,
+                          bool bf16, hipStream_t hs) {
+    f.chunk_len = q.fwd.chunk_len;
+    f.chunks = q.fwd.chunks;
+    f.waves = 1;
+    const bool bil = (flags & MS_BILINEAR) != 0;
+    f.agg = ws;
+    ws += pad64(q.agg);
+    if (bil) f.prod = ws; else f.sdt = ws;
+    ws += pad64(q.fdecay);
+    msscan::BwdLaunch L{};
+    L.mu = ws;
+    ws += pad64(q.mu);
+    if (bil) L.prod_b = ws; else L.sdt_b = ws;
+    ws += pad64(q.bdecay);
+    L.pbc = ws;
+    ws += pad64(q.pbc);
+    L.pparam = ws;
+    L.pgroup = ws + pad64(q.pparam);
+    L.f = f;
+    L.dy = dy; L.dh_last = dh_last; L.du = du; L.ddelta = ddelta; L.dz = f.z ? dz : nullptr;
+    L.dh0 = dh0; L.dA = dA; L.dB = dB; L.dC = dC; L.dD = f.D ? dD : nullptr; L.dbias = dbias;
+    L.bf16 = bf16;
+    L.disc = disc_of(flags);
+    // Segment summaries (forward and adjoint), both carries, the per-segment
+    // gradients and the fixed-order sums.
+    return msscan::launch_scan_bwd(L, hs);
+}
+
+// Backward for d_state 17..128: slices of 16 states (bwd_wide.hip).  The
+// workspace holds, in order (fp32, each region padded to 64 floats):
+//   g, u32, d32 (bf16 io), B32, C32 (bf16 io), y_pre, the fp32 forward's own
+//   workspace, the slice inputs (A_s, B_s, C_s, h0_s, dh_last_s), the slice
+//   outputs (du_s, ddelta_s, dA_s, dB_s, dC_s, dbias_s, dh0_s), the totals
+//   (du, ddelta, dbias), the dD partials, and the 16-state backward's workspace.
+struct WideLayout {
+    ms_dims d16, dfwd;
+    BwdPlan inner;
+    msscan::Plan fwd;
+    size_t off[32];
+    size_t total;  // floats
+};
+enum : int {
+    kWg, kWu32, kWd32, kWB32, kWC32, kWy32, kWfws, kWAs, kWBs, kWCs, kWh0s, kWdhls, kWdus,
+    kWdvs, kWdAs, kWdBs, kWdCs, kWdbs, kWdh0s, kWduacc, kWdvacc, kWdbacc, kWdDp, kWinner,
+    kWcount
+};
+
+WideLayout wide_layout(const ms_dims& d, uint32_t flags) {
+    WideLayout w{};
+    const size_t E = (size_t)d.batch * (size_t)d.seqlen * (size_t)d.d_inner;
+    const size_t BL = (size_t)d.batch * (size_t)d.seqlen, BD = (size_t)d.batch * (size_t)d.d_inner;
+    const size_t Dn = (size_t)d.d_inner, S = msscan::kWideSlice;
+    const bool bf16 = d.io == MS_BF16;
+    w.d16 = d;
+    w.d16.d_state = msscan::kWideSlice;
+    w.d16.io = MS_F32;
+    w.dfwd = d;
+    w.dfwd.io = MS_F32;
+    w.inner = bwd_plan(w.d16, flags);
+    w.fwd = make_plan(w.dfwd, flags);
+    size_t n[kWcount] = {};
+    n[kWg] = E;
+    n[kWu32] = bf16 ? E : 0;
+    n[kWd32] = bf16 ? E : 0;
+    n[kWB32] = bf16 ? BL * (size_t)d.d_state : 0;
+    n[kWC32] = n[kWB32];
+    n[kWy32] = E;
+    n[kWfws] = (ws_bytes(w.fwd, w.dfwd, flags) + 3) / 4;
+    n[kWAs] = Dn * S;
+    n[kWBs] = n[kWCs] = BL * S;
+    n[kWh0s] = n[kWdhls] = BD * S;
+    n[kWdus] = n[kWdvs] = E;
+    n[kWdAs] = Dn * S;
+    n[kWdBs] = n[kWdCs] = BL * S;
+    n[kWdbs] = Dn;
+    n[kWdh0s] = BD * S;
+    n[kWduacc] = n[kWdvacc] = E;
+    n[kWdbacc] = Dn;
+    n[kWdDp] = (size_t)msscan::kWideGroups * Dn;
+    n[kWinner] = bwd_ws_floats(w.inner);
+    size_t off = 0;
+    for (int i = 0; i < kWcount; ++i) {
+        w.off[i] = off;
+        off += pad64(n[i]);
+    }
+    w.total = off;
+    return w;
+}
 }  // namespace
 
 size_t ms_scan_bwd_workspace_bytes(const ms_dims* dims, uint32_t flags) {
     if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
-    if (dims->d_state > 16) return (size_t)-1;
+    if (dims->d_state > 16) return wide_layout(*dims, flags).total * sizeof(float);
     return bwd_ws_floats(bwd_plan(*dims, flags)) * sizeof(float);
 }
 
@@ -463,9 +557,6 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
     ms_status st = check_dims(dims);
     if (st != MS_OK) return st;
     if ((st = check_flags(flags)) != MS_OK) return st;
-    if (dims->d_state > 16)
-        return fail(MS_ERR_UNSUPPORTED, "ms_scan_bwd supports d_state <= 16 (got %d)",
-                    dims->d_state);
     if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC)
         return fail(MS_ERR_NULL, "u, delta, A, B, C, dy, du, ddelta, dA, dB and dC are required");
     if ((z && !dz) || (D && !dD))
@@ -474,43 +565,84 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
                           ddelta, dA, dB, dC, dD, dz, dbias, dh0, workspace};
     for (const void* p : ptrs)
         if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
-    const BwdPlan q = bwd_plan(*dims, flags);
-    const size_t need = bwd_ws_floats(q) * sizeof(float);
+    const size_t need = ms_scan_bwd_workspace_bytes(dims, flags);
     if (!workspace || workspace_bytes < need)
         return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
+    const bool bf16 = dims->io == MS_BF16;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    msscan::prof_call();
 
     msscan::ScanArgs a{};
     a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-    a.h0 = h0; a.L = dims->seqlen; a.chunk_len = q.fwd.chunk_len; a.batch = dims->batch;
-    a.Dn = dims->d_inner; a.N = dims->d_state; a.chunks = q.fwd.chunks;
-    a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0; a.waves = 1;
-    const bool bil = (flags & MS_BILINEAR) != 0;
+    a.h0 = h0; a.L = dims->seqlen; a.batch = dims->batch; a.Dn = dims->d_inner;
+    a.N = dims->d_state; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    hipError_t e;
+    if (dims->d_state <= 16) {
+        e = run_bwd_narrow(a, bwd_plan(*dims, flags), flags, static_cast<float*>(workspace), dy,
+                           dh_last, du, ddelta, dz, dA, dB, dC, dD, dbias, dh0, bf16, hs);
+        if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        return MS_OK;
+    }
+
+    // d_state 17..128: slices of 16 states, each an fp32 problem with the
+    // gate and D taken out (bwd_wide.hip).
+    const WideLayout wl = wide_layout(*dims, flags);
     float* ws = static_cast<float*>(workspace);
-    a.agg = ws;
-    ws += pad64(q.agg);
-    if (bil) a.prod = ws; else a.sdt = ws;
-    ws += pad64(q.fdecay);
-    msscan::BwdLaunch L{};
-    L.mu = ws;
-    ws += pad64(q.mu);
-    if (bil) L.prod_b = ws; else L.sdt_b = ws;
-    ws += pad64(q.bdecay);
-    L.pbc = ws;
-    ws += pad64(q.pbc);
-    L.pparam = ws;
-    L.pgroup = ws + pad64(q.pparam);
-    L.f = a;
-    L.dy = dy; L.dh_last = dh_last; L.du = du; L.ddelta = ddelta; L.dz = z ? dz : nullptr;
-    L.dh0 = dh0; L.dA = dA; L.dB = dB; L.dC = dC; L.dD = D ? dD : nullptr; L.dbias = dbias;
-    L.bf16 = dims->io == MS_BF16;
-    L.disc = disc_of(flags);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    msscan::prof_call();
-    // Segment summaries (forward and adjoint), both carries, the per-segment
-    // gradients and the fixed-order sums.
-    const hipError_t e = msscan::launch_scan_bwd(L, hs);
-    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    auto R = [&](int i) { return ws + wl.off[i]; };
+    msscan::WideArgs w{};
+    w.u = u; w.delta = delta; w.A = A; w.B = B; w.C = C; w.D = D; w.z = z; w.dy = dy;
+    w.h0 = h0; w.dh_last = dh_last;
+    w.E = (int64_t)dims->batch * dims->seqlen * dims->d_inner;
+    w.BL = (int64_t)dims->batch * dims->seqlen;
+    w.BD = (int64_t)dims->batch * dims->d_inner;
+    w.BLN = w.BL * dims->d_state;
+    w.Dn = dims->d_inner; w.N = dims->d_state;
+    w.g = R(kWg); w.y32 = R(kWy32);
+    w.u32 = bf16 ? R(kWu32) : nullptr; w.d32 = bf16 ? R(kWd32) : nullptr;
+    w.B32 = bf16 ? R(kWB32) : nullptr; w.C32 = bf16 ? R(kWC32) : nullptr;
+    w.As = R(kWAs); w.Bs = R(kWBs); w.Cs = R(kWCs);
+    w.h0s = h0 ? R(kWh0s) : nullptr; w.dhls = dh_last ? R(kWdhls) : nullptr;
+    w.du_s = R(kWdus); w.dv_s = R(kWdvs); w.dAs = R(kWdAs); w.dBs = R(kWdBs); w.dCs = R(kWdCs);
+    w.dbias_s = R(kWdbs); w.dh0s = dh0 ? R(kWdh0s) : nullptr;
+    w.du_acc = R(kWduacc); w.dv_acc = R(kWdvacc); w.dbias_acc = R(kWdbacc); w.dD_part = R(kWdDp);
+    w.du = du; w.ddelta = ddelta; w.dz = z ? dz : nullptr;
+    w.dA = dA; w.dB = dB; w.dC = dC; w.dD = D ? dD : nullptr; w.dbias = dbias; w.dh0 = dh0;
+    if ((e = msscan::launch_wide_prep(w, bf16, hs)) != hipSuccess)
+        return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    const float* u32 = bf16 ? w.u32 : static_cast<const float*>(u);
+    const float* d32 = bf16 ? w.d32 : static_cast<const float*>(delta);
+    // y_pre = sum_n C h + D u in fp32, for dz: the forward scan without the gate.
+    if (z) {
+        msscan::ScanArgs fa = a;
+        fa.u = u32; fa.delta = d32; fa.z = nullptr; fa.y = w.y32; fa.h_last = nullptr;
+        fa.B = bf16 ? w.B32 : B; fa.C = bf16 ? w.C32 : C;
+        fa.chunk_len = wl.fwd.chunk_len; fa.chunks = wl.fwd.chunks; fa.waves = wl.fwd.waves;
+        fa.tiles = wl.fwd.tiles;
+        bind_workspace(fa, wl.fwd, wl.dfwd, flags, R(kWfws));
+        const int disc = disc_of(flags);
+        if (wl.fwd.tile_path == 3)
+            e = msscan::launch_scan_rows(wl.fwd, fa, false, disc, hs);
+        else if (wl.fwd.tile_path == 2)
+            e = msscan::launch_scan_lanes(wl.fwd, fa, false, disc, hs);
+        else
+            e = msscan::launch_scan_tiles(wl.fwd, fa, false, disc, hs);
+        if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
+    for (int n0 = 0; n0 < dims->d_state; n0 += msscan::kWideSlice) {
+        if ((e = msscan::launch_wide_gather(w, n0, bf16, hs)) != hipSuccess)
+            return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        msscan::ScanArgs sa = a;
+        sa.u = u32; sa.delta = d32; sa.A = w.As; sa.B = w.Bs; sa.C = w.Cs; sa.D = nullptr;
+        sa.z = nullptr; sa.h0 = w.h0s; sa.N = msscan::kWideSlice;
+        e = run_bwd_narrow(sa, wl.inner, flags, R(kWinner), w.g, w.dhls, w.du_s, w.dv_s, nullptr,
+                           w.dAs, w.dBs, w.dCs, nullptr, w.dbias_s, w.dh0s, false, hs);
+        if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+        if ((e = msscan::launch_wide_accumulate(w, n0, hs)) != hipSuccess)
+            return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    }
+    if ((e = msscan::launch_wide_finish(w, bf16, hs)) != hipSuccess)
+        return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }
 

@@ -171,6 +171,40 @@ constexpr int kParamGroups = 16;  // first-level groups of the parameter sums
 constexpr int kBwdWaves = 4;  // backward segments per workgroup (one wave each)
 hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s);
 
+// Backward for d_state 17..128 (bwd_wide.hip): the state is differentiated
+// in slices of kWideSlice states by the kernels above, run as fp32 problems
+// with the gate and D taken out; these helpers prepare, gather, accumulate
+// and combine.  Sizes: E = batch*L*Dn, BL = batch*L, BD = batch*Dn,
+// BLN = batch*L*N.
+constexpr int kWideSlice = 16;
+constexpr int kWideGroups = 64;  // row groups of the dD partial sums
+struct WideArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const void* dy;
+    const float* h0;
+    const float* dh_last;
+    int64_t E, BL, BD, BLN;
+    int Dn, N;
+    // workspace (fp32)
+    float *g, *u32, *d32, *B32, *C32, *y32;
+    float *As, *Bs, *Cs, *h0s, *dhls;
+    float *du_s, *dv_s, *dAs, *dBs, *dCs, *dbias_s, *dh0s;
+    float *du_acc, *dv_acc, *dbias_acc, *dD_part;
+    // outputs
+    void *du, *ddelta, *dz;
+    float *dA, *dB, *dC, *dD, *dbias, *dh0;
+};
+hipError_t launch_wide_prep(const WideArgs& w, bool bf16, hipStream_t s);
+hipError_t launch_wide_gather(const WideArgs& w, int n0, bool bf16, hipStream_t s);
+hipError_t launch_wide_accumulate(const WideArgs& w, int n0, hipStream_t s);
+hipError_t launch_wide_finish(const WideArgs& w, bool bf16, hipStream_t s);
+
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;
 // ProfScope records the phase's begin event at construction and its end
 // event at destruction, around one kernel launch.  Both do nothing unless a

@@ -154,3 +154,101 @@ def test_bwd_zero_A_entries(gpu, disc):
     A[::3, 5] = -1e-6
     x["A"] = A
     _compare(gpu, x, "f32", disc)
+
+
+# ---- d_state 17..128: the state differentiated in slices of 16 ---------------------
+WIDE = [
+    # batch, L, Dn, N, io
+    (1, 40, 24, 32, "f32"),
+    (2, 70, 40, 64, "bf16"),
+    (1, 33, 17, 24, "f32"),    # last slice half padded
+    (1, 50, 16, 100, "bf16"),  # 7 slices, the last with 4 states
+    (1, 20, 8, 128, "f32"),
+    (1, 1, 64, 48, "f32"),     # a single timestep
+]
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "B{}L{}D{}N{}{}".format(*s))
+def test_bwd_wide_state(gpu, shape, disc):
+    batch, L, Dn, N, io = shape
+    x = _inputs(batch, L, Dn, N, io, seed=41)
+    _compare(gpu, x, io, disc)
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_wide_without_optional_terms(gpu, disc):
+    x = _inputs(2, 60, 48, 32, "bf16", seed=42, optional=False)
+    _compare(gpu, x, "bf16", disc)
+
+
+def test_bwd_wide_deterministic(gpu):
+    x = _inputs(2, 200, 96, 64, "bf16", seed=43)
+    args = (x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"])
+    kw = dict(D=x["D"], z=x["z"], delta_bias=x["delta_bias"], h0=x["h0"], dh_last=x["dh_last"])
+    g1 = gpu.scan_bwd(*args, **kw)
+    g2 = gpu.scan_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
+
+
+def test_bwd_wide_full_channels(gpu):
+    """d_state 64 over all 1536 channels of the long-context layer, 4096
+    steps (every gradient, dB and dC summed over every channel)."""
+    w = synth.workload("long", L=4096)
+    x = synth.scan_inputs(w, device=DEV, seed=5)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    x["dy"] = torch.randn(w.batch, w.L, w.Dn, generator=g, device=DEV).to(x["u"].dtype)
+    _compare(gpu, x, w.io, "euler", softplus=w.softplus)
+
+
+def _channels(x, idx):
+    """The sub-problem made of the channels idx (each channel's recurrence
+    is independent; B and C are shared)."""
+    ii = torch.as_tensor(idx, device=DEV)
+    sub = dict(x)
+    for k in ("u", "delta", "z", "dy"):
+        if x.get(k) is not None:
+            sub[k] = x[k].index_select(2, ii).contiguous()
+    for k in ("A", "D", "delta_bias"):
+        if x.get(k) is not None:
+            sub[k] = x[k].index_select(0, ii).contiguous()
+    return sub
+
+
+def test_bwd_wide_long_context_sampled(gpu):
+    """The long-context shape B1 L65536 D1536 N64 (bf16, Euler): the full
+    backward's per-channel gradients (du, ddelta, dz, dA, dD, dbias, dh0) on
+    48 sampled channels against the oracle run on those channels; and the
+    channel sums dB, dC of the sub-problem made of the sampled channels
+    (through the same kernels) against the oracle's."""
+    from helpers import sample_channels
+    w = synth.workload("long", L=65536)
+    x = synth.scan_inputs(w, device=DEV, seed=6)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(79)
+    x["dy"] = torch.randn(w.batch, w.L, w.Dn, generator=g, device=DEV).to(x["u"].dtype)
+    idx = sample_channels(w.Dn, 48, seed=3)
+    full = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
+                        delta_bias=x.get("delta_bias"), softplus=w.softplus)
+    torch.cuda.synchronize()
+    sub = _channels(x, idx)
+    ref = oracle.scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["dy"],
+                          D=sub["D"], z=sub["z"], delta_bias=sub.get("delta_bias"),
+                          softplus=w.softplus)
+    ii = torch.as_tensor(idx, device=DEV)
+    for k in ("du", "ddelta", "dz"):
+        _check(full[k].index_select(2, ii), ref[k], w.io, k)
+    _check(full["dA"].index_select(0, ii), ref["dA"], "f32", "dA")
+    _check(full["dD"].index_select(0, ii), ref["dD"], "f32", "dD")
+    part = gpu.scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["dy"],
+                        D=sub["D"], z=sub["z"], delta_bias=sub.get("delta_bias"),
+                        softplus=w.softplus)
+    torch.cuda.synchronize()
+    _check(part["dB"], ref["dB"], "f32", "dB")
+    _check(part["dC"], ref["dC"], "f32", "dC")
+    del x, full, part
+    torch.cuda.empty_cache()
