@@ -358,7 +358,9 @@ def measure_bwd(ms, reps=20, warm=3):
         return s0.elapsed_time(s1) / reps
 
     t_zoh, t_bil = other(True, False), other(False, True)
-    return {"workload": "gradients of the Mamba-130M-layer scan (ms_scan_bwd: du, ddelta, dz, "
+    wide = measure_bwd_wide(ms)
+    return {"wide_state": wide,
+            "workload": "gradients of the Mamba-130M-layer scan (ms_scan_bwd: du, ddelta, dz, "
                         "dA, dB, dC, dD, dbias, dh0), Euler, bf16",
             "zoh_ms_per_call": t_zoh, "bilinear_ms_per_call": t_bil,
             "ms_per_call": t_ms, "elem_per_s": elems / (t_ms * 1e-3),
@@ -367,6 +369,53 @@ def measure_bwd(ms, reps=20, warm=3):
                               / VALU_PEAK_TOPS,
             "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
                            if k != "calls" and v["launches"]}}
+
+
+def measure_bwd_wide(ms, reps=3):
+    """ms_scan_bwd above 16 states: the long-context layer shape shortened to
+    L 65536 (B1 D1536 N64, bf16, Euler, no softplus or bias), every
+    gradient; ms per call and the phases' kernel times per call."""
+    import torch
+    import synth
+    w = synth.workload("long", L=65536)
+    x = synth.scan_inputs(w, device="cuda", seed=0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    dy = torch.randn(w.batch, w.L, w.Dn, generator=g, device="cuda").to(x["u"].dtype)
+    ws = torch.empty(ms.scan_bwd_workspace_bytes(w.batch, w.L, w.Dn, w.N, ms.MS_BF16,
+                                                 ms.flags(w.softplus)),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        ms.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                    delta_bias=x.get("delta_bias"), softplus=w.softplus, workspace=ws,
+                    stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(reps):
+        call()
+    s1.record(stream)
+    torch.cuda.synchronize()
+    t_ms = s0.elapsed_time(s1) / reps
+    ms.profile_begin(reps)
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    ph = ms.profile_end()
+    elems = w.batch * w.L * w.Dn
+    out = {"workload": f"gradients of the long-context scan shape at L {w.L} (B{w.batch} "
+                       f"D{w.Dn} N{w.N}, bf16, Euler): d_state 64 in four 16-state slices",
+           "ms_per_call": t_ms, "elem_per_s": elems / (t_ms * 1e-3),
+           "workspace_bytes": int(ws.numel()),
+           "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
+                          if k != "calls" and v["launches"]}}
+    del x, dy, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def measure_dtproj(ms, rank=16, reps=20):
@@ -626,7 +675,7 @@ def fwd_item(ms, w_name, disc, steps, warmup, n_sets, warm_seconds):
 def measure_rates():
     """Chip rates from libmsprobe: v_exp_f32 and fp32 FMA issue (lane
     operations per second, 8 independent chains per lane, 2048 workgroups of
-    256 threads), and copy / read bandwidth over 2 GiB (bytes moved per
+    256 threads), and copy / read bandwidth over 1 GiB (bytes moved per
     second).  Each is the best of 3 timed launches after one warm launch."""
     import ctypes
     import torch
@@ -660,11 +709,11 @@ def measure_rates():
     lane_ops = blocks * 256 * 8 * iters
     t_exp = best(lambda: lib.msprobe_exp(out.data_ptr(), iters, blocks, sp))
     t_fma = best(lambda: lib.msprobe_fma(out.data_ptr(), iters, blocks, sp))
-    nbytes = 2 << 30
+    nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     words = nbytes // 16
-    cblocks = 256 * 16
+    cblocks = 16384
     acc = torch.empty(cblocks * 256, dtype=torch.int32, device="cuda")
     t_copy = best(lambda: lib.msprobe_copy(src.data_ptr(), dst.data_ptr(), words, cblocks, sp))
     t_read = best(lambda: lib.msprobe_read(src.data_ptr(), acc.data_ptr(), words, cblocks, sp))
@@ -675,7 +724,8 @@ def measure_rates():
             "copy_gbps": 2 * nbytes / t_copy / 1e9, "read_gbps": nbytes / t_read / 1e9,
             "valu_peak_lane_ops_per_s": VALU_PEAK_TOPS * 1e12,
             "method": "libmsprobe: 8 independent v_exp_f32 / v_fma_f32 chains per lane, "
-                      "2048 x 256 threads x 4096 steps; copy and read of 2 GiB with 16-byte "
+                      "2048 x 256 threads x 4096 steps; copy (one contiguous chunk per "
+                      "workgroup, 16384 workgroups) and read of 1 GiB with 16-byte "
                       "non-temporal accesses; best of 3"}
 
 

@@ -49,22 +49,24 @@ __global__ void __launch_bounds__(256) fma_chains(float* out, int iters) {
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-// Grid-stride passes of kUnroll words per thread, the loads of a pass issued
-// before its stores, so each wave keeps kUnroll 16-byte accesses in flight.
+// Each workgroup copies one contiguous chunk of `per` words, kUnroll words
+// per thread per pass with the pass's loads issued before its stores (of the
+// shapes tried -- grid-stride passes of 1, 4 or 8 words per thread, cached or
+// non-temporal, 1k to 16k workgroups -- the fastest on this GPU).
 constexpr int kUnroll = 4;
 
 __global__ void __launch_bounds__(256) copy16(const u4* __restrict__ src, u4* __restrict__ dst,
-                                              int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+                                              int64_t n, int64_t per) {
+    const int64_t b0 = (int64_t)blockIdx.x * per, b1 = min(n, b0 + per);
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += 256 * kUnroll) {
         u4 v[kUnroll];
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) v[k] = __builtin_nontemporal_load(&src[i + k * stride]);
+        for (int k = 0; k < kUnroll; ++k)
+            if (i + k * 256 < b1) v[k] = __builtin_nontemporal_load(&src[i + k * 256]);
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) __builtin_nontemporal_store(v[k], &dst[i + k * stride]);
+        for (int k = 0; k < kUnroll; ++k)
+            if (i + k * 256 < b1) __builtin_nontemporal_store(v[k], &dst[i + k * 256]);
     }
-    for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
 __global__ void __launch_bounds__(256) read16(const u4* __restrict__ src, uint32_t* out, int64_t n) {
@@ -105,8 +107,9 @@ int msprobe_fma(float* out, int iters, int blocks, void* stream) {
 // src, dst: n 16-byte words each, 16-byte aligned, not overlapping.
 int msprobe_copy(const void* src, void* dst, int64_t n, int blocks, void* stream) {
     if (!src || !dst || n < 1 || blocks < 1) return (int)hipErrorInvalidValue;
+    const int64_t per = ((n + blocks - 1) / blocks + 255) / 256 * 256;
     hipLaunchKernelGGL(copy16, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                       static_cast<const u4*>(src), static_cast<u4*>(dst), n);
+                       static_cast<const u4*>(src), static_cast<u4*>(dst), n, per);
     return (int)hipGetLastError();
 }
 
