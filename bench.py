@@ -12,7 +12,8 @@ kernel's roofline position, from its HIP-event kernel times recorded on the
 launch stream over the timed region (ms_profile_*); the whole call's HBM
 rate against the 8 TB/s peak and its VALU fraction; line items for the 3B
 layer (Euler, ZOH, bilinear), the long-context d_state 64 scan (with its
-exponential rate against the measured v_exp_f32 rate), decode, conv1d,
+exponential rate against the measured v_exp_f32 rate), the wide-state scans
+(d_state 128 Euler, d_state 64 ZOH; batch 2, L 8192, d_inner 1536), decode, conv1d,
 backward and the fused step projection; the chip rates measured by
 libmsprobe (v_exp_f32, fp32 FMA, copy and read bandwidth); and the fp64 CPU
 oracle timed on this host's cores on a bounded sample of the same workload.
@@ -60,7 +61,9 @@ MAIN_KERNEL_RE = (r"scan_row<(?:[^,>]*, ){3}false[,>]|scan_lane<(?:[^,>]*, ){6}f
                   r"scan_tile<[^>]*false>")
 WORKLOAD_TITLE = {"m130m": "Mamba-130M-layer selective scan (S6) forward",
                   "m3b": "Mamba-3B-layer selective scan (S6) forward",
-                  "long": "long-context selective scan (S6) forward, d_state 64"}
+                  "long": "long-context selective scan (S6) forward, d_state 64",
+                  "wide128": "wide-state selective scan (S6) forward, d_state 128",
+                  "wide64": "wide-state selective scan (S6) forward, d_state 64"}
 
 
 def parse():
@@ -70,7 +73,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warm-seconds", type=float, default=0.25,
                     help="minimum wall time of the untimed warm-up calls")
-    ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b", "long"])
+    ap.add_argument("--workload", default="m130m", choices=["m130m", "m3b", "long", "wide128", "wide64"])
     ap.add_argument("--zoh", action="store_true", help="zero-order hold instead of Euler")
     ap.add_argument("--bilinear", action="store_true", help="bilinear instead of Euler")
     ap.add_argument("--buffer-sets", type=int, default=4)
@@ -567,7 +570,7 @@ def _csv(dirname, suffix):
 def _short(name):
     m = re.search(r"(scan_row<[^>]*>|scan_lane<[^>]*>|scan_tile<[^>]*>|"
                   r"bc_prepare<[^>]*>|carry_chain<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
-                  r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|"
+                  r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|wide_\w+(?:<[^>]*>)?|"
                   r"reduce_param_groups|reduce_params|"
                   r"neg_kernel)", name)
     return m.group(1) if m else name[:60]
@@ -613,7 +616,7 @@ def rocprof_summary(args):
         for k in sorted(fetch):
             if k == "neg_kernel" or k not in write or not re.search(
                     r"scan_|carry_|bc_prep|step_quads|conv1d_kernel|bwd_main|"
-                    r"seg_summaries|reduce_|copy16|read16", k):
+                    r"seg_summaries|reduce_|wide_|copy16|read16", k):
                 continue
             mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
             print(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {mb:.2f} |")
@@ -626,7 +629,7 @@ def rocprof_summary(args):
         acc = {}
         for r in _csv(dirname, "counter_collection.csv"):
             k = _short(r["Kernel_Name"])
-            if not re.search(r"scan_|carry_|bc_prep|step_quads|bwd_main|seg_summ|conv1d", k):
+            if not re.search(r"scan_|carry_|bc_prep|step_quads|bwd_main|seg_summ|conv1d|wide_", k):
                 continue
             acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
@@ -818,6 +821,10 @@ def main():
         it["main_exp_frac_of_measured_rate"] = it["main_exp_per_s"] / rates["exp_lane_ops_per_s"]
         it["call_exp_per_s"] = exps / (it["ms_per_call"] * 1e-3)
         out["long"] = it
+        torch.cuda.empty_cache()
+        _, _, _, out["wide128_euler"] = fwd_item(ms, "wide128", "euler", 5, 2, 2, args.warm_seconds)
+        torch.cuda.empty_cache()
+        _, _, _, out["wide64_zoh"] = fwd_item(ms, "wide64", "zoh", 5, 2, 2, args.warm_seconds)
         torch.cuda.empty_cache()
         out["decode"] = measure_decode(ms)
         out["decode"]["frac_of_measured_copy"] = out["decode"]["hbm_gbps"] / rates["copy_gbps"]

@@ -61,16 +61,19 @@ int disc_of(uint32_t flags) {
                                  : ((flags & MS_ZOH) ? msscan::dev::kZoh : msscan::dev::kEuler);
 }
 
-// Fast paths.  Both map one 64-channel tile of one batch row to a
+// Paths, in the order they are tried:
+//   row path (below): a channel's states across the lanes of 1, 2 or 4 DPP
+//     rows -- d_state 9..16 always, 17..128 when batch x d_inner alone fills
+//     the chip (Euler at 33..64 excepted);
+//   lane path (d_state 8, 16, 32; 64 with Euler): one wave per workgroup,
+//     all states of a channel in one lane;
+//   tile path (d_state 128, 64 with ZOH or bilinear): several waves split
+//     d_state and share per-element work through LDS.
+// The lane and tile paths map one 64-channel tile of one batch row to a
 // workgroup and cut the sequence into segments until about kTargetWaves
 // waves exist (many waves per CU keep the VALU issuing; a segment after the
 // first costs a summary pass over it, so segments are not cut shorter than
 // kMinSegment).
-//   lane path (d_state 8, 16, 32; 64 with Euler): one wave per workgroup,
-//     all states of a channel in one lane;
-//   tile path (d_state 128, 64 with ZOH or bilinear, or the others when the lane path is
-//     compiled out): several waves split d_state and share per-element work
-//     through LDS.
 #ifndef MSSCAN_TILE_WAVES
 #define MSSCAN_TILE_WAVES 4
 #endif
@@ -108,13 +111,44 @@ void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p,
 #ifndef MSSCAN_ROW_MIN_SEGMENT
 #define MSSCAN_ROW_MIN_SEGMENT 256
 #endif
-bool row_plan(const ms_dims& d, msscan::Plan& p) {
-    if (d.d_state <= 8 || d.d_state > 16) return false;
+// d_state 17..128 spreads a channel over 2 or 4 rows (with 2 states per lane
+// past 64).  Each row repeats the channel's per-element work, so those shapes
+// take the row path only when they need no cut at all (batch x d_inner x rows
+// alone gives MSSCAN_ROW_WIDE_MIN_WAVES waves) and the io tiles move whole;
+// otherwise the lane or tile path, whose summaries are cheaper per state,
+// takes them.
+#ifndef MSSCAN_ROW_WIDE_MIN_WAVES
+#define MSSCAN_ROW_WIDE_MIN_WAVES 2048
+#endif
+static_assert(MSSCAN_ROW_WIDE_MIN_WAVES >= MSSCAN_ROW_TARGET_WAVES,
+              "wide rows run the sequence as one segment");
+bool row_plan(const ms_dims& d, int disc, msscan::Plan& p) {
+    if (d.d_state <= 8) return false;
+    // d_state 33..64 with Euler: the lane kernel (all 64 states in a lane)
+    // is as fast or faster there, summaries included (measured at batch 2,
+    // L 8192, d_inner 1536: 0.59 against 0.64 ms at d_state 64, equal at 48)
+    if (disc == msscan::dev::kEuler && d.d_state > 32 && d.d_state <= 64 &&
+        msscan::lane_variant_exists(64, disc))
+        return false;
+    int rows = 1, spl = 1;
+    if (d.d_state > 16) {
+        rows = d.d_state <= 32 ? 2 : 4;
+        spl = d.d_state <= 64 ? 1 : 2;
+        // io tiles of 16 / rows channels move in whole chunks (16 bytes, or
+        // 8 for 4 bf16 channels)
+        const int cw = d.io == MS_BF16 ? (rows == 4 ? 4 : 8) : 4;
+        if (d.d_inner % cw != 0) return false;
+    }
+    const int ch = msscan::kRowCh / rows;
+    const int tiles = (d.d_inner + ch - 1) / ch;
+    if (rows > 1 && (int64_t)d.batch * tiles * msscan::kRowWaves < MSSCAN_ROW_WIDE_MIN_WAVES)
+        return false;
     p.tile_path = 3;
-    p.ns = 16;
+    p.ns = 16 * rows * spl;
     p.waves = msscan::kRowWaves;
-    p.tiles = (d.d_inner + msscan::kRowCh - 1) / msscan::kRowCh;
-    cut_sequence(d, (int64_t)d.batch * p.tiles * msscan::kRowWaves, p, MSSCAN_ROW_TARGET_WAVES,
+    p.rows = rows;
+    p.tiles = tiles;
+    cut_sequence(d, (int64_t)d.batch * p.tiles * p.waves, p, MSSCAN_ROW_TARGET_WAVES,
                  MSSCAN_ROW_MIN_SEGMENT);
     return true;
 }
@@ -168,7 +202,8 @@ msscan::Plan make_plan(const ms_dims& d, uint32_t flags, bool rows = true) {
     // Per segment boundary and channel: N summary states, plus the segment
     // decay -- one sum of dt, or N products of A_bar for the bilinear form.
     const size_t per_channel = (size_t)N + ((flags & MS_BILINEAR) ? (size_t)N : 1);
-    if ((rows && row_plan(d, p)) || lane_plan(d, disc_of(flags), p) || tile_plan(d, p)) {
+    if ((rows && row_plan(d, disc_of(flags), p)) || lane_plan(d, disc_of(flags), p) ||
+        tile_plan(d, p)) {
         if (p.chunks > 1) {
             const size_t km1 = (size_t)(p.chunks - 1);
             p.ws_floats = km1 * (size_t)d.batch * (size_t)d.d_inner * per_channel;

@@ -34,7 +34,8 @@ struct Plan {
     int waves;          // waves per workgroup = ceil(d_state / ns)
     int chunks;         // pieces along L
     int64_t chunk_len;  // steps per piece (last piece may be shorter)
-    int tiles;          // channel tiles per batch row: ceil(d_inner / 64), or / kRowCh (rows)
+    int tiles;          // channel tiles per batch row: ceil(d_inner / 64), or / (kRowCh / rows)
+    int rows;           // row path: DPP rows per channel (1, 2, 4)
     size_t ws_floats;   // workspace floats (0 when chunks == 1)
     size_t bc_floats;   // tile path: fp32 B/C copy laid out per wave (0 if unused)
 };
@@ -124,10 +125,15 @@ constexpr int kCarryGroup = 8;  // slots whose loads one carry thread issues tog
 hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s);
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);  // the forward summaries of a
 bool tile_variant_exists(int ns, int waves);
-// Row path (scan_row.hip): d_state <= 16, one 16-lane DPP row per channel.
+// Row path (scan_row.hip, scan_row_wide.hip): a channel on 1, 2 or 4 16-lane
+// DPP rows of one wave (d_state up to 16, 32 or 64; 128 with two states per
+// lane); a workgroup is kRowWaves waves, kRowCh rows: kRowCh / rows channels.
 constexpr int kRowWaves = 4;            // waves per workgroup
-constexpr int kRowCh = 4 * kRowWaves;   // channels per workgroup (4 rows per wave)
+constexpr int kRowCh = 4 * kRowWaves;   // rows per workgroup (channels at one row each)
 hipError_t launch_scan_rows(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
+// several rows per channel (plan waves = kRowWaves * rows, ns = 16 * rows * states per lane)
+hipError_t launch_scan_rows_wide(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                 hipStream_t s);
 hipError_t launch_scan_lanes(const Plan& p, const ScanArgs& a, bool bf16, int disc, hipStream_t s);
 bool lane_variant_exists(int n, int disc);
 // Lane path with the low-rank dt projection fused in (a.dtx, a.wdt, a.rank).

@@ -23,6 +23,10 @@ pages' initialisation advice; each recipe is listed in full below):
   long      batch 1, L 1,048,576, d_inner 1536, d_state 64, bf16.
             A[d,n] = -exp(4n/63); delta itself log-uniform[1e-3, 1e-1]
             (softplus off, no bias); u, B, C, z, D ~ N(0,1).
+  wide128   batch 2, L 8192, d_inner 1536, d_state 128, bf16, value
+            distributions as ``tiny`` (the pages' d_state 64-128 advice for long
+            inputs, at a length the whole layer fits in a few hundred MB).
+  wide64    as ``wide128`` with d_state 64.
   decode    recurrent decode: batch 256, d_inner 5120, d_state 16; h ~ N(0,1)
             fp32; per step x, delta_raw, B, C, z drawn as ``tiny`` in bf16.
 """
@@ -64,6 +68,10 @@ WORKLOADS: Dict[str, Workload] = {
                     ("euler", "zoh")),
     "long": Workload("long", 1, 1 << 20, 1536, 64, "bf16", "neg_exp4", "logu_direct", False,
                      ("euler",)),
+    "wide128": Workload("wide128", 2, 8192, 1536, 128, "bf16", "neg_n1", "spinv_logu", True,
+                        ("euler", "zoh")),
+    "wide64": Workload("wide64", 2, 8192, 1536, 64, "bf16", "neg_n1", "spinv_logu", True,
+                       ("euler", "zoh")),
     "decode": Workload("decode", 256, 1, 5120, 16, "bf16", "neg_n1", "spinv_logu", True,
                        ("euler", "zoh"), steps=64),
 }

@@ -86,9 +86,15 @@ def test_workspace_size_function():
     def ws(b, L, D, N, flags=1):
         return lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(b, L, D, N, 1)), flags)
 
-    # d_state 100 runs padded on the 128-state tile kernels; over one piece its
-    # workspace is just their staged fp32 B/C rows, 128 states wide.
-    assert ws(64, 256, 4096, 100) == 64 * 256 * 2 * 128 * 4
+    # d_state 100 with few channels runs padded on the 128-state tile kernels;
+    # over one piece its workspace is just their staged fp32 B/C rows, 128
+    # states wide.
+    assert ws(1, 64, 1024, 100) == 1 * 64 * 2 * 128 * 4
+    # With batch x d_inner enough to fill the chip uncut, d_state 17..128 runs
+    # on row kernels with 2 or 4 rows per channel: one pass, no workspace.
+    assert ws(64, 256, 4096, 100) == 0
+    assert ws(8, 2048, 1536, 17) == 0 and ws(2, 8192, 1536, 64, 3) == 0
+    assert ws(2, 2048, 1536, 128) == 0 and ws(2, 2048, 1536, 128, 1 | 4) == 0
     # The row kernels (d_state 9..16) run the 130M and 3B layers whole: one
     # pass, no segment summaries, no workspace.
     assert ws(8, 2048, 1536, 16) == 0
@@ -100,20 +106,21 @@ def test_workspace_size_function():
     km1 = 32 - 1  # 64 waves per segment -> 2048 / 64 = 32 segments
     assert n == _seg_ws(1, 256, 16, km1)
     assert ws(1, 65536, 256, 16, 1 | 4) == _seg_ws(1, 256, 16, km1, bilinear=True)
-    # A d_state without a lane kernel of its own (17) runs padded on one: its
-    # segment summaries keep the true d_state.
-    n17 = ws(8, 2048, 1536, 17)
-    k17 = 2048 // 64 - 1  # lane plan: 16384 / 192 waves -> capped at 64-step segments
-    assert n17 == _seg_ws(8, 1536, 17, k17)
+    # A d_state without a lane kernel of its own (17), with too few channels
+    # for the wide rows (768 waves), runs padded on a lane kernel: its segment
+    # summaries keep the true d_state.
+    n17 = ws(1, 2048, 1536, 17)
+    k17 = 2048 // 64 - 1  # lane plan: 16384 / 24 waves -> capped at 64-step segments
+    assert n17 == _seg_ws(1, 1536, 17, k17)
     # Invalid dims -> (size_t)-1.
     assert ws(1, 0, 64, 16) == ctypes.c_size_t(-1).value
-    # The tile kernels (d_state 128, or 64 with ZOH) stage fp32 B/C rows: at
-    # least batch*L*2*N floats.
-    assert ws(2, 2048, 1536, 128) >= 2 * 2048 * 2 * 128 * 4
-    assert ws(2, 2048, 1536, 64, 3) >= 2 * 2048 * 2 * 64 * 4
+    # The tile kernels (d_state 128, or 64 with ZOH, when the wide rows would
+    # not fill the chip) stage fp32 B/C rows: at least batch*L*2*N floats.
+    assert ws(1, 2048, 1536, 128) >= 1 * 2048 * 2 * 128 * 4
+    assert ws(1, 2048, 1536, 64, 3) >= 1 * 2048 * 2 * 64 * 4
     # d_state 64 with Euler takes the lane kernels (summaries only, no staged
     # B/C rows), so it needs less than the same shape with ZOH.
-    assert ws(2, 2048, 1536, 64) < ws(2, 2048, 1536, 64, 3)
+    assert ws(1, 2048, 1536, 64) < ws(1, 2048, 1536, 64, 3)
     # Deterministic and independent of flags that do not change the plan.
     a = ws(1, 65536, 256, 16)
     assert a == ws(1, 65536, 256, 16, 3)

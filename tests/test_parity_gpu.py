@@ -71,6 +71,17 @@ EDGE = [
     (3, 5000, 33, 16, "bf16"),
     (1, 16, 16, 16, "f32"),
     (1, 17, 5, 13, "bf16"),
+    # row kernels with 2 or 4 rows per channel (d_state 17..64) and 2 states
+    # per lane (65..128): taken when batch x d_inner fills the chip uncut
+    # (2048 waves); padded states, and a channel tail inside the last
+    # 8-channel workgroup (fp32, 2 rows)
+    (2, 300, 2048, 32, "bf16"),
+    (2, 277, 2048, 20, "f32"),
+    (1, 250, 2048, 64, "bf16"),
+    (1, 190, 2056, 50, "bf16"),
+    (2, 190, 2052, 30, "f32"),
+    (1, 200, 2048, 128, "f32"),
+    (1, 150, 2048, 100, "bf16"),
 ]
 
 
@@ -172,11 +183,12 @@ def test_split_resume_matches_single_scan(gpu):
 # kernels, one segment), and segmented plans of the row, lane and tile kernels.
 ALIAS = [("m3b", None, "euler"), ("tiny", (1, 6000, 40, 16), "zoh"),
          ("tiny", (2, 3000, 64, 32), "euler"), ("tiny", (1, 3000, 64, 64), "zoh"),
-         ("tiny", (1, 4000, 64, 8), "bilinear")]
+         ("tiny", (1, 4000, 64, 8), "bilinear"), ("tiny", (1, 300, 2048, 128), "bilinear")]
 
 
 @pytest.mark.parametrize("name,shape,disc", ALIAS,
-                         ids=["m3b", "rows-seg", "lane32-seg", "tile64-seg", "lane8-seg"])
+                         ids=["m3b", "rows-seg", "lane32-seg", "tile64-seg", "lane8-seg",
+                              "rows128"])
 def test_h0_aliases_h_last(gpu, name, shape, disc):
     if shape is None:
         w = synth.workload(name)
@@ -243,8 +255,10 @@ def test_nan_stays_in_its_channel(gpu):
 # k = 0: every channel (the oracle runs at ~1e8 elements/s on the host: about a
 # second for the 130M layer, a few for the 3B layer)
 @pytest.mark.parametrize("name,zoh,k", [("m130m", "euler", 0), ("m3b", "euler", 0),
-                                         ("m3b", "zoh", 0), ("m3b", "bilinear", 0)],
-                         ids=["m130m-euler", "m3b-euler", "m3b-zoh", "m3b-bilinear"])
+                                         ("m3b", "zoh", 0), ("m3b", "bilinear", 0),
+                                         ("wide128", "euler", 96), ("wide64", "zoh", 96)],
+                         ids=["m130m-euler", "m3b-euler", "m3b-zoh", "m3b-bilinear",
+                              "wide128-euler", "wide64-zoh"])
 def test_layer_workloads_full(gpu, name, zoh, k):
     w = synth.workload(name)
     x = synth.scan_inputs(w, device=DEV, seed=0)
