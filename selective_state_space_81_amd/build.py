@@ -25,7 +25,7 @@ SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "scan_tile
            os.path.join(CSRC, "scan_row_wide.hip"),
            os.path.join(CSRC, "decode.hip"),
            os.path.join(CSRC, "conv.hip"), os.path.join(CSRC, "scan_bwd.hip"),
-           os.path.join(CSRC, "bwd_wide.hip"),
+           os.path.join(CSRC, "bwd_wide.hip"), os.path.join(CSRC, "bwd_row.hip"),
            os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "profile.cpp"),
            os.path.join(CSRC, "noalloc.hip")]
 ARCH = os.environ.get("MSSCAN_ARCH", "gfx950")

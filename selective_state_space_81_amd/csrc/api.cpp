@@ -441,18 +441,51 @@ ms_status ms_state_update(float* h, const void* x_t, const void* delta_t, const 
 }
 
 namespace {
-// Backward plan: segments of bwd_segment_len() steps, all states of a channel
-// in one lane (d_state <= 16).
+// Backward plan for d_state <= 16.
+//   rows (d_state 9..16, whole 16-byte io chunks, and at least
+//     MSSCAN_BWD_ROW_MIN_TILES 16-channel tiles over the batch): the row
+//     layout of bwd_row.hip -- a checkpointing forward walk, one reverse walk
+//     per tile over the whole sequence;
+//   else segments of bwd_segment_len() steps, all states of a channel in one
+//     lane (scan_bwd.hip).
+#ifndef MSSCAN_BWD_ROW_MIN_TILES
+#define MSSCAN_BWD_ROW_MIN_TILES 512
+#endif
 struct BwdPlan {
     msscan::Plan fwd;
     int64_t K, tiles;
-    size_t agg, fdecay, mu, bdecay, pbc, pparam, pgroup;  // floats of each region
+    bool rows;
+    size_t agg, fdecay, mu, bdecay, pbc, pparam, pgroup, ckpt;  // floats of each region
 };
 
 size_t pad64(size_t n) { return (n + 63) / 64 * 64; }
 
 BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
     BwdPlan q{};
+    {
+        const int64_t tiles = (d.d_inner + msscan::kRowCh - 1) / msscan::kRowCh;
+        if (d.d_state > 8 && d.d_state <= 16 && d.d_inner % (d.io == MS_BF16 ? 8 : 4) == 0 &&
+            (int64_t)d.batch * tiles >= MSSCAN_BWD_ROW_MIN_TILES) {
+            const size_t B = (size_t)d.batch, D = (size_t)d.d_inner, N = (size_t)d.d_state;
+            const size_t nblk = (size_t)((d.seqlen + 15) / 16);
+            q.rows = true;
+            q.K = 1;
+            q.tiles = tiles;
+            q.ckpt = B * nblk * D * N;
+            q.pbc = (size_t)tiles * B * (size_t)d.seqlen * 2 * N;
+            q.pparam = B * D * (N + 2);
+            q.pgroup = (size_t)msscan::kParamGroups * D * (N + 2);
+            msscan::Plan& p = q.fwd;
+            p.tile_path = 3;
+            p.ns = 16;
+            p.waves = msscan::kRowWaves;
+            p.rows = 1;
+            p.tiles = (int)tiles;
+            p.chunks = 1;
+            p.chunk_len = d.seqlen;
+            return q;
+        }
+    }
     const int64_t seg = msscan::bwd_segment_len();
     q.K = (d.seqlen + seg - 1) / seg;
     q.tiles = (d.d_inner + 63) / 64;
@@ -478,7 +511,7 @@ BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
 
 size_t bwd_ws_floats(const BwdPlan& q) {
     return pad64(q.agg) + pad64(q.fdecay) + pad64(q.mu) + pad64(q.bdecay) + pad64(q.pbc) +
-           pad64(q.pparam) + pad64(q.pgroup);
+           pad64(q.pparam) + pad64(q.pgroup) + pad64(q.ckpt);
 }
 
 // Launches the 16-states-or-fewer backward kernels on one problem (the
@@ -489,6 +522,22 @@ hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, 
                           bool bf16, hipStream_t hs) {
     f.chunk_len = q.fwd.chunk_len;
     f.chunks = q.fwd.chunks;
+    if (q.rows) {
+        f.tiles = (int)q.tiles;
+        f.waves = msscan::kRowWaves;
+        msscan::BwdRowLaunch L{};
+        L.ckpt = ws;
+        L.pbc = (ws += pad64(q.ckpt));
+        L.pparam = (ws += pad64(q.pbc));
+        L.pgroup = ws + pad64(q.pparam);
+        L.f = f;
+        L.dy = dy; L.dh_last = dh_last; L.du = du; L.ddelta = ddelta; L.dz = f.z ? dz : nullptr;
+        L.dh0 = dh0; L.dA = dA; L.dB = dB; L.dC = dC; L.dD = f.D ? dD : nullptr; L.dbias = dbias;
+        L.bf16 = bf16;
+        L.disc = disc_of(flags);
+        // Checkpointing forward walk, reverse walk, fixed-order sums.
+        return msscan::launch_scan_bwd_rows(L, hs);
+    }
     f.waves = 1;
     const bool bil = (flags & MS_BILINEAR) != 0;
     f.agg = ws;

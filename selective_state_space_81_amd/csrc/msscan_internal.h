@@ -176,6 +176,37 @@ int bwd_segment_len();
 constexpr int kParamGroups = 16;  // first-level groups of the parameter sums
 constexpr int kBwdWaves = 4;  // backward segments per workgroup (one wave each)
 hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s);
+// The fixed-order sums that end every backward: dB | dC over `tiles` tile
+// partials [tiles][batch][L][2N], dA | dD | dbias over the batch x
+// ceil(f.chunks / kBwdWaves) rows of pparam [rows][Dn][N+2] (first in
+// kParamGroups groups, into pgroup, then the groups in order).
+hipError_t launch_bwd_reductions(const ScanArgs& f, float* pbc, int tiles, float* pparam,
+                                 float* pgroup, float* dA, float* dB, float* dC, float* dD,
+                                 float* dbias, hipStream_t s);
+// Row-layout backward for d_state 9..16 (bwd_row.hip): a checkpointing
+// forward walk, the reverse walk over 16-channel tiles, then the sums above.
+// f.tiles = ceil(Dn / kRowCh); d_inner a multiple of 8 (bf16 io) or 4 (fp32).
+struct BwdRowLaunch {
+    ScanArgs f;
+    const void* dy;
+    const float* dh_last;
+    void* du;
+    void* ddelta;
+    void* dz;
+    float* dh0;
+    float* dA;
+    float* dB;
+    float* dC;
+    float* dD;
+    float* dbias;
+    float* ckpt;    // [batch][ceil(L / 16)][Dn][N]: the state before each 16-step block
+    float* pbc;     // [tiles][batch][L][2N]
+    float* pparam;  // [batch][Dn][N+2]
+    float* pgroup;  // [kParamGroups][Dn][N+2]
+    bool bf16;
+    int disc;
+};
+hipError_t launch_scan_bwd_rows(const BwdRowLaunch& L, hipStream_t s);
 
 // Backward for d_state 17..128 (bwd_wide.hip): the state is differentiated
 // in slices of kWideSlice states by the kernels above, run as fp32 problems

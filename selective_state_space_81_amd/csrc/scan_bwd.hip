@@ -775,6 +775,38 @@ __global__ void __launch_bounds__(256) reduce_bc(BwdArgs a, float* dB, float* dC
         dC[row * f.N + k - f.N] = acc;
 }
 
+// reduce_bc with four consecutive outputs per thread and 16-byte loads (when
+// batch * L * 2N is a multiple of 4); each output's tiles are added in the
+// same order, so the sums are the same.
+__global__ void __launch_bounds__(256) reduce_bc4(BwdArgs a, float* dB, float* dC, int tiles) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const ScanArgs& f = a.f;
+    const int64_t per = (int64_t)f.batch * f.L * 2 * f.N;
+    const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (idx >= per) return;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    int tl = 0;
+    for (; tl + 8 <= tiles; tl += 8) {
+        f4v v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = *reinterpret_cast<const f4v*>(a.pbc + (int64_t)(tl + i) * per + idx);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += v[i];
+    }
+    for (; tl < tiles; ++tl) acc += *reinterpret_cast<const f4v*>(a.pbc + (int64_t)tl * per + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t o = idx + i;
+        const int k = (int)(o % (2 * f.N));
+        const int64_t row = o / (2 * f.N);
+        if (k < f.N)
+            dB[row * f.N + k] = acc[i];
+        else
+            dC[row * f.N + k - f.N] = acc[i];
+    }
+}
+
 // Parameter sums over the batch x ceil(K/kBwdWaves) rows of pparam, in two fixed-order
 // levels: group g (blockIdx.y) adds the rows r with r mod kParamGroups == g
 // in increasing order, then reduce_param_groups adds the groups in order.
@@ -854,25 +886,7 @@ hipError_t launch_bwd(const BwdArgs& a, float* dA, float* dB, float* dC, float* 
                            0, s, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t nbc = (int64_t)f.batch * f.L * 2 * f.N;
-    {
-        ProfScope ps(s, kPhaseReduce);
-        hipLaunchKernelGGL(reduce_bc, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a,
-                           dB, dC, tiles);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t npar = (int64_t)f.Dn * (f.N + 2);
-    const unsigned pblocks = (unsigned)((npar + 255) / 256);
-    {
-        ProfScope ps(s, kPhaseReduce);
-        hipLaunchKernelGGL(reduce_params, dim3(pblocks, kParamGroups), dim3(256), 0, s, a);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    {
-        ProfScope ps(s, kPhaseReduce);
-        hipLaunchKernelGGL(reduce_param_groups, dim3(pblocks), dim3(256), 0, s, a, dA, dD, dbias);
-    }
-    return hipGetLastError();
+    return launch_bwd_reductions(f, a.pbc, tiles, a.pparam, a.pgroup, dA, dB, dC, dD, dbias, s);
 }
 
 template <bool BF16, int DISC>
@@ -888,6 +902,40 @@ hipError_t launch_ns(const BwdArgs& a, float* dA, float* dB, float* dC, float* d
 }  // namespace
 
 int bwd_segment_len() { return kSeg; }
+
+hipError_t launch_bwd_reductions(const ScanArgs& f, float* pbc, int tiles, float* pparam,
+                                 float* pgroup, float* dA, float* dB, float* dC, float* dD,
+                                 float* dbias, hipStream_t s) {
+    BwdArgs a{};
+    a.f = f;
+    a.pbc = pbc;
+    a.pparam = pparam;
+    a.pgroup = pgroup;
+    hipError_t e;
+    const int64_t nbc = (int64_t)f.batch * f.L * 2 * f.N;
+    {
+        ProfScope ps(s, kPhaseReduce);
+        if (nbc % 4 == 0)
+            hipLaunchKernelGGL(reduce_bc4, dim3((unsigned)((nbc / 4 + 255) / 256)), dim3(256), 0,
+                               s, a, dB, dC, tiles);
+        else
+            hipLaunchKernelGGL(reduce_bc, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, a,
+                               dB, dC, tiles);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t npar = (int64_t)f.Dn * (f.N + 2);
+    const unsigned pblocks = (unsigned)((npar + 255) / 256);
+    {
+        ProfScope ps(s, kPhaseReduce);
+        hipLaunchKernelGGL(reduce_params, dim3(pblocks, kParamGroups), dim3(256), 0, s, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        ProfScope ps(s, kPhaseReduce);
+        hipLaunchKernelGGL(reduce_param_groups, dim3(pblocks), dim3(256), 0, s, a, dA, dD, dbias);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s) {
     BwdArgs a{};

@@ -127,6 +127,26 @@ __device__ __forceinline__ void row_reduce_16_to_4(const float (&p)[16], float (
         : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]),
           "v"(q[7]));
 }
+// Stage 1 for one register pair, p[m] = a and p[m + 8] = b: lets a caller
+// that forms the 16 terms one at a time combine each pair as soon as both
+// exist (with the rest of the reduce in row_reduce_finish).
+__device__ __forceinline__ float row_reduce_pair(float a, float b) {
+    float q;
+    asm("s_nop 1\n" MS_S1_(0, 1, 2) : "=&v"(q) : "v"(a), "v"(b));
+    return q;
+}
+// Stage 2 for one pair, q[m] = a and q[m + 4] = b.
+__device__ __forceinline__ float row_reduce_pair2(float a, float b) {
+    float r;
+    asm("s_nop 1\n" MS_S2_(0, 1, 2) : "=&v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ void row_reduce_8_to_4(const float (&q)[8], float (&r)[4]) {
+    asm("s_nop 1\n" MS_S2_(0, 4, 8) MS_S2_(1, 5, 9) MS_S2_(2, 6, 10) MS_S2_(3, 7, 11)
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]),
+          "v"(q[7]));
+}
 #undef MS_S1_
 #undef MS_S2_
 
@@ -153,6 +173,25 @@ __device__ __forceinline__ float row_reduce_scatter(const float (&p)[16], bool b
     const float u0 = s0 + qperm<kQpXor1>(s0);
     const float u1 = s1 + qperm<kQpXor1>(s1);
     return bit0 ? u1 : u0;
+}
+
+// Stages 3-4 of the readout (r[m] from stage 2).
+__device__ __forceinline__ float row_reduce_quads(const float (&r)[4], bool bit1, bool bit0) {
+    const float t0 = r[0] + qperm<kQpXor2>(r[0]);
+    const float t1 = r[1] + qperm<kQpXor2>(r[1]);
+    const float t2 = r[2] + qperm<kQpXor2>(r[2]);
+    const float t3 = r[3] + qperm<kQpXor2>(r[3]);
+    const float s0 = bit1 ? t2 : t0;
+    const float s1 = bit1 ? t3 : t1;
+    const float u0 = s0 + qperm<kQpXor1>(s0);
+    const float u1 = s1 + qperm<kQpXor1>(s1);
+    return bit0 ? u1 : u0;
+}
+// The rest of the readout after stage 1 (q[m] from row_reduce_pair).
+__device__ __forceinline__ float row_reduce_finish(const float (&q)[8], bool bit1, bool bit0) {
+    float r[4];
+    row_reduce_8_to_4(q, r);
+    return row_reduce_quads(r, bit1, bit0);
 }
 
 // Sum over the 16 lanes of a row, in every lane.
@@ -200,8 +239,15 @@ __device__ __forceinline__ void put_bc(float* dst, const RT (&v)[VB], W widen) {
 // holds kRT * RPC * SPL states: lane n of the channel's row g holds states
 // q * kRT * RPC + kRT * g + n for q < SPL.  A workgroup is 4 waves, 16 rows:
 // CH = 16 / RPC channels, every row of a channel in one wave.
-template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP, int RPC, int SPL>
+//
+// CKPT (with SUMMARY, one row per channel, one segment): the forward walk of
+// the backward pass.  From h0 (or zero) over the whole sequence, storing the
+// state before every block into a.agg as [batch][block][d_inner][d_state];
+// no readout, no output.
+template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP, int RPC, int SPL,
+          bool CKPT = false>
 __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
+    static_assert(!CKPT || (SUMMARY && RPC == 1 && SPL == 1), "checkpoint walk");
     static_assert(RPC == 1 || RPC == 2 || RPC == 4, "a channel's rows share one wave");
     static_assert(SPL == 1 || SPL == 2, "states per lane");
     static_assert(COOP || RPC == 1, "several rows per channel move io as whole tiles");
@@ -246,7 +292,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     const int lane = tid & 63;
     const int n = lane & 15;  // this lane's state; also its timestep slot
     const int tiles = a.tiles;
-    const int segs = SUMMARY ? a.chunks - 1 : a.chunks;
+    const int segs = (SUMMARY && !CKPT) ? a.chunks - 1 : a.chunks;
     const uint32_t l = xcd_logical(blockIdx.x, gridDim.x);
     const int tile = (int)(l % (uint32_t)tiles);
     const int seg = (int)((l / (uint32_t)tiles) % (uint32_t)segs);
@@ -272,7 +318,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         invA[q] = 0.f;
         if constexpr (ZOH) invA[q] = av != 0.f ? 1.f / av : 0.f;
         h[q] = 0.f;
-        if constexpr (!SUMMARY) {
+        if constexpr (!SUMMARY || CKPT) {
             if (svalid[q]) {
                 if (seg == 0) {
                     // With several segments h0 is read from the carry pass's copy,
@@ -312,6 +358,10 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                               ? (uint32_t)crow * rowb + (uint32_t)cchan * R::kSize
                               : kOutOfRange;
     const int ntiles_io = SUMMARY ? 2 : (has_z ? 3 : 2);
+    // CKPT: this lane's offset in a checkpoint slab [Dn][N]
+    const uint32_t ck_off = (CKPT && cvalid && svalid[0])
+                                ? ((uint32_t)c * (uint32_t)Nr + (uint32_t)st[0]) * 4u
+                                : kOutOfRange;
     // this thread's elements of a block's B/C tile (kRT x kNS values): state
     // bs, timesteps VB * tq .. VB * tq + VB - 1.  Each load instruction covers
     // consecutive states of one timestep; the VB values of a state go to LDS
@@ -433,6 +483,15 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     // The recurrence over the block at rel (staged in buffer buf) and, unless
     // SUMMARY, its readout and output (y tile ybuf with COOP).
     auto compute = [&](int rel, int buf, int ybuf, const Elem& e) __attribute__((always_inline)) {
+        if constexpr (CKPT) {
+            // the block's [Dn][N] slab, addressed per block (wave-uniform
+            // base), this lane's state at a fixed offset
+            const int64_t slab = (int64_t)a.Dn * Nr;
+            const float* ck = a.agg + ((int64_t)b * ((a.L + kRT - 1) / kRT) + rel / kRT) * slab;
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(h[0]), make_rsrc(ck, rel < len ? (uint32_t)slab * 4u : 0u),
+                ck_off, 0, 0);
+        }
         float p[16];
         static_for([&](auto qc) {
         constexpr int q = decltype(qc)::value;
@@ -479,7 +538,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
             },
             std::make_integer_sequence<int, kRT>{});
         }, std::make_integer_sequence<int, SPL>{});
-        if constexpr (SUMMARY) {
+        if constexpr (SUMMARY && !CKPT) {
             if constexpr (!PROD) {
                 const float yk = e.dt - s_comp;
                 const float tk = s_sum + yk;
@@ -552,7 +611,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         store_y_tile((nblk - 1) * kRT, (nblk - 1) & 1);
     }
 
-    if constexpr (SUMMARY) {
+    if constexpr (SUMMARY && !CKPT) {
         const int64_t sb = (int64_t)b * km1 + seg;
         if constexpr (PROD) {
 #pragma unroll
@@ -569,7 +628,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                 if (cvalid && svalid[q]) a.agg[(sb * Nr + st[q]) * a.Dn + c] = h[q];
             if (cvalid && n == 0 && sg == 0) a.sdt[sb * a.Dn + c] = total;
         }
-    } else if (seg == a.chunks - 1 && a.h_last && cvalid) {
+    } else if (!SUMMARY && seg == a.chunks - 1 && a.h_last && cvalid) {
 #pragma unroll
         for (int q = 0; q < SPL; ++q)
             if (svalid[q]) a.h_last[((int64_t)b * a.Dn + c) * Nr + st[q]] = h[q];

@@ -87,6 +87,47 @@ SHAPES = [
     (3, 16, 64, 1, "f32"),
 ]
 
+# Shapes with at least 512 16-channel tiles over the batch and d_state 9..16
+# take the row-layout backward (a checkpointing forward walk and one reverse
+# walk per tile): ragged last blocks, padded states, a channel tail inside the
+# last tile (d_inner 4104).
+ROWS = [
+    (4, 300, 2048, 16, "bf16"),
+    (2, 129, 4096, 12, "f32"),
+    (1, 77, 8192, 9, "bf16"),
+    (2, 20, 4104, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("disc", DISCS)
+@pytest.mark.parametrize("shape", ROWS, ids=lambda s: "B{}L{}D{}N{}{}".format(*s))
+def test_bwd_rows(gpu, shape, disc):
+    batch, L, Dn, N, io = shape
+    x = _inputs(batch, L, Dn, N, io, seed=41)
+    _compare(gpu, x, io, disc)
+
+
+@pytest.mark.parametrize("softplus", [True, False], ids=["softplus", "raw_step"])
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_rows_options_off(gpu, disc, softplus):
+    """Row-layout backward with no gate, D, bias, h0 or dh_last."""
+    x = _inputs(4, 70, 2048, 16, "bf16", seed=42, optional=False)
+    if not softplus:
+        x["delta"] = (x["delta"].float().abs() * 0.05 + 0.01).to(x["delta"].dtype)
+    _compare(gpu, x, "bf16", disc, softplus=softplus)
+
+
+def test_bwd_rows_deterministic(gpu):
+    x = _inputs(4, 200, 2048, 16, "bf16", seed=43)
+    g1 = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
+                      delta_bias=x["delta_bias"], h0=x["h0"], dh_last=x["dh_last"])
+    g2 = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
+                      delta_bias=x["delta_bias"], h0=x["h0"], dh_last=x["dh_last"])
+    torch.cuda.synchronize()
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
+
 
 @pytest.mark.parametrize("disc", DISCS)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}L{}D{}N{}{}".format(*s))
@@ -133,14 +174,15 @@ def test_bwd_deterministic(gpu):
             assert torch.equal(v, g2[k]), k
 
 
-def test_bwd_130m_layer(gpu):
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_130m_layer(gpu, disc):
     """The 130M-layer shape (B8 L2048 D1536 N16, bf16), every gradient."""
     w = synth.workload("m130m")
     x = synth.scan_inputs(w, device=DEV, seed=0)
     g = torch.Generator(device=DEV)
     g.manual_seed(77)
     x["dy"] = torch.randn(w.batch, w.L, w.Dn, generator=g, device=DEV).to(x["u"].dtype)
-    _compare(gpu, x, "bf16", "euler")
+    _compare(gpu, x, "bf16", disc)
 
 
 @pytest.mark.parametrize("disc", DISCS)
