@@ -86,6 +86,18 @@ constexpr int bitrev4(int m) { return ((m & 1) << 3) | ((m & 2) << 1) | ((m & 4)
 constexpr int slot_of(int j) { return bitrev4(15 - j); }
 constexpr int step_of(int m) { return 15 - bitrev4(m); }
 
+// acc + (v broadcast from lane M of the row) * x as one v_fmac_f32_dpp (the
+// compiler folds DPP moves into v_mul but not into v_fmac).  The leading
+// s_nop 1 gives the two wait states a DPP read needs after a VALU write of v.
+template <int M>
+__device__ __forceinline__ float fmac_bcast(float acc, float v, float x) {
+    asm("s_nop 1\n"
+        "v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(v), "v"(x), "n"(M));
+    return acc;
+}
+
 __device__ __forceinline__ float sigmoid_f(float v) {
     return hw_rcp(1.f + hw_exp2(-v * kLog2e));
 }
@@ -305,10 +317,9 @@ __global__ void __launch_bounds__(64 * kRowWaves) bwd_row(BwdRowArgs a) {
                 }
                 const float bj = Bg[j % 4];
                 const float cj = Cg[j % 4];
-                const float gj = row_bcast_b<slot_of(j)>(e.g);
                 const float hp = j == 0 ? e.hk : h[j - 1];
-                const float lam = fmaf(cj, gj, mu);
-                const float cC = gj * h[j];
+                const float lam = fmac_bcast<slot_of(j)>(mu, e.g, cj);  // C_j g_j + mu
+                const float cC = row_bcast_b<slot_of(j)>(e.g) * h[j];
                 float cB, r1, r2;
                 if constexpr (DISC == kEuler) {
                     // A_bar = e^{dt a}, f = dt:  d(dt) = sum l (a A_bar h_{t-1} + B u),
@@ -316,7 +327,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) bwd_row(BwdRowArgs a) {
                     cB = lam * row_bcast_b<slot_of(j)>(e.xv);
                     const float q = ab[j] * lam;
                     const float w = q * hp;
-                    dA = fmaf(w, row_bcast_b<slot_of(j)>(e.dt), dA);
+                    dA = fmac_bcast<slot_of(j)>(dA, e.dt, w);
                     r1 = w * A2;
                     r2 = lam * bj;
                     mu = q;
@@ -329,9 +340,12 @@ __global__ void __launch_bounds__(64 * kRowWaves) bwd_row(BwdRowArgs a) {
                     const float uj = row_bcast_b<slot_of(j)>(e.u);
                     const float t2 = dtj * A2;
                     const float abar = ab[j];
+                    // both branches formed, one kept (a select, not a branch: a
+                    // divergent branch here kept twice the registers live)
                     const bool small = fabsf(t2) < kZohSwitch;
-                    const float fz = small ? dtj * fmaf(t2, fmaf(t2, kZohT2, kZohT1), 1.f)
-                                           : fmaf(abar, invA, -invA);
+                    const float fz_ser = dtj * fmaf(t2, fmaf(t2, kZohT2, kZohT1), 1.f);
+                    const float fz_big = fmaf(abar, invA, -invA);
+                    const float fz = small ? fz_ser : fz_big;
                     const float lb = lam * bj;
                     cB = (lam * fz) * uj;
                     const float q = abar * lam;
@@ -339,8 +353,9 @@ __global__ void __launch_bounds__(64 * kRowWaves) bwd_row(BwdRowArgs a) {
                     r1 = fmaf(w * A2, kLn2, (abar * lb) * uj);
                     r2 = fz * lb;
                     const float x = t2 * kLn2;
-                    const float dfda = small ? (dtj * dtj) * fmaf(x, fmaf(x, 0.125f, 1.f / 3.f), 0.5f)
-                                             : fmaf(dtj, abar, -fz) * invA;
+                    const float dfda_ser = (dtj * dtj) * fmaf(x, fmaf(x, 0.125f, 1.f / 3.f), 0.5f);
+                    const float dfda_big = fmaf(dtj, abar, -fz_big) * invA;
+                    const float dfda = small ? dfda_ser : dfda_big;
                     dA = fmaf(lb * uj, dfda, fmaf(w, dtj, dA));
                     mu = q;
                 } else {
