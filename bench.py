@@ -570,7 +570,8 @@ def _csv(dirname, suffix):
 def _short(name):
     m = re.search(r"(scan_row<[^>]*>|scan_lane<[^>]*>|scan_tile<[^>]*>|"
                   r"bc_prepare<[^>]*>|carry_chain<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
-                  r"bwd_main<[^>]*>|seg_summaries<[^>]*>|reduce_bc|wide_\w+(?:<[^>]*>)?|"
+                  r"bwd_main<[^>]*>|bwd_row<[^>]*>|seg_summaries<[^>]*>|reduce_bc4|reduce_bc|"
+                  r"wide_\w+(?:<[^>]*>)?|"
                   r"reduce_param_groups|reduce_params|"
                   r"neg_kernel)", name)
     return m.group(1) if m else name[:60]
@@ -616,7 +617,7 @@ def rocprof_summary(args):
         for k in sorted(fetch):
             if k == "neg_kernel" or k not in write or not re.search(
                     r"scan_|carry_|bc_prep|step_quads|conv1d_kernel|bwd_main|"
-                    r"seg_summaries|reduce_|wide_|copy16|read16", k):
+                    r"seg_summaries|bwd_row|reduce_|wide_|copy16|read16", k):
                 continue
             mb = (fetch[k] * f_fetch + write[k] * f_write) * 1024 / 1e6
             print(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {mb:.2f} |")
@@ -629,7 +630,8 @@ def rocprof_summary(args):
         acc = {}
         for r in _csv(dirname, "counter_collection.csv"):
             k = _short(r["Kernel_Name"])
-            if not re.search(r"scan_|carry_|bc_prep|step_quads|bwd_main|seg_summ|conv1d|wide_", k):
+            if not re.search(r"scan_|carry_|bc_prep|step_quads|bwd_main|bwd_row|seg_summ|conv1d|"
+                             r"wide_|reduce_", k):
                 continue
             acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))

@@ -64,3 +64,22 @@ def test_profile_times_every_backward_launch(gpu):
     assert prof["summary"]["launches"] == 3 and prof["main"]["launches"] == 3
     for k in ("carry", "reduce", "summary", "main"):
         assert prof[k]["mean_ms"] > 0
+
+
+def test_profile_times_row_backward_launches(gpu):
+    """The row-layout backward (at least 512 16-channel tiles): one
+    checkpointing forward walk (summary phase), one reverse walk (main) and
+    three reduction kernels per call; no carries."""
+    w = synth.workload("m130m", batch=4, L=64, Dn=2048)
+    x = synth.scan_inputs(w, device="cuda", seed=4)
+    dy = torch.randn(w.batch, w.L, w.Dn, device="cuda").to(x["u"].dtype)
+    gpu.profile_begin(3)
+    for _ in range(3):
+        gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                     delta_bias=x["delta_bias"])
+    prof = gpu.profile_end()
+    assert prof["calls"] == 3
+    assert prof["carry"]["launches"] == 0 and prof["reduce"]["launches"] == 9
+    assert prof["summary"]["launches"] == 3 and prof["main"]["launches"] == 3
+    for k in ("reduce", "summary", "main"):
+        assert prof[k]["mean_ms"] > 0
