@@ -458,9 +458,7 @@ def measure_dtproj(ms, rank=16, reps=20):
                     stream=stream)
 
     def timed(fn):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
+        warm_up(fn, 3, 0.25)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
         for i in range(reps):

@@ -353,9 +353,18 @@ size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags) {
     return ws_bytes(make_plan(*dims, flags), *dims, flags);
 }
 
+// The fused step projection runs on the row kernel when the plan is one row
+// per channel (d_state 9..16) with whole io tiles, else on the lane kernels
+// (d_state 8 and 16).
+static msscan::Plan dtproj_plan(const ms_dims& d, uint32_t flags) {
+    const msscan::Plan p = make_plan(d, flags, true);
+    if (p.tile_path == 3 && p.rows == 1 && d.d_inner % (d.io == MS_BF16 ? 8 : 4) == 0) return p;
+    return make_plan(d, flags, false);
+}
+
 size_t ms_scan_dtproj_workspace_bytes(const ms_dims* dims, uint32_t flags) {
     if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
-    return ws_bytes(make_plan(*dims, flags, false), *dims, flags);
+    return ws_bytes(dtproj_plan(*dims, flags), *dims, flags);
 }
 
 ms_status ms_scan_fwd(const void* u, const void* delta, const float* A, const void* B,
@@ -385,9 +394,13 @@ ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt
     const void* ptrs[] = {u, dt_low, W_dt, A, B, C, D, z, delta_bias, y, h0, h_last, workspace};
     for (const void* p : ptrs)
         if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
-    const msscan::Plan p = make_plan(*dims, flags, false);
-    if (p.tile_path != 2 || p.ns != dims->d_state || !msscan::dtproj_variant_exists(dims->d_state))
-        return fail(MS_ERR_UNSUPPORTED, "the fused dt projection needs d_state 8 or 16 (got %d)",
+    const msscan::Plan p = dtproj_plan(*dims, flags);
+    const bool rows = p.tile_path == 3;
+    if (!rows &&
+        (p.tile_path != 2 || p.ns != dims->d_state || !msscan::dtproj_variant_exists(dims->d_state)))
+        return fail(MS_ERR_UNSUPPORTED,
+                    "the fused dt projection needs d_state 8, or 9..16 (got %d; 9..15 also need "
+                    "d_inner a multiple of 8 for bf16, 4 for fp32)",
                     dims->d_state);
     const size_t need = ws_bytes(p, *dims, flags);
     if (need && (!workspace || workspace_bytes < need))
@@ -406,7 +419,8 @@ ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt
     hipStream_t hs = static_cast<hipStream_t>(stream);
     msscan::prof_call();
     const hipError_t e =
-        msscan::launch_scan_lanes_dtproj(p, a, dims->io == MS_BF16, disc_of(flags), hs);
+        rows ? msscan::launch_scan_rows_dtproj(p, a, dims->io == MS_BF16, disc_of(flags), hs)
+             : msscan::launch_scan_lanes_dtproj(p, a, dims->io == MS_BF16, disc_of(flags), hs);
     if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }

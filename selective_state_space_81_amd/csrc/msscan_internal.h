@@ -140,6 +140,10 @@ bool lane_variant_exists(int n, int disc);
 hipError_t launch_scan_lanes_dtproj(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                                     hipStream_t s);
 bool dtproj_variant_exists(int n);
+// The row kernel with the projection fused in (scan_row_dtproj.hip): a row
+// plan with one row per channel; d_inner a multiple of 8 (bf16) or 4 (fp32).
+hipError_t launch_scan_rows_dtproj(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                   hipStream_t s);
 hipError_t launch_bc_prepare(const ScanArgs& a, int np, bool bf16, hipStream_t s);  // rows np wide
 // Causal depthwise conv1d (+ silu), width 1..8.
 hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s);

@@ -41,6 +41,7 @@
 
 #include "device_common.h"
 #include "dpp_common.h"
+#include "dtproj_frag.h"
 #include "msscan_internal.h"
 
 namespace msscan {
@@ -66,70 +67,10 @@ using namespace dev;
 
 constexpr int kPT = 16;   // timesteps per projected delta tile
 constexpr int kPTS = 20;  // LDS row stride of the turned tile (floats; 16-byte rows)
-constexpr int kMaxRank = 64;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Eight consecutive io values k0 .. k0+7 of one row (row byte offset `row`,
-// row length `rank`), zero at k >= rank and outside the resource.  `vec`:
-// rows are 16-byte multiples, so whole 16-byte loads apply.
-template <bool BF16>
-struct Frag8;
-template <>
-struct Frag8<true> {
-    u4 v;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row, int k0, int rank,
-                                         bool vec) {
-        if (vec) {
-            v = __builtin_amdgcn_raw_buffer_load_b128(r, k0 < rank ? row + 2u * k0 : kOutOfRange,
-                                                      0, 0);
-        } else {
-            uint32_t e[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                e[j] = __builtin_amdgcn_raw_buffer_load_b16(
-                    r, k0 + j < rank ? row + 2u * (k0 + j) : kOutOfRange, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = e[2 * j] | (e[2 * j + 1] << 16);
-            __builtin_amdgcn_sched_barrier(0);  // one fragment's loads in flight at a time
-        }
-    }
-    __device__ __forceinline__ void mma(const Frag8& w, f4& acc) const {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v),
-                                                      __builtin_bit_cast(bf16x8, w.v), acc, 0, 0, 0);
-    }
-};
-template <>
-struct Frag8<false> {
-    float v[8];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t row, int k0, int rank,
-                                         bool vec) {
-        if (vec) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = k0 + 4 * h;
-                const u4 w = __builtin_amdgcn_raw_buffer_load_b128(
-                    r, k < rank ? row + 4u * k : kOutOfRange, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[4 * h + j] = __uint_as_float(w[j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                v[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    r, k0 + j < rank ? row + 4u * (k0 + j) : kOutOfRange, 0, 0));
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    // Eight K=4 products; lane group q supplies element j as its k, on both
-    // operands alike, so the pairing of x and W along r is exact.
-    __device__ __forceinline__ void mma(const Frag8& w, f4& acc) const {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[j], w.v[j], acc, 0, 0, 0);
-    }
-};
 
 template <int N, int TB, bool DB, bool BF16, int DISC, bool SP, bool SUMMARY, bool DTP = false,
           bool PAD = false>

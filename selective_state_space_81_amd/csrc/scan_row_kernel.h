@@ -69,6 +69,7 @@
 
 #include "device_common.h"
 #include "dpp_common.h"
+#include "dtproj_frag.h"
 #include "msscan_internal.h"
 
 namespace msscan {
@@ -244,10 +245,18 @@ __device__ __forceinline__ void put_bc(float* dst, const RT (&v)[VB], W widen) {
 // the backward pass.  From h0 (or zero) over the whole sequence, storing the
 // state before every block into a.agg as [batch][block][d_inner][d_state];
 // no readout, no output.
+//
+// DTP (one row per channel, whole io tiles): the raw step is not read but
+// projected, delta[t][d] = sum_r W[d][r] x[t][r] (dtproj_frag.h).  Wave 1,
+// which would move the delta tile, loads the block's 16 x rank tile of x
+// instead and, at staging, forms the block's 16-step x 16-channel delta tile
+// on the matrix cores against W fragments it loaded once; the tile goes to
+// LDS in fp32 (never rounded to the io type).
 template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP, int RPC, int SPL,
-          bool CKPT = false>
+          bool CKPT = false, bool DTP = false>
 __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     static_assert(!CKPT || (SUMMARY && RPC == 1 && SPL == 1), "checkpoint walk");
+    static_assert(!DTP || (COOP && RPC == 1 && SPL == 1 && !CKPT), "projected step");
     static_assert(RPC == 1 || RPC == 2 || RPC == 4, "a channel's rows share one wave");
     static_assert(SPL == 1 || SPL == 2, "states per lane");
     static_assert(COOP || RPC == 1, "several rows per channel move io as whole tiles");
@@ -257,7 +266,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     constexpr int VB = kRT * kNS / kThreads;     // B (and C) tile values per thread
     // Two states per lane take twice as long per block, so half the blocks
     // in flight hide the same load latency, with half the load registers.
-    constexpr int PF = SPL == 2 ? 2 : kRowPf;
+    constexpr int PF = (SPL == 2 || DTP) ? 2 : kRowPf;
     // 128 states make a 16 KB B/C tile per buffer: three buffers (the fewest
     // the pipeline allows) keep two workgroups per CU.
     constexpr int NB = SPL == 2 ? 3 : kNb;
@@ -287,6 +296,8 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) float s_bc[NB][SUMMARY ? 1 : 2][kNS][kBcS];
     __shared__ __attribute__((aligned(16))) RT s_io[COOP ? NB : 1][COOP ? kIoT : 1][kRT][kIoS];
     __shared__ __attribute__((aligned(16))) RT s_y[(COOP && !SUMMARY) ? 2 : 1][kRT][kIoS];
+    // DTP: the projected delta tile of a staged block, [channel][step] fp32
+    __shared__ __attribute__((aligned(16))) float s_dt[DTP ? NB : 1][DTP ? kRowCh : 1][kBcS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -358,6 +369,22 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                               ? (uint32_t)crow * rowb + (uint32_t)cchan * R::kSize
                               : kOutOfRange;
     const int ntiles_io = SUMMARY ? 2 : (has_z ? 3 : 2);
+    // DTP: this lane's operand row / column (m) and k quarter (q), the x and
+    // W row strides, and the tile's W fragments (channels past d_inner read 0)
+    const int fm = lane & 15, fq = lane >> 4;
+    const uint32_t xrow = DTP ? (uint32_t)a.rank * R::kSize : 0u;
+    const bool xvec = DTP && (a.rank % (BF16 ? 8 : 4)) == 0;
+    Frag8<BF16> wfr[DTP ? 2 : 1];
+    if constexpr (DTP) {
+        if (wv == 1) {
+            const auto rW = make_rsrc(a.wdt, (uint32_t)a.Dn * xrow);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+                if (kc * 32 < a.rank)
+                    wfr[kc].load(rW, (uint32_t)(tile * kRowCh + fm) * xrow, kc * 32 + 8 * fq,
+                                 a.rank, xvec);
+        }
+    }
     // CKPT: this lane's offset in a checkpoint slab [Dn][N]
     const uint32_t ck_off = (CKPT && cvalid && svalid[0])
                                 ? ((uint32_t)c * (uint32_t)Nr + (uint32_t)st[0]) * 4u
@@ -389,11 +416,23 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         RT u, d, z;          // without COOP
         RT bb[VB], cb[VB];
         Chunk t;             // COOP: this lane's chunk of io tile wv
+        Frag8<BF16> xf[DTP ? 2 : 1];  // DTP, wave 1: the block's x rows
     };
     auto load = [&](Raw& r, int rel) {
         const uint32_t nr = rows_of(rel);
         if constexpr (COOP) {
-            if (wv < ntiles_io) {
+            bool projected = false;
+            if constexpr (DTP) {
+                if (wv == 1) {
+                    const auto rX = make_rsrc(base(a.dtx, rel, xrow), nr * xrow);  // rows past L: 0
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc)
+                        if (kc * 32 < a.rank)
+                            r.xf[kc].load(rX, (uint32_t)fm * xrow, kc * 32 + 8 * fq, a.rank, xvec);
+                    projected = true;
+                }
+            }
+            if (!projected && wv < ntiles_io) {
                 const void* src = wv == 0 ? a.u : (wv == 1 ? a.delta : a.z);
                 const auto rs = make_rsrc(base(src, rel, rowb), nr * rowb);
                 if constexpr (kChB == 16)
@@ -425,7 +464,19 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         put_bc<VB>(&s_bc[buf][0][bs][tq * VB], r.bb, widen);
         if constexpr (!SUMMARY) put_bc<VB>(&s_bc[buf][1][bs][tq * VB], r.cb, widen);
         if constexpr (COOP) {
-            if (wv < ntiles_io && lane < kRT * kCpr)
+            bool projected = false;
+            if constexpr (DTP) {
+                if (wv == 1) {
+                    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc)
+                        if (kc * 32 < a.rank) r.xf[kc].mma(wfr[kc], acc);
+                    // acc[i]: delta at step 4 fq + i of channel fm
+                    *reinterpret_cast<f4*>(&s_dt[buf][fm][4 * fq]) = acc;
+                    projected = true;
+                }
+            }
+            if (!projected && wv < ntiles_io && lane < kRT * kCpr)
                 *reinterpret_cast<Chunk*>(&s_io[buf][wv][crow][cch * kCw]) = r.t;
         } else {
             sg.u = permute_bits(r.u, to_row);
@@ -446,7 +497,10 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         float draw;
         if constexpr (COOP) {
             e.u = R::widen(s_io[buf][0][n][cl]);
-            draw = R::widen(s_io[buf][1][n][cl]);
+            if constexpr (DTP)
+                draw = s_dt[buf][cl][n];
+            else
+                draw = R::widen(s_io[buf][1][n][cl]);
             if constexpr (!SUMMARY) {
                 if (has_z) e.z = R::widen(s_io[buf][2][n][cl]);
             }

@@ -137,9 +137,12 @@ def test_dtproj_workspace_size_function():
     def ws(b, L, D, N, flags=1):
         return lib.ms_scan_dtproj_workspace_bytes(ctypes.byref(ms.dims(b, L, D, N, 1)), flags)
 
-    # The fused projection runs on the lane kernels (one lane per channel),
-    # which cut the 130M layer into 64-step segments.
-    assert ws(8, 2048, 1536, 16) == _seg_ws(8, 1536, 16, 2048 // 64 - 1)
+    # d_state 9..16 (whole io tiles): the row kernel, one pass at the 130M
+    # layer, no workspace; d_inner not a multiple of 8 (bf16) falls back to the
+    # lane kernels, as does d_state 8: they cut the 130M layer into 64-step
+    # segments.
+    assert ws(8, 2048, 1536, 16) == 0 and ws(8, 2048, 1536, 12) == 0
+    assert ws(8, 2048, 1540, 16) == _seg_ws(8, 1540, 16, 2048 // 64 - 1)
     assert ws(8, 2048, 1536, 8) == _seg_ws(8, 1536, 8, 2048 // 64 - 1)
     assert ws(1, 0, 64, 16) == ctypes.c_size_t(-1).value
 

@@ -48,6 +48,13 @@ SHAPES = [
     (1, 1009, 96, 16, 1, "bf16"),    # rank 1, several segments, ragged end
     (3, 40, 33, 8, 33, "f32"),       # rank 33: a one-column second slice
     (2, 2100, 192, 16, 16, "bf16"),  # many segments
+    # the row kernel (d_state 9..16, d_inner a multiple of 8 / 4): the delta
+    # tile formed on the matrix cores by one wave of each workgroup
+    (2, 300, 96, 12, 16, "bf16"),    # padded states
+    (1, 500, 64, 9, 33, "f32"),      # rank 33: element loads, one-column second slice
+    (2, 1100, 128, 13, 48, "bf16"),  # a cut sequence: summary and main with the projection
+    (2, 200, 64, 16, 20, "bf16"),    # rank not a multiple of 8: element loads
+    (1, 77, 4104, 16, 64, "bf16"),   # a channel tail inside the last workgroup
 ]
 
 
