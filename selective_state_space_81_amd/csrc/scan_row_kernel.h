@@ -195,6 +195,24 @@ __device__ __forceinline__ float row_reduce_finish(const float (&q)[8], bool bit
     return row_reduce_quads(r, bit1, bit0);
 }
 
+// out[i] = (v broadcast from lane J0 + i of the row) * x_i, as four
+// v_mul_f32_dpp.  The compiler folds a broadcast into the consuming v_mul
+// (row_bcast), but in the summary and checkpoint walks it scheduled the moves
+// apart from their multiplies and left them unfolded: 32 extra moves per
+// block.  The leading s_nop 1 gives the two wait states a DPP read needs.
+template <int J0>
+__device__ __forceinline__ void mul_bcast4(float* out, float v, float x0, float x1, float x2,
+                                           float x3) {
+    asm("s_nop 1\n"
+        "v_mul_f32_dpp %0, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %1, %4, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %2, %4, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf\n"
+        "v_mul_f32_dpp %3, %4, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
+        : "v"(v), "v"(x0), "v"(x1), "v"(x2), "v"(x3), "n"(J0), "n"(J0 + 1), "n"(J0 + 2),
+          "n"(J0 + 3));
+}
+
 // Sum over the 16 lanes of a row, in every lane.
 __device__ __forceinline__ float row_allsum(float v) {
     v += qperm<kQpXor1>(v);
@@ -559,19 +577,37 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
             if constexpr (!SUMMARY)
                 Cq[i] = *reinterpret_cast<const f4*>(&s_bc[buf][1][st[q]][4 * i]);
         }
+        // the walks without a readout form the block's broadcast products
+        // up front (mul_bcast4); the main pass leaves them to the compiler
+        float argv[SUMMARY ? kRT : 1], ubv[SUMMARY ? kRT : 1];
+        if constexpr (SUMMARY) {
+            static_for(
+                [&](auto gc) {
+                    constexpr int g = decltype(gc)::value;
+                    mul_bcast4<4 * g>(&argv[4 * g], e.dt, A2[q], A2[q], A2[q], A2[q]);
+                    mul_bcast4<4 * g>(&ubv[4 * g], e.xv, Bq[g][0], Bq[g][1], Bq[g][2], Bq[g][3]);
+                },
+                std::make_integer_sequence<int, 4>{});
+        }
         static_for(
             [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const float bj = Bq[j / 4][j % 4];
-                const float arg = row_bcast<j>(e.dt) * A2[q];
+                float arg, ub;
+                if constexpr (SUMMARY) {
+                    arg = argv[j];
+                    ub = ubv[j];
+                } else {
+                    arg = row_bcast<j>(e.dt) * A2[q];
+                    ub = row_bcast<j>(e.xv) * bj;
+                }
                 float abar, bx;
                 if constexpr (BIL) {
                     const float r = bilinear_r(arg);
                     abar = fmaf(2.f, r, -1.f);
-                    bx = (row_bcast<j>(e.xv) * bj) * r;
+                    bx = ub * r;
                 } else {
                     abar = hw_exp2(arg);
-                    const float ub = row_bcast<j>(e.xv) * bj;
                     if constexpr (ZOH) {
                         const float ser =
                             row_bcast<j>(e.dt) * fmaf(arg, fmaf(arg, kZohT2, kZohT1), 1.f);
