@@ -421,15 +421,15 @@ def measure_bwd_wide(ms, reps=3):
     return out
 
 
-def measure_dtproj(ms, rank=16, reps=20):
-    """ms_scan_fwd_dtproj on the 130M-layer workload with a rank-`rank` step
-    projection (dt_low [8, 2048, rank] and W_dt [1536, rank], bf16): ms per
-    call over rotated buffers and the kernels' HIP-event times.  Beside it,
-    the same result computed in two steps -- torch's matmul writing the raw
-    step in bf16, then ms_scan_fwd -- for comparison."""
+def measure_dtproj(ms, name="m130m", rank=16, reps=20):
+    """ms_scan_fwd_dtproj (Euler) on workload `name` with a rank-`rank` step
+    projection (dt_low [batch, L, rank] and W_dt [d_inner, rank], in the io
+    dtype): ms per call over rotated buffers and the kernels' HIP-event times.
+    Beside it, the same result computed in two steps -- torch's matmul writing
+    the raw step in the io dtype, then ms_scan_fwd -- for comparison."""
     import torch
     import synth
-    w = synth.workload("m130m")
+    w = synth.workload(name)
     base = synth.scan_inputs(w, device="cuda", seed=0)
     sets = []
     for i in range(4):
@@ -477,11 +477,11 @@ def measure_dtproj(ms, rank=16, reps=20):
     elems = w.batch * w.L * w.Dn
     main_ms = ph["main"]["mean_ms"]
     ops = valu_ops_per_element(w.N, "euler", softplus=w.softplus) * elems
-    return {"workload": f"Mamba-130M-layer scan with the rank-{rank} step projection fused "
-                        f"(ms_scan_fwd_dtproj), Euler, bf16",
+    return {"workload": f"{WORKLOAD_TITLE[name]} with the rank-{rank} step projection "
+                        f"fused (ms_scan_fwd_dtproj), Euler, {w.io}",
             "ms_per_call": t_fused, "elem_per_s": elems / (t_fused * 1e-3),
             "two_step_ms_per_call": t_two,
-            "two_step": "torch.matmul (raw step written in bf16) + ms_scan_fwd",
+            "two_step": f"torch.matmul (raw step written in {w.io}) + ms_scan_fwd",
             "main_valu_frac": ops / (main_ms * 1e-3) / 1e12 / VALU_PEAK_TOPS,
             "projection_flops_per_call": 2 * rank * elems,
             "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
@@ -835,6 +835,9 @@ def main():
         out["backward"] = measure_bwd(ms)
         torch.cuda.empty_cache()
         out["dtproj"] = measure_dtproj(ms)
+        torch.cuda.empty_cache()
+        # d_model 768 for d_inner 1536: rank ceil(768 / 16) = 48
+        out["dtproj_wide128"] = measure_dtproj(ms, "wide128", rank=48, reps=10)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, disc)

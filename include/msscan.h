@@ -180,8 +180,14 @@ ms_status ms_scan_fwd_noalloc(const void* u, const void* delta, const float* A, 
  *   kernels of its own, whose plan may need more than ms_scan_fwd's).
  *
  * Statuses as for ms_scan_fwd; MS_ERR_SHAPE for dt_rank outside 1..64;
- * MS_ERR_UNSUPPORTED for d_state other than 8 .. 16, and for 9 .. 15 when
- * d_inner is not a multiple of 8 (bf16 io) or 4 (fp32 io).  Deterministic.
+ * MS_ERR_UNSUPPORTED unless one of these holds:
+ *   d_state 8 or 16;
+ *   d_state 9 .. 15 and d_inner a multiple of 8 (bf16 io) or 4 (fp32 io);
+ *   d_state 17 .. 32, d_inner a multiple of 8 (bf16) or 4 (fp32) and
+ *     batch * ceil(d_inner / 8) >= 512;
+ *   d_state 33 .. 128, d_inner a multiple of 4 and
+ *     batch * ceil(d_inner / 4) >= 512.
+ * Deterministic.
  */
 size_t ms_scan_dtproj_workspace_bytes(const ms_dims* dims, uint32_t flags);
 ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt,

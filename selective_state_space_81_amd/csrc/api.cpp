@@ -122,12 +122,14 @@ void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p,
 #endif
 static_assert(MSSCAN_ROW_WIDE_MIN_WAVES >= MSSCAN_ROW_TARGET_WAVES,
               "wide rows run the sequence as one segment");
-bool row_plan(const ms_dims& d, int disc, msscan::Plan& p) {
+// lane_euler: leave d_state 33..64 with Euler to the lane kernel (the plain
+// forward; the fused projection has no lane kernel there).
+bool row_plan(const ms_dims& d, int disc, msscan::Plan& p, bool lane_euler = true) {
     if (d.d_state <= 8) return false;
     // d_state 33..64 with Euler: the lane kernel (all 64 states in a lane)
     // is as fast or faster there, summaries included (measured at batch 2,
     // L 8192, d_inner 1536: 0.59 against 0.64 ms at d_state 64, equal at 48)
-    if (disc == msscan::dev::kEuler && d.d_state > 32 && d.d_state <= 64 &&
+    if (lane_euler && disc == msscan::dev::kEuler && d.d_state > 32 && d.d_state <= 64 &&
         msscan::lane_variant_exists(64, disc))
         return false;
     int rows = 1, spl = 1;
@@ -194,15 +196,19 @@ bool tile_plan(const ms_dims& d, msscan::Plan& p) {
     return true;
 }
 
-// rows: whether the row path may be chosen (the fused step projection runs on
-// the lane kernels only).
-msscan::Plan make_plan(const ms_dims& d, uint32_t flags, bool rows = true) {
+// Which row plans make_plan may choose: none, those of the plain forward, or
+// those of the fused step projection (which has no lane kernel above d_state
+// 16, so it keeps the rows at d_state 33..64 with Euler too).
+enum RowChoice { kNoRows, kForwardRows, kProjectionRows };
+
+msscan::Plan make_plan(const ms_dims& d, uint32_t flags, RowChoice rows = kForwardRows) {
     msscan::Plan p{};
     const int N = d.d_state;
     // Per segment boundary and channel: N summary states, plus the segment
     // decay -- one sum of dt, or N products of A_bar for the bilinear form.
     const size_t per_channel = (size_t)N + ((flags & MS_BILINEAR) ? (size_t)N : 1);
-    if ((rows && row_plan(d, disc_of(flags), p)) || lane_plan(d, disc_of(flags), p) ||
+    if ((rows != kNoRows && row_plan(d, disc_of(flags), p, rows == kForwardRows)) ||
+        lane_plan(d, disc_of(flags), p) ||
         tile_plan(d, p)) {
         if (p.chunks > 1) {
             const size_t km1 = (size_t)(p.chunks - 1);
@@ -353,13 +359,13 @@ size_t ms_scan_workspace_bytes(const ms_dims* dims, uint32_t flags) {
     return ws_bytes(make_plan(*dims, flags), *dims, flags);
 }
 
-// The fused step projection runs on the row kernel when the plan is one row
-// per channel (d_state 9..16) with whole io tiles, else on the lane kernels
-// (d_state 8 and 16).
+// The fused step projection runs on the row kernel whenever a row plan with
+// whole io tiles exists (d_state 9..16; 17..128 when batch x d_inner fills
+// the chip uncut), else on the lane kernels (d_state 8 and 16).
 static msscan::Plan dtproj_plan(const ms_dims& d, uint32_t flags) {
-    const msscan::Plan p = make_plan(d, flags, true);
-    if (p.tile_path == 3 && p.rows == 1 && d.d_inner % (d.io == MS_BF16 ? 8 : 4) == 0) return p;
-    return make_plan(d, flags, false);
+    const msscan::Plan p = make_plan(d, flags, kProjectionRows);
+    if (p.tile_path == 3 && (p.rows > 1 || d.d_inner % (d.io == MS_BF16 ? 8 : 4) == 0)) return p;
+    return make_plan(d, flags, kNoRows);
 }
 
 size_t ms_scan_dtproj_workspace_bytes(const ms_dims* dims, uint32_t flags) {
@@ -399,7 +405,8 @@ ms_status ms_scan_fwd_dtproj(const void* u, const void* dt_low, const void* W_dt
     if (!rows &&
         (p.tile_path != 2 || p.ns != dims->d_state || !msscan::dtproj_variant_exists(dims->d_state)))
         return fail(MS_ERR_UNSUPPORTED,
-                    "the fused dt projection needs d_state 8, or 9..16 (got %d; 9..15 also need "
+                    "the fused dt projection needs d_state 8, 9..16, or 17..128 with "
+                    "batch x d_inner filling the GPU uncut (got %d; all but 8 and 16 also need "
                     "d_inner a multiple of 8 for bf16, 4 for fp32)",
                     dims->d_state);
     const size_t need = ws_bytes(p, *dims, flags);

@@ -264,17 +264,18 @@ __device__ __forceinline__ void put_bc(float* dst, const RT (&v)[VB], W widen) {
 // state before every block into a.agg as [batch][block][d_inner][d_state];
 // no readout, no output.
 //
-// DTP (one row per channel, whole io tiles): the raw step is not read but
-// projected, delta[t][d] = sum_r W[d][r] x[t][r] (dtproj_frag.h).  Wave 1,
-// which would move the delta tile, loads the block's 16 x rank tile of x
-// instead and, at staging, forms the block's 16-step x 16-channel delta tile
-// on the matrix cores against W fragments it loaded once; the tile goes to
-// LDS in fp32 (never rounded to the io type).
+// DTP (whole io tiles): the raw step is not read but projected,
+// delta[t][d] = sum_r W[d][r] x[t][r] (dtproj_frag.h).  Wave 1, which would
+// move the delta tile, loads the block's 16 x rank tile of x instead and, at
+// staging, forms a 16-step x 16-channel delta tile on the matrix cores
+// against W fragments it loaded once (the workgroup's CH channels first;
+// with several rows per channel the rest of the 16 are computed and unused);
+// the tile goes to LDS in fp32 (never rounded to the io type).
 template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP, int RPC, int SPL,
           bool CKPT = false, bool DTP = false>
 __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     static_assert(!CKPT || (SUMMARY && RPC == 1 && SPL == 1), "checkpoint walk");
-    static_assert(!DTP || (COOP && RPC == 1 && SPL == 1 && !CKPT), "projected step");
+    static_assert(!DTP || (COOP && !CKPT), "projected step");
     static_assert(RPC == 1 || RPC == 2 || RPC == 4, "a channel's rows share one wave");
     static_assert(SPL == 1 || SPL == 2, "states per lane");
     static_assert(COOP || RPC == 1, "several rows per channel move io as whole tiles");
@@ -399,7 +400,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
                 if (kc * 32 < a.rank)
-                    wfr[kc].load(rW, (uint32_t)(tile * kRowCh + fm) * xrow, kc * 32 + 8 * fq,
+                    wfr[kc].load(rW, (uint32_t)(tile * CH + fm) * xrow, kc * 32 + 8 * fq,
                                  a.rank, xvec);
         }
     }
@@ -439,7 +440,17 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     auto load = [&](Raw& r, int rel) {
         const uint32_t nr = rows_of(rel);
         if constexpr (COOP) {
-            bool projected = false;
+            // DTP: wave 1's chunk load reads nothing (an empty range: zeros,
+            // no memory access); the chunk path stays the same for every
+            // wave, so its registers are the plain kernel's
+            if (wv < ntiles_io) {
+                const void* src = wv == 0 ? a.u : (wv == 1 ? (DTP ? a.u : a.delta) : a.z);
+                const auto rs = make_rsrc(base(src, rel, rowb), (DTP && wv == 1) ? 0u : nr * rowb);
+                if constexpr (kChB == 16)
+                    r.t = __builtin_amdgcn_raw_buffer_load_b128(rs, coff, 0, 0);
+                else
+                    r.t = __builtin_amdgcn_raw_buffer_load_b64(rs, coff, 0, 0);
+            }
             if constexpr (DTP) {
                 if (wv == 1) {
                     const auto rX = make_rsrc(base(a.dtx, rel, xrow), nr * xrow);  // rows past L: 0
@@ -447,16 +458,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                     for (int kc = 0; kc < 2; ++kc)
                         if (kc * 32 < a.rank)
                             r.xf[kc].load(rX, (uint32_t)fm * xrow, kc * 32 + 8 * fq, a.rank, xvec);
-                    projected = true;
                 }
-            }
-            if (!projected && wv < ntiles_io) {
-                const void* src = wv == 0 ? a.u : (wv == 1 ? a.delta : a.z);
-                const auto rs = make_rsrc(base(src, rel, rowb), nr * rowb);
-                if constexpr (kChB == 16)
-                    r.t = __builtin_amdgcn_raw_buffer_load_b128(rs, coff, 0, 0);
-                else
-                    r.t = __builtin_amdgcn_raw_buffer_load_b64(rs, coff, 0, 0);
             }
         } else {
             r.u = R::load(make_rsrc(base(a.u, rel, rowb), nr * rowb), eoff);
@@ -482,7 +484,8 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         put_bc<VB>(&s_bc[buf][0][bs][tq * VB], r.bb, widen);
         if constexpr (!SUMMARY) put_bc<VB>(&s_bc[buf][1][bs][tq * VB], r.cb, widen);
         if constexpr (COOP) {
-            bool projected = false;
+            if (wv < ntiles_io && lane < kRT * kCpr)  // DTP: wave 1's zeros go unread
+                *reinterpret_cast<Chunk*>(&s_io[buf][wv][crow][cch * kCw]) = r.t;
             if constexpr (DTP) {
                 if (wv == 1) {
                     f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -491,11 +494,8 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                         if (kc * 32 < a.rank) r.xf[kc].mma(wfr[kc], acc);
                     // acc[i]: delta at step 4 fq + i of channel fm
                     *reinterpret_cast<f4*>(&s_dt[buf][fm][4 * fq]) = acc;
-                    projected = true;
                 }
             }
-            if (!projected && wv < ntiles_io && lane < kRT * kCpr)
-                *reinterpret_cast<Chunk*>(&s_io[buf][wv][crow][cch * kCw]) = r.t;
         } else {
             sg.u = permute_bits(r.u, to_row);
             sg.d = permute_bits(r.d, to_row);

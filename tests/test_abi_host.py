@@ -144,6 +144,12 @@ def test_dtproj_workspace_size_function():
     assert ws(8, 2048, 1536, 16) == 0 and ws(8, 2048, 1536, 12) == 0
     assert ws(8, 2048, 1540, 16) == _seg_ws(8, 1540, 16, 2048 // 64 - 1)
     assert ws(8, 2048, 1536, 8) == _seg_ws(8, 1536, 8, 2048 // 64 - 1)
+    # d_state 17..128 with batch x d_inner filling the chip: the row kernels
+    # with 2 or 4 rows per channel, uncut; also d_state 33..64 with Euler,
+    # which the plain forward leaves to the lane kernels.
+    assert ws(8, 2048, 1536, 32) == 0 and ws(2, 8192, 1536, 128) == 0
+    assert ws(2, 8192, 1536, 64) == 0 and ws(2, 8192, 1536, 48, 3) == 0
+    assert lib.ms_scan_workspace_bytes(ctypes.byref(ms.dims(2, 8192, 1536, 64, 1)), 1) > 0
     assert ws(1, 0, 64, 16) == ctypes.c_size_t(-1).value
 
 
@@ -184,6 +190,7 @@ def test_dtproj_validation_host_only():
     assert call(x=None) == 1 and call(w=None) == 1 and call(u=None) == 1 and call(y=None) == 1
     assert call(flags=8) == 4                                # unknown flag
     assert call(x=24) == 5 and call(w=40) == 5               # misaligned
-    assert call(N=32) == 7 and call(N=4) == 7                # only d_state 8 and 16
+    # d_state 4, and 32 with too few channels for the wide rows
+    assert call(N=32) == 7 and call(N=4) == 7
     assert b"d_state" in lib.ms_last_error()
     assert call(L=4096) == 6                                 # several segments, no workspace

@@ -55,6 +55,14 @@ SHAPES = [
     (2, 1100, 128, 13, 48, "bf16"),  # a cut sequence: summary and main with the projection
     (2, 200, 64, 16, 20, "bf16"),    # rank not a multiple of 8: element loads
     (1, 77, 4104, 16, 64, "bf16"),   # a channel tail inside the last workgroup
+    # row kernels with 2 or 4 rows per channel (d_state 17..128, batch x
+    # d_inner filling the chip uncut): the 16-channel delta tile is formed
+    # whole and the workgroup's 8 or 4 channels read from it
+    (2, 70, 2048, 32, 16, "bf16"),   # 2 rows per channel
+    (1, 45, 2052, 48, 33, "f32"),    # 4 rows, padded states, element loads of x and W
+    (1, 20, 4100, 24, 16, "f32"),    # 2 rows, a channel tail inside the last workgroup
+    (1, 40, 2048, 100, 64, "bf16"),  # 4 rows x 2 states per lane, padded
+    (2, 33, 1024, 128, 20, "bf16"),  # 4 rows x 2 states per lane, rank not a multiple of 8
 ]
 
 
@@ -117,3 +125,31 @@ def test_dtproj_130m_layer_full(gpu):
                                delta_bias=b.index_select(0, ii) if b is not None else None,
                                softplus=w.softplus)
     assert_within(y.index_select(2, ii), ry, "bf16", "y")
+
+
+@pytest.mark.parametrize("name,disc,rank", [("wide128", "euler", 48), ("wide64", "euler", 48),
+                                            ("wide64", "zoh", 16)],
+                         ids=["wide128-euler", "wide64-euler", "wide64-zoh"])
+def test_dtproj_wide_workloads_sampled(gpu, name, disc, rank):
+    """The wide-state workloads (B2 L8192 D1536, d_state 128 or 64, bf16) with
+    the step projection fused, on the row kernels with 4 rows per channel;
+    96 sampled channels against the oracle."""
+    w = synth.workload(name)
+    x = synth.scan_inputs(w, device=DEV, seed=0)
+    x.update(synth.dtproj_inputs(w, rank, device=DEV, seed=0))
+    y = gpu.scan_fwd_dtproj(x["u"], x["dt_low"], x["W_dt"], x["A"], x["B"], x["C"], D=x["D"],
+                            z=x["z"], delta_bias=x.get("delta_bias"), softplus=w.softplus,
+                            **disc_kw(disc))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    ii = torch.as_tensor(sample_channels(w.Dn, 96, seed=3), device=DEV)
+    b = x.get("delta_bias")
+    ry, _ = oracle.scan_dtproj(x["u"].index_select(2, ii), x["dt_low"],
+                               x["W_dt"].index_select(0, ii), x["A"].index_select(0, ii),
+                               x["B"], x["C"], D=x["D"].index_select(0, ii),
+                               z=x["z"].index_select(2, ii),
+                               delta_bias=b.index_select(0, ii) if b is not None else None,
+                               softplus=w.softplus, **disc_kw(disc))
+    assert_within(y.index_select(2, ii), ry, "bf16", "y")
+    del x, y
+    torch.cuda.empty_cache()
