@@ -362,7 +362,8 @@ def measure_bwd(ms, reps=20, warm=3):
 
     t_zoh, t_bil = other(True, False), other(False, True)
     wide = measure_bwd_wide(ms)
-    return {"wide_state": wide,
+    ckpt = measure_checkpointed_pair(ms, w, x, dy, reps, warm)
+    return {"wide_state": wide, "checkpointed": ckpt,
             "workload": "gradients of the Mamba-130M-layer scan (ms_scan_bwd: du, ddelta, dz, "
                         "dA, dB, dC, dD, dbias, dh0), Euler, bf16",
             "zoh_ms_per_call": t_zoh, "bilinear_ms_per_call": t_bil,
@@ -372,6 +373,68 @@ def measure_bwd(ms, reps=20, warm=3):
                               / VALU_PEAK_TOPS,
             "kernels_ms": {k: v["per_call_ms"] for k, v in ph.items()
                            if k != "calls" and v["launches"]}}
+
+
+def measure_checkpointed_pair(ms, w, x, dy, reps, warm):
+    """The training pair with forward-saved checkpoints
+    (ms_scan_fwd_checkpoint + ms_scan_bwd_checkpoint) on workload w, beside
+    the recomputing pair (ms_scan_fwd + ms_scan_bwd): ms per call of each,
+    in the three discretisations, and the checkpointed backward's kernel
+    times."""
+    import torch
+    io = ms.MS_BF16 if w.io == "bf16" else ms.MS_F32
+    stream = torch.cuda.current_stream()
+    y = torch.empty_like(x["u"])
+    ck = torch.empty(w.batch, (w.L + 15) // 16, w.Dn, w.N, dtype=torch.float32, device="cuda")
+    opt = dict(D=x["D"], z=x["z"], delta_bias=x.get("delta_bias"), softplus=w.softplus)
+
+    def timed(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(reps):
+            fn()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / reps
+
+    out = {"checkpoint_bytes": ms.checkpoint_bytes(w.batch, w.L, w.Dn, w.N, io,
+                                                   ms.flags(w.softplus))}
+    for disc in ("euler", "zoh", "bilinear"):
+        kw = dict(zoh=disc == "zoh", bilinear=disc == "bilinear")
+        fl = ms.flags(w.softplus, **kw)
+        ws = torch.empty(ms.scan_bwd_workspace_bytes(w.batch, w.L, w.Dn, w.N, io, fl),
+                         dtype=torch.uint8, device="cuda")
+        wsc = torch.empty(ms.scan_bwd_checkpoint_workspace_bytes(w.batch, w.L, w.Dn, w.N, io,
+                                                                 fl),
+                          dtype=torch.uint8, device="cuda")
+        fwd = lambda: ms.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], **opt,  # noqa
+                                  **kw, y=y, stream=stream)
+        fwd_ck = lambda: ms.scan_fwd_checkpoint(x["u"], x["delta"], x["A"], x["B"], x["C"],  # noqa
+                                                **opt, **kw, y=y, checkpoint=ck, stream=stream)
+        bwd = lambda: ms.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, **opt,  # noqa
+                                  **kw, workspace=ws, stream=stream)
+        bwd_ck = lambda: ms.scan_bwd_checkpoint(x["u"], x["delta"], x["A"], x["B"], x["C"],  # noqa
+                                                dy, ck, **opt, **kw, workspace=wsc,
+                                                stream=stream)
+        t = {"fwd_ms": timed(fwd), "fwd_checkpoint_ms": timed(fwd_ck), "bwd_ms": timed(bwd)}
+        fwd_ck()
+        t["bwd_checkpoint_ms"] = timed(bwd_ck)
+        t["pair_recompute_ms"] = t["fwd_ms"] + t["bwd_ms"]
+        t["pair_checkpoint_ms"] = t["fwd_checkpoint_ms"] + t["bwd_checkpoint_ms"]
+        if disc == "euler":
+            ms.profile_begin(reps)
+            for _ in range(reps):
+                bwd_ck()
+            torch.cuda.synchronize()
+            ph = ms.profile_end()
+            t["bwd_checkpoint_kernels_ms"] = {k: v["per_call_ms"] for k, v in ph.items()
+                                              if k != "calls" and v["launches"]}
+        out[disc] = t
+        del ws, wsc
+    return out
 
 
 def measure_bwd_wide(ms, reps=3):

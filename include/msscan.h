@@ -254,6 +254,57 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
                       size_t workspace_bytes, void* stream);
 
 /*
+ * Training pair with forward-saved checkpoints: the forward stores the state
+ * before every 16-step block beside its outputs, and the backward reads them
+ * instead of walking the sequence forward again to recompute them (the first
+ * of ms_scan_bwd's passes where it runs on the one-row layout).  Same
+ * recurrence and gradients as ms_scan_fwd / ms_scan_bwd (for training end to
+ * end: jsqmd page, section 4.2; lmnt page, section 4.2); memory traded for
+ * time: the checkpoints take
+ * 4 * d_state / 16 bytes per element (4 for d_state 16), against 2 for a bf16
+ * input tensor.
+ *
+ * ms_scan_checkpoint_bytes(dims, flags): bytes of the checkpoint buffer, a
+ *   multiple of 256; 0 when this pair does not serve these dims and flags
+ *   (then use ms_scan_fwd and ms_scan_bwd); (size_t)-1 for invalid dims or
+ *   flags.  It serves d_state 9..16, d_inner a multiple of 8 (bf16 io) or 4
+ *   (fp32 io), and batch * ceil(d_inner / 16) >= 512.
+ *
+ * ms_scan_fwd_checkpoint: ms_scan_fwd (same arguments, outputs and
+ *   statuses; no workspace) that also fills
+ *     checkpoint : [batch][ceil(seqlen / 16)][d_inner][d_state] fp32
+ *                  (required; 16-byte aligned; must not overlap any other
+ *                  argument): entry (b, k, d, n) is h[n] of channel d of
+ *                  sequence b before step 16k -- h0 (or 0) at k = 0.
+ *   MS_ERR_UNSUPPORTED when ms_scan_checkpoint_bytes is 0.  Deterministic.
+ *
+ * ms_scan_bwd_checkpoint: ms_scan_bwd for the same dims and flags, with the
+ *   checkpoint filled by ms_scan_fwd_checkpoint on the same u, delta, A, B,
+ *   delta_bias and h0 (read only; h0 itself is not an argument: its
+ *   contribution is in the checkpoint), and a workspace of
+ *   ms_scan_bwd_checkpoint_workspace_bytes(dims, flags) bytes ((size_t)-1
+ *   when ms_scan_checkpoint_bytes is 0, or for invalid dims).  Other
+ *   arguments, outputs and statuses as for ms_scan_bwd; MS_ERR_UNSUPPORTED
+ *   when ms_scan_checkpoint_bytes is 0.  Deterministic; its gradients are
+ *   those ms_scan_bwd computes from the states it recomputes.
+ */
+size_t ms_scan_checkpoint_bytes(const ms_dims* dims, uint32_t flags);
+ms_status ms_scan_fwd_checkpoint(const void* u, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z,
+                                 const float* delta_bias, uint32_t flags, void* y,
+                                 const float* h0, float* h_last, float* checkpoint,
+                                 const ms_dims* dims, void* stream);
+size_t ms_scan_bwd_checkpoint_workspace_bytes(const ms_dims* dims, uint32_t flags);
+ms_status ms_scan_bwd_checkpoint(const void* u, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z,
+                                 const float* delta_bias, uint32_t flags,
+                                 const float* checkpoint, const void* dy, const float* dh_last,
+                                 void* du, void* ddelta, float* dA, float* dB, float* dC,
+                                 float* dD, void* dz, float* dbias, float* dh0,
+                                 const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * Causal depthwise conv1d over the sequence, optionally followed by silu: the
  * step of the block that turns the x branch into the scan input u (the
  * lmnt.cn page, section 3.1, puts a depthwise 1D convolution of width about 4

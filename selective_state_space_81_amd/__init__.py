@@ -29,7 +29,9 @@ STATUS = {0: "MS_OK", 1: "MS_ERR_NULL", 2: "MS_ERR_SHAPE", 3: "MS_ERR_DTYPE",
 EXPORTS = ("ms_scan_workspace_bytes", "ms_scan_fwd", "ms_state_update", "ms_status_string",
            "ms_last_error", "ms_abi_version", "ms_profile_begin", "ms_profile_end",
            "ms_conv1d_silu", "ms_scan_bwd_workspace_bytes", "ms_scan_bwd",
-           "ms_scan_fwd_dtproj", "ms_scan_dtproj_workspace_bytes", "ms_scan_fwd_noalloc")
+           "ms_scan_fwd_dtproj", "ms_scan_dtproj_workspace_bytes", "ms_scan_fwd_noalloc",
+           "ms_scan_checkpoint_bytes", "ms_scan_fwd_checkpoint",
+           "ms_scan_bwd_checkpoint_workspace_bytes", "ms_scan_bwd_checkpoint")
 
 PHASES = ("prep", "summary", "carry", "main", "step", "conv", "reduce")  # ms_phase order
 
@@ -100,6 +102,16 @@ def load(path: Optional[str] = None):
     lib.ms_scan_bwd.restype = ctypes.c_int
     lib.ms_scan_bwd.argtypes = [vp] * 8 + [u32] + [vp] * 12 + [ctypes.POINTER(MsDims), vp,
                                                                 ctypes.c_size_t, vp]
+    lib.ms_scan_checkpoint_bytes.argtypes = [ctypes.POINTER(MsDims), u32]
+    lib.ms_scan_checkpoint_bytes.restype = ctypes.c_size_t
+    lib.ms_scan_fwd_checkpoint.argtypes = [vp] * 8 + [u32] + [vp] * 4 + [ctypes.POINTER(MsDims),
+                                                                          vp]
+    lib.ms_scan_fwd_checkpoint.restype = ctypes.c_int
+    lib.ms_scan_bwd_checkpoint_workspace_bytes.argtypes = [ctypes.POINTER(MsDims), u32]
+    lib.ms_scan_bwd_checkpoint_workspace_bytes.restype = ctypes.c_size_t
+    lib.ms_scan_bwd_checkpoint.argtypes = [vp] * 8 + [u32] + [vp] * 12 + [
+        ctypes.POINTER(MsDims), vp, ctypes.c_size_t, vp]
+    lib.ms_scan_bwd_checkpoint.restype = ctypes.c_int
     lib.ms_conv1d_silu.restype = ctypes.c_int
     lib.ms_conv1d_silu.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, ctypes.c_int64, i32, i32,
                                    vp]
@@ -327,37 +339,50 @@ def _scan_function():
 
         class ScanFn(torch.autograd.Function):
             @staticmethod
-            def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, softplus, zoh, bilinear):
-                y = scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
-                             softplus=softplus, zoh=zoh, bilinear=bilinear, h0=h0)
-                ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0)
+            def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, softplus, zoh, bilinear,
+                        save_states):
+                kw = dict(D=D, z=z, delta_bias=delta_bias, softplus=softplus, zoh=zoh,
+                          bilinear=bilinear, h0=h0)
+                ck = None
+                if save_states and checkpoint_bytes(*u.shape, B.shape[-1], _io(u),
+                                                    flags(softplus, zoh, bilinear)):
+                    y, ck = scan_fwd_checkpoint(u, delta, A, B, C, **kw)
+                else:
+                    y = scan_fwd(u, delta, A, B, C, **kw)
+                ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0, ck)
                 ctx.disc = (softplus, zoh, bilinear)
                 return y
 
             @staticmethod
             def backward(ctx, dy):
-                u, delta, A, B, C, D, z, delta_bias, h0 = ctx.saved_tensors
+                u, delta, A, B, C, D, z, delta_bias, h0, ck = ctx.saved_tensors
                 softplus, zoh, bilinear = ctx.disc
-                g = scan_bwd(u, delta, A, B, C, dy.contiguous(), D=D, z=z,
-                             delta_bias=delta_bias, softplus=softplus, zoh=zoh,
-                             bilinear=bilinear, h0=h0,
-                             want_dh0=h0 is not None and ctx.needs_input_grad[8])
+                kw = dict(D=D, z=z, delta_bias=delta_bias, softplus=softplus, zoh=zoh,
+                          bilinear=bilinear, want_dh0=h0 is not None and ctx.needs_input_grad[8])
+                if ck is not None:
+                    g = scan_bwd_checkpoint(u, delta, A, B, C, dy.contiguous(), ck, **kw)
+                else:
+                    g = scan_bwd(u, delta, A, B, C, dy.contiguous(), h0=h0, **kw)
                 return (g["du"], g["ddelta"], g["dA"], g["dB"].to(B.dtype),
                         g["dC"].to(C.dtype), g["dD"], g["dz"],
                         g["dbias"] if delta_bias is not None else None,
-                        g["dh0"] if h0 is not None else None, None, None, None)
+                        g["dh0"] if h0 is not None else None, None, None, None, None)
 
         _scan_fn = ScanFn
     return _scan_fn
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None, *,
-                   softplus=True, zoh=False, bilinear=False):
+                   softplus=True, zoh=False, bilinear=False, save_states=True):
     """The scan as a differentiable torch operation: the forward is
     ms_scan_fwd and the backward ms_scan_bwd (gradients of every tensor
-    argument; dB and dC are returned in B's and C's dtype).  Returns y."""
+    argument; dB and dC are returned in B's and C's dtype).  With save_states,
+    where the checkpointed pair serves the dims (ms_scan_checkpoint_bytes > 0)
+    the forward is ms_scan_fwd_checkpoint and its block states are kept for
+    ms_scan_bwd_checkpoint (4 * d_state / 16 bytes per element) instead of
+    being recomputed.  Returns y."""
     return _scan_function().apply(u, delta, A, B, C, D, z, delta_bias, h0, softplus, zoh,
-                                  bilinear)
+                                  bilinear, save_states)
 
 
 def profile_begin(max_calls: int) -> None:
@@ -453,5 +478,91 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, *, softplus
                             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
                             _ptr(out["dbias"]), _ptr(out["dh0"]), ctypes.byref(d),
                             _ptr(workspace), ws_size, _stream(stream))
+    _check(rc)
+    return out
+
+
+def checkpoint_bytes(batch: int, seqlen: int, d_inner: int, d_state: int, io: int,
+                     flag_bits: int = MS_SOFTPLUS) -> int:
+    """ms_scan_checkpoint_bytes: size of the forward-saved checkpoints (0 when
+    the checkpointed pair does not serve these dims)."""
+    d = dims(batch, seqlen, d_inner, d_state, io)
+    n = load().ms_scan_checkpoint_bytes(ctypes.byref(d), flag_bits)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsError(2, "invalid dims")
+    return int(n)
+
+
+def scan_fwd_checkpoint(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, softplus=True,
+                        zoh=False, bilinear=False, y=None, h0=None, h_last=None,
+                        checkpoint=None, stream=None):
+    """ms_scan_fwd_checkpoint on torch device tensors: the forward scan that
+    also saves the backward's block-state checkpoints.  Allocates y and the
+    checkpoint ([batch, ceil(L/16), d_inner, d_state] fp32) when not given.
+    Returns (y, checkpoint)."""
+    import torch
+    batch, L, Dn, N, _ = _chk_scan(u, delta, A, B, C, D, z, delta_bias, h0, h_last, y)
+    io = _io(u)
+    fl = flags(softplus, zoh, bilinear)
+    if checkpoint_bytes(batch, L, Dn, N, io, fl) == 0:
+        raise MsError(7, "no forward checkpoints for these dims")
+    if y is None:
+        y = torch.empty_like(u)
+    if checkpoint is None:
+        checkpoint = torch.empty(batch, (L + 15) // 16, Dn, N, dtype=torch.float32,
+                                 device=u.device)
+    _chk(checkpoint, "checkpoint", torch.float32, (batch, (L + 15) // 16, Dn, N))
+    d = dims(batch, L, Dn, N, io)
+    rc = load().ms_scan_fwd_checkpoint(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(z), _ptr(delta_bias), fl, _ptr(y), _ptr(h0),
+                                       _ptr(h_last), _ptr(checkpoint), ctypes.byref(d),
+                                       _stream(stream))
+    _check(rc)
+    return y, checkpoint
+
+
+def scan_bwd_checkpoint_workspace_bytes(batch: int, seqlen: int, d_inner: int, d_state: int,
+                                        io: int, flag_bits: int = MS_SOFTPLUS) -> int:
+    d = dims(batch, seqlen, d_inner, d_state, io)
+    n = load().ms_scan_bwd_checkpoint_workspace_bytes(ctypes.byref(d), flag_bits)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsError(7, "no checkpointed backward for these dims")
+    return int(n)
+
+
+def scan_bwd_checkpoint(u, delta, A, B, C, dy, checkpoint, D=None, z=None, delta_bias=None, *,
+                        softplus=True, zoh=False, bilinear=False, dh_last=None, workspace=None,
+                        stream=None, want_dh0=True):
+    """ms_scan_bwd_checkpoint on torch device tensors: scan_bwd with the
+    checkpoint that scan_fwd_checkpoint saved (h0 is in it).  Returns the
+    dict of scan_bwd."""
+    import torch
+    batch, L, Dn, N, iod = _chk_scan(u, delta, A, B, C, D, z, delta_bias)
+    _chk(dy, "dy", iod, (batch, L, Dn))
+    _chk(dh_last, "dh_last", torch.float32, (batch, Dn, N))
+    _chk(checkpoint, "checkpoint", torch.float32, (batch, (L + 15) // 16, Dn, N))
+    io = _io(u)
+    fl = flags(softplus, zoh, bilinear)
+    dev = u.device
+    f32 = torch.float32
+    out = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+           "dz": torch.empty_like(u) if z is not None else None,
+           "dA": torch.empty(Dn, N, dtype=f32, device=dev),
+           "dB": torch.empty(batch, L, N, dtype=f32, device=dev),
+           "dC": torch.empty(batch, L, N, dtype=f32, device=dev),
+           "dD": torch.empty(Dn, dtype=f32, device=dev) if D is not None else None,
+           "dbias": torch.empty(Dn, dtype=f32, device=dev),
+           "dh0": torch.empty(batch, Dn, N, dtype=f32, device=dev) if want_dh0 else None}
+    ws_n = scan_bwd_checkpoint_workspace_bytes(batch, L, Dn, N, io, fl)
+    if workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    ws_size = workspace.numel() * workspace.element_size()
+    d = dims(batch, L, Dn, N, io)
+    rc = load().ms_scan_bwd_checkpoint(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), fl,
+        _ptr(checkpoint), _ptr(dy), _ptr(dh_last), _ptr(out["du"]), _ptr(out["ddelta"]),
+        _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+        _ptr(out["dbias"]), _ptr(out["dh0"]), ctypes.byref(d), _ptr(workspace), ws_size,
+        _stream(stream))
     _check(rc)
     return out

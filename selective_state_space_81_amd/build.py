@@ -23,6 +23,7 @@ PROBE_LIB = os.path.join(HERE, "libmsprobe.so")
 SOURCES = [os.path.join(CSRC, "scan_kernels.hip"), os.path.join(CSRC, "scan_tile.hip"),
            os.path.join(CSRC, "scan_lane.hip"), os.path.join(CSRC, "scan_row.hip"),
            os.path.join(CSRC, "scan_row_wide.hip"), os.path.join(CSRC, "scan_row_dtproj.hip"),
+           os.path.join(CSRC, "scan_row_ckpt.hip"),
            os.path.join(CSRC, "decode.hip"),
            os.path.join(CSRC, "conv.hip"), os.path.join(CSRC, "scan_bwd.hip"),
            os.path.join(CSRC, "bwd_wide.hip"), os.path.join(CSRC, "bwd_row.hip"),

@@ -530,25 +530,45 @@ BwdPlan bwd_plan(const ms_dims& d, uint32_t flags) {
     return q;
 }
 
-size_t bwd_ws_floats(const BwdPlan& q) {
+// with_ckpt: whether the workspace holds the checkpoints (not when the
+// forward saved them).
+size_t bwd_ws_floats(const BwdPlan& q, bool with_ckpt = true) {
     return pad64(q.agg) + pad64(q.fdecay) + pad64(q.mu) + pad64(q.bdecay) + pad64(q.pbc) +
-           pad64(q.pparam) + pad64(q.pgroup) + pad64(q.ckpt);
+           pad64(q.pparam) + pad64(q.pgroup) + (with_ckpt ? pad64(q.ckpt) : 0);
+}
+
+// Forward-saved checkpoints: offered where the backward runs on the row layout
+// (bwd_plan's rows) and the forward's own plan is the uncut one-row kernel
+// with whole io tiles, which the same conditions give.
+bool ckpt_plan(const ms_dims& d, uint32_t flags, BwdPlan* q, msscan::Plan* p) {
+    *q = bwd_plan(d, flags);
+    *p = make_plan(d, flags);
+    return q->rows && p->tile_path == 3 && p->rows == 1 && p->chunks == 1 &&
+           d.d_inner % (d.io == MS_BF16 ? 8 : 4) == 0;
 }
 
 // Launches the 16-states-or-fewer backward kernels on one problem (the
 // inputs in `f`, the workspace at ws laid out by bwd_plan).
+// ckpt: the forward's checkpoints (row plans only; null: the backward walks
+// the sequence for them, into the workspace).
 hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, float* ws,
                           const void* dy, const float* dh_last, void* du, void* ddelta, void* dz,
                           float* dA, float* dB, float* dC, float* dD, float* dbias, float* dh0,
-                          bool bf16, hipStream_t hs) {
+                          bool bf16, hipStream_t hs, const float* ckpt = nullptr) {
     f.chunk_len = q.fwd.chunk_len;
     f.chunks = q.fwd.chunks;
     if (q.rows) {
         f.tiles = (int)q.tiles;
         f.waves = msscan::kRowWaves;
         msscan::BwdRowLaunch L{};
-        L.ckpt = ws;
-        L.pbc = (ws += pad64(q.ckpt));
+        L.walk = ckpt == nullptr;
+        if (ckpt) {
+            L.ckpt = const_cast<float*>(ckpt);  // read only (no walk)
+        } else {
+            L.ckpt = ws;
+            ws += pad64(q.ckpt);
+        }
+        L.pbc = ws;
         L.pparam = (ws += pad64(q.pbc));
         L.pgroup = ws + pad64(q.pparam);
         L.f = f;
@@ -748,6 +768,98 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
     }
     if ((e = msscan::launch_wide_finish(w, bf16, hs)) != hipSuccess)
         return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
+size_t ms_scan_checkpoint_bytes(const ms_dims* dims, uint32_t flags) {
+    if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
+    BwdPlan q;
+    msscan::Plan p;
+    return ckpt_plan(*dims, flags, &q, &p) ? pad64(q.ckpt) * sizeof(float) : 0;
+}
+
+ms_status ms_scan_fwd_checkpoint(const void* u, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z,
+                                 const float* delta_bias, uint32_t flags, void* y,
+                                 const float* h0, float* h_last, float* checkpoint,
+                                 const ms_dims* dims, void* stream) {
+    g_err[0] = '\0';
+    ms_status st = check_dims(dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (!u || !delta || !A || !B || !C || !y || !checkpoint)
+        return fail(MS_ERR_NULL, "u, delta, A, B, C, y and checkpoint are required");
+    const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, y, h0, h_last, checkpoint};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    BwdPlan q;
+    msscan::Plan p;
+    if (!ckpt_plan(*dims, flags, &q, &p))
+        return fail(MS_ERR_UNSUPPORTED,
+                    "no forward checkpoints for these dims (ms_scan_checkpoint_bytes is 0)");
+    msscan::ScanArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+    a.h0 = h0; a.h_last = h_last; a.y = y; a.agg = checkpoint;
+    a.L = dims->seqlen; a.chunk_len = p.chunk_len; a.batch = dims->batch; a.Dn = dims->d_inner;
+    a.N = dims->d_state; a.chunks = p.chunks; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    a.waves = p.waves;
+    a.tiles = p.tiles;
+    msscan::prof_call();
+    const hipError_t e = msscan::launch_scan_rows_ckpt(p, a, dims->io == MS_BF16, disc_of(flags),
+                                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return MS_OK;
+}
+
+size_t ms_scan_bwd_checkpoint_workspace_bytes(const ms_dims* dims, uint32_t flags) {
+    if (check_dims(dims) != MS_OK || check_flags(flags) != MS_OK) return (size_t)-1;
+    BwdPlan q;
+    msscan::Plan p;
+    if (!ckpt_plan(*dims, flags, &q, &p)) return (size_t)-1;
+    return bwd_ws_floats(q, false) * sizeof(float);
+}
+
+ms_status ms_scan_bwd_checkpoint(const void* u, const void* delta, const float* A,
+                                 const void* B, const void* C, const float* D, const void* z,
+                                 const float* delta_bias, uint32_t flags,
+                                 const float* checkpoint, const void* dy, const float* dh_last,
+                                 void* du, void* ddelta, float* dA, float* dB, float* dC,
+                                 float* dD, void* dz, float* dbias, float* dh0,
+                                 const ms_dims* dims, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    g_err[0] = '\0';
+    ms_status st = check_dims(dims);
+    if (st != MS_OK) return st;
+    if ((st = check_flags(flags)) != MS_OK) return st;
+    if (!u || !delta || !A || !B || !C || !checkpoint || !dy || !du || !ddelta || !dA || !dB ||
+        !dC)
+        return fail(MS_ERR_NULL,
+                    "u, delta, A, B, C, checkpoint, dy, du, ddelta, dA, dB and dC are required");
+    if ((z && !dz) || (D && !dD))
+        return fail(MS_ERR_NULL, "dz (dD) is required when z (D) is given");
+    const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, checkpoint, dy, dh_last, du,
+                          ddelta, dA, dB, dC, dD, dz, dbias, dh0, workspace};
+    for (const void* p : ptrs)
+        if (misaligned(p)) return fail(MS_ERR_ALIGN, "pointer %p is not 16-byte aligned", p);
+    BwdPlan q;
+    msscan::Plan p;
+    if (!ckpt_plan(*dims, flags, &q, &p))
+        return fail(MS_ERR_UNSUPPORTED,
+                    "no forward checkpoints for these dims (ms_scan_checkpoint_bytes is 0)");
+    const size_t need = bwd_ws_floats(q, false) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+        return fail(MS_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    msscan::ScanArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+    a.L = dims->seqlen; a.batch = dims->batch; a.Dn = dims->d_inner;
+    a.N = dims->d_state; a.softplus = (flags & MS_SOFTPLUS) ? 1 : 0;
+    msscan::prof_call();
+    const hipError_t e =
+        run_bwd_narrow(a, q, flags, static_cast<float*>(workspace), dy, dh_last, du, ddelta, dz,
+                       dA, dB, dC, dD, dbias, dh0, dims->io == MS_BF16,
+                       static_cast<hipStream_t>(stream), checkpoint);
+    if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return MS_OK;
 }
 

@@ -13,7 +13,8 @@
 //
 // Two passes.
 //   1. The forward walk (scan_row with CKPT) stores the state before every
-//      16-step block: [batch][block][d_inner][d_state].
+//      16-step block: [batch][block][d_inner][d_state].  It is skipped when
+//      the forward pass saved them (ms_scan_fwd_checkpoint).
 //   2. bwd_row walks the blocks from the last to the first.  Per block it
 //      recomputes the 16 states of each lane from the stored one, keeping
 //      h_t and A_bar_t of all 16 steps in registers (one state per lane makes
@@ -509,7 +510,7 @@ hipError_t launch_rows_bwd(const BwdRowLaunch& L, hipStream_t s) {
     f.chunks = 1;
     f.chunk_len = f.L;
     const unsigned grid = (unsigned)f.batch * (unsigned)f.tiles;
-    {
+    if (L.walk) {
         ProfScope ps(s, kPhaseSummary);
         hipLaunchKernelGGL((scan_row<BF16, DISC, SP, true, true, 1, 1, true>), dim3(grid),
                            dim3(64 * kRowWaves), 0, s, f);

@@ -144,6 +144,11 @@ bool dtproj_variant_exists(int n);
 // plan with one row per channel; d_inner a multiple of 8 (bf16) or 4 (fp32).
 hipError_t launch_scan_rows_dtproj(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                                    hipStream_t s);
+// The forward that also stores the backward's checkpoints into a.agg
+// ([batch][ceil(L / 16)][Dn][N], scan_row_ckpt.hip): a row plan with one row
+// per channel and one segment; d_inner a multiple of 8 (bf16) or 4 (fp32).
+hipError_t launch_scan_rows_ckpt(const Plan& p, const ScanArgs& a, bool bf16, int disc,
+                                 hipStream_t s);
 hipError_t launch_bc_prepare(const ScanArgs& a, int np, bool bf16, hipStream_t s);  // rows np wide
 // Causal depthwise conv1d (+ silu), width 1..8.
 hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s);
@@ -204,6 +209,7 @@ struct BwdRowLaunch {
     float* dD;
     float* dbias;
     float* ckpt;    // [batch][ceil(L / 16)][Dn][N]: the state before each 16-step block
+    bool walk;      // compute ckpt first (false: it holds the forward's checkpoints; only read)
     float* pbc;     // [tiles][batch][L][2N]
     float* pparam;  // [batch][Dn][N+2]
     float* pgroup;  // [kParamGroups][Dn][N+2]

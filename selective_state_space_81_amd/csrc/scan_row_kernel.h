@@ -259,10 +259,11 @@ __device__ __forceinline__ void put_bc(float* dst, const RT (&v)[VB], W widen) {
 // q * kRT * RPC + kRT * g + n for q < SPL.  A workgroup is 4 waves, 16 rows:
 // CH = 16 / RPC channels, every row of a channel in one wave.
 //
-// CKPT (with SUMMARY, one row per channel, one segment): the forward walk of
-// the backward pass.  From h0 (or zero) over the whole sequence, storing the
-// state before every block into a.agg as [batch][block][d_inner][d_state];
-// no readout, no output.
+// CKPT (one row per channel, one segment): store the state before every
+// block into a.agg as [batch][block][d_inner][d_state], from h0 (or zero)
+// over the whole sequence.  With SUMMARY it is the backward's forward walk
+// (no readout, no output); without, the forward pass saving the backward's
+// checkpoints beside y.
 //
 // DTP (whole io tiles): the raw step is not read but projected,
 // delta[t][d] = sum_r W[d][r] x[t][r] (dtproj_frag.h).  Wave 1, which would
@@ -274,7 +275,7 @@ __device__ __forceinline__ void put_bc(float* dst, const RT (&v)[VB], W widen) {
 template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP, int RPC, int SPL,
           bool CKPT = false, bool DTP = false>
 __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
-    static_assert(!CKPT || (SUMMARY && RPC == 1 && SPL == 1), "checkpoint walk");
+    static_assert(!CKPT || (RPC == 1 && SPL == 1), "checkpoints of one-row channels");
     static_assert(!DTP || (COOP && !CKPT), "projected step");
     static_assert(RPC == 1 || RPC == 2 || RPC == 4, "a channel's rows share one wave");
     static_assert(SPL == 1 || SPL == 2, "states per lane");
@@ -293,7 +294,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     static_assert(U % PF == 0 && U % NB == 0 && U % 2 == 0, "sets, buffers and y tiles cycle");
     constexpr bool ZOH = DISC == kZoh;
     constexpr bool BIL = DISC == kBilinear;
-    constexpr bool PROD = SUMMARY && BIL;  // bilinear summary: product of A_bar
+    constexpr bool PROD = SUMMARY && BIL && !CKPT;  // bilinear summary: product of A_bar
     using R = Io<BF16>;
     using RT = typename R::T;
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -628,8 +629,8 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
             },
             std::make_integer_sequence<int, kRT>{});
         }, std::make_integer_sequence<int, SPL>{});
-        if constexpr (SUMMARY && !CKPT) {
-            if constexpr (!PROD) {
+        if constexpr (SUMMARY) {
+            if constexpr (!PROD && !CKPT) {
                 const float yk = e.dt - s_comp;
                 const float tk = s_sum + yk;
                 s_comp = (tk - s_sum) - yk;

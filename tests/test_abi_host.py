@@ -194,3 +194,43 @@ def test_dtproj_validation_host_only():
     assert call(N=32) == 7 and call(N=4) == 7
     assert b"d_state" in lib.ms_last_error()
     assert call(L=4096) == 6                                 # several segments, no workspace
+
+
+def test_checkpoint_pair_sizes_and_validation_host_only():
+    lib = ms.load()
+
+    def ck(b, L, D, N, io=1, flags=1):
+        return lib.ms_scan_checkpoint_bytes(ctypes.byref(ms.dims(b, L, D, N, io)), flags)
+
+    def bws(b, L, D, N, io=1, flags=1):
+        return lib.ms_scan_bwd_checkpoint_workspace_bytes(ctypes.byref(ms.dims(b, L, D, N, io)),
+                                                          flags)
+
+    none = ctypes.c_size_t(-1).value
+    # the 130M layer: [8][128 blocks][1536][16] fp32
+    assert ck(8, 2048, 1536, 16) == 8 * 128 * 1536 * 16 * 4
+    assert ck(8, 2048, 1536, 16, flags=3) == ck(8, 2048, 1536, 16, flags=5)
+    assert ck(2, 129, 4096, 12, io=0) == 2 * 9 * 4096 * 12 * 4  # ragged last block
+    # not served: d_state above 16 or below 9, too few channels, a bf16
+    # d_inner that is not a multiple of 8
+    assert ck(8, 2048, 1536, 32) == 0 and ck(8, 2048, 1536, 8) == 0
+    assert ck(1, 2048, 1536, 16) == 0 and ck(8, 2048, 1540, 16) == 0
+    assert ck(0, 2048, 1536, 16) == none and ck(8, 2048, 1536, 16, flags=6) == none
+    # the backward's workspace without its checkpoint region
+    full = lib.ms_scan_bwd_workspace_bytes(ctypes.byref(ms.dims(8, 2048, 1536, 16, 1)), 1)
+    assert bws(8, 2048, 1536, 16) == full - ck(8, 2048, 1536, 16)
+    assert bws(1, 2048, 1536, 16) == none
+    p = 16
+    d = ms.dims(8, 2048, 1536, 16, 1)
+    fwd = lambda ckp=p, dd=d: lib.ms_scan_fwd_checkpoint(  # noqa: E731
+        p, p, p, p, p, None, None, None, 1, p, None, None, ckp, ctypes.byref(dd), None)
+    assert fwd(ckp=None) == 1                               # MS_ERR_NULL
+    assert fwd(ckp=24) == 5                                 # MS_ERR_ALIGN
+    assert fwd(dd=ms.dims(1, 2048, 64, 16, 1)) == 7         # not served
+    assert b"checkpoint" in lib.ms_last_error()
+    bwd = lambda ckp=p, dd=d, ws=p, wsb=1 << 40: lib.ms_scan_bwd_checkpoint(  # noqa: E731
+        p, p, p, p, p, None, None, None, 1, ckp, p, None, p, p, p, p, p, None, None, None, None,
+        ctypes.byref(dd), ws, wsb, None)
+    assert bwd(ckp=None) == 1
+    assert bwd(dd=ms.dims(1, 2048, 64, 16, 1)) == 7
+    assert bwd(ws=None) == 6 and bwd(wsb=16) == 6           # MS_ERR_WORKSPACE
