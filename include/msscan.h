@@ -86,6 +86,12 @@ typedef enum { MS_F32 = 0, MS_BF16 = 1 } ms_dtype;
 #define MS_ZOH (1u << 1)      /* zero-order hold B_bar; else Euler B_bar = dt * B     */
 #define MS_BILINEAR (1u << 2) /* bilinear A_bar, B_bar (exclusive with MS_ZOH)        */
 
+/*
+ * Problem sizes.  Besides the per-field ranges (MS_ERR_SHAPE), batch and
+ * ceil(d_inner / 64) must be <= 65535 (MS_ERR_UNSUPPORTED), and
+ * batch * seqlen * d_inner * d_state must be <= 2^56 (MS_ERR_SHAPE), which
+ * keeps every size the library computes inside size_t.
+ */
 typedef struct {
     int32_t batch;   /* >= 1                                   */
     int64_t seqlen;  /* L >= 1, any value (no power-of-two rule), <= 2^31 - 1 */

@@ -42,6 +42,12 @@ ms_status check_dims(const ms_dims* d) {
     // grid limits: tiles and batch go to grid y/z
     if ((d->d_inner + 63) / 64 > 65535 || d->batch > 65535)
         return fail(MS_ERR_UNSUPPORTED, "d_inner/64 and batch must be <= 65535");
+    // every buffer and workspace size (at most tens of bytes per element and
+    // state) then stays far inside size_t
+    const double states = (double)d->batch * (double)d->seqlen * (double)d->d_inner * d->d_state;
+    if (states > 0x1p56)
+        return fail(MS_ERR_SHAPE, "batch x seqlen x d_inner x d_state = %.3g exceeds 2^56",
+                    states);
     return MS_OK;
 }
 
@@ -879,6 +885,9 @@ ms_status ms_conv1d_silu(const void* x, const float* weight, const float* bias,
     msscan::ConvArgs a{};
     a.x = x; a.w = weight; a.bias = bias; a.x_prev = width > 1 ? x_prev : nullptr; a.u = u;
     a.L = seqlen; a.batch = batch; a.Dn = d_inner; a.width = width;
+    if (msscan::conv_workgroups(a) > msscan::kMaxConvWorkgroups)
+        return fail(MS_ERR_UNSUPPORTED, "batch x seqlen x d_inner needs more than 2^31-1 conv "
+                                        "workgroups");
     msscan::prof_call();
     hipError_t e = msscan::launch_conv1d(a, io == MS_BF16, silu != 0,
                                          static_cast<hipStream_t>(stream));

@@ -98,5 +98,14 @@ __device__ __forceinline__ float zoh_factor_q(float dt, float q1, float q2, floa
     return fabsf(t) < kZohSwitch ? ser : big;
 }
 
+// Workgroup id -> logical workgroup: XCD x (= id mod 8, the order in which
+// the hardware deals workgroups to the 8 XCDs) gets a contiguous range of
+// logical indices, in order, so that neighbouring logical workgroups share an
+// L2.  A bijection on [0, G) for any G.
+__device__ __forceinline__ uint32_t xcd_logical(uint32_t bid, uint32_t G) {
+    const uint32_t q = G >> 3, rem = G & 7u, x = bid & 7u, i = bid >> 3;
+    return x * q + (x < rem ? x : rem) + i;
+}
+
 }  // namespace dev
 }  // namespace msscan

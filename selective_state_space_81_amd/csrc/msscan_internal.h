@@ -83,6 +83,7 @@ struct ConvArgs {
     int batch;
     int Dn;
     int width;
+    int64_t tgroups, cgroups;  // set by launch_conv1d: workgroups along time and channels
 };
 
 struct StepArgs {
@@ -150,7 +151,10 @@ hipError_t launch_scan_rows_dtproj(const Plan& p, const ScanArgs& a, bool bf16, 
 hipError_t launch_scan_rows_ckpt(const Plan& p, const ScanArgs& a, bool bf16, int disc,
                                  hipStream_t s);
 hipError_t launch_bc_prepare(const ScanArgs& a, int np, bool bf16, hipStream_t s);  // rows np wide
-// Causal depthwise conv1d (+ silu), width 1..8.
+// Causal depthwise conv1d (+ silu), width 1..8.  One-dimensional grid of
+// conv_workgroups(a) workgroups, at most kMaxConvWorkgroups.
+constexpr int64_t kMaxConvWorkgroups = 0x7fffffffLL;
+int64_t conv_workgroups(const ConvArgs& a);
 hipError_t launch_conv1d(const ConvArgs& a, bool bf16, bool silu, hipStream_t s);
 // Decode step with 4 states per lane (d_state in {4, 8, ..., 128}).
 bool step_quads_supported(int batch, int d_inner, int n);

@@ -90,13 +90,6 @@ static_assert(kRowUnroll % kRowPf == 0 && kRowUnroll % kNb == 0,
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// Workgroup id -> logical workgroup: XCD x (= id mod 8) gets a contiguous
-// range of logical indices, in order.  A bijection on [0, G) for any G.
-__device__ __forceinline__ uint32_t xcd_logical(uint32_t bid, uint32_t G) {
-    const uint32_t q = G >> 3, rem = G & 7u, x = bid & 7u, i = bid >> 3;
-    return x * q + (x < rem ? x : rem) + i;
-}
-
 // Readout reduce-scatter, stages 1-2: p[j] (this lane's term for timestep
 // j) -> r[m], the sum over 4 lanes for timestep 8*bit3 + 4*bit2 + m of the
 // lane index within the row.

@@ -98,6 +98,25 @@ static void check_validation() {
     CHECK(ms_scan_fwd_dtproj(fake(0), fake(1), fake(2), 0, (const float*)fake(3), fake(4),
                              fake(5), nullptr, nullptr, nullptr, 1, fake(6), nullptr, nullptr,
                              &good, nullptr, 0, nullptr) == MS_ERR_SHAPE);
+    // checkpointed pair: required checkpoint, a shape it does not serve
+    CHECK(ms_scan_fwd_checkpoint(fake(0), fake(1), (const float*)fake(2), fake(3), fake(4),
+                                 nullptr, nullptr, nullptr, 1, fake(5), nullptr, nullptr, nullptr,
+                                 &good, nullptr) == MS_ERR_NULL);
+    CHECK(ms_scan_fwd_checkpoint(fake(0), fake(1), (const float*)fake(2), fake(3), fake(4),
+                                 nullptr, nullptr, nullptr, 1, fake(5), nullptr, nullptr,
+                                 (float*)fake(6), &good, nullptr) == MS_ERR_UNSUPPORTED);
+    CHECK(ms_scan_bwd_checkpoint(fake(0), fake(1), (const float*)fake(2), fake(3), fake(4),
+                                 nullptr, nullptr, nullptr, 1, (const float*)fake(5), fake(6),
+                                 nullptr, fake(7), fake(8), (float*)fake(9), (float*)fake(10),
+                                 (float*)fake(11), nullptr, nullptr, nullptr, nullptr, &good,
+                                 fake(12), 1 << 20, nullptr) == MS_ERR_UNSUPPORTED);
+    // conv workgroup count beyond the grid
+    CHECK(ms_conv1d_silu(fake(0), (const float*)fake(1), nullptr, nullptr, 4, 1, fake(2), 65535,
+                         0x7fffffff, 4, 1, nullptr) == MS_ERR_UNSUPPORTED);
+    // sizes whose product leaves size_t's comfortable range
+    const ms_dims huge{65535, 0x7fffffff, 1 << 20, 128, MS_BF16};
+    CHECK(scan(&huge, 1, fake(0), fake(5)) == MS_ERR_SHAPE);
+    CHECK(ms_scan_workspace_bytes(&huge, 1) == (size_t)-1);
     // status strings
     for (int s = 0; s <= 9; ++s) CHECK(ms_status_string((ms_status)s) != nullptr);
     CHECK(ms_abi_version() == MS_ABI_VERSION);
@@ -127,6 +146,11 @@ static void check_workspace_sizes() {
                             CHECK(wd == (size_t)-1 || wd % 256 == 0);
                             const size_t wb = ms_scan_bwd_workspace_bytes(&d, f);
                             CHECK(wb == (size_t)-1 || wb % 4 == 0);
+                            const size_t ck = ms_scan_checkpoint_bytes(&d, f);
+                            CHECK(ck == (size_t)-1 || ck % 256 == 0);
+                            const size_t wc = ms_scan_bwd_checkpoint_workspace_bytes(&d, f);
+                            CHECK((ck == 0 || ck == (size_t)-1) ? wc == (size_t)-1
+                                                                : wc == wb - ck);
                         }
     const ms_dims a{1, 65536, 256, 16, 1}, c{1, 2 * 65536, 256, 16, 1};
     CHECK(ms_scan_workspace_bytes(&c, 1) >= ms_scan_workspace_bytes(&a, 1));
