@@ -82,7 +82,7 @@ __device__ __forceinline__ void store_ch(__amdgpu_buffer_rsrc_t r, uint32_t off,
 }
 
 #ifndef MSSCAN_CONV_WAVES
-#define MSSCAN_CONV_WAVES 4
+#define MSSCAN_CONV_WAVES 8
 #endif
 // waves per workgroup: consecutive time chunks of the same channels
 constexpr int kConvWaves = MSSCAN_CONV_WAVES;
