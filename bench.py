@@ -631,7 +631,7 @@ def _csv(dirname, suffix):
 def _short(name):
     m = re.search(r"(scan_row<[^>]*>|scan_lane<[^>]*>|scan_tile<[^>]*>|"
                   r"bc_prepare<[^>]*>|carry_chain<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
-                  r"bwd_main<[^>]*>|bwd_row<[^>]*>|seg_summaries<[^>]*>|reduce_bc4|reduce_bc|"
+                  r"bwd_main<[^>]*>|bwd_row<[^>]*>|seg_summaries<[^>]*>|reduce_bc4_params|reduce_bc4|reduce_bc|"
                   r"wide_\w+(?:<[^>]*>)?|"
                   r"reduce_param_groups|reduce_params|"
                   r"neg_kernel)", name)

@@ -778,21 +778,24 @@ __global__ void __launch_bounds__(256) reduce_bc(BwdArgs a, float* dB, float* dC
 // reduce_bc with four consecutive outputs per thread and 16-byte loads (when
 // batch * L * 2N is a multiple of 4); each output's tiles are added in the
 // same order, so the sums are the same.
-__global__ void __launch_bounds__(256) reduce_bc4(BwdArgs a, float* dB, float* dC, int tiles) {
+constexpr int kBcBatch = 8;  // loads in flight per thread
+// Thread `t` of the float4 range: the four outputs idx .. idx + 3 of dB | dC.
+__device__ __forceinline__ void bc4_sum(const BwdArgs& a, float* dB, float* dC, int tiles,
+                                        int64_t t) {
     typedef float f4v __attribute__((ext_vector_type(4)));
     const ScanArgs& f = a.f;
     const int64_t per = (int64_t)f.batch * f.L * 2 * f.N;
-    const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const int64_t idx = t * 4;
     if (idx >= per) return;
     f4v acc = {0.f, 0.f, 0.f, 0.f};
     int tl = 0;
-    for (; tl + 8 <= tiles; tl += 8) {
-        f4v v[8];
+    for (; tl + kBcBatch <= tiles; tl += kBcBatch) {
+        f4v v[kBcBatch];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kBcBatch; ++i)
             v[i] = *reinterpret_cast<const f4v*>(a.pbc + (int64_t)(tl + i) * per + idx);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc += v[i];
+        for (int i = 0; i < kBcBatch; ++i) acc += v[i];
     }
     for (; tl < tiles; ++tl) acc += *reinterpret_cast<const f4v*>(a.pbc + (int64_t)tl * per + idx);
 #pragma unroll
@@ -805,6 +808,46 @@ __global__ void __launch_bounds__(256) reduce_bc4(BwdArgs a, float* dB, float* d
         else
             dC[row * f.N + k - f.N] = acc[i];
     }
+}
+
+__global__ void __launch_bounds__(256) reduce_bc4(BwdArgs a, float* dB, float* dC, int tiles) {
+    bc4_sum(a, dB, dC, tiles, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// The dA | dD | dbias output of entry idx = (d, k), k < N + 2.
+__device__ __forceinline__ void put_param(const ScanArgs& f, int64_t idx, float v, float* dA,
+                                          float* dD, float* dbias) {
+    const int k = (int)(idx % (f.N + 2));
+    const int64_t d = idx / (f.N + 2);
+    if (k < f.N)
+        dA[d * f.N + k] = v;
+    else if (k == f.N) {
+        if (dD) dD[d] = v;
+    } else if (dbias) {
+        dbias[d] = v;
+    }
+}
+
+// reduce_bc4 and the parameter sums in one launch, for pparam of at most
+// kParamGroups rows (the row layout: one per batch row): blocks past
+// bc_blocks add each entry's rows in increasing order, which gives the bits
+// of the two-level sum below (each group holds one row; adding the empty
+// groups' zeros changes nothing but the sign of a zero).
+__global__ void __launch_bounds__(256) reduce_bc4_params(BwdArgs a, float* dB, float* dC,
+                                                         int tiles, unsigned bc_blocks, float* dA,
+                                                         float* dD, float* dbias) {
+    if (blockIdx.x < bc_blocks) {
+        bc4_sum(a, dB, dC, tiles, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+        return;
+    }
+    const ScanArgs& f = a.f;
+    const int64_t idx = (int64_t)(blockIdx.x - bc_blocks) * blockDim.x + threadIdx.x;
+    const int64_t per = (int64_t)f.Dn * (f.N + 2);
+    if (idx >= per) return;
+    const int64_t rows = (int64_t)f.batch * ((f.chunks + kBwdWaves - 1) / kBwdWaves);
+    float acc = 0.f;
+    for (int64_t r = 0; r < rows; ++r) acc += a.pparam[r * per + idx];
+    put_param(f, idx, acc, dA, dD, dbias);
 }
 
 // Parameter sums over the batch x ceil(K/kBwdWaves) rows of pparam, in two fixed-order
@@ -841,15 +884,7 @@ __global__ void __launch_bounds__(256) reduce_param_groups(BwdArgs a, float* dA,
     float acc = 0.f;
 #pragma unroll
     for (int g = 0; g < kParamGroups; ++g) acc += a.pgroup[(int64_t)g * per + idx];
-    const int k = (int)(idx % (f.N + 2));
-    const int64_t d = idx / (f.N + 2);
-    if (k < f.N)
-        dA[d * f.N + k] = acc;
-    else if (k == f.N) {
-        if (dD) dD[d] = acc;
-    } else if (dbias) {
-        dbias[d] = acc;
-    }
+    put_param(f, idx, acc, dA, dD, dbias);
 }
 
 template <int NS, bool BF16, int DISC>
@@ -913,6 +948,16 @@ hipError_t launch_bwd_reductions(const ScanArgs& f, float* pbc, int tiles, float
     a.pgroup = pgroup;
     hipError_t e;
     const int64_t nbc = (int64_t)f.batch * f.L * 2 * f.N;
+    const int64_t npar = (int64_t)f.Dn * (f.N + 2);
+    const unsigned pblocks = (unsigned)((npar + 255) / 256);
+    const int64_t prows = (int64_t)f.batch * ((f.chunks + kBwdWaves - 1) / kBwdWaves);
+    if (nbc % 4 == 0 && prows <= kParamGroups) {
+        const unsigned bc_blocks = (unsigned)((nbc / 4 + 255) / 256);
+        ProfScope ps(s, kPhaseReduce);
+        hipLaunchKernelGGL(reduce_bc4_params, dim3(bc_blocks + pblocks), dim3(256), 0, s, a, dB,
+                           dC, tiles, bc_blocks, dA, dD, dbias);
+        return hipGetLastError();
+    }
     {
         ProfScope ps(s, kPhaseReduce);
         if (nbc % 4 == 0)
@@ -923,8 +968,6 @@ hipError_t launch_bwd_reductions(const ScanArgs& f, float* pbc, int tiles, float
                                dB, dC, tiles);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t npar = (int64_t)f.Dn * (f.N + 2);
-    const unsigned pblocks = (unsigned)((npar + 255) / 256);
     {
         ProfScope ps(s, kPhaseReduce);
         hipLaunchKernelGGL(reduce_params, dim3(pblocks, kParamGroups), dim3(256), 0, s, a);
