@@ -311,6 +311,14 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) RT s_y[(COOP && !SUMMARY) ? 2 : 1][kRT][kIoS];
     // DTP: the projected delta tile of a staged block, [channel][step] fp32
     __shared__ __attribute__((aligned(16))) float s_dt[DTP ? NB : 1][DTP ? kRowCh : 1][kBcS];
+    // ZOH main pass: each row's per-step (dt, x) of a block,
+    // [parity][row][step][2]; every lane of the row reads them back as LDS
+    // broadcasts, so the recurrence's products take plain VGPR operands (no
+    // DPP source).  ZOH reads dt twice per state-step, and there this beat
+    // the DPP broadcasts (3B layer 1.27 -> 1.21 ms); for Euler it lost (the
+    // 130M layer 0.140 -> 0.147 ms).
+    constexpr bool LDSB = !SUMMARY && ZOH;
+    __shared__ __attribute__((aligned(16))) float s_dx[LDSB ? 2 : 1][LDSB ? kRowCh : 1][kRT][2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -504,7 +512,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     struct Elem {
         float dt, xv, u, z;
     };
-    auto prologue = [&](int rel, int buf, const Staged& sg) -> Elem {
+    auto prologue = [&](int rel, int buf, const Staged& sg, int par) -> Elem {
         Elem e{};
         float draw;
         if constexpr (COOP) {
@@ -525,6 +533,12 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         if constexpr (SP) dt = softplus_f(dt);
         e.dt = n < (int)rows_of(rel) ? dt : 0.f;  // steps past the end change nothing
         e.xv = ZOH ? e.u : e.dt * e.u;            // B is scaled by u (ZOH) or dt*u
+        if constexpr (LDSB) {
+            float2 v;
+            v.x = e.dt;
+            v.y = e.xv;
+            *reinterpret_cast<float2*>(&s_dx[par][grow][n][0]) = v;
+        }
         return e;
     };
     // COOP: wave 3 stores the y tile of the block at rel from buffer buf.
@@ -583,17 +597,26 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                 },
                 std::make_integer_sequence<int, 4>{});
         }
+        f4 dx[2];  // main pass: (dt, x) of steps 4g .. 4g + 3 of the current group
         static_for(
             [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const float bj = Bq[j / 4][j % 4];
-                float arg, ub;
+                float arg, ub, dtj = 0.f;
                 if constexpr (SUMMARY) {
                     arg = argv[j];
                     ub = ubv[j];
-                } else {
+                } else if constexpr (!LDSB) {
                     arg = row_bcast<j>(e.dt) * A2[q];
                     ub = row_bcast<j>(e.xv) * bj;
+                } else {
+                    if constexpr (j % 4 == 0) {
+                        dx[0] = *reinterpret_cast<const f4*>(&s_dx[ybuf][grow][j][0]);
+                        dx[1] = *reinterpret_cast<const f4*>(&s_dx[ybuf][grow][j + 2][0]);
+                    }
+                    dtj = dx[(j % 4) / 2][2 * (j % 2)];
+                    arg = dtj * A2[q];
+                    ub = dx[(j % 4) / 2][2 * (j % 2) + 1] * bj;
                 }
                 float abar, bx;
                 if constexpr (BIL) {
@@ -603,8 +626,8 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                 } else {
                     abar = hw_exp2(arg);
                     if constexpr (ZOH) {
-                        const float ser =
-                            row_bcast<j>(e.dt) * fmaf(arg, fmaf(arg, kZohT2, kZohT1), 1.f);
+                        const float dtb = LDSB ? dtj : row_bcast<j>(e.dt);
+                        const float ser = dtb * fmaf(arg, fmaf(arg, kZohT2, kZohT1), 1.f);
                         const float big = fmaf(abar, invA[q], -invA[q]);
                         bx = (fabsf(arg) < kZohSwitch ? ser : big) * ub;
                     } else {
@@ -669,7 +692,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         Staged sg;
         stage(r[0], 0, 0, sg);
         __syncthreads();
-        e = prologue(0, 0, sg);
+        e = prologue(0, 0, sg, 0);
     }
     auto do_block = [&](auto ic, int j) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;  // j mod U
@@ -677,7 +700,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         stage(r[(i + 1) % PF], (j + 1) * kRT, (i + 1) % NB, sg);
         __syncthreads();
         if (j > 0) store_y_tile((j - 1) * kRT, (i + 1) & 1);
-        const Elem en = prologue((j + 1) * kRT, (i + 1) % NB, sg);
+        const Elem en = prologue((j + 1) * kRT, (i + 1) % NB, sg, (i + 1) & 1);
         compute(j * kRT, i % NB, i & 1, e);
         e = en;
     };
