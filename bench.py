@@ -321,9 +321,7 @@ def measure_bwd(ms, reps=20, warm=3):
                     delta_bias=x.get("delta_bias"), softplus=w.softplus, workspace=ws,
                     stream=stream)
 
-    for _ in range(warm):
-        call()
-    torch.cuda.synchronize()
+    warm_up(lambda i: call(), warm, 0.25)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(reps):
@@ -349,9 +347,7 @@ def measure_bwd(ms, reps=20, warm=3):
                         delta_bias=x.get("delta_bias"), softplus=w.softplus, zoh=zoh,
                         bilinear=bilinear, workspace=ws2, stream=stream)
 
-        for _ in range(warm):
-            c()
-        torch.cuda.synchronize()
+        warm_up(lambda i: c(), warm, 0.25)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record(stream)
         for _ in range(reps):
@@ -389,9 +385,7 @@ def measure_checkpointed_pair(ms, w, x, dy, reps, warm):
     opt = dict(D=x["D"], z=x["z"], delta_bias=x.get("delta_bias"), softplus=w.softplus)
 
     def timed(fn):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(lambda i: fn(), warm, 0.25)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record(stream)
         for _ in range(reps):
