@@ -282,8 +282,13 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     constexpr int PF = (SPL == 2 || DTP) ? 2 : kRowPf;
     // 128 states make a 16 KB B/C tile per buffer: three buffers (the fewest
     // the pipeline allows) keep two workgroups per CU.
-    constexpr int NB = SPL == 2 ? 3 : kNb;
-    constexpr int U = SPL == 2 ? 6 : kRowUnroll;  // blocks per unrolled loop body
+    // Two states per lane make a 128-state B/C tile (20 KB per buffer): the
+    // pipeline then runs on two buffers (NB2, below), which keeps the LDS of
+    // three workgroups within a CU.
+    constexpr bool NB2 = SPL == 2;
+    static_assert(!NB2 || COOP, "the two-buffer pipeline stages io tiles in LDS");
+    constexpr int NB = NB2 ? 2 : kNb;
+    constexpr int U = NB2 ? 2 : kRowUnroll;  // blocks per unrolled loop body
     static_assert(U % PF == 0 && U % NB == 0 && U % 2 == 0, "sets, buffers and y tiles cycle");
     constexpr bool ZOH = DISC == kZoh;
     constexpr bool BIL = DISC == kBilinear;
@@ -683,6 +688,11 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     // staged while slower waves may still read block j's buffer, and block
     // j + 2 only after every wave has passed block j + 1's barrier, so
     // NB >= 3 buffers suffice.  Blocks past the end stage zeros, harmlessly.
+    // NB2: barrier, store the y tile of block j - 1, form block j's
+    // per-element values, stage block j + 1, run block j.  Every wave has
+    // left block j - 1 (the other buffer) when it passes the barrier, so two
+    // buffers suffice; the per-element values are formed just before their
+    // block.
     const int nblk = (len + kRT - 1) / kRT;
     Raw r[PF];
     static_for([&](auto ic) { load(r[decltype(ic)::value], decltype(ic)::value * kRT); },
@@ -691,18 +701,28 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     {
         Staged sg;
         stage(r[0], 0, 0, sg);
-        __syncthreads();
-        e = prologue(0, 0, sg, 0);
+        if constexpr (!NB2) {
+            __syncthreads();
+            e = prologue(0, 0, sg, 0);
+        }
     }
     auto do_block = [&](auto ic, int j) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;  // j mod U
         Staged sg;
-        stage(r[(i + 1) % PF], (j + 1) * kRT, (i + 1) % NB, sg);
-        __syncthreads();
-        if (j > 0) store_y_tile((j - 1) * kRT, (i + 1) & 1);
-        const Elem en = prologue((j + 1) * kRT, (i + 1) % NB, sg, (i + 1) & 1);
-        compute(j * kRT, i % NB, i & 1, e);
-        e = en;
+        if constexpr (NB2) {
+            __syncthreads();
+            if (j > 0) store_y_tile((j - 1) * kRT, (i + 1) & 1);
+            const Elem ej = prologue(j * kRT, i % NB, sg, i & 1);
+            stage(r[(i + 1) % PF], (j + 1) * kRT, (i + 1) % NB, sg);
+            compute(j * kRT, i % NB, i & 1, ej);
+        } else {
+            stage(r[(i + 1) % PF], (j + 1) * kRT, (i + 1) % NB, sg);
+            __syncthreads();
+            if (j > 0) store_y_tile((j - 1) * kRT, (i + 1) & 1);
+            const Elem en = prologue((j + 1) * kRT, (i + 1) % NB, sg, (i + 1) & 1);
+            compute(j * kRT, i % NB, i & 1, e);
+            e = en;
+        }
     };
     int blk = 0;
     for (; blk + U - 1 < nblk; blk += U)
