@@ -128,14 +128,20 @@ void cut_sequence(const ms_dims& d, int64_t waves_per_segment, msscan::Plan& p,
 #endif
 static_assert(MSSCAN_ROW_WIDE_MIN_WAVES >= MSSCAN_ROW_TARGET_WAVES,
               "wide rows run the sequence as one segment");
+#ifndef MSSCAN_ROW_EULER64_MIN_CHANNELS
+#define MSSCAN_ROW_EULER64_MIN_CHANNELS 8192
+#endif
 // lane_euler: leave d_state 33..64 with Euler to the lane kernel (the plain
 // forward; the fused projection has no lane kernel there).
 bool row_plan(const ms_dims& d, int disc, msscan::Plan& p, bool lane_euler = true) {
     if (d.d_state <= 8) return false;
-    // d_state 33..64 with Euler: the lane kernel (all 64 states in a lane)
-    // is as fast or faster there, summaries included (measured at batch 2,
-    // L 8192, d_inner 1536: 0.59 against 0.64 ms at d_state 64, equal at 48)
+    // d_state 33..64 with Euler and few channels: the lane kernel (all 64
+    // states in a lane) is as fast or faster there, summaries included
+    // (batch 2, L 8192, d_inner 1536, d_state 64: 0.57 against 0.59 ms).
+    // With more channels the rows win (batch 8, L 2048, d_inner 1536: 0.56
+    // against 0.60 ms; batch 4, L 8192, d_inner 5120: 3.42 against 3.50).
     if (lane_euler && disc == msscan::dev::kEuler && d.d_state > 32 && d.d_state <= 64 &&
+        (int64_t)d.batch * d.d_inner < MSSCAN_ROW_EULER64_MIN_CHANNELS &&
         msscan::lane_variant_exists(64, disc))
         return false;
     int rows = 1, spl = 1;

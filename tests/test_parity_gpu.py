@@ -82,6 +82,10 @@ EDGE = [
     (2, 190, 2052, 30, "f32"),
     (1, 200, 2048, 128, "f32"),
     (1, 150, 2048, 100, "bf16"),
+    # d_state 33..64 with Euler: rows once batch x d_inner >= 8192 (the lane
+    # kernel below that); padded states and a channel tail
+    (4, 100, 2048, 48, "bf16"),
+    (2, 70, 4100, 64, "f32"),
 ]
 
 
