@@ -497,6 +497,9 @@ def measure_dtproj(ms, name="m130m", rank=16, reps=20):
     ws = torch.empty(max(1, ms.dtproj_workspace_bytes(w.batch, w.L, w.Dn, w.N, io,
                                                ms.flags(w.softplus))),
                      dtype=torch.uint8, device="cuda")
+    # the plain scan's own plan (it may differ from the fused call's)
+    ws2 = torch.empty(max(1, ms.workspace_bytes(w.batch, w.L, w.Dn, w.N, io, ms.flags(w.softplus))),
+                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def fused(i):
@@ -511,7 +514,7 @@ def measure_dtproj(ms, name="m130m", rank=16, reps=20):
         x, y = sets[i % len(sets)]
         torch.matmul(x["dt_low"], x["W_dt"].t(), out=delta)
         ms.scan_fwd(x["u"], delta, x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
-                    delta_bias=x.get("delta_bias"), softplus=w.softplus, y=y, workspace=ws,
+                    delta_bias=x.get("delta_bias"), softplus=w.softplus, y=y, workspace=ws2,
                     stream=stream)
 
     def timed(fn):
