@@ -280,11 +280,9 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     // Two states per lane take twice as long per block, so half the blocks
     // in flight hide the same load latency, with half the load registers.
     constexpr int PF = (SPL == 2 || DTP) ? 2 : kRowPf;
-    // 128 states make a 16 KB B/C tile per buffer: three buffers (the fewest
-    // the pipeline allows) keep two workgroups per CU.
     // Two states per lane make a 128-state B/C tile (20 KB per buffer): the
     // pipeline then runs on two buffers (NB2, below), which keeps the LDS of
-    // three workgroups within a CU.
+    // three workgroups within a CU (three buffers allowed two).
     constexpr bool NB2 = SPL == 2;
     static_assert(!NB2 || COOP, "the two-buffer pipeline stages io tiles in LDS");
     constexpr int NB = NB2 ? 2 : kNb;
@@ -687,7 +685,8 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     // recurrence with the values formed one block earlier.  Block j + 1 is
     // staged while slower waves may still read block j's buffer, and block
     // j + 2 only after every wave has passed block j + 1's barrier, so
-    // NB >= 3 buffers suffice.  Blocks past the end stage zeros, harmlessly.
+    // NB >= 3 buffers suffice (NB2: two, below).  Blocks past the end stage
+    // zeros, harmlessly.
     // NB2: barrier, store the y tile of block j - 1, form block j's
     // per-element values, stage block j + 1, run block j.  Every wave has
     // left block j - 1 (the other buffer) when it passes the barrier, so two
