@@ -621,11 +621,16 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                     arg = dtj * A2[q];
                     ub = dx[(j % 4) / 2][2 * (j % 2) + 1] * bj;
                 }
-                float abar, bx;
+                float abar = 0.f, bx = 0.f;
                 if constexpr (BIL) {
                     const float r = bilinear_r(arg);
-                    abar = fmaf(2.f, r, -1.f);
-                    bx = ub * r;
+                    if constexpr (PROD) {
+                        abar = fmaf(2.f, r, -1.f);
+                        bx = ub * r;
+                    } else {
+                        // (2r - 1) h + r ub = r (2h + ub) - h: two fmas
+                        h[q] = fmaf(r, fmaf(2.f, h[q], ub), -h[q]);
+                    }
                 } else {
                     abar = hw_exp2(arg);
                     if constexpr (ZOH) {
@@ -637,7 +642,7 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
                         bx = ub;
                     }
                 }
-                h[q] = fmaf(abar, h[q], bx);
+                if constexpr (!BIL || PROD) h[q] = fmaf(abar, h[q], bx);
                 if constexpr (PROD) P[q] *= abar;
                 if constexpr (!SUMMARY) {
                     if constexpr (q == 0)
