@@ -365,16 +365,17 @@ __global__ void __launch_bounds__(64 * kRowWaves)
                     const float fz_big = fmaf(abar, invA, -invA);
                     const float fz = small ? fz_ser : fz_big;
                     const float lb = lam * bj;
+                    const float lbu = lb * uj;
                     cB = (lam * fz) * uj;
                     const float q = abar * lam;
                     const float w = q * hp;
-                    r1 = fmaf(w * A2, kLn2, (abar * lb) * uj);
+                    r1 = fmaf(w, av, abar * lbu);  // a A_bar h_{t-1} l + A_bar l B u
                     r2 = fz * lb;
-                    const float x = t2 * kLn2;
-                    const float dfda_ser = (dtj * dtj) * fmaf(x, fmaf(x, 0.125f, 1.f / 3.f), 0.5f);
+                    // dt^2 (1/2 + x/3 + x^2/8) with x = t2 ln 2
+                    const float dfda_ser = (dtj * dtj) * fmaf(t2, fmaf(t2, kZohD2, kZohD1), 0.5f);
                     const float dfda_big = fmaf(dtj, abar, -fz_big) * invA;
                     const float dfda = small ? dfda_ser : dfda_big;
-                    dA = fmaf(lb * uj, dfda, fmaf(w, dtj, dA));
+                    dA = fmaf(lbu, dfda, fmaf(w, dtj, dA));
                     mu = q;
                 } else {
                     // r = 1/(1 - dt a/2): A_bar = 2r - 1, f = dt r; derivatives

@@ -81,6 +81,10 @@ __device__ __forceinline__ float bilinear_r(float t) {
 constexpr float kZohT1 = 0.34657359027997264f;  // ln2 / 2
 constexpr float kZohT2 = 0.08007550231970023f;  // ln2^2 / 6
 constexpr float kZohSwitch = 0.045084220027780106f;  // (1/32) / ln2
+// dB_bar/dA's series near A = 0, dt^2 (1/2 + x/3 + x^2/8) with x = t ln2:
+// the coefficients of t and t^2
+constexpr float kZohD1 = 0.23104906018664842f;  // ln2 / 3
+constexpr float kZohD2 = 0.06005662673977517f;  // ln2^2 / 8
 __device__ __forceinline__ float zoh_factor(float dt, float t, float abar, float invA) {
     const float ser = dt * fmaf(t, fmaf(t, kZohT2, kZohT1), 1.f);
     const float big = fmaf(abar, invA, -invA);
