@@ -212,11 +212,17 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
             [&](auto nc) {
                 constexpr int n = decltype(nc)::value;
                 const float arg = dt * A2[n];
-                float abar, bx;
+                float abar = 0.f, bx = 0.f;
                 if constexpr (BIL) {
                     const float r = bilinear_r(arg);
-                    abar = fmaf(2.f, r, -1.f);
-                    bx = row_bcast<n % RW>(vbt[n / RW]) * (xv * r);  // B * dt*r*u
+                    const float ub = row_bcast<n % RW>(vbt[n / RW]) * xv;  // B * dt*u
+                    if constexpr (PROD) {
+                        abar = fmaf(2.f, r, -1.f);
+                        bx = ub * r;
+                    } else {
+                        // (2r - 1) h + r (B dt u) = r (2h + B dt u) - h: two fma
+                        h[n] = fmaf(r, fmaf(2.f, h[n], ub), -h[n]);
+                    }
                 } else {
                     abar = hw_exp2(arg);
                     const float bu = row_bcast<n % RW>(vbt[n / RW]) * xv;  // B*x (Euler) or B*u (ZOH)
@@ -225,7 +231,7 @@ __global__ void __launch_bounds__(64, N >= 32 ? 2 : MSSCAN_LANE_WPE) scan_lane(S
                     else
                         bx = bu;
                 }
-                h[n] = fmaf(abar, h[n], bx);
+                if constexpr (!BIL || PROD) h[n] = fmaf(abar, h[n], bx);
                 if constexpr (PROD) P[n] *= abar;
                 // With 32+ states the scheduler would otherwise start every
                 // exponential before the first update and run out of VGPRs.

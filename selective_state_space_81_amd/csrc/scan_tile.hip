@@ -163,11 +163,17 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
             [&](auto jc) {
                 constexpr int j = decltype(jc)::value;
                 const float arg = dx.x * A2[j];
-                float abar, bx;
+                float abar = 0.f, bx = 0.f;
                 if constexpr (BIL) {
                     const float r = bilinear_r(arg);
-                    abar = fmaf(2.f, r, -1.f);
-                    bx = row_bcast<j>(vbt) * (dx.y * r);  // B * dt*r*u
+                    const float ub = row_bcast<j>(vbt) * dx.y;  // B * dt*u
+                    if constexpr (PROD) {
+                        abar = fmaf(2.f, r, -1.f);
+                        bx = ub * r;
+                    } else {
+                        // (2r - 1) h + r (B dt u) = r (2h + B dt u) - h: two fma
+                        h[j] = fmaf(r, fmaf(2.f, h[j], ub), -h[j]);
+                    }
                 } else {
                     abar = hw_exp2(arg);
                     const float bu = row_bcast<j>(vbt) * dx.y;  // B*x (Euler) or B*u (ZOH)
@@ -176,7 +182,7 @@ __global__ void __launch_bounds__(64 * S) scan_tile(ScanArgs a) {
                     else
                         bx = bu;
                 }
-                h[j] = fmaf(abar, h[j], bx);
+                if constexpr (!BIL || PROD) h[j] = fmaf(abar, h[j], bx);
                 if constexpr (PROD) P[j] *= abar;
                 // With a block's steps unrolled, the scheduler would start the
                 // exponentials of many steps ahead of their updates and spill.
