@@ -264,10 +264,15 @@ __device__ __forceinline__ void put_bc(float* dst, const RT (&v)[VB], W widen) {
 // staging, forms a 16-step x 16-channel delta tile on the matrix cores
 // against W fragments it loaded once (the workgroup's CH channels first;
 // with several rows per channel the rest of the 16 are computed and unused);
-// the tile goes to LDS in fp32 (never rounded to the io type).
+// the tile goes to LDS in fp32 (never rounded to the io type).  With two
+// states per lane and bf16 io that variant asks for three waves per SIMD
+// (168 registers, no spills), which the LDS of three workgroups allows; at
+// the 200 it takes unasked, two fit, and a d_state 128 grid at batch 2 x
+// d_inner 1536 ran in one and a half rounds (1.27 against 1.00 ms).
 template <bool BF16, int DISC, bool SP, bool SUMMARY, bool COOP, int RPC, int SPL,
           bool CKPT = false, bool DTP = false>
-__global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
+__global__ void __launch_bounds__(64 * kRowWaves)
+    __attribute__((amdgpu_waves_per_eu(DTP && SPL == 2 && BF16 ? 3 : 1))) scan_row(ScanArgs a) {
     static_assert(!CKPT || (RPC == 1 && SPL == 1), "checkpoints of one-row channels");
     static_assert(!DTP || (COOP && !CKPT), "projected step");
     static_assert(RPC == 1 || RPC == 2 || RPC == 4, "a channel's rows share one wave");
@@ -279,7 +284,9 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
     constexpr int VB = kRT * kNS / kThreads;     // B (and C) tile values per thread
     // Two states per lane take twice as long per block, so half the blocks
     // in flight hide the same load latency, with half the load registers.
-    constexpr int PF = (SPL == 2 || DTP) ? 2 : kRowPf;
+    // With the projection's x rows as well (bf16), one block ahead: that and
+    // the register cap below keep three workgroups per CU, as without it.
+    constexpr int PF = (SPL == 2 && DTP && BF16) ? 1 : (SPL == 2 || DTP) ? 2 : kRowPf;
     // Two states per lane make a 128-state B/C tile (20 KB per buffer): the
     // pipeline then runs on two buffers (NB2, below), which keeps the LDS of
     // three workgroups within a CU (three buffers allowed two).
@@ -443,6 +450,9 @@ __global__ void __launch_bounds__(64 * kRowWaves) scan_row(ScanArgs a) {
         Frag8<BF16> xf[DTP ? 2 : 1];  // DTP, wave 1: the block's x rows
     };
     auto load = [&](Raw& r, int rel) {
+        // With one load set the compiler otherwise carries the block start
+        // in a VGPR and wraps every load below in a waterfall loop.
+        if constexpr (PF == 1) rel = __builtin_amdgcn_readfirstlane(rel);
         const uint32_t nr = rows_of(rel);
         if constexpr (COOP) {
             // DTP: wave 1's chunk load reads nothing (an empty range: zeros,
