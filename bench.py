@@ -292,11 +292,57 @@ def measure_conv(ms, reps=20, width=4):
     k_ms = ms.profile_end()["conv"]["mean_ms"]
     e = 2 if w.io == "bf16" else 4
     nb = 2 * w.batch * w.L * w.Dn * e + w.Dn * (width + 1) * 4
+    del sets
+    # the same bytes moved by a plain copy (libmsprobe's 16-byte copy, x-sized
+    # source to u-sized destination, rotated over 4 pairs like the conv):
+    # the rate an op of this size can reach on this machine
+    c_ms = copy_ms(w.batch * w.L * w.Dn * e, reps)
+    c_gbps = 2 * w.batch * w.L * w.Dn * e / (c_ms * 1e-3) / 1e9
+    gbps = nb / (t_ms * 1e-3) / 1e9
     return {"workload": f"causal depthwise conv1d + silu (ms_conv1d_silu): batch {w.batch}, "
                         f"L {w.L}, d_inner {w.Dn}, width {width}, {w.io}",
             "ms_per_call": t_ms, "kernel_ms": k_ms, "bytes_per_call": nb,
-            "hbm_gbps": nb / (t_ms * 1e-3) / 1e9, "hbm_frac": nb / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9}
+            "hbm_gbps": gbps, "hbm_frac": gbps / HBM_PEAK_GBPS,
+            "kernel_hbm_gbps": nb / (k_ms * 1e-3) / 1e9,
+            "same_size_copy_ms": c_ms, "same_size_copy_gbps": c_gbps,
+            "frac_of_same_size_copy": gbps / c_gbps}
+
+
+def copy_ms(nbytes, reps):
+    """ms per call of libmsprobe's copy of nbytes (a multiple of 16) into
+    another buffer, over 4 rotated source/destination pairs, timed back to
+    back like the ops it is set beside."""
+    import ctypes
+    import torch
+    from selective_state_space_81_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.msprobe_copy.argtypes = [vp, vp, i64, i32, vp]
+    words = nbytes // 16
+    pairs = [(torch.ones(nbytes // 4, dtype=torch.float32, device="cuda"),
+              torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")) for _ in range(4)]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    blocks = max(1, min(16384, (words + 255) // 256))
+
+    def call(i):
+        s, d = pairs[i % len(pairs)]
+        rc = lib.msprobe_copy(s.data_ptr(), d.data_ptr(), words, blocks, sp)
+        if rc != 0:
+            raise RuntimeError(f"probe copy failed: {rc}")
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(reps):
+        call(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t = start.elapsed_time(end) / reps
+    del pairs
+    return t
 
 
 def measure_bwd(ms, reps=20, warm=3):
