@@ -354,7 +354,7 @@ int ms_abi_version(void);
  * Kernel timing, for benchmarks and profiling (not an operation of the
  * method).  Between ms_profile_begin and ms_profile_end, each of the next
  * `max_calls` successful calls of the library's entry points records a pair
- * of HIP events on its own stream around every kernel it launches (up to 16
+ * of HIP events on its own stream around every kernel it launches (up to 64
  * per call), and ms_profile_end waits for those events and returns, per
  * phase, the number of timed launches and their summed kernel time (a call
  * that launches two kernels of one phase, like the backward's two carries,
@@ -371,7 +371,7 @@ int ms_abi_version(void);
  * max_calls are not timed (out->calls counts the timed ones).  The event
  * records add a few microseconds per kernel to a call's wall time.
  *
- * ms_profile_begin: max_calls in [1, 4096]; creates the events on the current
+ * ms_profile_begin: max_calls in [1, 1024]; creates the events on the current
  *   device (MS_ERR_SHAPE for a bad count, MS_ERR_HIP on event creation
  *   failure, MS_ERR_UNSUPPORTED when a profile is already open).
  * ms_profile_end: out may be NULL (results dropped).  Synchronises on the

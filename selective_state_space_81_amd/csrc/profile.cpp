@@ -15,8 +15,9 @@
 namespace msscan {
 namespace {
 
-constexpr int kMaxCalls = 4096;
-constexpr int kMaxLaunchesPerCall = 16;  // event pairs kept per timed call
+constexpr int kMaxCalls = 1024;
+constexpr int kMaxLaunchesPerCall = 64;  // event pairs kept per timed call (the d_state 17-128
+                                         // backward launches ~40 kernels)
 
 // One pair of events per kernel launch: a call may launch several kernels of
 // one phase (the backward's two carries), and each launch is timed on its own.

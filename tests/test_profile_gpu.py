@@ -86,3 +86,27 @@ def test_profile_times_row_backward_launches(gpu):
     assert prof["summary"]["launches"] == 3 and prof["main"]["launches"] == 3
     for k in ("reduce", "summary", "main"):
         assert prof[k]["mean_ms"] > 0
+
+
+def test_profile_times_every_wide_backward_launch(gpu):
+    """The d_state 17-128 backward runs each 16-state slice as its own
+    segment-layout backward (gather, walk, carries, gradient pass, sums,
+    accumulate): ~40 timed launches per call at d_state 64, every one of them
+    recorded, the same number for each call."""
+    w = synth.workload("long", L=512, Dn=256)
+    x = synth.scan_inputs(w, device="cuda", seed=5)
+    dy = torch.randn(w.batch, w.L, w.Dn, device="cuda").to(x["u"].dtype)
+
+    def launches(calls):
+        gpu.profile_begin(calls)
+        for _ in range(calls):
+            gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                         delta_bias=x.get("delta_bias"), softplus=w.softplus)
+        prof = gpu.profile_end()
+        assert prof["calls"] == calls
+        return {k: v["launches"] for k, v in prof.items() if isinstance(v, dict)}
+
+    one, two = launches(1), launches(2)
+    assert sum(one.values()) > 16
+    assert all(two[k] == 2 * one[k] for k in one)
+    assert one["reduce"] >= 4 and one["main"] >= 4  # at least one of each per slice
