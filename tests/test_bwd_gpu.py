@@ -294,3 +294,42 @@ def test_bwd_wide_long_context_sampled(gpu):
     _check(part["dC"], ref["dC"], "f32", "dC")
     del x, full, part
     torch.cuda.empty_cache()
+
+
+def test_bwd_past_2_31_elements_sampled(gpu):
+    """More than 2^31 elements in one backward call (B1, L = 2^21 + 37,
+    d_inner 1024, d_state 16, bf16, Euler, softplus and bias): the per-channel
+    gradients on 24 sampled channels against the oracle run on those
+    channels, and the channel sums dB, dC of the sub-problem made of those
+    channels.  Any element index or byte offset kept in 32 bits would wrap in
+    the last 37 timesteps."""
+    from helpers import sample_channels
+    w = synth.workload("m130m", batch=1, L=(1 << 21) + 37, Dn=1024)
+    assert w.batch * w.L * w.Dn > 2**31
+    x = synth.scan_inputs(w, device=DEV, seed=12)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(81)
+    x["dy"] = torch.randn(w.batch, w.L, w.Dn, generator=g, device=DEV).to(x["u"].dtype)
+    idx = sample_channels(w.Dn, 24, seed=4)
+    full = gpu.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"], D=x["D"], z=x["z"],
+                        delta_bias=x.get("delta_bias"), softplus=w.softplus)
+    torch.cuda.synchronize()
+    sub = _channels(x, idx)
+    ref = oracle.scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["dy"],
+                          D=sub["D"], z=sub["z"], delta_bias=sub.get("delta_bias"),
+                          softplus=w.softplus)
+    ii = torch.as_tensor(idx, device=DEV)
+    for k in ("du", "ddelta", "dz"):
+        _check(full[k].index_select(2, ii), ref[k], w.io, k)
+    for k in ("dA", "dD", "dbias"):
+        _check(full[k].index_select(0, ii), ref[k], "f32", k)
+    del full
+    torch.cuda.empty_cache()
+    part = gpu.scan_bwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], sub["dy"],
+                        D=sub["D"], z=sub["z"], delta_bias=sub.get("delta_bias"),
+                        softplus=w.softplus)
+    torch.cuda.synchronize()
+    _check(part["dB"], ref["dB"], "f32", "dB")
+    _check(part["dC"], ref["dC"], "f32", "dC")
+    del x, part
+    torch.cuda.empty_cache()
