@@ -48,3 +48,28 @@ def test_conv_past_2_31_elements(gpu):
     ref = oracle.conv1d(c["x"].index_select(2, ii), c["weight"].index_select(0, ii),
                         c["bias"].index_select(0, ii))
     assert_within(u.index_select(2, ii), ref, "bf16")
+
+
+def test_decode_past_2_31_states(gpu):
+    """A decode state of more than 2^31 values (batch 4096 x d_inner 32768 x
+    d_state 16 + one batch row: 8.6 GB of fp32 h), two steps; sampled channels
+    of every batch row against the oracle's own fp64 state."""
+    w = synth.workload("decode", batch=4097, Dn=32768, steps=2)
+    assert w.batch * w.Dn * w.N > 2**31
+    x = synth.decode_inputs(w, device=DEV, seed=99)
+    h = x["h0"].clone()
+    idx = sample_channels(w.Dn, 8, seed=10)
+    ii = torch.as_tensor(idx, device=DEV)
+    href = x["h0"].index_select(1, ii).double().cpu().numpy()
+    b = x.get("delta_bias")
+    for t in range(w.steps):
+        y = gpu.state_update(h, x["x"][t], x["delta"][t], x["A"], x["B"][t], x["C"][t],
+                             D=x["D"], z_t=x["z"][t], delta_bias=b, softplus=w.softplus)
+        torch.cuda.synchronize()
+        yr, href = oracle.step(href, x["x"][t].index_select(1, ii), x["delta"][t].index_select(1, ii),
+                               x["A"].index_select(0, ii), x["B"][t], x["C"][t],
+                               D=x["D"].index_select(0, ii), z=x["z"][t].index_select(1, ii),
+                               delta_bias=b.index_select(0, ii) if b is not None else None,
+                               softplus=w.softplus)
+        assert_within(y.index_select(1, ii), yr, "bf16", f"y step {t}")
+        assert_within(h.index_select(1, ii), href, "f32", f"h step {t}")
