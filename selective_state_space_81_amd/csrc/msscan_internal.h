@@ -122,7 +122,11 @@ struct CarryArgs {
     int N;
     int Dn;
 };
-constexpr int kCarryGroup = 8;  // slots whose loads one carry thread issues together
+// slots whose loads one carry thread issues together: 8, or 32 for chains of
+// at least kCarryLongChain slots
+constexpr int kCarryGroup = 8;
+constexpr int kCarryGroupLong = 32;
+constexpr int kCarryLongChain = 1024;
 hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s);
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);  // the forward summaries of a
 bool tile_variant_exists(int ns, int waves);

@@ -30,11 +30,16 @@ using namespace dev;
 //
 // The kernel streams the summaries once in and once out (at the 130M layer's
 // backward about 200 MB per call) and is bound by HBM bandwidth.  Loads of a
-// group of slots are issued before its updates, so the chain waits on memory
-// once per group, not once per slot.  A two-level form (waves of one
-// workgroup folding runs of slots, then one barrier) and 16-byte accesses
-// over four channels per thread both measured slower.
-template <bool REV>
+// group of G slots are issued before its updates, so the chain waits on
+// memory once per group, not once per slot.  With few (b, n, d) threads and
+// long chains (the d_state 17-128 backward: 16-step segments, one 16-state
+// slice of 1536 channels at a time) the loads in flight bound the rate, and
+// G = 32 instead of 8 took the L 65536 backward's carries from 5.7 to 4.3 ms
+// per call; for chains of a few hundred slots it measured no better.  A
+// two-level form (waves of one workgroup folding runs of slots, then one
+// barrier) and 16-byte accesses over four channels per thread both measured
+// slower.
+template <bool REV, int G>
 __global__ void __launch_bounds__(256) carry_chain(CarryArgs c) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = (int64_t)c.batch * c.N * c.Dn;
@@ -47,10 +52,10 @@ __global__ void __launch_bounds__(256) carry_chain(CarryArgs c) {
     float h = c.init ? c.init[((int64_t)b * c.Dn + d) * c.N + n] : 0.f;
     if (c.start0) c.start0[((int64_t)b * c.Dn + d) * c.N + n] = h;
     const int km1 = c.km1;
-    for (int i0 = 0; i0 < km1; i0 += kCarryGroup) {
-        float dv[kCarryGroup], gv[kCarryGroup];
+    for (int i0 = 0; i0 < km1; i0 += G) {
+        float dv[G], gv[G];
 #pragma unroll
-        for (int j = 0; j < kCarryGroup; ++j) {
+        for (int j = 0; j < G; ++j) {
             dv[j] = 0.f;
             gv[j] = 0.f;
             const int i = i0 + j;
@@ -61,7 +66,7 @@ __global__ void __launch_bounds__(256) carry_chain(CarryArgs c) {
             }
         }
 #pragma unroll
-        for (int j = 0; j < kCarryGroup; ++j) {
+        for (int j = 0; j < G; ++j) {
             const int i = i0 + j;
             if (i < km1) {
                 const int64_t base = (int64_t)b * km1 + (REV ? km1 - 1 - i : i);
@@ -80,10 +85,18 @@ hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s) {
     const int64_t total = (int64_t)c.batch * c.N * c.Dn;
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
     ProfScope ps(s, kPhaseCarry);
-    if (reverse)
-        hipLaunchKernelGGL(carry_chain<true>, grid, block, 0, s, c);
-    else
-        hipLaunchKernelGGL(carry_chain<false>, grid, block, 0, s, c);
+    const bool lng = c.km1 >= kCarryLongChain;
+    if (reverse) {
+        if (lng)
+            hipLaunchKernelGGL((carry_chain<true, kCarryGroupLong>), grid, block, 0, s, c);
+        else
+            hipLaunchKernelGGL((carry_chain<true, kCarryGroup>), grid, block, 0, s, c);
+    } else {
+        if (lng)
+            hipLaunchKernelGGL((carry_chain<false, kCarryGroupLong>), grid, block, 0, s, c);
+        else
+            hipLaunchKernelGGL((carry_chain<false, kCarryGroup>), grid, block, 0, s, c);
+    }
     return hipGetLastError();
 }
 
