@@ -122,11 +122,8 @@ struct CarryArgs {
     int N;
     int Dn;
 };
-// slots whose loads one carry thread issues together: 8, or 32 for chains of
-// at least kCarryLongChain slots
-constexpr int kCarryGroup = 8;
-constexpr int kCarryGroupLong = 32;
-constexpr int kCarryLongChain = 1024;
+constexpr int kCarryGroup = 8;         // slots whose loads one carry thread issues together
+constexpr int kCarryLongChain = 1024;  // chains this long are split over several waves
 hipError_t launch_carry(const CarryArgs& c, bool reverse, hipStream_t s);
 hipError_t launch_carry(const ScanArgs& a, hipStream_t s);  // the forward summaries of a
 bool tile_variant_exists(int ns, int waves);

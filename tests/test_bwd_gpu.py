@@ -333,3 +333,24 @@ def test_bwd_past_2_31_elements_sampled(gpu):
     _check(part["dC"], ref["dC"], "f32", "dC")
     del x, part
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("disc", DISCS)
+def test_bwd_long_chain_of_segments(gpu, disc):
+    """A segment-layout backward with 1100 16-step segments (L = 17605, a
+    ragged last segment): its two carries take the split form for chains of
+    1024 or more segments (runs of slots folded per wave, then re-walked from
+    their composed starts), forward with h0 and in reverse with dh_last, and
+    with the bilinear form's products of A_bar.  Every gradient of every
+    channel against the oracle, and bitwise equal on a second call."""
+    x = _inputs(1, 16 * 1100 + 5, 64, 16, "f32", seed=44)
+    _compare(gpu, x, "f32", disc)
+    kw = disc_kw(disc)
+    args = (x["u"], x["delta"], x["A"], x["B"], x["C"], x["dy"])
+    opt = dict(D=x["D"], z=x["z"], delta_bias=x["delta_bias"], h0=x["h0"],
+               dh_last=x["dh_last"], **kw)
+    g1, g2 = gpu.scan_bwd(*args, **opt), gpu.scan_bwd(*args, **opt)
+    torch.cuda.synchronize()
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
