@@ -673,12 +673,18 @@ def _csv(dirname, suffix):
 
 def _short(name):
     m = re.search(r"(scan_row<[^>]*>|scan_lane<[^>]*>|scan_tile<[^>]*>|"
-                  r"bc_prepare<[^>]*>|carry_chain<[^>]*>|step_quads<[^>]*>|conv1d_kernel<[^>]*>|"
+                  r"bc_prepare<[^>]*>|carry_chain<[^>]*>|carry_parts<[^>]*>?|step_quads<[^>]*>|"
+                  r"conv1d_kernel<[^>]*>|"
                   r"bwd_main<[^>]*>|bwd_row<[^>]*>|seg_summaries<[^>]*>|reduce_bc4_params|reduce_bc4|reduce_bc|"
                   r"wide_\w+(?:<[^>]*>)?|"
                   r"reduce_param_groups|reduce_params|"
                   r"neg_kernel)", name)
-    return m.group(1) if m else name[:60]
+    if not m:
+        return name[:60]
+    k = m.group(1)
+    # a name cut at 60 characters before it reached the profiler's csv can
+    # lack the template's closing bracket
+    return k + ">" if k.startswith("carry_parts<") and not k.endswith(">") else k
 
 
 def _pmc_per_dispatch(dirname, counter):
