@@ -185,14 +185,19 @@ def test_split_resume_matches_single_scan(gpu):
 # lanes read h0 before they write h_last; with several, the first segment
 # starts from the carry pass's copy of h0.  Cases: the full 3B layer (row
 # kernels, one segment), and segmented plans of the row, lane and tile kernels.
+# The last two cut the sequence into 2049 segments of 64 steps (one wave per
+# segment), so their carries take the split form for chains of 1024 or more
+# segments, with h0 as the initial state (the bilinear one with products of
+# A_bar as decays).
 ALIAS = [("m3b", None, "euler"), ("tiny", (1, 6000, 40, 16), "zoh"),
          ("tiny", (2, 3000, 64, 32), "euler"), ("tiny", (1, 3000, 64, 64), "zoh"),
-         ("tiny", (1, 4000, 64, 8), "bilinear"), ("tiny", (1, 300, 2048, 128), "bilinear")]
+         ("tiny", (1, 4000, 64, 8), "bilinear"), ("tiny", (1, 300, 2048, 128), "bilinear"),
+         ("tiny", (1, 131077, 64, 8), "euler"), ("tiny", (1, 131077, 64, 8), "bilinear")]
 
 
 @pytest.mark.parametrize("name,shape,disc", ALIAS,
                          ids=["m3b", "rows-seg", "lane32-seg", "tile64-seg", "lane8-seg",
-                              "rows128"])
+                              "rows128", "lane8-long-chain", "lane8-long-chain-bil"])
 def test_h0_aliases_h_last(gpu, name, shape, disc):
     if shape is None:
         w = synth.workload(name)
