@@ -566,7 +566,8 @@ bool ckpt_plan(const ms_dims& d, uint32_t flags, BwdPlan* q, msscan::Plan* p) {
 hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, float* ws,
                           const void* dy, const float* dh_last, void* du, void* ddelta, void* dz,
                           float* dA, float* dB, float* dC, float* dD, float* dbias, float* dh0,
-                          bool bf16, hipStream_t hs, const float* ckpt = nullptr) {
+                          bool bf16, hipStream_t hs, const float* ckpt = nullptr,
+                          float* ypart = nullptr, bool ypart_add = false) {
     f.chunk_len = q.fwd.chunk_len;
     f.chunks = q.fwd.chunks;
     if (q.rows) {
@@ -611,6 +612,8 @@ hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, 
     L.dh0 = dh0; L.dA = dA; L.dB = dB; L.dC = dC; L.dD = f.D ? dD : nullptr; L.dbias = dbias;
     L.bf16 = bf16;
     L.disc = disc_of(flags);
+    L.ypart = ypart;  // the row layout above has no such output: callers check
+    L.ypart_add = ypart_add ? 1 : 0;
     // Segment summaries (forward and adjoint), both carries, the per-segment
     // gradients and the fixed-order sums.
     return msscan::launch_scan_bwd(L, hs);
@@ -619,7 +622,7 @@ hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, 
 // Backward for d_state 17..128: slices of 16 states (bwd_wide.hip).  The
 // workspace holds, in order (fp32, each region padded to 64 floats):
 //   g, u32, d32 (bf16 io), B32, C32 (bf16 io), y_pre, the fp32 forward's own
-//   workspace, the slice inputs (A_s, B_s, C_s, h0_s, dh_last_s), the slice
+//   workspace (row-layout slices only), the slice inputs (A_s, B_s, C_s, h0_s, dh_last_s), the slice
 //   outputs (du_s, ddelta_s, dA_s, dB_s, dC_s, dbias_s, dh0_s), the totals
 //   (du, ddelta, dbias), the dD partials, and the 16-state backward's workspace.
 struct WideLayout {
@@ -655,7 +658,8 @@ WideLayout wide_layout(const ms_dims& d, uint32_t flags) {
     n[kWB32] = bf16 ? BL * (size_t)d.d_state : 0;
     n[kWC32] = n[kWB32];
     n[kWy32] = E;
-    n[kWfws] = (ws_bytes(w.fwd, w.dfwd, flags) + 3) / 4;
+    // the forward that forms y_pre runs only for row-layout slices
+    n[kWfws] = w.inner.rows ? (ws_bytes(w.fwd, w.dfwd, flags) + 3) / 4 : 0;
     n[kWAs] = Dn * S;
     n[kWBs] = n[kWCs] = BL * S;
     n[kWh0s] = n[kWdhls] = BD * S;
@@ -749,8 +753,14 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
         return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     const float* u32 = bf16 ? w.u32 : static_cast<const float*>(u);
     const float* d32 = bf16 ? w.d32 : static_cast<const float*>(delta);
-    // y_pre = sum_n C h + D u in fp32, for dz: the forward scan without the gate.
-    if (z) {
+    // y_pre = sum_n C h + D u in fp32, for dz.  With the segment layout for
+    // the slices, each slice's gradient pass adds its states' sum_n C h to
+    // y32 from the states it recomputes anyway (in slice order, so the sum
+    // is deterministic) and the combine adds D u; the row layout has no such
+    // output, and there the forward scan without the gate forms y_pre.
+    const bool fuse_ypre = z && !wl.inner.rows;
+    w.y32_add_du = fuse_ypre ? 1 : 0;
+    if (z && !fuse_ypre) {
         msscan::ScanArgs fa = a;
         fa.u = u32; fa.delta = d32; fa.z = nullptr; fa.y = w.y32; fa.h_last = nullptr;
         fa.B = bf16 ? w.B32 : B; fa.C = bf16 ? w.C32 : C;
@@ -773,7 +783,8 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
         sa.u = u32; sa.delta = d32; sa.A = w.As; sa.B = w.Bs; sa.C = w.Cs; sa.D = nullptr;
         sa.z = nullptr; sa.h0 = w.h0s; sa.N = msscan::kWideSlice;
         e = run_bwd_narrow(sa, wl.inner, flags, R(kWinner), w.g, w.dhls, w.du_s, w.dv_s, nullptr,
-                           w.dAs, w.dBs, w.dCs, nullptr, w.dbias_s, w.dh0s, false, hs);
+                           w.dAs, w.dBs, w.dCs, nullptr, w.dbias_s, w.dh0s, false, hs, nullptr,
+                           fuse_ypre ? w.y32 : nullptr, n0 > 0);
         if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
         if ((e = msscan::launch_wide_accumulate(w, n0, hs)) != hipSuccess)
             return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

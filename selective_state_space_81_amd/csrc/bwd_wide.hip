@@ -11,7 +11,10 @@
 //   du     = sum_s du_s + g * D
 //   ddelta = sum_s ddelta_s          (each already through the softplus)
 //   dz     = dy * y_pre * sigma(z) * (1 + z (1 - sigma(z))),
-//            y_pre = sum_n C h + D u from an fp32 forward pass
+//            y_pre = sum_n C h + D u: each slice's gradient pass adds its
+//            states' sum_n C h from the states it recomputes (segment
+//            layout; the combine adds D u), or, for row-layout slices, an
+//            fp32 forward pass forms it
 //   dD     = sum over batch and time of g * u
 // while dA, dB, dC and dh0 are the slices' own, and dbias the slices' sum.
 // The slices are added in order, so the result is deterministic.
@@ -42,7 +45,8 @@ __global__ void __launch_bounds__(256) wide_prep(WideArgs w) {
     }
 }
 
-// fp32 copies of B and C (bf16 io), for the fp32 forward pass.
+// fp32 copies of B and C (bf16 io), for the fp32 forward pass (row-layout
+// slices).
 __global__ void __launch_bounds__(256) wide_bc32(WideArgs w) {
     const int64_t n = w.BLN;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -126,7 +130,9 @@ __global__ void __launch_bounds__(256) wide_combine(WideArgs w) {
         if (w.z) {
             const float zv = ld<BF16>(w.z, e);
             const float sg = sigmoid_f(zv);
-            st<BF16>(w.dz, e, ld<BF16>(w.dy, e) * w.y32[e] * sg * fmaf(zv, 1.f - sg, 1.f));
+            float ypre = w.y32[e];
+            if (w.y32_add_du && w.D) ypre = fmaf(w.D[d], ld<BF16>(w.u, e), ypre);
+            st<BF16>(w.dz, e, ld<BF16>(w.dy, e) * ypre * sg * fmaf(zv, 1.f - sg, 1.f));
         }
     }
 }

@@ -185,6 +185,10 @@ struct BwdLaunch {
     float* pgroup;  // [kParamGroups][Dn][N+2]: first-level sums of pparam
     bool bf16;
     int disc;
+    // fp32 [batch][L][Dn] or null: receives sum_n C h + D u of every element
+    // (ypart_add: added to what it holds), from the gradient pass's recompute
+    float* ypart = nullptr;
+    int ypart_add = 0;
 };
 int bwd_segment_len();
 constexpr int kParamGroups = 16;  // first-level groups of the parameter sums
@@ -245,6 +249,7 @@ struct WideArgs {
     int Dn, N;
     // workspace (fp32)
     float *g, *u32, *d32, *B32, *C32, *y32;
+    int y32_add_du;  // y32 holds sum_n C h only: the combine adds D u
     float *As, *Bs, *Cs, *h0s, *dhls;
     float *du_s, *dv_s, *dAs, *dBs, *dCs, *dbias_s, *dh0s;
     float *du_acc, *dv_acc, *dbias_acc, *dD_part;

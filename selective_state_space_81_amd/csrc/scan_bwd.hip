@@ -111,6 +111,8 @@ struct BwdArgs {
     float* pbc;          // [tiles][batch][L][2N]: per-tile partial dB | dC
     float* pparam;       // [batch][ceil(K/kBwdWaves)][Dn][N+2]: partial dA | dD | dbias per group
     float* pgroup;       // [kParamGroups][Dn][N+2]: first-level sums of pparam
+    float* ypart;        // [batch][L][Dn] fp32 or null: y_pre of each element, stored
+    int ypart_add;       //   or (ypart_add) added to what the buffer holds
 };
 
 template <bool BF16>
@@ -524,6 +526,15 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 2) bwd_main(BwdArgs a) {
         if (tb >= t1) return;
         Rows r;
         load_rows(r, tb, true);
+        // y_pre accumulated so far for these steps: loaded before the
+        // recompute, so that the loads are in flight while it runs
+        float yprev[kSub];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            yprev[j] = 0.f;
+            if (a.ypart && a.ypart_add && wvalid && tb + j < t1)
+                yprev[j] = a.ypart[(row0 + tb + j) * f.Dn + dd];
+        }
         float hs[kSub][NS];  // hs[j] = state after step tb + j
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
@@ -544,6 +555,7 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 2) bwd_main(BwdArgs a) {
             const float dyv = r.dy[j];
             // y_pre from the recomputed state, for the gate's derivative
             const float ypre = dpp_dot<NS>(Dd * uv, cl, hs[j]);
+            if (a.ypart && wvalid) a.ypart[e] = yprev[j] + ypre;
             float g = dyv;
             if constexpr (kMasks) {
                 const float zv = r.z[j];  // 0 when there is no gate
@@ -995,6 +1007,8 @@ hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s) {
     a.pbc = L.pbc;
     a.pparam = L.pparam;
     a.pgroup = L.pgroup;
+    a.ypart = L.ypart;
+    a.ypart_add = L.ypart_add;
     switch (L.disc) {
 #define MS_BWD_(DI)                                                                     \
     case DI:                                                                            \

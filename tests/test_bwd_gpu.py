@@ -207,6 +207,7 @@ WIDE = [
     (1, 50, 16, 100, "bf16"),  # 7 slices, the last with 4 states
     (1, 20, 8, 128, "f32"),
     (1, 1, 64, 48, "f32"),     # a single timestep
+    (1, 40, 8192, 32, "bf16"), # 512 16-channel tiles: row-layout slices, y_pre from a forward
 ]
 
 
