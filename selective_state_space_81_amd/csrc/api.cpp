@@ -782,9 +782,12 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
         msscan::ScanArgs sa = a;
         sa.u = u32; sa.delta = d32; sa.A = w.As; sa.B = w.Bs; sa.C = w.Cs; sa.D = nullptr;
         sa.z = nullptr; sa.h0 = w.h0s; sa.N = msscan::kWideSlice;
-        e = run_bwd_narrow(sa, wl.inner, flags, R(kWinner), w.g, w.dhls, w.du_s, w.dv_s, nullptr,
+        // the first slice's du and ddelta go straight into the totals
+        const bool first = n0 == 0;
+        e = run_bwd_narrow(sa, wl.inner, flags, R(kWinner), w.g, w.dhls,
+                           first ? w.du_acc : w.du_s, first ? w.dv_acc : w.dv_s, nullptr,
                            w.dAs, w.dBs, w.dCs, nullptr, w.dbias_s, w.dh0s, false, hs, nullptr,
-                           fuse_ypre ? w.y32 : nullptr, n0 > 0);
+                           fuse_ypre ? w.y32 : nullptr, !first);
         if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
         if ((e = msscan::launch_wide_accumulate(w, n0, hs)) != hipSuccess)
             return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));

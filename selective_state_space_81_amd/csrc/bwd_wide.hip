@@ -85,15 +85,18 @@ __global__ void __launch_bounds__(256) wide_gather(WideArgs w, int n0) {
 }
 
 // Slice n0's results into the totals: du / ddelta partials and dbias added
-// (first slice: copied), dA, dB, dC and dh0 scattered to their states.
+// (the first slice writes its du / ddelta straight into the totals, and its
+// dbias is copied), dA, dB, dC and dh0 scattered to their states.
 __global__ void __launch_bounds__(256) wide_accumulate(WideArgs w, int n0) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool first = n0 == 0;
     const int N = w.N;
-    for (int64_t e = i0; e < w.E; e += stride) {
-        w.du_acc[e] = first ? w.du_s[e] : w.du_acc[e] + w.du_s[e];
-        w.dv_acc[e] = first ? w.dv_s[e] : w.dv_acc[e] + w.dv_s[e];
+    if (!first) {
+        for (int64_t e = i0; e < w.E; e += stride) {
+            w.du_acc[e] += w.du_s[e];
+            w.dv_acc[e] += w.dv_s[e];
+        }
     }
     for (int64_t i = i0; i < w.BL * kWideSlice; i += stride) {
         const int j = (int)(i % kWideSlice);
