@@ -567,7 +567,7 @@ hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, 
                           const void* dy, const float* dh_last, void* du, void* ddelta, void* dz,
                           float* dA, float* dB, float* dC, float* dD, float* dbias, float* dh0,
                           bool bf16, hipStream_t hs, const float* ckpt = nullptr,
-                          float* ypart = nullptr, bool ypart_add = false) {
+                          float* ypart = nullptr, bool ypart_add = false, bool out_add = false) {
     f.chunk_len = q.fwd.chunk_len;
     f.chunks = q.fwd.chunks;
     if (q.rows) {
@@ -614,6 +614,7 @@ hipError_t run_bwd_narrow(msscan::ScanArgs f, const BwdPlan& q, uint32_t flags, 
     L.disc = disc_of(flags);
     L.ypart = ypart;  // the row layout above has no such output: callers check
     L.ypart_add = ypart_add ? 1 : 0;
+    L.out_add = (out_add && !bf16) ? 1 : 0;
     // Segment summaries (forward and adjoint), both carries, the per-segment
     // gradients and the fixed-order sums.
     return msscan::launch_scan_bwd(L, hs);
@@ -782,14 +783,17 @@ ms_status ms_scan_bwd(const void* u, const void* delta, const float* A, const vo
         msscan::ScanArgs sa = a;
         sa.u = u32; sa.delta = d32; sa.A = w.As; sa.B = w.Bs; sa.C = w.Cs; sa.D = nullptr;
         sa.z = nullptr; sa.h0 = w.h0s; sa.N = msscan::kWideSlice;
-        // the first slice's du and ddelta go straight into the totals
+        // du and ddelta go straight into the totals: written by the first
+        // slice, added by the later ones' gradient passes (segment layout;
+        // row-layout slices write their own and the accumulate adds them)
         const bool first = n0 == 0;
+        const bool inplace = first || !wl.inner.rows;
         e = run_bwd_narrow(sa, wl.inner, flags, R(kWinner), w.g, w.dhls,
-                           first ? w.du_acc : w.du_s, first ? w.dv_acc : w.dv_s, nullptr,
+                           inplace ? w.du_acc : w.du_s, inplace ? w.dv_acc : w.dv_s, nullptr,
                            w.dAs, w.dBs, w.dCs, nullptr, w.dbias_s, w.dh0s, false, hs, nullptr,
-                           fuse_ypre ? w.y32 : nullptr, !first);
+                           fuse_ypre ? w.y32 : nullptr, !first, !first && inplace);
         if (e != hipSuccess) return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-        if ((e = msscan::launch_wide_accumulate(w, n0, hs)) != hipSuccess)
+        if ((e = msscan::launch_wide_accumulate(w, n0, !inplace, hs)) != hipSuccess)
             return fail(MS_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     }
     if ((e = msscan::launch_wide_finish(w, bf16, hs)) != hipSuccess)

@@ -84,15 +84,16 @@ __global__ void __launch_bounds__(256) wide_gather(WideArgs w, int n0) {
     }
 }
 
-// Slice n0's results into the totals: du / ddelta partials and dbias added
-// (the first slice writes its du / ddelta straight into the totals, and its
-// dbias is copied), dA, dB, dC and dh0 scattered to their states.
-__global__ void __launch_bounds__(256) wide_accumulate(WideArgs w, int n0) {
+// Slice n0's results into the totals: du / ddelta partials added when the
+// slice wrote them apart (add_du; otherwise its gradient pass wrote or added
+// them into the totals itself), dbias added (first slice: copied), dA, dB,
+// dC and dh0 scattered to their states.
+__global__ void __launch_bounds__(256) wide_accumulate(WideArgs w, int n0, int add_du) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool first = n0 == 0;
     const int N = w.N;
-    if (!first) {
+    if (add_du) {
         for (int64_t e = i0; e < w.E; e += stride) {
             w.du_acc[e] += w.du_s[e];
             w.dv_acc[e] += w.dv_s[e];
@@ -201,9 +202,10 @@ hipError_t launch_wide_gather(const WideArgs& w, int n0, bool bf16, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_wide_accumulate(const WideArgs& w, int n0, hipStream_t s) {
+hipError_t launch_wide_accumulate(const WideArgs& w, int n0, bool add_du, hipStream_t s) {
     ProfScope ps(s, kPhaseReduce);
-    hipLaunchKernelGGL(wide_accumulate, dim3(grid_of(w.E)), dim3(256), 0, s, w, n0);
+    const int64_t n = add_du ? w.E : max(w.BL, w.BD) * kWideSlice;
+    hipLaunchKernelGGL(wide_accumulate, dim3(grid_of(n)), dim3(256), 0, s, w, n0, add_du ? 1 : 0);
     return hipGetLastError();
 }
 

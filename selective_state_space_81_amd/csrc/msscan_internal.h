@@ -189,6 +189,8 @@ struct BwdLaunch {
     // (ypart_add: added to what it holds), from the gradient pass's recompute
     float* ypart = nullptr;
     int ypart_add = 0;
+    // fp32 io only: du and ddelta are added to what their buffers hold
+    int out_add = 0;
 };
 int bwd_segment_len();
 constexpr int kParamGroups = 16;  // first-level groups of the parameter sums
@@ -259,7 +261,7 @@ struct WideArgs {
 };
 hipError_t launch_wide_prep(const WideArgs& w, bool bf16, hipStream_t s);
 hipError_t launch_wide_gather(const WideArgs& w, int n0, bool bf16, hipStream_t s);
-hipError_t launch_wide_accumulate(const WideArgs& w, int n0, hipStream_t s);
+hipError_t launch_wide_accumulate(const WideArgs& w, int n0, bool add_du, hipStream_t s);
 hipError_t launch_wide_finish(const WideArgs& w, bool bf16, hipStream_t s);
 
 // Kernel timing hooks (profile.cpp).  prof_call starts a new timed call;

@@ -113,6 +113,7 @@ struct BwdArgs {
     float* pgroup;       // [kParamGroups][Dn][N+2]: first-level sums of pparam
     float* ypart;        // [batch][L][Dn] fp32 or null: y_pre of each element, stored
     int ypart_add;       //   or (ypart_add) added to what the buffer holds
+    int out_add;         // fp32 io: du and ddelta added to what their buffers hold
 };
 
 template <bool BF16>
@@ -528,12 +529,19 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 2) bwd_main(BwdArgs a) {
         load_rows(r, tb, true);
         // y_pre accumulated so far for these steps: loaded before the
         // recompute, so that the loads are in flight while it runs
-        float yprev[kSub];
+        // (and, with out_add, the du and ddelta totals the results add to)
+        float yprev[kSub], duprev[kSub], dvprev[kSub];
 #pragma unroll
         for (int j = 0; j < kSub; ++j) {
-            yprev[j] = 0.f;
-            if (a.ypart && a.ypart_add && wvalid && tb + j < t1)
-                yprev[j] = a.ypart[(row0 + tb + j) * f.Dn + dd];
+            yprev[j] = duprev[j] = dvprev[j] = 0.f;
+            const int64_t ej = (row0 + tb + j) * f.Dn + dd;
+            if (a.ypart && a.ypart_add && wvalid && tb + j < t1) yprev[j] = a.ypart[ej];
+            if constexpr (!BF16) {
+                if (a.out_add && wvalid && tb + j < t1) {
+                    duprev[j] = static_cast<const float*>(a.du)[ej];
+                    dvprev[j] = static_cast<const float*>(a.ddelta)[ej];
+                }
+            }
         }
         float hs[kSub][NS];  // hs[j] = state after step tb + j
 #pragma unroll
@@ -679,8 +687,8 @@ __global__ void __launch_bounds__(64 * kBwdWaves, 2) bwd_main(BwdArgs a) {
                 Io<true>::store(rDu, ooff + (uint32_t)(t - t0) * orowb, du);
                 Io<true>::store(rDdl, ooff + (uint32_t)(t - t0) * orowb, dv);
             } else if (wvalid) {
-                st<BF16>(a.du, e, du);
-                st<BF16>(a.ddelta, e, dv);
+                st<BF16>(a.du, e, du + duprev[j]);
+                st<BF16>(a.ddelta, e, dv + dvprev[j]);
             }
             // Sum the 2N contributions of this step over the wave's channels:
             // lane l adds half (l & 1) of row l >> 1, the pair is combined
@@ -1009,6 +1017,7 @@ hipError_t launch_scan_bwd(const BwdLaunch& L, hipStream_t s) {
     a.pgroup = L.pgroup;
     a.ypart = L.ypart;
     a.ypart_add = L.ypart_add;
+    a.out_add = L.out_add;
     switch (L.disc) {
 #define MS_BWD_(DI)                                                                     \
     case DI:                                                                            \
